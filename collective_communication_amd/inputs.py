@@ -1,0 +1,88 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the oracle checks.
+
+This module holds no arithmetic of the method (no reduction, no codec, no
+bf16 rounding rule of its own): it draws numbers with numpy and converts fp32
+to bf16 with PyTorch's CPU conversion (round to nearest even), and nothing
+else.  The same host bytes feed both the GPU path and the oracle.
+
+Workloads (tensor shapes of gradients, weights and activations as the pages
+describe them; the pages' nccl-tests sweeps span 2 MB to 1 GB per message):
+
+* ``ring_f32``   -- R=4 ranks x 2^20 fp32, N(0, 1)
+* ``ring_bf16``  -- R=8 ranks x 2^26 bf16, N(0, 1e-3), 1% of entries zero
+* ``codec``      -- 2^28 bf16 each: weights N(0, 0.02); activations a 50/50
+  per-element mixture of N(0, 1) and Laplace(0, 4); gradients N(0, 1e-4)
+* ``compressed`` -- R=8 ranks x 2^25 bf16, N(0, 1e-3)
+* ``contention`` -- R=8 ranks x 2^28 bf16, N(0, 1e-3)
+
+N(mu, s) names the standard deviation s.  Seeds are
+``SeedSequence([20261202, workload_id, index])``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+ROOT_SEED = 20261202
+
+WORKLOAD_IDS = {"ring_f32": 1, "ring_bf16": 2, "codec": 3, "compressed": 4, "contention": 5,
+                "test": 99}
+
+
+def rng_for(workload: str | int, index: int) -> np.random.Generator:
+    wid = WORKLOAD_IDS[workload] if isinstance(workload, str) else int(workload)
+    return np.random.default_rng(np.random.SeedSequence([ROOT_SEED, wid, int(index)]))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16) by PyTorch's CPU conversion (nearest even)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def normal_f32(workload, index: int, n: int, sigma: float = 1.0) -> np.ndarray:
+    g = rng_for(workload, index)
+    x = g.standard_normal(n, dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    return x
+
+
+def normal_bf16(workload, index: int, n: int, sigma: float, zero_frac: float = 0.0) -> np.ndarray:
+    g = rng_for(workload, index)
+    x = g.standard_normal(n, dtype=np.float32)
+    x *= np.float32(sigma)
+    if zero_frac > 0.0:
+        x[g.random(n, dtype=np.float32) < zero_frac] = 0.0
+    return f32_to_bf16_bits(x)
+
+
+def activation_bf16(workload, index: int, n: int) -> np.ndarray:
+    """Per-element 50/50 mixture of N(0, 1) and Laplace(0, scale 4)."""
+    g = rng_for(workload, index)
+    pick = g.random(n, dtype=np.float32) < 0.5
+    x = g.standard_normal(n, dtype=np.float32)
+    lap = g.laplace(0.0, 4.0, n).astype(np.float32)
+    x[pick] = lap[pick]
+    return f32_to_bf16_bits(x)
+
+
+def ring_inputs(workload: str, R: int, n: int):
+    """Per-rank inputs of a ring workload (list of R arrays)."""
+    if workload == "ring_f32":
+        return [normal_f32(workload, r, n, 1.0) for r in range(R)]
+    if workload == "ring_bf16":
+        return [normal_bf16(workload, r, n, 1e-3, zero_frac=0.01) for r in range(R)]
+    if workload in ("compressed", "contention"):
+        return [normal_bf16(workload, r, n, 1e-3) for r in range(R)]
+    raise KeyError(workload)
+
+
+def codec_inputs(n: int):
+    """The three codec tensors: weights, activations, gradients (bf16 bits)."""
+    return {
+        "weights": normal_bf16("codec", 0, n, 0.02),
+        "activations": activation_bf16("codec", 1, n),
+        "gradients": normal_bf16("codec", 2, n, 1e-4),
+    }
