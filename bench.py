@@ -1,0 +1,383 @@
+#!/usr/bin/env python3
+"""Benchmark of the emulated ring AllReduce data path on one MI355X.
+
+Default workload (the one the printed JSON line is about): ring AllReduce
+(sum) over R=8 emulated ranks of 2^26 bf16 elements each, N(0, 1e-3) with 1%
+exact zeros, fp32 accumulation per hop with bf16 nearest-even output, chunk
+~1% of the buffer, reduce-scatter then all-gather.  One "step" is one whole
+allreduce (14 ring steps) over inputs already resident in HBM.
+
+Other workloads (--workload): ring_f32 (R=4 x 2^20 fp32), codec (2^28 bf16
+compress/decompress of weights, activations, gradients), compressed (the
+fused compressed ring, R=8 x 2^25 bf16), contention (R=8 reduce-scatter of
+2^28 bf16 on a CU-budget stream next to a bf16 8192^3 GEMM).  Each prints one
+JSON line of its own.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+The per-kernel figures come from HIP events that the library records at
+ring-step boundaries on the launch stream (hc_opts_t.step_events).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0       # dense bf16 MFMA, published
+N_CU = 256
+
+METRIC = "AllReduce algbw GB/s and achieved HBM GB/s (% of peak), R=8, 1 MI355X"
+
+
+def kernel_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str, files):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, when
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = data.get(f"{kernel}:{workload}")
+    if not rec or rec.get("source_hash") != kernel_hash(files):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def median(xs):
+    s = sorted(xs)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def cpu_baseline_ring(R: int, n_sample: int):
+    """The oracle's ring step simulator, as it stands, on a bounded sample of
+    the same workload (first n_sample elements of every rank), one thread."""
+    import oracle
+    from collective_communication_amd import inputs
+
+    xs = [inputs.host_bits(t) for t in inputs.ring_inputs_cuda("ring_bf16", R, n_sample)]
+    t0 = time.perf_counter()
+    oracle.allreduce_ring(xs)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_sample * 2 / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"R={R} ranks x {n_sample} bf16 elements (same recipe), ring step simulator, "
+                      f"{dt:.2f} s"}
+
+
+def bench_ring(args, workload: str):
+    import torch
+
+    from collective_communication_amd import binding as hc
+    from collective_communication_amd import inputs
+
+    if workload == "ring_bf16":
+        R, n, es, dtype = 8, 1 << 26, 2, "bf16"
+    else:
+        R, n, es, dtype = 4, 1 << 20, 4, "f32"
+    send = inputs.ring_inputs_cuda(workload, R, n)
+    recv = [torch.empty_like(s) for s in send]
+    steps = hc.hc_step_count(hc.HC_OP_ALLREDUCE, R)
+    for _ in range(args.warmup):
+        hc.hc_allreduce(send, recv)
+    torch.cuda.synchronize()
+    evsets = [hc.StepEvents([torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)])
+              for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        hc.hc_allreduce(send, recv, step_events=evsets[k])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms = total_ms / args.steps
+    red, cpy = [], []
+    for ev in evsets:
+        d = ev.elapsed_ms()
+        red += d[: R - 1]
+        cpy += d[R - 1:]
+    avg_red, avg_cpy = sum(red) / len(red), sum(cpy) / len(cpy)
+    L = n // R
+    rs_bytes = 3 * es * n * (R - 1)                    # per allreduce
+    ag_bytes = 2 * es * n * (R - 1)
+    alg_bytes = rs_bytes + ag_bytes
+    red_launch_bytes = 3 * es * n                        # one reduce step: R receivers x L elements
+    algbw = n * es / (ms / 1e3) / 1e9
+    hbm = alg_bytes / (ms / 1e3) / 1e9
+    achieved = red_launch_bytes / (avg_red / 1e3) / 1e9
+    files = ["collective_communication_amd/csrc/ring_kernels.hip", "collective_communication_amd/csrc/common.hpp"]
+    traffic = load_traffic("reduce_step", workload, files)
+    line = {
+        "metric": METRIC, "value": round(algbw, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {"workload": f"emulated ring allreduce (sum), R={R} ranks x {n} {dtype} per rank, "
+                               f"{'N(0,1e-3) with 1% zeros, fp32 add + bf16 RNE per hop' if dtype == 'bf16' else 'N(0,1), fp32 add per hop'}, "
+                               f"chunk ~1%, reduce-scatter then all-gather",
+                   "ranks": R, "elems_per_rank": n, "slice": L, "chunk": hc.hc_chunk_elems(n)},
+        "busbw_gbps": round(algbw * 2 * (R - 1) / R, 3),
+        "hbm_gbps": round(hbm, 2), "hbm_frac_of_peak": round(hbm / PEAK_HBM_GBPS, 4),
+        "alg_bytes_per_step": alg_bytes,
+        "reduce_launch_ms": round(avg_red, 6), "copy_launch_ms": round(avg_cpy, 6),
+        "copy_launch_gbps": round(2 * es * n / (avg_cpy / 1e3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "kernel": "step_kernel<reduce> (one reduce-scatter step)",
+                     "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "alg_bytes_per_launch": red_launch_bytes},
+    }
+    if not args.no_cpu_baseline and workload == "ring_bf16":
+        line["cpu_baseline"] = cpu_baseline_ring(R, args.cpu_sample)
+    return line
+
+
+def bench_codec(args):
+    import torch
+
+    from collective_communication_amd import binding as hc
+    from collective_communication_amd import inputs
+
+    n = 1 << 28
+    cap = hc.hc_compress_bound_bf16(n)
+    out = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    nbytes = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ws = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_COMPRESS, n, 1), dtype=torch.uint8, device="cuda")
+    back = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rows = {}
+    for name, maker in (("weights", lambda: inputs.normal_bf16_cuda("codec", 0, n, 0.02)),
+                        ("activations", lambda: inputs.activation_bf16_cuda("codec", 1, n)),
+                        ("gradients", lambda: inputs.normal_bf16_cuda("codec", 2, n, 1e-4))):
+        x = maker()
+        for _ in range(args.warmup):
+            hc.hc_compress_bf16(x, n, out, nbytes, ws)
+            hc.hc_decompress_bf16(out, cap, back, n, status)
+        torch.cuda.synchronize()
+        size = int(nbytes.item())
+        ok = int(status.item()) == 0 and torch.equal(back.view(torch.int16), x.view(torch.int16))
+        tc, td = [], []
+        for _ in range(args.steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            hc.hc_compress_bf16(x, n, out, nbytes, ws)
+            e[1].record()
+            hc.hc_decompress_bf16(out, cap, back, n, status)
+            e[2].record()
+            torch.cuda.synchronize()
+            tc.append(e[0].elapsed_time(e[1]))
+            td.append(e[1].elapsed_time(e[2]))
+        mc, md = median(tc), median(td)
+        raw = 2 * n
+        rows[name] = {"ratio": round(size / raw, 5), "compressed_bytes": size,
+                      "compress_ms": round(mc, 4), "decompress_ms": round(md, 4),
+                      "compress_raw_gbps": round(raw / mc / 1e6, 1), "decompress_raw_gbps": round(raw / md / 1e6, 1),
+                      "compress_hbm_gbps": round((raw + size) / mc / 1e6, 1),
+                      "decompress_hbm_gbps": round((raw + size) / md / 1e6, 1),
+                      "round_trip_exact": ok}
+        del x
+    worst = min(min(r["compress_hbm_gbps"], r["decompress_hbm_gbps"]) for r in rows.values())
+    return {"metric": "HCZ1 bf16 codec throughput (HBM GB/s, raw GB/s) and ratio, 2^28 elements",
+            "value": worst, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "standalone lossless bf16 codec, 2^28 elements per tensor"},
+            "tensors": rows, "hbm_frac_of_peak_worst": round(worst / PEAK_HBM_GBPS, 4)}
+
+
+def bench_compressed(args):
+    import torch
+
+    from collective_communication_amd import binding as hc
+    from collective_communication_amd import inputs
+
+    R, n = 8, 1 << 25
+    send = inputs.ring_inputs_cuda("compressed", R, n)
+    recv = [torch.empty_like(s) for s in send]
+    ws = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_COMPRESSED_ALLREDUCE, n, R), dtype=torch.uint8, device="cuda")
+    wire = torch.zeros(1, dtype=torch.int64, device="cuda")
+    steps = hc.hc_step_count(hc.HC_OP_COMPRESSED_ALLREDUCE, R)
+    for _ in range(args.warmup):
+        hc.hc_compressed_allreduce(send, recv, n, ws, wire)
+    torch.cuda.synchronize()
+    evsets = [hc.StepEvents([torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)])
+              for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for k in range(args.steps):
+        hc.hc_compressed_allreduce(send, recv, n, ws, wire, step_events=evsets[k])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    wire_bytes = int(wire.item())
+    chunk = hc.hc_chunk_elems(n, 0.01, hc.HC_BLOCK_ELEMS)
+    L = n // R
+    nchunks = -(-L // chunk)
+    framing = 0
+    for c in range(nchunks):
+        ln = min(chunk, L - c * chunk)
+        framing += 32 + 16 * (-(-8 * (-(-ln // hc.HC_BLOCK_ELEMS)) // 16))
+    framing *= R * 2 * (R - 1)
+    rec_bytes = wire_bytes - framing
+    alg = 4 * R * n + 2 * rec_bytes     # see the design doc: raw reads/writes + each record written and read once
+    parts = {"first": [], "rs": [], "ag": []}
+    for ev in evsets:
+        d = ev.elapsed_ms()
+        parts["first"].append(d[0])
+        parts["rs"] += d[1:R]
+        parts["ag"] += d[R:]
+    raw_wire = 2 * (R - 1) * n * 2
+    return {"metric": "Compressed ring AllReduce algbw and achieved HBM GB/s, R=8, 2^25 bf16",
+            "value": round(n * 2 / (ms / 1e3) / 1e9, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": f"fused compressed ring allreduce, R={R} x {n} bf16 N(0,1e-3), chunk {chunk}"},
+            "hbm_gbps": round(alg / (ms / 1e3) / 1e9, 1), "hbm_frac_of_peak": round(alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "alg_bytes": alg, "wire_bytes": wire_bytes, "wire_ratio": round(wire_bytes / raw_wire, 5),
+            "first_ms": round(sum(parts["first"]) / len(parts["first"]), 5),
+            "rs_step_ms": round(sum(parts["rs"]) / len(parts["rs"]), 5),
+            "ag_step_ms": round(sum(parts["ag"]) / len(parts["ag"]), 5)}
+
+
+def bench_contention(args):
+    import torch
+
+    from collective_communication_amd import binding as hc
+    from collective_communication_amd import inputs
+
+    R, n = 8, 1 << 28
+    L = n // R
+    send = inputs.ring_inputs_cuda("contention", R, n)
+    recv = [torch.empty(L, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    ws = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_REDUCE_SCATTER, n, R, hc.HC_BF16), dtype=torch.uint8,
+                     device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(inputs.seed64("contention", 100))
+    A = torch.randn(8192, 8192, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    Bm = torch.randn(8192, 8192, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    C = torch.empty(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    main = torch.cuda.current_stream()
+    rs_bytes = 3 * 2 * n * (R - 1)
+
+    def gemm_alone(iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main)
+        for _ in range(iters):
+            torch.matmul(A, Bm, out=C)
+        e1.record(main)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    for _ in range(3):
+        torch.matmul(A, Bm, out=C)
+    t_gemm = gemm_alone(10)
+    rows = []
+    for k in (8, 16, 32, 0):
+        handle = hc.hc_stream_create_cu_budget(k) if k else None
+        side = torch.cuda.ExternalStream(handle) if k else torch.cuda.Stream()
+        budget = k
+        # reduce-scatter alone on the side stream
+        for _ in range(2):
+            hc.hc_reduce_scatter(send, recv, L, ws, cu_budget=budget, stream=side)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(side)
+        hc.hc_reduce_scatter(send, recv, L, ws, cu_budget=budget, stream=side)
+        e1.record(side)
+        torch.cuda.synchronize()
+        t_rs_alone = e0.elapsed_time(e1)
+        # concurrent: the GEMM loop on the main stream for as long as the reduce runs
+        iters = max(4, int(t_rs_alone / t_gemm) + 2)
+        base = torch.cuda.Event(enable_timing=True)
+        ge = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        base.record(main)
+        side.wait_event(base)
+        r0.record(side)
+        hc.hc_reduce_scatter(send, recv, L, ws, cu_budget=budget, stream=side)
+        r1.record(side)
+        ge[0].record(main)
+        for i in range(iters):
+            torch.matmul(A, Bm, out=C)
+            ge[i + 1].record(main)
+        torch.cuda.synchronize()
+        gt = [base.elapsed_time(e) for e in ge]
+        rs_t0, rs_t1 = base.elapsed_time(r0), base.elapsed_time(r1)
+        overl = [gt[i + 1] - gt[i] for i in range(iters) if gt[i] < rs_t1 and gt[i + 1] > rs_t0]
+        t_gemm_conc = median(overl) if overl else float("nan")
+        cu_used = k if k else N_CU
+        # contention rate: share of CUs held by the reduce while the GEMM runs
+        comp = [(gt[i], gt[i + 1]) for i in range(iters)]
+        num = den = 0.0
+        for a, b in comp:
+            lo, hi = max(a, rs_t0), min(b, rs_t1)
+            den += b - a
+            if hi > lo:
+                num += (hi - lo) * cu_used / N_CU
+        rows.append({"cu_budget": k if k else "all", "rs_alone_ms": round(t_rs_alone, 4),
+                     "rs_concurrent_ms": round(rs_t1 - rs_t0, 4),
+                     "rs_alone_gbps": round(rs_bytes / t_rs_alone / 1e6, 1),
+                     "rs_concurrent_gbps": round(rs_bytes / (rs_t1 - rs_t0) / 1e6, 1),
+                     "gemm_alone_ms": round(t_gemm, 4), "gemm_concurrent_ms": round(t_gemm_conc, 4),
+                     "gemm_slowdown": round(t_gemm_conc / t_gemm - 1, 4),
+                     "contention_rate": round(num / den, 5) if den else None})
+        if k:
+            del side
+            hc.hc_stream_destroy(handle)
+    return {"metric": "Reduce-scatter under a CU budget beside a bf16 GEMM: contention rate, GEMM slowdown, RS GB/s",
+            "value": rows[0]["rs_concurrent_gbps"], "unit": "GB/s", "n_gpus": 1, "steps": 1, "warmup": 2,
+            "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"R={R} reduce-scatter of {R} x {n} bf16 N(0,1e-3) on a CU-masked side stream, "
+                                   "main stream torch.matmul 8192^3 bf16"},
+            "gemm_tflops_alone": round(2 * 8192 ** 3 / (t_gemm / 1e3) / 1e12, 1), "rows": rows}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ring_bf16",
+                    choices=["ring_bf16", "ring_f32", "codec", "compressed", "contention"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 24,
+                    help="elements per rank the oracle baseline runs on")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build emulates the R ranks on one GPU; runs on more than one GPU "
+                                   "are not part of it (see DESIGN.md for how the path would shard)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    if args.workload in ("ring_bf16", "ring_f32"):
+        line = bench_ring(args, args.workload)
+    elif args.workload == "codec":
+        line = bench_codec(args)
+    elif args.workload == "compressed":
+        line = bench_compressed(args)
+    else:
+        line = bench_contention(args)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

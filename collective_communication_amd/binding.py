@@ -1,0 +1,311 @@
+"""ctypes binding of libhc (C ABI in include/hc.h), argument marshalling only.
+
+Every function has the C name and order of arguments; torch device tensors
+stand in for device pointers and torch streams for hipStream_t.  The only
+logic here is turning tensors into pointers and sizes, checking that the
+tensors are large enough for what the C call will touch, and raising
+``HcError`` for a non-zero status.  There is no CPU fallback: when libhc.so
+is missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhc.so")
+
+HC_SUCCESS = 0
+HC_ERR_INVALID_ARGUMENT = 1
+HC_ERR_UNSUPPORTED = 2
+HC_ERR_INSUFFICIENT_CAPACITY = 3
+HC_ERR_CORRUPT_STREAM = 4
+HC_ERR_DEVICE = 5
+HC_F32 = 0
+HC_BF16 = 1
+HC_OP_REDUCE_SCATTER = 0
+HC_OP_COMPRESS = 1
+HC_OP_COMPRESSED_ALLREDUCE = 2
+HC_OP_ALLREDUCE = 3
+HC_OP_ALL_GATHER = 4
+HC_BLOCK_ELEMS = 16384
+HC_MAX_RANKS = 64
+
+EXPORTED = [
+    "hc_allreduce", "hc_reduce_scatter", "hc_all_gather", "hc_compress_bound_bf16",
+    "hc_compress_bf16", "hc_decompress_bf16", "hc_compressed_allreduce", "hc_workspace_bytes",
+    "hc_stream_create_cu_budget", "hc_stream_destroy", "hc_chunk_elems", "hc_ring_tasks",
+    "hc_status_string", "hc_last_error", "hc_version", "hc_step_count",
+]
+
+
+class HcError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"hc status {status}: {message}")
+        self.status = status
+
+
+class hc_opts_t(ctypes.Structure):
+    _fields_ = [("chunk_fraction", ctypes.c_double), ("cu_budget", ctypes.c_int32),
+                ("n_step_events", ctypes.c_int32), ("step_events", ctypes.c_void_p)]
+
+
+class hc_task_t(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_int32), ("dst", ctypes.c_int32), ("step", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("op", ctypes.c_int32), ("slice", ctypes.c_int32),
+                ("off", ctypes.c_uint64), ("len", ctypes.c_uint64)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libhc.so (raises when it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                           "(there is no fallback implementation)")
+    L = ctypes.CDLL(path)
+    P, S, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    O = ctypes.POINTER(hc_opts_t)
+    L.hc_allreduce.argtypes = [PP, PP, S, I, I, O, P]
+    L.hc_reduce_scatter.argtypes = [PP, PP, S, I, I, P, S, O, P]
+    L.hc_all_gather.argtypes = [PP, PP, S, I, I, O, P]
+    L.hc_compress_bound_bf16.argtypes = [S]
+    L.hc_compress_bound_bf16.restype = S
+    L.hc_compress_bf16.argtypes = [P, S, P, S, P, P, S, P]
+    L.hc_decompress_bf16.argtypes = [P, S, P, S, P, P]
+    L.hc_compressed_allreduce.argtypes = [PP, PP, S, I, P, S, P, O, P]
+    L.hc_workspace_bytes.argtypes = [I, S, I, I]
+    L.hc_workspace_bytes.restype = S
+    L.hc_stream_create_cu_budget.argtypes = [I, ctypes.POINTER(ctypes.c_void_p)]
+    L.hc_stream_destroy.argtypes = [P]
+    L.hc_chunk_elems.argtypes = [S, ctypes.c_double, S]
+    L.hc_chunk_elems.restype = S
+    L.hc_ring_tasks.argtypes = [I, S, S, ctypes.POINTER(hc_task_t), S]
+    L.hc_step_count.argtypes = [I, I]
+    L.hc_step_count.restype = I
+    L.hc_ring_tasks.restype = S
+    for name in ("hc_allreduce", "hc_reduce_scatter", "hc_all_gather", "hc_compress_bf16",
+                 "hc_decompress_bf16", "hc_compressed_allreduce", "hc_stream_create_cu_budget",
+                 "hc_stream_destroy"):
+        getattr(L, name).restype = I
+    L.hc_status_string.argtypes = [I]
+    L.hc_status_string.restype = ctypes.c_char_p
+    L.hc_last_error.argtypes = []
+    L.hc_last_error.restype = ctypes.c_char_p
+    L.hc_version.argtypes = []
+    L.hc_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != HC_SUCCESS:
+        L = load()
+        raise HcError(status, f"{L.hc_status_string(status).decode()}: {L.hc_last_error().decode()}")
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return HC_F32
+    if t.dtype == torch.bfloat16:
+        return HC_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class StepEvents:
+    """Caller-owned HIP events for hc_opts_t.step_events (see include/hc.h).
+    ``handles`` are the raw hipEvent_t values of torch.cuda.Event objects."""
+
+    def __init__(self, events):
+        self.events = list(events)
+        for e in self.events:
+            e.record()  # makes torch create the underlying hipEvent_t
+        self._arr = (ctypes.c_void_p * len(self.events))(*[e.cuda_event for e in self.events])
+
+    def elapsed_ms(self):
+        return [self.events[k].elapsed_time(self.events[k + 1]) for k in range(len(self.events) - 1)]
+
+
+def _opts(chunk_fraction: float = 0.0, cu_budget: int = 0, step_events: StepEvents | None = None):
+    if chunk_fraction == 0.0 and cu_budget == 0 and step_events is None:
+        return None
+    o = hc_opts_t(chunk_fraction, cu_budget, 0, None)
+    if step_events is not None:
+        o.n_step_events = len(step_events.events)
+        o.step_events = ctypes.cast(step_events._arr, ctypes.c_void_p)
+    return ctypes.pointer(o)
+
+
+def _ptr_array(tensors: Sequence[torch.Tensor], need_elems: int, name: str):
+    ptrs = []
+    for r, t in enumerate(tensors):
+        if not t.is_cuda:
+            raise ValueError(f"{name}[{r}] is not a device tensor")
+        if not t.is_contiguous() or t.numel() < need_elems:
+            raise ValueError(f"{name}[{r}] must be contiguous with >= {need_elems} elements")
+        ptrs.append(t.data_ptr())
+    arr = (ctypes.c_void_p * max(len(ptrs), 1))(*ptrs)
+    return ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), arr
+
+
+def _dptr(t: torch.Tensor | None, need_bytes: int, name: str) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if t.numel() * t.element_size() < need_bytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {need_bytes}")
+    return t.data_ptr()
+
+
+# ----------------------------------------------------------------------------- ring
+
+def hc_allreduce(sendbufs, recvbufs, count: int | None = None, *, chunk_fraction: float = 0.0,
+                 cu_budget: int = 0, step_events: StepEvents | None = None, stream=None):
+    L = load()
+    R = len(sendbufs)
+    if count is None:
+        count = sendbufs[0].numel()
+    if len(recvbufs) != R:
+        raise ValueError("sendbufs and recvbufs need one tensor per rank")
+    dt = _dtype(sendbufs[0])
+    if any(t.dtype != sendbufs[0].dtype for t in list(sendbufs) + list(recvbufs)):
+        raise TypeError("all buffers need one dtype")
+    sp, _k1 = _ptr_array(sendbufs, count, "sendbufs")
+    rp, _k2 = _ptr_array(recvbufs, count, "recvbufs")
+    _check(L.hc_allreduce(sp, rp, count, dt, R, _opts(chunk_fraction, cu_budget, step_events),
+                          _stream_handle(stream)))
+
+
+def hc_reduce_scatter(sendbufs, recvbufs, recvcount: int | None = None, ws=None, *,
+                      chunk_fraction: float = 0.0, cu_budget: int = 0,
+                      step_events: StepEvents | None = None, stream=None):
+    L = load()
+    R = len(sendbufs)
+    if recvcount is None:
+        recvcount = recvbufs[0].numel()
+    dt = _dtype(sendbufs[0])
+    if any(t.dtype != sendbufs[0].dtype for t in list(sendbufs) + list(recvbufs)):
+        raise TypeError("all buffers need one dtype")
+    sp, _k1 = _ptr_array(sendbufs, recvcount * R, "sendbufs")
+    rp, _k2 = _ptr_array(recvbufs, recvcount, "recvbufs")
+    need = hc_workspace_bytes(HC_OP_REDUCE_SCATTER, recvcount * R, R, dt)
+    wsp = _dptr(ws, need, "ws") if ws is not None else None
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(L.hc_reduce_scatter(sp, rp, recvcount, dt, R, wsp, ws_bytes,
+                               _opts(chunk_fraction, cu_budget, step_events), _stream_handle(stream)))
+
+
+def hc_all_gather(sendbufs, recvbufs, sendcount: int | None = None, *, chunk_fraction: float = 0.0,
+                  cu_budget: int = 0, step_events: StepEvents | None = None, stream=None):
+    L = load()
+    R = len(sendbufs)
+    if sendcount is None:
+        sendcount = sendbufs[0].numel()
+    dt = _dtype(sendbufs[0])
+    if any(t.dtype != sendbufs[0].dtype for t in list(sendbufs) + list(recvbufs)):
+        raise TypeError("all buffers need one dtype")
+    sp, _k1 = _ptr_array(sendbufs, sendcount, "sendbufs")
+    rp, _k2 = _ptr_array(recvbufs, sendcount * R, "recvbufs")
+    _check(L.hc_all_gather(sp, rp, sendcount, dt, R, _opts(chunk_fraction, cu_budget, step_events),
+                           _stream_handle(stream)))
+
+
+def hc_workspace_bytes(op: int, count: int, nranks: int, dtype: int = HC_BF16) -> int:
+    return int(load().hc_workspace_bytes(op, count, nranks, dtype))
+
+
+def hc_chunk_elems(count: int, chunk_fraction: float = 0.01, align: int = 1024) -> int:
+    return int(load().hc_chunk_elems(count, chunk_fraction, align))
+
+
+def hc_ring_tasks(nranks: int, count: int, chunk: int):
+    L = load()
+    n = int(L.hc_ring_tasks(nranks, count, chunk, None, 0))
+    buf = (hc_task_t * max(n, 1))()
+    L.hc_ring_tasks(nranks, count, chunk, buf, n)
+    return [(t.src, t.dst, t.step, t.chunk, t.op, t.slice, t.off, t.len) for t in buf[:n]]
+
+
+# ----------------------------------------------------------------------------- codec
+
+def hc_compress_bound_bf16(n: int) -> int:
+    return int(load().hc_compress_bound_bf16(n))
+
+
+def hc_compress_bf16(d_in: torch.Tensor, n: int, d_out: torch.Tensor, d_out_bytes: torch.Tensor,
+                     ws: torch.Tensor, *, stream=None):
+    L = load()
+    if d_in.element_size() != 2:
+        raise TypeError("input must hold 16-bit words")
+    inp = _dptr(d_in, 2 * n, "d_in") if n else (d_in.data_ptr() if d_in.numel() else None)
+    out_cap = d_out.numel() * d_out.element_size()
+    outp = _dptr(d_out, 1, "d_out")
+    ob = _dptr(d_out_bytes, 8, "d_out_bytes")
+    wsp = _dptr(ws, 1, "ws")
+    _check(L.hc_compress_bf16(inp, n, outp, out_cap, ob, wsp, ws.numel() * ws.element_size(),
+                              _stream_handle(stream)))
+
+
+def hc_decompress_bf16(d_in: torch.Tensor, in_bytes: int, d_out: torch.Tensor, n: int,
+                       d_status: torch.Tensor, *, stream=None):
+    L = load()
+    inp = _dptr(d_in, in_bytes, "d_in")
+    outp = _dptr(d_out, 2 * n, "d_out") if n else None
+    st = _dptr(d_status, 4, "d_status")
+    _check(L.hc_decompress_bf16(inp, in_bytes, outp, n, st, _stream_handle(stream)))
+
+
+def hc_compressed_allreduce(sendbufs, recvbufs, count: int | None, ws: torch.Tensor,
+                            d_wire_bytes: torch.Tensor | None = None, *, chunk_fraction: float = 0.0,
+                            step_events: StepEvents | None = None, stream=None):
+    L = load()
+    R = len(sendbufs)
+    if count is None:
+        count = sendbufs[0].numel()
+    if any(t.dtype != torch.bfloat16 for t in list(sendbufs) + list(recvbufs)):
+        raise TypeError("compressed allreduce is bf16 only")
+    sp, _k1 = _ptr_array(sendbufs, count, "sendbufs")
+    rp, _k2 = _ptr_array(recvbufs, count, "recvbufs")
+    wsp = _dptr(ws, 1, "ws")
+    wb = _dptr(d_wire_bytes, 8, "d_wire_bytes") if d_wire_bytes is not None else None
+    _check(L.hc_compressed_allreduce(sp, rp, count, R, wsp, ws.numel() * ws.element_size(), wb,
+                                     _opts(chunk_fraction, 0, step_events), _stream_handle(stream)))
+
+
+# ----------------------------------------------------------------------------- streams
+
+def hc_stream_create_cu_budget(k: int) -> int:
+    """Returns the raw hipStream_t handle; wrap it with torch.cuda.ExternalStream."""
+    L = load()
+    s = ctypes.c_void_p(0)
+    _check(L.hc_stream_create_cu_budget(k, ctypes.byref(s)))
+    return int(s.value)
+
+
+def hc_stream_destroy(handle: int):
+    _check(load().hc_stream_destroy(handle))
+
+
+def hc_step_count(op: int, nranks: int) -> int:
+    return int(load().hc_step_count(op, nranks))
+
+
+def hc_version() -> str:
+    return load().hc_version().decode()

@@ -1,0 +1,469 @@
+// codec_kernels.hip -- HCZ1 compress / decompress and the fused compressed
+// ring allreduce, for gfx950.
+//
+// compress: one workgroup per 32 KB block, blocks taken in order from an
+// atomic ticket.  A block publishes its record size as soon as it has chosen
+// its code length, then encodes into LDS, then looks back over its
+// predecessors' published sizes for its byte offset (a decoupled look-back
+// scan) and writes the record straight into the final stream: one read of
+// the input, one write of the output, no temporary buffers and no coalescing
+// pass ("CCCL: In-GPU Compression-Coupled Collective Communication", section
+// 4.4).  The look-back waits only on blocks that took earlier tickets, which
+// are already resident, and every wait is bounded.
+//
+// decompress: one workgroup per block; every block validates the stream
+// header and its own record before it reads it; reads never leave in_bytes.
+//
+// compressed ring allreduce: "CCCL ...", section 5 (selective compression):
+// the sender compresses what it sends, the receiver decompresses it, reduces
+// with its own uncompressed data and compresses the result for the next hop;
+// the fused kernel does decompress -> hop -> compress per block in one pass
+// with the block's values in registers.  Wire records sit in fixed-size
+// slots, one per block (the preallocated regions of section 4.4).
+#include "codec.hpp"
+#include "launch.hpp"
+#include "schedule.hpp"
+
+namespace hc {
+
+using namespace codec;
+
+namespace {
+
+constexpr uint64_t kFlagAgg = 1ull << 62;
+constexpr uint64_t kFlagIncl = 2ull << 62;
+constexpr uint64_t kValueMask = (1ull << 62) - 1;
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+// Workspace of hc_compress_bf16: a ticket counter, an error word, then one
+// 64-bit look-back descriptor per block.
+struct CompressWs {
+  uint32_t ticket;
+  uint32_t error;
+  uint32_t pad[14];
+  uint64_t desc[1];
+};
+constexpr size_t kCompressWsHeader = 64;
+
+__device__ __forceinline__ void publish(uint64_t* d, uint64_t v) {
+  __hip_atomic_store(d, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t peek(uint64_t* d) {
+  return __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ void fill_u32_kernel(uint32_t* dst, uint32_t value, size_t words) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+       i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = value;
+}
+
+__global__ void set_u64_kernel(uint64_t* dst, uint64_t value) { *dst = value; }
+
+__device__ __forceinline__ uint32_t header_bytes(uint32_t nb) { return 32u + ((8u * nb + 15u) & ~15u); }
+
+__device__ void write_stream_header(uint8_t* out, uint64_t n, uint32_t nb, uint64_t total) {
+  uint32_t* h = reinterpret_cast<uint32_t*>(out);
+  h[0] = kMagic;
+  h[1] = kB;
+  *reinterpret_cast<uint64_t*>(out + 8) = n;
+  h[4] = nb;
+  h[5] = 0;
+  *reinterpret_cast<uint64_t*>(out + 24) = total;
+  if (nb & 1u) *reinterpret_cast<uint64_t*>(out + 32 + 8ull * nb) = 0;  // table padding
+}
+
+// Validates a stream that holds no elements: just the 32-byte header.
+__global__ void check_empty_stream_kernel(const uint8_t* in, uint64_t in_bytes, int32_t* status) {
+  bool ok = in_bytes >= 32;
+  if (ok) {
+    const uint32_t* h = reinterpret_cast<const uint32_t*>(in);
+    ok = h[0] == kMagic && h[1] == kB && *reinterpret_cast<const uint64_t*>(in + 8) == 0 && h[4] == 0 &&
+         h[5] == 0 && *reinterpret_cast<const uint64_t*>(in + 24) == 32;
+  }
+  if (!ok) *status = HC_ERR_CORRUPT_STREAM;
+}
+
+__global__ void empty_stream_kernel(uint8_t* out, uint64_t* out_bytes) {
+  write_stream_header(out, 0, 0, 32);
+  *out_bytes = 32;
+}
+
+__global__ __launch_bounds__(kThreads) void compress_kernel(const uint16_t* __restrict__ in, uint64_t n,
+                                                            uint8_t* __restrict__ out,
+                                                            uint64_t* __restrict__ out_bytes,
+                                                            CompressWs* __restrict__ ws, uint32_t nb) {
+  __shared__ Smem s;
+  const int t = threadIdx.x;
+  if (t == 0) s.plan[6] = atomicAdd(&ws->ticket, 1u);
+  __syncthreads();
+  const uint32_t bid = s.plan[6];
+  const uint64_t first = (uint64_t)bid * kB;
+  const uint32_t m = (uint32_t)((n - first) < kB ? (n - first) : kB);
+  uint4 v[kPer];
+  load_block(in + first, m, v);
+  const Plan p = plan_block(v, m, s);
+  if (t == 0) publish(&ws->desc[bid], (bid == 0 ? kFlagIncl : kFlagAgg) | p.rec_bytes);
+  write_block(v, p, s);
+  if (t == 0) {
+    uint64_t excl = 0;
+    for (int64_t j = (int64_t)bid - 1; j >= 0; --j) {
+      uint64_t d = peek(&ws->desc[j]);
+      uint32_t spins = 0;
+      while ((d >> 62) == 0 && spins < kSpinLimit) {
+        __builtin_amdgcn_s_sleep(1);
+        d = peek(&ws->desc[j]);
+        ++spins;
+      }
+      if ((d >> 62) == 0) {  // a predecessor never published: give up, flag it
+        atomicExch(&ws->error, 1u);
+        break;
+      }
+      excl += d & kValueMask;
+      if ((d >> 62) == 2) break;
+    }
+    if (bid != 0) publish(&ws->desc[bid], kFlagIncl | (excl + p.rec_bytes));
+    s.misc[0] = excl;
+  }
+  __syncthreads();
+  const uint64_t off = header_bytes(nb) + s.misc[0];
+  copy_out(s, out + off, p.rec_bytes);
+  if (t == 0) {
+    reinterpret_cast<uint64_t*>(out + 32)[bid] = off;
+    if (bid == nb - 1) {
+      const uint64_t total = off + p.rec_bytes;
+      write_stream_header(out, n, nb, total);
+      *out_bytes = __hip_atomic_load(&ws->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? 0 : total;
+    }
+  }
+}
+
+// Validates the stream header and the record of block bid; on success fills
+// the record fields.  Thread 0 only.
+__device__ bool check_record(const uint8_t* in, uint64_t in_bytes, uint64_t n, uint32_t nb, uint32_t bid,
+                             uint32_t* mode, uint32_t* b, uint32_t* n_esc, uint32_t* rec_bytes,
+                             uint64_t* off_out) {
+  const uint64_t hdr = header_bytes(nb);
+  if (in_bytes < hdr) return false;
+  const uint32_t* h = reinterpret_cast<const uint32_t*>(in);
+  if (h[0] != kMagic || h[1] != kB || *reinterpret_cast<const uint64_t*>(in + 8) != n || h[4] != nb || h[5] != 0)
+    return false;
+  const uint64_t total = *reinterpret_cast<const uint64_t*>(in + 24);
+  if (total > in_bytes || total < hdr) return false;
+  if (bid == 0 && (nb & 1u) && *reinterpret_cast<const uint64_t*>(in + 32 + 8ull * nb) != 0) return false;
+  const uint64_t* offs = reinterpret_cast<const uint64_t*>(in + 32);
+  const uint64_t off = offs[bid];
+  const uint64_t next = bid + 1 < nb ? offs[bid + 1] : total;
+  if (bid == 0 && off != hdr) return false;
+  if ((off & 15u) || off < hdr || off + 16 > total || next > total || next < off) return false;
+  const uint8_t* rec = in + off;
+  const uint32_t* r = reinterpret_cast<const uint32_t*>(rec);
+  const uint32_t md = rec[0], bb = rec[1], reserved = r[0] >> 16, rm = r[1], ne = r[2], rb = r[3];
+  const uint32_t m = (uint32_t)(((uint64_t)bid + 1) * kB <= n ? kB : n - (uint64_t)bid * kB);
+  if (reserved != 0 || rm != m || off + rb != next) return false;
+  if (md == 0) {
+    if (bb != 0 || ne != 0 || rb != raw_bytes(m)) return false;
+  } else if (md == 1) {
+    if (m != kB || bb < 1 || bb > 7 || ne > kB || rb != coded_bytes(bb, ne)) return false;
+  } else {
+    return false;
+  }
+  *mode = md; *b = bb; *n_esc = ne; *rec_bytes = rb; *off_out = off;
+  return true;
+}
+
+__global__ __launch_bounds__(kThreads) void decompress_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes,
+                                                              uint16_t* __restrict__ out, uint64_t n,
+                                                              int32_t* __restrict__ status, uint32_t nb) {
+  __shared__ Smem s;
+  const int t = threadIdx.x;
+  const uint32_t bid = blockIdx.x;
+  if (t == 0) {
+    uint32_t mode = 0, b = 0, n_esc = 0, rb = 0;
+    uint64_t off = 0;
+    const bool ok = check_record(in, in_bytes, n, nb, bid, &mode, &b, &n_esc, &rb, &off);
+    s.plan[0] = ok; s.plan[1] = mode; s.plan[2] = b; s.plan[3] = n_esc; s.plan[4] = rb;
+    s.misc[0] = off;
+  }
+  __syncthreads();
+  if (!s.plan[0]) {
+    if (t == 0) atomicExch(status, (int32_t)HC_ERR_CORRUPT_STREAM);
+    return;
+  }
+  const uint32_t mode = s.plan[1], b = s.plan[2], n_esc = s.plan[3], rb = s.plan[4];
+  const uint64_t first = (uint64_t)bid * kB;
+  const uint32_t m = (uint32_t)((n - first) < kB ? (n - first) : kB);
+  copy_in(s, in + s.misc[0], rb);
+  __syncthreads();
+  uint4 v[kPer];
+  const bool ok = read_block(s, mode, b, m, n_esc, rb, v);
+  if (!ok) {
+    if (t == 0) atomicExch(status, (int32_t)HC_ERR_CORRUPT_STREAM);
+    return;
+  }
+  store_block(out + first, m, v);
+}
+
+// After decoding: a corrupt stream leaves the whole output zero.
+__global__ void zero_if_corrupt_kernel(const int32_t* status, uint32_t* out, size_t words, uint16_t* tail,
+                                       int has_tail) {
+  if (*status == 0) return;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (size_t)gridDim.x * blockDim.x)
+    out[i] = 0;
+  if (has_tail && blockIdx.x == 0 && threadIdx.x == 0) *tail = 0;
+}
+
+// ---------------------------------------------------------------------------
+// compressed ring allreduce
+// ---------------------------------------------------------------------------
+
+struct RingPtrs {
+  const uint16_t* send[kMaxRanks];
+  uint16_t* recv[kMaxRanks];
+};
+
+struct CarGeom {
+  uint64_t count;      // elements per rank buffer
+  uint64_t L;          // slice length
+  uint32_t R;
+  uint32_t nbs;        // block slots per slice
+  uint8_t* wire;       // R x 2 x nbs slots of kRawFull bytes
+  uint64_t* wire_bytes;
+};
+
+__device__ __forceinline__ uint8_t* slot(const CarGeom& g, uint32_t rank, uint32_t buf, uint32_t blk) {
+  return g.wire + (((uint64_t)rank * 2 + buf) * g.nbs + blk) * kRawFull;
+}
+
+// Elements of block blk of slice j (0 when the block lies past the slice).
+__device__ __forceinline__ uint32_t block_elems(const CarGeom& g, uint32_t j, uint32_t blk) {
+  uint64_t lo = (uint64_t)j * g.L, hi = lo + g.L;
+  if (lo > g.count) lo = g.count;
+  if (hi > g.count) hi = g.count;
+  const uint64_t b0 = lo + (uint64_t)blk * kB;
+  if (b0 >= hi) return 0;
+  return (uint32_t)((hi - b0) < kB ? (hi - b0) : kB);
+}
+
+__device__ __forceinline__ void count_wire(const CarGeom& g, uint32_t rec_bytes) {
+  if (g.wire_bytes && threadIdx.x == 0) atomicAdd((unsigned long long*)g.wire_bytes, (unsigned long long)rec_bytes);
+}
+
+// Reads a wire record produced by this library from a slot into LDS and
+// decodes it.  The record header is clamped to the slot so that a damaged
+// slot can never send a read out of bounds.
+__device__ void read_slot(Smem& s, const uint8_t* src, uint32_t m, uint4 (&v)[kPer]) {
+  if (threadIdx.x == 0) {
+    const uint32_t* r = reinterpret_cast<const uint32_t*>(src);
+    uint32_t mode = src[0], b = src[1], ne = r[2], rb = r[3];
+    const bool ok = (mode == 0 && rb == raw_bytes(m)) ||
+                    (mode == 1 && m == kB && b >= 1 && b <= 7 && ne <= kB && rb == coded_bytes(b, ne));
+    if (!ok) { mode = 0; b = 0; ne = 0; rb = raw_bytes(m); }
+    s.plan[1] = mode; s.plan[2] = b; s.plan[3] = ne; s.plan[4] = rb;
+  }
+  __syncthreads();
+  const uint32_t mode = s.plan[1], b = s.plan[2], ne = s.plan[3], rb = s.plan[4];
+  copy_in(s, src, rb);
+  __syncthreads();
+  read_block(s, mode, b, m, ne, rb, v);
+}
+
+// Reduce-scatter step 0: every rank compresses the slice it sends first.
+__global__ __launch_bounds__(kThreads) void car_first_kernel(RingPtrs ptr, CarGeom g) {
+  __shared__ Smem s;
+  const uint32_t p = blockIdx.x / g.nbs, blk = blockIdx.x % g.nbs;
+  const uint32_t j = (p + g.R - 1) % g.R;  // sender p sends slice p-1
+  const uint32_t m = block_elems(g, j, blk);
+  if (m == 0) return;
+  uint4 v[kPer];
+  load_block(ptr.send[p] + (uint64_t)j * g.L + (uint64_t)blk * kB, m, v);
+  const Plan pl = plan_block(v, m, s);
+  write_block(v, pl, s);
+  copy_out(s, slot(g, p, 0, blk), pl.rec_bytes);
+  count_wire(g, pl.rec_bytes);
+}
+
+// Reduce-scatter step s: receiver q decompresses what q-1 sent, folds in its
+// own slice, writes the result if this is the last step, and compresses it
+// for the next hop.
+__global__ __launch_bounds__(kThreads) void car_rs_kernel(RingPtrs ptr, CarGeom g, uint32_t step) {
+  __shared__ Smem s;
+  const uint32_t q = blockIdx.x / g.nbs, blk = blockIdx.x % g.nbs;
+  const uint32_t p = (q + g.R - 1) % g.R;
+  const uint32_t j = (q + 2 * g.R - 2 - step) % g.R;
+  const uint32_t m = block_elems(g, j, blk);
+  if (m == 0) return;
+  const uint64_t e0 = (uint64_t)j * g.L + (uint64_t)blk * kB;
+  uint4 own[kPer];
+  load_block(ptr.send[q] + e0, m, own);
+  uint4 v[kPer];
+  read_slot(s, slot(g, p, step & 1, blk), m, v);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) v[k] = hop_bf16x8(v[k], own[k]);
+  if (step == g.R - 2) store_block(ptr.recv[q] + e0, m, v);
+  const Plan pl = plan_block(v, m, s);
+  write_block(v, pl, s);
+  copy_out(s, slot(g, q, (step + 1) & 1, blk), pl.rec_bytes);
+  count_wire(g, pl.rec_bytes);
+}
+
+// All-gather step s: receiver q decompresses the finished slice from q-1 into
+// its output and, unless this is the last step, forwards the same bytes.
+__global__ __launch_bounds__(kThreads) void car_ag_kernel(RingPtrs ptr, CarGeom g, uint32_t step,
+                                                          uint32_t buf_in) {
+  __shared__ Smem s;
+  const uint32_t q = blockIdx.x / g.nbs, blk = blockIdx.x % g.nbs;
+  const uint32_t p = (q + g.R - 1) % g.R;
+  const uint32_t j = (q + 2 * g.R - 1 - step) % g.R;
+  const uint32_t m = block_elems(g, j, blk);
+  if (m == 0) return;
+  const uint64_t e0 = (uint64_t)j * g.L + (uint64_t)blk * kB;
+  uint4 v[kPer];
+  read_slot(s, slot(g, p, buf_in, blk), m, v);
+  store_block(ptr.recv[q] + e0, m, v);
+  if (step + 2 < g.R) {
+    const uint32_t rb = s.plan[4];
+    copy_out(s, slot(g, q, buf_in ^ 1u, blk), rb);
+    count_wire(g, rb);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fill_u32(void* dst, uint32_t value, size_t words, hipStream_t stream) {
+  if (words == 0) return hipSuccess;
+  size_t grid = (words + 255) / 256;
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((uint32_t)grid), dim3(256), 0, stream,
+                     static_cast<uint32_t*>(dst), value, words);
+  return hipGetLastError();
+}
+
+size_t compress_ws_bytes(size_t n) { return kCompressWsHeader + 8 * ceil_div(n, kB); }
+
+hipError_t launch_compress(const uint16_t* in, size_t n, void* out, uint64_t* out_bytes, void* ws,
+                           hipStream_t stream) {
+  const size_t nb = ceil_div(n, kB);
+  if (nb == 0) {
+    hipLaunchKernelGGL(empty_stream_kernel, dim3(1), dim3(1), 0, stream, static_cast<uint8_t*>(out), out_bytes);
+    return hipGetLastError();
+  }
+  if (nb >= (1ull << 31)) return hipErrorInvalidValue;
+  hipError_t e = launch_fill_u32(ws, 0u, compress_ws_bytes(n) / 4, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compress_kernel, dim3((uint32_t)nb), dim3(kThreads), 0, stream, in, (uint64_t)n,
+                     static_cast<uint8_t*>(out), out_bytes, static_cast<CompressWs*>(ws), (uint32_t)nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_decompress(const void* in, size_t in_bytes, uint16_t* out, size_t n, int32_t* status,
+                             hipStream_t stream) {
+  hipError_t e = launch_fill_u32(status, 0u, 1, stream);
+  if (e != hipSuccess) return e;
+  const size_t nb = ceil_div(n, kB);
+  if (nb >= (1ull << 31)) return hipErrorInvalidValue;
+  if (nb == 0) {
+    hipLaunchKernelGGL(check_empty_stream_kernel, dim3(1), dim3(1), 0, stream, static_cast<const uint8_t*>(in),
+                       (uint64_t)in_bytes, status);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(decompress_kernel, dim3((uint32_t)nb), dim3(kThreads), 0, stream,
+                     static_cast<const uint8_t*>(in), (uint64_t)in_bytes, out, (uint64_t)n, status, (uint32_t)nb);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t words = n / 2;
+  size_t grid = (words + 255) / 256;
+  if (grid > 1024) grid = 1024;
+  if (grid == 0) grid = 1;
+  hipLaunchKernelGGL(zero_if_corrupt_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, status,
+                     reinterpret_cast<uint32_t*>(out), words, out + n - 1, (int)(n & 1));
+  return hipGetLastError();
+}
+
+size_t compressed_ar_ws_bytes(size_t count, int R) {
+  if (R < 1) return 0;
+  const size_t L = ceil_div(count, (size_t)R);
+  const size_t nbs = ceil_div(L, kB);
+  return (size_t)R * 2 * nbs * kRawFull + 16;
+}
+
+hipError_t launch_compressed_allreduce(void* const* send, void* const* recv, size_t count, int R, size_t chunk,
+                                       void* ws, uint64_t* wire_bytes, hipEvent_t* events, int n_events,
+                                       hipStream_t stream) {
+  int k_event = 0;
+  auto mark = [&]() -> hipError_t {
+    if (!events || k_event >= n_events) return hipSuccess;
+    return hipEventRecord(events[k_event++], stream);
+  };
+  if (count == 0) {
+    if (wire_bytes) hipLaunchKernelGGL(set_u64_kernel, dim3(1), dim3(1), 0, stream, wire_bytes, (uint64_t)0);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = mark();
+    if (e == hipSuccess) e = mark();
+    return e;
+  }
+  const size_t L = ceil_div(count, (size_t)R);
+  const size_t nbs = ceil_div(L, kB);
+  // Per (hop, chunk) stream framing bytes: the 32-byte header and the
+  // offset table of every stream that crosses a link.  Records are added on
+  // the device as they are produced.
+  uint64_t framing = 0;
+  for (int j = 0; j < R; ++j) {
+    size_t lo = (size_t)j * L, hi = lo + L;
+    if (lo > count) lo = count;
+    if (hi > count) hi = count;
+    for (size_t c0 = lo; c0 < hi; c0 += chunk) {
+      const size_t len = (hi - c0) < chunk ? (hi - c0) : chunk;
+      framing += 32 + round_up(8 * ceil_div(len, kB), 16);
+    }
+  }
+  framing *= (uint64_t)2 * (R - 1);  // every slice crosses R-1 links in each phase
+  if (wire_bytes) {
+    hipLaunchKernelGGL(set_u64_kernel, dim3(1), dim3(1), 0, stream, wire_bytes, R > 1 ? framing : 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (R == 1) {
+    hipError_t e = mark();
+    if (e == hipSuccess && send[0] != recv[0]) {
+      Seg seg{send[0], nullptr, recv[0], count};
+      e = launch_copy_step(&seg, 1, 2, 0, stream);
+    }
+    if (e == hipSuccess) e = mark();
+    return e;
+  }
+  if ((uint64_t)R * nbs >= (1ull << 31)) return hipErrorInvalidValue;
+  RingPtrs ptr;
+  for (int r = 0; r < R; ++r) {
+    ptr.send[r] = static_cast<const uint16_t*>(send[r]);
+    ptr.recv[r] = static_cast<uint16_t*>(recv[r]);
+  }
+  CarGeom g;
+  g.count = count;
+  g.L = L;
+  g.R = (uint32_t)R;
+  g.nbs = (uint32_t)nbs;
+  g.wire = static_cast<uint8_t*>(ws);
+  g.wire_bytes = wire_bytes;
+  const dim3 grid((uint32_t)(R * nbs)), block(kThreads);
+  hipError_t e = mark();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(car_first_kernel, grid, block, 0, stream, ptr, g);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int s = 0; s + 1 < R; ++s) {
+    if ((e = mark()) != hipSuccess) return e;
+    hipLaunchKernelGGL(car_rs_kernel, grid, block, 0, stream, ptr, g, (uint32_t)s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // After reduce-scatter step R-2 the finished slice's record is in buffer (R-1)&1.
+  uint32_t buf = (uint32_t)((R - 1) & 1);
+  for (int s = 0; s + 1 < R; ++s) {
+    if ((e = mark()) != hipSuccess) return e;
+    hipLaunchKernelGGL(car_ag_kernel, grid, block, 0, stream, ptr, g, (uint32_t)s, buf);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    buf ^= 1u;
+  }
+  return mark();
+}
+
+}  // namespace hc

@@ -1,0 +1,58 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of libhc.
+//
+// Number rules (the hop of the ring, written for the GPU):
+//  * fp32 hop: one IEEE binary32 add.  The library is built without fast-math
+//    and with -ffp-contract=off, and gfx9 keeps fp32 subnormals by default.
+//  * bf16 hop: widen both operands exactly (bf16 is the top half of an fp32
+//    word), one fp32 add, round the sum to bf16 nearest-even.
+//  * a NaN sum becomes the canonical quiet NaN (0x7FC00000 / 0x7FC0).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hc {
+
+constexpr int kMaxRanks = 64;
+constexpr int kThreads = 256;          // 4 wave64 per workgroup
+constexpr int kWaves = kThreads / 64;
+
+__device__ __forceinline__ uint32_t f32_bits(float f) { return __float_as_uint(f); }
+__device__ __forceinline__ float bits_f32(uint32_t u) { return __uint_as_float(u); }
+
+// Round an fp32 word to bf16, nearest even, by integer arithmetic: adding
+// 0x7FFF plus the lowest kept bit carries into the kept half exactly when the
+// dropped half is above the midpoint, or at it with an odd kept half.  A carry
+// out of the largest finite value lands on the infinity encoding, which is
+// IEEE overflow under round-to-nearest.
+__device__ __forceinline__ uint32_t bf16_rne(uint32_t u) {
+  uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : r;
+}
+
+__device__ __forceinline__ uint32_t hop_f32(uint32_t a, uint32_t b) {
+  float s = bits_f32(a) + bits_f32(b);
+  return (s != s) ? 0x7FC00000u : f32_bits(s);
+}
+
+// Two bf16 hops on a packed pair (low and high halves of a 32-bit word).
+__device__ __forceinline__ uint32_t hop_bf16x2(uint32_t a, uint32_t b) {
+  float lo = bits_f32(a << 16) + bits_f32(b << 16);
+  float hi = bits_f32(a & 0xFFFF0000u) + bits_f32(b & 0xFFFF0000u);
+  return bf16_rne(f32_bits(lo)) | (bf16_rne(f32_bits(hi)) << 16);
+}
+
+__device__ __forceinline__ uint4 hop_bf16x8(uint4 a, uint4 b) {
+  return make_uint4(hop_bf16x2(a.x, b.x), hop_bf16x2(a.y, b.y), hop_bf16x2(a.z, b.z),
+                    hop_bf16x2(a.w, b.w));
+}
+
+__device__ __forceinline__ uint4 hop_f32x4(uint4 a, uint4 b) {
+  return make_uint4(hop_f32(a.x, b.x), hop_f32(a.y, b.y), hop_f32(a.z, b.z), hop_f32(a.w, b.w));
+}
+
+// Streaming 16-byte global accesses.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+}  // namespace hc

@@ -1,0 +1,467 @@
+// hc_api.cpp -- the C ABI of libhc: argument checks, the ring launcher, the
+// codec and compressed-ring entry points, CU-budget streams.
+//
+// Every check runs on the host before anything is enqueued; a call that
+// returns an error has launched nothing.  Calls are asynchronous on the
+// caller's stream and never synchronize it.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "hc.h"
+#include "launch.hpp"
+#include "schedule.hpp"
+
+extern "C" int hc_step_count(hc_op_t op, int nranks);
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hc_status_t fail(hc_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+hc_status_t fail(hc_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+hc_status_t device_fail(hipError_t e, const char* where) {
+  return fail(HC_ERR_DEVICE, "%s: %s", where, hipGetErrorString(e));
+}
+
+size_t esize(hc_dtype_t d) { return d == HC_F32 ? 4 : 2; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+hc_status_t check_common(int nranks, hc_dtype_t dtype, const hc_opts_t* opts) {
+  if (nranks < 1 || nranks > HC_MAX_RANKS)
+    return fail(HC_ERR_INVALID_ARGUMENT, "nranks %d outside 1..%d", nranks, HC_MAX_RANKS);
+  if (dtype != HC_F32 && dtype != HC_BF16)
+    return fail(HC_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+  if (opts) {
+    if (opts->chunk_fraction != 0.0 && !(opts->chunk_fraction > 0.0 && opts->chunk_fraction <= 1.0))
+      return fail(HC_ERR_INVALID_ARGUMENT, "chunk_fraction %g outside (0, 1]", opts->chunk_fraction);
+    if (opts->cu_budget < 0 || opts->cu_budget > 4096)
+      return fail(HC_ERR_INVALID_ARGUMENT, "cu_budget %d outside 0..4096", opts->cu_budget);
+    if (opts->n_step_events < 0) return fail(HC_ERR_INVALID_ARGUMENT, "n_step_events < 0");
+  }
+  return HC_SUCCESS;
+}
+
+// Records the caller's step events (hc_opts_t.step_events), if any.
+struct Tap {
+  hipEvent_t* ev = nullptr;
+  int n = 0, k = 0;
+  hipError_t mark(hipStream_t stream) {
+    if (!ev || k >= n) return hipSuccess;
+    return hipEventRecord(ev[k++], stream);
+  }
+};
+
+hc_status_t make_tap(const hc_opts_t* o, hc_op_t op, int nranks, Tap* tap) {
+  if (!o || !o->step_events) return HC_SUCCESS;
+  const int steps = hc_step_count(op, nranks);
+  if (o->n_step_events < steps + 1)
+    return fail(HC_ERR_INVALID_ARGUMENT, "n_step_events %d < %d", o->n_step_events, steps + 1);
+  tap->ev = o->step_events;
+  tap->n = o->n_step_events;
+  return HC_SUCCESS;
+}
+
+double chunk_fraction(const hc_opts_t* o) {
+  return (o && o->chunk_fraction != 0.0) ? o->chunk_fraction : 0.01;
+}
+int cu_budget(const hc_opts_t* o) { return o ? o->cu_budget : 0; }
+
+// Checks a pointer array: non-NULL and aligned to `align` bytes.
+hc_status_t check_ptrs(void* const* bufs, int R, const char* name, size_t align) {
+  if (!bufs) return fail(HC_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  for (int r = 0; r < R; ++r) {
+    if (!bufs[r]) return fail(HC_ERR_INVALID_ARGUMENT, "%s[%d] is NULL", name, r);
+    if ((uintptr_t)bufs[r] % align)
+      return fail(HC_ERR_INVALID_ARGUMENT, "%s[%d] is not %zu-byte aligned", name, r, align);
+  }
+  return HC_SUCCESS;
+}
+
+// Output ranges must be pairwise disjoint and disjoint from every input range
+// except the allowed in-place alias (input r == the given offset inside
+// output r, checked by the caller as `inplace_ok`).
+hc_status_t check_disjoint(const std::vector<Range>& in, const std::vector<Range>& out,
+                           const std::vector<bool>& inplace_ok) {
+  for (size_t i = 0; i < out.size(); ++i)
+    for (size_t j = i + 1; j < out.size(); ++j)
+      if (overlap(out[i], out[j]))
+        return fail(HC_ERR_INVALID_ARGUMENT, "recvbufs[%zu] and recvbufs[%zu] overlap", i, j);
+  for (size_t i = 0; i < out.size(); ++i)
+    for (size_t j = 0; j < in.size(); ++j) {
+      if (i == j && inplace_ok[i]) continue;
+      if (overlap(out[i], in[j]))
+        return fail(HC_ERR_INVALID_ARGUMENT, "recvbufs[%zu] overlaps sendbufs[%zu]", i, j);
+    }
+  return HC_SUCCESS;
+}
+
+const char* cp(const void* p, size_t bytes) { return static_cast<const char*>(p) + bytes; }
+char* mp(void* p, size_t bytes) { return static_cast<char*>(p) + bytes; }
+
+// Runs the allreduce task list one ring step per launch: all receivers of a
+// step in one kernel, their chunks merged into one segment per receiver.
+hc_status_t run_allreduce(void* const* send, void* const* recv, size_t count, hc_dtype_t dtype,
+                          int R, size_t chunk, int budget, Tap& tap, hipStream_t stream) {
+  const size_t es = esize(dtype);
+  std::vector<hc_task_t> tasks = hc::ring_tasks(R, count, chunk);
+  size_t k = 0;
+  while (k < tasks.size()) {
+    const int op = tasks[k].op, step = tasks[k].step;
+    hc::Seg segs[hc::kMaxSegs];
+    int nseg = 0, last_dst = -1;
+    uint64_t last_end = 0;
+    while (k < tasks.size() && tasks[k].op == op && tasks[k].step == step) {
+      const hc_task_t& t = tasks[k];
+      const size_t off = t.off * es;
+      if (t.dst == last_dst && t.off == last_end) {
+        segs[nseg - 1].len += t.len;  // next chunk of the same receiver's slice
+      } else {
+        segs[nseg].a = (op == 1 && step == 0) ? cp(send[t.src], off) : cp(recv[t.src], off);
+        segs[nseg].b = cp(send[t.dst], off);
+        segs[nseg].dst = mp(recv[t.dst], off);
+        segs[nseg].len = t.len;
+        ++nseg;
+      }
+      last_dst = t.dst;
+      last_end = t.off + t.len;
+      ++k;
+    }
+    hipError_t e = tap.mark(stream);
+    if (e != hipSuccess) return device_fail(e, "hipEventRecord");
+    e = op == 1 ? hc::launch_reduce_step(segs, nseg, dtype, budget, stream)
+                : hc::launch_copy_step(segs, nseg, es, budget, stream);
+    if (e != hipSuccess) return device_fail(e, op == 1 ? "reduce step launch" : "copy step launch");
+  }
+  hipError_t e = tap.mark(stream);
+  return e == hipSuccess ? HC_SUCCESS : device_fail(e, "hipEventRecord");
+}
+
+// One-rank operations: a single step that copies (or nothing in place).
+hc_status_t run_single(const void* src, void* dst, size_t count, size_t es, int budget, Tap& tap,
+                       hipStream_t stream) {
+  hipError_t e = tap.mark(stream);
+  if (e == hipSuccess && src != dst) {
+    hc::Seg seg{src, nullptr, dst, count};
+    e = hc::launch_copy_step(&seg, 1, es, budget, stream);
+  }
+  if (e == hipSuccess) e = tap.mark(stream);
+  return e == hipSuccess ? HC_SUCCESS : device_fail(e, "copy launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hc_status_string(hc_status_t s) {
+  switch (s) {
+    case HC_SUCCESS: return "success";
+    case HC_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case HC_ERR_UNSUPPORTED: return "unsupported";
+    case HC_ERR_INSUFFICIENT_CAPACITY: return "insufficient capacity";
+    case HC_ERR_CORRUPT_STREAM: return "corrupt stream";
+    case HC_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* hc_last_error(void) { return g_last_error.c_str(); }
+const char* hc_version(void) { return "hc 0.1 gfx950"; }
+
+int hc_step_count(hc_op_t op, int nranks) {
+  if (nranks < 1 || nranks > HC_MAX_RANKS) return -1;
+  if (nranks == 1) return 1;
+  switch (op) {
+    case HC_OP_ALLREDUCE: return 2 * (nranks - 1);
+    case HC_OP_REDUCE_SCATTER: return nranks - 1;
+    case HC_OP_ALL_GATHER: return nranks - 1;
+    case HC_OP_COMPRESSED_ALLREDUCE: return 2 * nranks - 1;
+    case HC_OP_COMPRESS: return -1;
+  }
+  return -1;
+}
+
+size_t hc_chunk_elems(size_t count, double fraction, size_t align) {
+  return hc::chunk_elems(count, fraction, align);
+}
+
+size_t hc_ring_tasks(int nranks, size_t count, size_t chunk, hc_task_t* tasks, size_t cap) {
+  std::vector<hc_task_t> t = hc::ring_tasks(nranks, count, chunk);
+  if (tasks)
+    for (size_t i = 0; i < t.size() && i < cap; ++i) tasks[i] = t[i];
+  return t.size();
+}
+
+hc_status_t hc_allreduce(void* const* sendbufs, void* const* recvbufs, size_t count,
+                         hc_dtype_t dtype, int nranks, const hc_opts_t* opts, hipStream_t stream) {
+  g_last_error.clear();
+  hc_status_t st = check_common(nranks, dtype, opts);
+  if (st) return st;
+  if (count == 0) return HC_SUCCESS;
+  if ((st = check_ptrs(sendbufs, nranks, "sendbufs", esize(dtype)))) return st;
+  if ((st = check_ptrs(recvbufs, nranks, "recvbufs", esize(dtype)))) return st;
+  const size_t es = esize(dtype);
+  if (count > ((size_t)1 << 40)) return fail(HC_ERR_INVALID_ARGUMENT, "count %zu too large", count);
+  std::vector<Range> in, out;
+  std::vector<bool> ok;
+  for (int r = 0; r < nranks; ++r) {
+    in.push_back({(uintptr_t)sendbufs[r], (uintptr_t)sendbufs[r] + count * es});
+    out.push_back({(uintptr_t)recvbufs[r], (uintptr_t)recvbufs[r] + count * es});
+    ok.push_back(sendbufs[r] == recvbufs[r]);
+  }
+  if ((st = check_disjoint(in, out, ok))) return st;
+  Tap tap;
+  if ((st = make_tap(opts, HC_OP_ALLREDUCE, nranks, &tap))) return st;
+  const size_t chunk = hc::chunk_elems(count, chunk_fraction(opts), 1024);
+  if (nranks == 1) return run_single(sendbufs[0], recvbufs[0], count, es, cu_budget(opts), tap, stream);
+  return run_allreduce(sendbufs, recvbufs, count, dtype, nranks, chunk, cu_budget(opts), tap, stream);
+}
+
+size_t hc_workspace_bytes(hc_op_t op, size_t count, int nranks, hc_dtype_t dtype) {
+  if (nranks < 1 || nranks > HC_MAX_RANKS) return 0;
+  switch (op) {
+    case HC_OP_REDUCE_SCATTER:
+      if (count % (size_t)nranks) return 0;
+      return 2 * count * esize(dtype);          // two slices per rank, R ranks
+    case HC_OP_COMPRESS:
+      return hc::compress_ws_bytes(count);
+    case HC_OP_COMPRESSED_ALLREDUCE:
+      if (dtype != HC_BF16) return 0;
+      return hc::compressed_ar_ws_bytes(count, nranks);
+    case HC_OP_ALLREDUCE:
+    case HC_OP_ALL_GATHER:
+      return 0;
+  }
+  return 0;
+}
+
+hc_status_t hc_reduce_scatter(void* const* sendbufs, void* const* recvbufs, size_t recvcount,
+                              hc_dtype_t dtype, int nranks, void* d_ws, size_t ws_bytes,
+                              const hc_opts_t* opts, hipStream_t stream) {
+  g_last_error.clear();
+  hc_status_t st = check_common(nranks, dtype, opts);
+  if (st) return st;
+  if (recvcount == 0) return HC_SUCCESS;
+  if ((st = check_ptrs(sendbufs, nranks, "sendbufs", esize(dtype)))) return st;
+  if ((st = check_ptrs(recvbufs, nranks, "recvbufs", esize(dtype)))) return st;
+  if (recvcount > ((size_t)1 << 40))
+    return fail(HC_ERR_INVALID_ARGUMENT, "recvcount %zu too large", recvcount);
+  const int R = nranks;
+  const size_t es = esize(dtype), L = recvcount, n = L * (size_t)R;
+  std::vector<Range> in, out;
+  std::vector<bool> ok;
+  for (int r = 0; r < R; ++r) {
+    in.push_back({(uintptr_t)sendbufs[r], (uintptr_t)sendbufs[r] + n * es});
+    out.push_back({(uintptr_t)recvbufs[r], (uintptr_t)recvbufs[r] + L * es});
+    ok.push_back(recvbufs[r] == cp(sendbufs[r], (size_t)r * L * es));
+  }
+  if ((st = check_disjoint(in, out, ok))) return st;
+  Tap tap;
+  if ((st = make_tap(opts, HC_OP_REDUCE_SCATTER, R, &tap))) return st;
+  if (R == 1) return run_single(sendbufs[0], recvbufs[0], L, es, cu_budget(opts), tap, stream);
+  const size_t need = 2 * n * es;
+  if (!d_ws) return fail(HC_ERR_INVALID_ARGUMENT, "d_ws is NULL");
+  if (!aligned16(d_ws)) return fail(HC_ERR_INVALID_ARGUMENT, "d_ws is not 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(HC_ERR_INSUFFICIENT_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, need);
+  Range wr{(uintptr_t)d_ws, (uintptr_t)d_ws + need};
+  for (int r = 0; r < R; ++r)
+    if (overlap(wr, in[r]) || overlap(wr, out[r]))
+      return fail(HC_ERR_INVALID_ARGUMENT, "d_ws overlaps rank %d buffers", r);
+  // Partials of rank q ping-pong between ws slot (q, s%2); the last step lands
+  // in recvbufs[q].  Chunks of one receiver merge into one segment per step.
+  const int budget = cu_budget(opts);
+  for (int s = 0; s + 1 < R; ++s) {
+    hc::Seg segs[hc::kMaxSegs];
+    for (int q = 0; q < R; ++q) {
+      const int p = hc::ring_mod(q - 1, R);
+      const int j = hc::ring_slice(0, q, s, R);
+      const void* a = s == 0 ? cp(sendbufs[p], (size_t)j * L * es)
+                             : cp(d_ws, ((size_t)(2 * p + ((s - 1) & 1)) * L) * es);
+      void* dst = (s == R - 2) ? recvbufs[q] : mp(d_ws, ((size_t)(2 * q + (s & 1)) * L) * es);
+      segs[q] = hc::Seg{a, cp(sendbufs[q], (size_t)j * L * es), dst, L};
+    }
+    hipError_t e = tap.mark(stream);
+    if (e == hipSuccess) e = hc::launch_reduce_step(segs, R, dtype, budget, stream);
+    if (e != hipSuccess) return device_fail(e, "reduce step launch");
+  }
+  hipError_t e = tap.mark(stream);
+  return e == hipSuccess ? HC_SUCCESS : device_fail(e, "hipEventRecord");
+}
+
+hc_status_t hc_all_gather(void* const* sendbufs, void* const* recvbufs, size_t sendcount,
+                          hc_dtype_t dtype, int nranks, const hc_opts_t* opts, hipStream_t stream) {
+  g_last_error.clear();
+  hc_status_t st = check_common(nranks, dtype, opts);
+  if (st) return st;
+  if (sendcount == 0) return HC_SUCCESS;
+  if ((st = check_ptrs(sendbufs, nranks, "sendbufs", esize(dtype)))) return st;
+  if ((st = check_ptrs(recvbufs, nranks, "recvbufs", esize(dtype)))) return st;
+  if (sendcount > ((size_t)1 << 40))
+    return fail(HC_ERR_INVALID_ARGUMENT, "sendcount %zu too large", sendcount);
+  const int R = nranks;
+  const size_t es = esize(dtype), L = sendcount, n = L * (size_t)R;
+  std::vector<Range> in, out;
+  std::vector<bool> ok;
+  for (int r = 0; r < R; ++r) {
+    in.push_back({(uintptr_t)sendbufs[r], (uintptr_t)sendbufs[r] + L * es});
+    out.push_back({(uintptr_t)recvbufs[r], (uintptr_t)recvbufs[r] + n * es});
+    ok.push_back(sendbufs[r] == cp(recvbufs[r], (size_t)r * L * es));
+  }
+  if ((st = check_disjoint(in, out, ok))) return st;
+  const int budget = cu_budget(opts);
+  Tap tap;
+  if ((st = make_tap(opts, HC_OP_ALL_GATHER, R, &tap))) return st;
+  hipError_t e0 = tap.mark(stream);
+  if (e0 != hipSuccess) return device_fail(e0, "hipEventRecord");
+  // Local copies (each rank's own slice into its own output), skipped in place.
+  {
+    hc::Seg segs[hc::kMaxSegs];
+    int nseg = 0;
+    for (int r = 0; r < R; ++r)
+      if (!ok[r]) segs[nseg++] = hc::Seg{sendbufs[r], nullptr, mp(recvbufs[r], (size_t)r * L * es), L};
+    hipError_t e = hc::launch_copy_step(segs, nseg, es, budget, stream);
+    if (e != hipSuccess) return device_fail(e, "local copy launch");
+  }
+  for (int s = 0; s + 1 < R; ++s) {
+    hc::Seg segs[hc::kMaxSegs];
+    for (int q = 0; q < R; ++q) {
+      const int p = hc::ring_mod(q - 1, R);
+      const int j = hc::ring_slice(1, q, s, R);
+      const void* a = s == 0 ? sendbufs[p] : cp(recvbufs[p], (size_t)j * L * es);
+      segs[q] = hc::Seg{a, nullptr, mp(recvbufs[q], (size_t)j * L * es), L};
+    }
+    hipError_t e = s > 0 ? tap.mark(stream) : hipSuccess;  // step 0 began before the local copies
+    if (e == hipSuccess) e = hc::launch_copy_step(segs, R, es, budget, stream);
+    if (e != hipSuccess) return device_fail(e, "copy step launch");
+  }
+  hipError_t e = tap.mark(stream);
+  return e == hipSuccess ? HC_SUCCESS : device_fail(e, "hipEventRecord");
+}
+
+size_t hc_compress_bound_bf16(size_t n) {
+  const size_t B = HC_BLOCK_ELEMS, nb = hc::ceil_div(n, B);
+  size_t total = 32 + hc::round_up(8 * nb, 16);
+  if (nb) total += (nb - 1) * (16 + 2 * B) + 16 + hc::round_up(2 * (n - (nb - 1) * B), 16);
+  return total;
+}
+
+hc_status_t hc_compress_bf16(const uint16_t* d_in, size_t n, void* d_out, size_t out_cap,
+                             uint64_t* d_out_bytes, void* d_ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  if (!d_out || !d_out_bytes || !d_ws || (n && !d_in))
+    return fail(HC_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if ((d_in && !aligned16(d_in)) || !aligned16(d_out) || !aligned16(d_ws) || ((uintptr_t)d_out_bytes & 7u))
+    return fail(HC_ERR_INVALID_ARGUMENT, "misaligned pointer argument");
+  if (n > ((size_t)1 << 40)) return fail(HC_ERR_INVALID_ARGUMENT, "n %zu too large", n);
+  const size_t bound = hc_compress_bound_bf16(n);
+  if (out_cap < bound)
+    return fail(HC_ERR_INSUFFICIENT_CAPACITY, "out_cap %zu < bound %zu", out_cap, bound);
+  const size_t need = hc::compress_ws_bytes(n);
+  if (ws_bytes < need)
+    return fail(HC_ERR_INSUFFICIENT_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, need);
+  Range ir{(uintptr_t)d_in, (uintptr_t)d_in + 2 * n}, orr{(uintptr_t)d_out, (uintptr_t)d_out + bound},
+      wr{(uintptr_t)d_ws, (uintptr_t)d_ws + need};
+  if (overlap(ir, orr) || overlap(ir, wr) || overlap(orr, wr))
+    return fail(HC_ERR_INVALID_ARGUMENT, "input, output and workspace must not overlap");
+  hipError_t e = hc::launch_compress(d_in, n, d_out, d_out_bytes, d_ws, stream);
+  if (e == hipErrorNotSupported) return fail(HC_ERR_UNSUPPORTED, "compress not built");
+  return e == hipSuccess ? HC_SUCCESS : device_fail(e, "compress launch");
+}
+
+hc_status_t hc_decompress_bf16(const void* d_in, size_t in_bytes, uint16_t* d_out, size_t n,
+                               int32_t* d_status, hipStream_t stream) {
+  g_last_error.clear();
+  if (!d_in || !d_status || (n && !d_out)) return fail(HC_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned16(d_in) || (d_out && !aligned16(d_out)) || ((uintptr_t)d_status & 3u))
+    return fail(HC_ERR_INVALID_ARGUMENT, "misaligned pointer argument");
+  if (n > ((size_t)1 << 40)) return fail(HC_ERR_INVALID_ARGUMENT, "n %zu too large", n);
+  Range ir{(uintptr_t)d_in, (uintptr_t)d_in + in_bytes}, orr{(uintptr_t)d_out, (uintptr_t)d_out + 2 * n};
+  if (n && overlap(ir, orr)) return fail(HC_ERR_INVALID_ARGUMENT, "input and output overlap");
+  hipError_t e = hc::launch_decompress(d_in, in_bytes, d_out, n, d_status, stream);
+  if (e == hipErrorNotSupported) return fail(HC_ERR_UNSUPPORTED, "decompress not built");
+  return e == hipSuccess ? HC_SUCCESS : device_fail(e, "decompress launch");
+}
+
+hc_status_t hc_compressed_allreduce(void* const* sendbufs, void* const* recvbufs, size_t count,
+                                    int nranks, void* d_ws, size_t ws_bytes, uint64_t* d_wire_bytes,
+                                    const hc_opts_t* opts, hipStream_t stream) {
+  g_last_error.clear();
+  hc_status_t st = check_common(nranks, HC_BF16, opts);
+  if (st) return st;
+  if (opts && opts->cu_budget != 0)
+    return fail(HC_ERR_UNSUPPORTED, "cu_budget is not supported by the compressed allreduce");
+  if (d_wire_bytes && ((uintptr_t)d_wire_bytes & 7u))
+    return fail(HC_ERR_INVALID_ARGUMENT, "d_wire_bytes is not 8-byte aligned");
+  if ((st = check_ptrs(sendbufs, nranks, "sendbufs", 16))) return st;
+  if ((st = check_ptrs(recvbufs, nranks, "recvbufs", 16))) return st;
+  if (count > ((size_t)1 << 40)) return fail(HC_ERR_INVALID_ARGUMENT, "count %zu too large", count);
+  std::vector<Range> in, out;
+  std::vector<bool> ok;
+  for (int r = 0; r < nranks; ++r) {
+    in.push_back({(uintptr_t)sendbufs[r], (uintptr_t)sendbufs[r] + count * 2});
+    out.push_back({(uintptr_t)recvbufs[r], (uintptr_t)recvbufs[r] + count * 2});
+    ok.push_back(sendbufs[r] == recvbufs[r]);
+  }
+  if ((st = check_disjoint(in, out, ok))) return st;
+  const size_t need = hc::compressed_ar_ws_bytes(count, nranks);
+  if (!d_ws) return fail(HC_ERR_INVALID_ARGUMENT, "d_ws is NULL");
+  if (!aligned16(d_ws)) return fail(HC_ERR_INVALID_ARGUMENT, "d_ws is not 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(HC_ERR_INSUFFICIENT_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, need);
+  Range wr{(uintptr_t)d_ws, (uintptr_t)d_ws + need};
+  for (int r = 0; r < nranks; ++r)
+    if (overlap(wr, in[r]) || overlap(wr, out[r]))
+      return fail(HC_ERR_INVALID_ARGUMENT, "d_ws overlaps rank %d buffers", r);
+  Tap tap;
+  if ((st = make_tap(opts, HC_OP_COMPRESSED_ALLREDUCE, nranks, &tap))) return st;
+  const size_t chunk = hc::chunk_elems(count, chunk_fraction(opts), HC_BLOCK_ELEMS);
+  hipError_t e = hc::launch_compressed_allreduce(sendbufs, recvbufs, count, nranks, chunk, d_ws,
+                                                 d_wire_bytes, tap.ev, tap.n, stream);
+  if (e == hipErrorNotSupported) return fail(HC_ERR_UNSUPPORTED, "compressed allreduce not built");
+  return e == hipSuccess ? HC_SUCCESS : device_fail(e, "compressed allreduce launch");
+}
+
+hc_status_t hc_stream_create_cu_budget(int k, hipStream_t* out) {
+  g_last_error.clear();
+  if (!out) return fail(HC_ERR_INVALID_ARGUMENT, "out is NULL");
+  int dev = 0, ncu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return device_fail(e, "hipDeviceGetAttribute");
+  if (k < 1 || k > ncu) return fail(HC_ERR_INVALID_ARGUMENT, "k %d outside 1..%d", k, ncu);
+  // The first k mask bits: the driver spreads mask bits round-robin over the
+  // XCDs and shader engines, so a prefix is an even spread.
+  std::vector<uint32_t> mask((size_t)(ncu + 31) / 32, 0u);
+  for (int i = 0; i < k; ++i) mask[(size_t)i / 32] |= 1u << (i % 32);
+  e = hipExtStreamCreateWithCUMask(out, (uint32_t)mask.size(), mask.data());
+  if (e != hipSuccess) return device_fail(e, "hipExtStreamCreateWithCUMask");
+  return HC_SUCCESS;
+}
+
+hc_status_t hc_stream_destroy(hipStream_t stream) {
+  g_last_error.clear();
+  hipError_t e = hipStreamDestroy(stream);
+  return e == hipSuccess ? HC_SUCCESS : device_fail(e, "hipStreamDestroy");
+}
+
+}  // extern "C"

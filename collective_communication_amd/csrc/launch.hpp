@@ -1,0 +1,45 @@
+// launch.hpp -- internal launch interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "hc.h"
+
+namespace hc {
+
+// One contiguous piece of a ring step for one receiver: dst = hop(a, b) for
+// a reduce step (a = what arrived from the sender, b = the receiver's own
+// data), dst = a for a copy step.  len in elements.
+struct Seg {
+  const void* a;
+  const void* b;
+  void* dst;
+  uint64_t len;
+};
+
+constexpr int kMaxSegs = 64;
+constexpr int kWgPerCuBudget = 8;   // workgroups per CU of a CU-budget grid
+
+hipError_t launch_reduce_step(const Seg* segs, int nseg, hc_dtype_t dtype, int cu_budget,
+                              hipStream_t stream);
+hipError_t launch_copy_step(const Seg* segs, int nseg, size_t elem_bytes, int cu_budget,
+                            hipStream_t stream);
+
+// Codec.
+hipError_t launch_fill_u32(void* dst, uint32_t value, size_t words, hipStream_t stream);
+hipError_t launch_compress(const uint16_t* in, size_t n, void* out, uint64_t* out_bytes,
+                           void* ws, hipStream_t stream);
+hipError_t launch_decompress(const void* in, size_t in_bytes, uint16_t* out, size_t n,
+                             int32_t* status, hipStream_t stream);
+size_t compress_ws_bytes(size_t n);
+
+// Compressed ring allreduce (bf16).
+size_t compressed_ar_ws_bytes(size_t count, int R);
+// events: optional step events (n of them, >= 2R when R > 1, else >= 2).
+hipError_t launch_compressed_allreduce(void* const* send, void* const* recv, size_t count, int R,
+                                       size_t chunk, void* ws, uint64_t* wire_bytes,
+                                       hipEvent_t* events, int n_events, hipStream_t stream);
+
+}  // namespace hc

@@ -1,0 +1,159 @@
+// ring_kernels.hip -- the recvReduceCopy hop and the copy hop of an emulated
+// ring step, for gfx950.
+//
+// "ResCCL: Resource-Efficient Scheduling for Collective Communication"
+// (section 1) names the primitives: a receiver folds what its predecessor
+// sent into its own data (recvReduceCopy) during reduce-scatter, and copies
+// it (recv) during all-gather.  "CCCL: In-GPU Compression-Coupled
+// Collective Communication" (Figure 2, section 5) shows NCCL's version moving
+// 16-byte packs; here every lane moves 16-byte vectors too (4 fp32 or 8
+// bf16), four of them per operand in flight, so a wave64 issues fully
+// coalesced 1 KB loads.  Both kernels are HBM bound: a reduce hop reads 2
+// and writes 1 element per element of the step, a copy hop reads 1, writes 1.
+//
+// One launch covers one whole ring step: up to 64 segments (one per
+// receiver), cut into 8192-element (bf16) / 4096-element (fp32) tiles, one
+// tile per workgroup, or a persistent grid-stride loop when the caller gives
+// a CU budget.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace hc {
+namespace {
+
+constexpr int kUnroll = 4;
+
+struct SegArgs {
+  const void* a[kMaxSegs];
+  const void* b[kMaxSegs];
+  void* dst[kMaxSegs];
+  uint64_t len[kMaxSegs];
+  uint32_t tile0[kMaxSegs + 1];  // first tile of each segment; tile0[nseg] = total
+  int32_t nseg;
+};
+
+template <int ES>
+__device__ __forceinline__ uint32_t scalar_hop(uint32_t a, uint32_t b) {
+  if constexpr (ES == 4) {
+    return hop_f32(a, b);
+  } else {
+    return bf16_rne(f32_bits(bits_f32(a << 16) + bits_f32(b << 16)));
+  }
+}
+
+template <int ES>
+__device__ __forceinline__ uint32_t ld_elem(const char* p, uint64_t i) {
+  if constexpr (ES == 4) return reinterpret_cast<const uint32_t*>(p)[i];
+  else return reinterpret_cast<const uint16_t*>(p)[i];
+}
+
+template <int ES>
+__device__ __forceinline__ void st_elem(char* p, uint64_t i, uint32_t v) {
+  if constexpr (ES == 4) reinterpret_cast<uint32_t*>(p)[i] = v;
+  else reinterpret_cast<uint16_t*>(p)[i] = (uint16_t)v;
+}
+
+template <int ES>
+__device__ __forceinline__ uint4 vec_hop(uint4 a, uint4 b) {
+  if constexpr (ES == 4) return hop_f32x4(a, b);
+  else return hop_bf16x8(a, b);
+}
+
+// ES: element bytes (4 fp32, 2 bf16).  REDUCE: recvReduceCopy, else copy.
+// VEC: every segment pointer is 16-byte aligned, so whole tiles move as
+// 16-byte vectors; otherwise (odd slice offsets) each lane moves elements.
+template <int ES, bool REDUCE, bool VEC>
+__global__ __launch_bounds__(kThreads) void step_kernel(SegArgs args) {
+  constexpr int V = 16 / ES;
+  constexpr uint64_t kTile = (uint64_t)kThreads * V * kUnroll;
+  const uint32_t total = args.tile0[args.nseg];
+  const int tid = threadIdx.x;
+  for (uint32_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    int lo = 0, hi = args.nseg - 1;
+    while (lo < hi) {  // last segment whose first tile is <= tile
+      const int mid = (lo + hi + 1) >> 1;
+      if (args.tile0[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    const int s = lo;
+    const uint64_t base = (uint64_t)(tile - args.tile0[s]) * kTile;
+    const uint64_t len = args.len[s];
+    const char* pa = static_cast<const char*>(args.a[s]);
+    const char* pb = static_cast<const char*>(args.b[s]);
+    char* pd = static_cast<char*>(args.dst[s]);
+    if (VEC && base + kTile <= len) {
+      uint4 va[kUnroll], vb[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint64_t off = (base + (uint64_t)(u * kThreads + tid) * V) * ES;
+        va[u] = ld16(pa + off);
+        if constexpr (REDUCE) vb[u] = ld16(pb + off);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint64_t off = (base + (uint64_t)(u * kThreads + tid) * V) * ES;
+        if constexpr (REDUCE) st16(pd + off, vec_hop<ES>(va[u], vb[u]));
+        else st16(pd + off, va[u]);
+      }
+    } else {
+      const uint64_t end = base + kTile < len ? base + kTile : len;
+      for (uint64_t i = base + tid; i < end; i += kThreads) {
+        const uint32_t x = ld_elem<ES>(pa, i);
+        if constexpr (REDUCE) st_elem<ES>(pd, i, scalar_hop<ES>(x, ld_elem<ES>(pb, i)));
+        else st_elem<ES>(pd, i, x);
+      }
+    }
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+template <int ES, bool REDUCE>
+hipError_t launch_step(const Seg* segs, int nseg, int cu_budget, hipStream_t stream) {
+  constexpr uint64_t kTile = (uint64_t)kThreads * (16 / ES) * kUnroll;
+  if (nseg <= 0) return hipSuccess;
+  if (nseg > kMaxSegs) return hipErrorInvalidValue;
+  SegArgs args;
+  uint64_t tiles = 0;
+  bool vec = true;
+  int k = 0;
+  for (int i = 0; i < nseg; ++i) {
+    if (segs[i].len == 0) continue;
+    args.a[k] = segs[i].a;
+    args.b[k] = REDUCE ? segs[i].b : segs[i].a;
+    args.dst[k] = segs[i].dst;
+    args.len[k] = segs[i].len;
+    args.tile0[k] = (uint32_t)tiles;
+    tiles += (segs[i].len + kTile - 1) / kTile;
+    vec = vec && aligned16(segs[i].a) && aligned16(segs[i].dst) &&
+          (!REDUCE || aligned16(segs[i].b));
+    ++k;
+  }
+  if (k == 0) return hipSuccess;
+  if (tiles >= 0xFFFFFFFFull) return hipErrorInvalidValue;
+  args.nseg = k;
+  args.tile0[k] = (uint32_t)tiles;
+  uint32_t grid = (uint32_t)tiles;
+  if (cu_budget > 0) {
+    const uint64_t cap = (uint64_t)cu_budget * kWgPerCuBudget;
+    if (grid > cap) grid = (uint32_t)cap;
+  }
+  if (vec) hipLaunchKernelGGL((step_kernel<ES, REDUCE, true>), dim3(grid), dim3(kThreads), 0, stream, args);
+  else hipLaunchKernelGGL((step_kernel<ES, REDUCE, false>), dim3(grid), dim3(kThreads), 0, stream, args);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_reduce_step(const Seg* segs, int nseg, hc_dtype_t dtype, int cu_budget,
+                              hipStream_t stream) {
+  if (dtype == HC_F32) return launch_step<4, true>(segs, nseg, cu_budget, stream);
+  return launch_step<2, true>(segs, nseg, cu_budget, stream);
+}
+
+hipError_t launch_copy_step(const Seg* segs, int nseg, size_t elem_bytes, int cu_budget,
+                            hipStream_t stream) {
+  if (elem_bytes == 4) return launch_step<4, false>(segs, nseg, cu_budget, stream);
+  return launch_step<2, false>(segs, nseg, cu_budget, stream);
+}
+
+}  // namespace hc

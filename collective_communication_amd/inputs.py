@@ -16,7 +16,12 @@ describe them; the pages' nccl-tests sweeps span 2 MB to 1 GB per message):
 * ``contention`` -- R=8 ranks x 2^28 bf16, N(0, 1e-3)
 
 N(mu, s) names the standard deviation s.  Seeds are
-``SeedSequence([20261202, workload_id, index])``.
+``SeedSequence([20261202, workload_id, index])``.  Two generators draw from
+that seed: numpy's default generator on the host (``device="cpu"``, used for
+test-sized inputs) and torch's Philox generator on the GPU (``device="cuda"``,
+for the full-size workloads, whose billions of draws the host generator would
+take minutes over); the GPU path returns a device tensor whose host copy is
+what the oracle sees.
 """
 from __future__ import annotations
 
@@ -31,6 +36,86 @@ WORKLOAD_IDS = {"ring_f32": 1, "ring_bf16": 2, "codec": 3, "compressed": 4, "con
 def rng_for(workload: str | int, index: int) -> np.random.Generator:
     wid = WORKLOAD_IDS[workload] if isinstance(workload, str) else int(workload)
     return np.random.default_rng(np.random.SeedSequence([ROOT_SEED, wid, int(index)]))
+
+
+def seed64(workload: str | int, index: int) -> int:
+    wid = WORKLOAD_IDS[workload] if isinstance(workload, str) else int(workload)
+    return int(np.random.SeedSequence([ROOT_SEED, wid, int(index)]).generate_state(1, np.uint64)[0] >> 1)
+
+
+def _cuda_gen(workload, index):
+    import torch
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed64(workload, index))
+    return g
+
+
+def normal_bf16_cuda(workload, index: int, n: int, sigma: float, zero_frac: float = 0.0):
+    """Device bf16 tensor: N(0, sigma) rounded to bf16 (nearest even), with an
+    independent Bernoulli(zero_frac) mask of exact zeros."""
+    import torch
+
+    g = _cuda_gen(workload, index)
+    x = torch.randn(n, generator=g, device="cuda", dtype=torch.float32)
+    x.mul_(sigma)
+    if zero_frac > 0.0:
+        u = torch.rand(n, generator=g, device="cuda", dtype=torch.float32)
+        x.masked_fill_(u < zero_frac, 0.0)
+        del u
+    return x.to(torch.bfloat16)
+
+
+def activation_bf16_cuda(workload, index: int, n: int):
+    """Device bf16 tensor: per-element 50/50 mixture of N(0, 1) and Laplace(0, 4)
+    (Laplace drawn by the inverse CDF of a uniform on (-1/2, 1/2))."""
+    import torch
+
+    g = _cuda_gen(workload, index)
+    pick = torch.rand(n, generator=g, device="cuda") < 0.5
+    x = torch.randn(n, generator=g, device="cuda", dtype=torch.float32)
+    u = torch.rand(n, generator=g, device="cuda", dtype=torch.float64) - 0.5
+    lap = (-4.0 * torch.sign(u) * torch.log1p(-2.0 * u.abs())).to(torch.float32)
+    x = torch.where(pick, lap, x)
+    return x.to(torch.bfloat16)
+
+
+def normal_f32_cuda(workload, index: int, n: int, sigma: float = 1.0):
+    import torch
+
+    g = _cuda_gen(workload, index)
+    x = torch.randn(n, generator=g, device="cuda", dtype=torch.float32)
+    if sigma != 1.0:
+        x.mul_(sigma)
+    return x
+
+
+def ring_inputs_cuda(workload: str, R: int, n: int):
+    """Per-rank device tensors of a ring workload."""
+    if workload == "ring_f32":
+        return [normal_f32_cuda(workload, r, n, 1.0) for r in range(R)]
+    if workload == "ring_bf16":
+        return [normal_bf16_cuda(workload, r, n, 1e-3, zero_frac=0.01) for r in range(R)]
+    if workload in ("compressed", "contention"):
+        return [normal_bf16_cuda(workload, r, n, 1e-3) for r in range(R)]
+    raise KeyError(workload)
+
+
+def codec_inputs_cuda(n: int):
+    return {
+        "weights": normal_bf16_cuda("codec", 0, n, 0.02),
+        "activations": activation_bf16_cuda("codec", 1, n),
+        "gradients": normal_bf16_cuda("codec", 2, n, 1e-4),
+    }
+
+
+def host_bits(t) -> np.ndarray:
+    """Device tensor -> host bit patterns (uint16 for bf16, float32 as is)."""
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:

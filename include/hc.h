@@ -1,0 +1,255 @@
+/*
+ * hc.h -- C ABI of the MI355X (gfx950) emulated ring AllReduce data path and
+ * the HCZ1 lossless bf16 exponent codec (library: libhc.so).
+ *
+ * The ring is emulated on ONE GPU: R "ranks" are R device buffers in the same
+ * HBM; a hop's link transfer is the receiver reading the sender's buffer.  All
+ * calls are asynchronous and stream ordered, like the NCCL-style
+ * allreduce(sendbuf, recvbuf, count, dtype, op, comm, stream) interface that
+ * "CCCL: In-GPU Compression-Coupled Collective Communication" keeps (section
+ * 3, "CCCL Overview"); argument errors are found on the host before anything
+ * is enqueued.  The only reduction is sum.
+ *
+ * Memory and ownership
+ *   - Every data pointer below is a DEVICE pointer unless it says HOST.
+ *     sendbufs/recvbufs are HOST arrays of nranks DEVICE pointers.
+ *   - The caller owns every buffer, workspace and stream.  The library never
+ *     allocates or frees device memory and keeps no state between calls
+ *     except a thread-local copy of the last error message.
+ *   - Alignment (else HC_ERR_INVALID_ARGUMENT): rank buffers of the
+ *     uncompressed ring calls to their element size (16-byte alignment of
+ *     every slice takes the vector path, anything else a per-element path);
+ *     every pointer of the codec and compressed calls to 16 bytes.
+ *   - Buffers of different ranks must not overlap, except for the in-place
+ *     forms stated per call.  Sizes are in elements unless named *_bytes.
+ *
+ * Errors
+ *   - HC_ERR_INVALID_ARGUMENT: NULL pointer, nranks outside 1..HC_MAX_RANKS,
+ *     misaligned pointer, count constraints, unknown dtype or option value.
+ *   - HC_ERR_INSUFFICIENT_CAPACITY: workspace or output capacity too small.
+ *   - HC_ERR_DEVICE: a HIP call failed; hc_last_error() has the text.
+ *   - HC_ERR_CORRUPT_STREAM: only ever written by the device into the
+ *     caller's status word of hc_decompress_bf16.
+ *   Nothing is enqueued when a call returns an error.  No call aborts or
+ *   throws across the ABI.
+ */
+#ifndef HC_H
+#define HC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HC_MAX_RANKS 64
+#define HC_BLOCK_ELEMS 16384u        /* codec block: 16384 bf16 = 32 KB */
+#define HC_HCZ1_MAGIC 0x315A4348u    /* "HCZ1" little-endian */
+
+typedef enum {
+    HC_SUCCESS = 0,
+    HC_ERR_INVALID_ARGUMENT = 1,
+    HC_ERR_UNSUPPORTED = 2,
+    HC_ERR_INSUFFICIENT_CAPACITY = 3,
+    HC_ERR_CORRUPT_STREAM = 4,
+    HC_ERR_DEVICE = 5
+} hc_status_t;
+
+typedef enum { HC_F32 = 0, HC_BF16 = 1 } hc_dtype_t;
+
+/* Options.  Pass NULL for the defaults (all fields zero mean default).
+ *   chunk_fraction: chunk size as a fraction of the per-rank buffer, default
+ *     0.01 ("a chunk is about 1% of the data", "ResCCL: Resource-Efficient
+ *     Scheduling for Collective Communication", section 1).  The chunk is
+ *     rounded up to 1024 elements (uncompressed) or to whole 16384-element
+ *     codec blocks (compressed).  It changes scheduling only, never a value.
+ *   cu_budget: 0 = size grids for the whole GPU; k > 0 = launch a persistent
+ *     grid sized for k compute units (pair it with a stream from
+ *     hc_stream_create_cu_budget(k)).
+ *   step_events / n_step_events: optional timing hook.  When step_events is
+ *     not NULL it holds n_step_events caller-created HIP events; the call
+ *     records step_events[k] on its stream right before ring step k and
+ *     step_events[steps] after the last step, where steps =
+ *     hc_step_count(op, nranks).  n_step_events < steps + 1 is
+ *     HC_ERR_INVALID_ARGUMENT.  NULL records nothing. */
+typedef struct {
+    double chunk_fraction;
+    int32_t cu_budget;
+    int32_t n_step_events;
+    hipEvent_t *step_events;
+} hc_opts_t;
+
+/*
+ * hc_allreduce -- ring AllReduce (sum) over nranks emulated ranks.
+ * "Breaking the computation and communication abstraction barrier in
+ * distributed machine learning workloads" ("The idea"): AllReduce is a
+ * ReduceScatter followed by an AllGather, and every rank ends with the same
+ * full result (local -> replicated).  Runs R-1 recvReduceCopy steps then R-1
+ * copy steps ("ResCCL ...", section 1).  At reduce-scatter step s receiver q
+ * folds slice (q-2-s) mod R received from q-1 into its own data; at
+ * all-gather step s it copies slice (q-1-s) mod R from q-1.  Element i of
+ * slice j is therefore hop(...hop(x[j+1][i], x[j+2][i])..., x[j][i]).
+ *   fp32: hop = one IEEE binary32 add (round to nearest even, subnormals
+ *         kept); bf16: both operands widened exactly to fp32, one add, the
+ *         sum rounded to bf16 nearest-even.  A NaN sum becomes the canonical
+ *         quiet NaN (0x7FC00000 / 0x7FC0).
+ *   sendbufs[r], recvbufs[r]: count elements each.  In place is allowed:
+ *   sendbufs[r] == recvbufs[r] for every r.  Slices are ceil(count/R) long
+ *   (the last ones short or empty when R does not divide count).
+ */
+hc_status_t hc_allreduce(void *const *sendbufs, void *const *recvbufs, size_t count,
+                         hc_dtype_t dtype, int nranks, const hc_opts_t *opts,
+                         hipStream_t stream);
+
+/*
+ * hc_reduce_scatter -- ring ReduceScatter (sum): rank r receives slice r of
+ * the elementwise sum ("Breaking the computation and communication
+ * abstraction barrier ...", "The idea": each rank keeps its 1/N slice;
+ * local -> sliced).  Same hop and fold order as hc_allreduce.
+ *   sendbufs[r]: recvcount*nranks elements; recvbufs[r]: recvcount elements.
+ *   In place is allowed: recvbufs[r] == sendbufs[r] + r*recvcount elements.
+ *   d_ws: device workspace of at least hc_workspace_bytes(HC_OP_REDUCE_SCATTER,
+ *   recvcount*nranks, nranks, dtype) bytes; it holds the partials in flight.
+ */
+hc_status_t hc_reduce_scatter(void *const *sendbufs, void *const *recvbufs, size_t recvcount,
+                              hc_dtype_t dtype, int nranks, void *d_ws, size_t ws_bytes,
+                              const hc_opts_t *opts, hipStream_t stream);
+
+/*
+ * hc_all_gather -- ring AllGather: every rank receives the concatenation of
+ * all ranks' sendbufs, slice j = rank j's data (sliced -> replicated, same
+ * page).  Step 0 also copies each rank's own data into its own output.
+ *   sendbufs[r]: sendcount elements; recvbufs[r]: sendcount*nranks elements.
+ *   In place is allowed: sendbufs[r] == recvbufs[r] + r*sendcount elements.
+ */
+hc_status_t hc_all_gather(void *const *sendbufs, void *const *recvbufs, size_t sendcount,
+                          hc_dtype_t dtype, int nranks, const hc_opts_t *opts,
+                          hipStream_t stream);
+
+/* Largest HCZ1 stream for n bf16 elements (every block stored raw):
+ * 32 + round_up(8*n_blocks, 16) + sum over blocks of 16 + round_up(2*m, 16). */
+size_t hc_compress_bound_bf16(size_t n);
+
+/*
+ * hc_compress_bf16 -- lossless bf16 compression into one HCZ1 stream.
+ * "CCCL ...", section 4.1: sign and fraction are sent raw, the 8-bit exponent
+ * is coded from a frequency table; section 4.3: each block builds its own
+ * table and uses fixed-length codes; section 4.4: one pass, each block writes
+ * straight into the output; section 5 "Handling data alignment": a partial
+ * tail block is stored raw.
+ * Format (little-endian, all padding zero): 32-byte header {u32 magic
+ * 0x315A4348, u32 block_elems 16384, u64 n, u32 n_blocks, u32 flags 0, u64
+ * total_bytes}; u64 rec_off[n_blocks] padded to 16 bytes; the records in
+ * block order.  Record: 16-byte header {u8 mode (0 raw, 1 coded), u8 b, u16
+ * 0, u32 m, u32 n_esc, u32 rec_bytes}; raw: m words padded to 16; coded
+ * (m == 16384 only): dictionary of the K = 2^b-1 most frequent exponents
+ * (count descending, exponent ascending) in max(16, 2^b) bytes; b code
+ * planes of 2048 bytes (bit i%8 of byte i/8 of plane k = bit k of code[i],
+ * code = dictionary index or K for an escape); the sign/fraction plane
+ * sm[i] = sign<<7 | fraction (16384 bytes); the escaped exponents in index
+ * order, padded to 16.  b is the smallest 1..7 with the fewest bytes; a block
+ * is raw when that is not below 16 + 32768 bytes.
+ *   d_in: n bf16 words.  d_out: out_cap >= hc_compress_bound_bf16(n) bytes.
+ *   d_out_bytes: one device u64, receives the stream size.
+ *   d_ws: >= hc_workspace_bytes(HC_OP_COMPRESS, n, 1, HC_BF16) bytes (block
+ *   offsets in flight).  Calls sharing a workspace must not overlap.
+ */
+hc_status_t hc_compress_bf16(const uint16_t *d_in, size_t n, void *d_out, size_t out_cap,
+                             uint64_t *d_out_bytes, void *d_ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/*
+ * hc_decompress_bf16 -- exact inverse of hc_compress_bf16.
+ *   d_in: in_bytes readable bytes holding a stream of n elements (the stream
+ *   may be shorter than in_bytes).  d_out: n bf16 words.  d_status: one
+ *   device int32, required; set to HC_SUCCESS, or to HC_ERR_CORRUPT_STREAM
+ *   when any field fails validation (magic, block size, n, block count,
+ *   contiguous in-bounds offsets, record sizes against the format, b in
+ *   1..7, escape count, zero padding) -- then d_out is left all zero.  Reads
+ *   never go past in_bytes, whatever the stream holds.
+ */
+hc_status_t hc_decompress_bf16(const void *d_in, size_t in_bytes, uint16_t *d_out, size_t n,
+                               int32_t *d_status, hipStream_t stream);
+
+/*
+ * hc_compressed_allreduce -- the ring of hc_allreduce on bf16 with every hop
+ * payload sent compressed ("CCCL ...", section 5, "Selective compression":
+ * the sender compresses what it sends, the receiver decompresses what it
+ * receives and reduces it with its own uncompressed data).  Reduce-scatter
+ * hop: decompress -> bf16 hop -> compress (the last one also writes the
+ * output); all-gather hop: decompress into the output and forward the same
+ * bytes.  Chunks are whole codec blocks; a slice's unaligned end travels as a
+ * raw block.  Lossless, so the result is bit-identical to hc_allreduce.
+ *   sendbufs/recvbufs: as hc_allreduce (bf16 only; in place allowed).
+ *   d_ws: >= hc_workspace_bytes(HC_OP_COMPRESSED_ALLREDUCE, count, nranks,
+ *   HC_BF16) bytes: two wire buffers per rank, one fixed-size slot per codec
+ *   block (the preallocated regions of "CCCL ...", section 4.4).
+ *   d_wire_bytes: optional device u64; receives the bytes that would cross
+ *   the links: the sum over every (hop, chunk) stream of its HCZ1 size.
+ */
+hc_status_t hc_compressed_allreduce(void *const *sendbufs, void *const *recvbufs, size_t count,
+                                    int nranks, void *d_ws, size_t ws_bytes,
+                                    uint64_t *d_wire_bytes, const hc_opts_t *opts,
+                                    hipStream_t stream);
+
+typedef enum {
+    HC_OP_REDUCE_SCATTER = 0,
+    HC_OP_COMPRESS = 1,
+    HC_OP_COMPRESSED_ALLREDUCE = 2,
+    HC_OP_ALLREDUCE = 3,
+    HC_OP_ALL_GATHER = 4
+} hc_op_t;
+
+/* Workspace bytes for an operation; count = elements per rank buffer
+ * (the send buffer for reduce-scatter, the input for compress).  Returns 0
+ * on invalid arguments and for operations that need no workspace. */
+size_t hc_workspace_bytes(hc_op_t op, size_t count, int nranks, hc_dtype_t dtype);
+
+/* Ring steps of an operation (for hc_opts_t.step_events): allreduce 2(R-1),
+ * reduce-scatter R-1, all-gather R-1 (step 0 includes the local copies),
+ * compressed allreduce 2R-1 (the first compression is step 0); an operation
+ * over one rank counts 1.  Returns -1 for an unknown op or nranks. */
+int hc_step_count(hc_op_t op, int nranks);
+
+/*
+ * hc_stream_create_cu_budget -- a HIP stream whose kernels may run only on k
+ * compute units (hipExtStreamCreateWithCUMask, default priority), for
+ * running a collective beside compute on fewer CUs; "HOCCL: Offloading
+ * Collective Communication from GPU Cores to Accelerate Distributed Training"
+ * (section 2) measures the share of cores such traffic holds while compute
+ * runs.  The k CUs are spread evenly over the GPU's XCDs.  *out receives the
+ * stream; the caller destroys it with hc_stream_destroy.
+ */
+hc_status_t hc_stream_create_cu_budget(int k, hipStream_t *out);
+hc_status_t hc_stream_destroy(hipStream_t stream);
+
+/* Chunk size in elements for a per-rank buffer of count elements
+ * (align = 1024 uncompressed, 16384 compressed); 0 on invalid input. */
+size_t hc_chunk_elems(size_t count, double chunk_fraction, size_t align);
+
+/* One Transfer(srcRank, dstRank, step, chunkId, opType) task of the ring
+ * ("ResCCL ...", section 3), with the element range it moves. */
+typedef struct {
+    int32_t src, dst, step, chunk;
+    int32_t op;        /* 1 = recvReduceCopy (reduce-scatter), 2 = copy (all-gather) */
+    int32_t slice;
+    uint64_t off, len; /* element range inside the per-rank buffer */
+} hc_task_t;
+
+/* Host-only: the allreduce task list the launcher executes (reduce-scatter
+ * steps then all-gather steps; receiver-major, then chunk, in each step).
+ * Returns the number of tasks; writes at most cap (tasks may be NULL). */
+size_t hc_ring_tasks(int nranks, size_t count, size_t chunk, hc_task_t *tasks, size_t cap);
+
+const char *hc_status_string(hc_status_t status);
+const char *hc_last_error(void);  /* thread-local, "" when none */
+const char *hc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HC_H */

@@ -1,0 +1,39 @@
+"""Helpers for the GPU tests: numpy bit patterns <-> torch device tensors."""
+import numpy as np
+import torch
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev(x: np.ndarray) -> torch.Tensor:
+    """uint16 bf16 bit patterns -> bfloat16 tensor; float32 -> float32 tensor."""
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).to(dev())
+    if x.dtype == np.float32:
+        return torch.from_numpy(x.copy()).to(dev())
+    raise TypeError(x.dtype)
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> numpy bit patterns (uint16 for bf16, uint32 for fp32, uint8 bytes)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.cpu().numpy().view(np.uint32)
+    if t.dtype == torch.uint8:
+        return t.cpu().numpy()
+    raise TypeError(t.dtype)
+
+
+def bits(x: np.ndarray) -> np.ndarray:
+    return x.view(np.uint32) if x.dtype == np.float32 else x
+
+
+def first_mismatch(a: np.ndarray, b: np.ndarray) -> str:
+    d = np.nonzero(a != b)[0]
+    if d.size == 0:
+        return "equal"
+    i = int(d[0])
+    return f"{d.size} mismatches, first at {i}: got 0x{int(a[i]):x} want 0x{int(b[i]):x}"

@@ -1,0 +1,163 @@
+"""GPU parity of the ring reduce-scatter / all-gather / allreduce (libhc,
+gfx950) against the oracle, bit for bit.
+
+Ring: "ResCCL: Resource-Efficient Scheduling for Collective Communication"
+(section 1, recvReduceCopy and copy hops, ~1% chunks); AllReduce =
+ReduceScatter then AllGather ("Breaking the computation and communication
+abstraction barrier in distributed machine learning workloads", "The idea").
+The fold order is fixed, so the bar is bit-exact for fp32 and bf16."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from collective_communication_amd import binding as hc
+from collective_communication_amd import inputs
+from hc_util import bits, first_mismatch, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def rand(R, n, dtype, seed, scale=1.0):
+    g = np.random.default_rng(seed)
+    xs = [(g.standard_normal(n) * scale).astype(np.float32) for _ in range(R)]
+    if dtype == "bf16":
+        xs = [inputs.f32_to_bf16_bits(x) for x in xs]
+    return xs
+
+
+def run_ar(xs, inplace=False, **kw):
+    send = [to_dev(x) for x in xs]
+    recv = send if inplace else [torch.empty_like(s) for s in send]
+    hc.hc_allreduce(send, recv, **kw)
+    torch.cuda.synchronize()
+    return [to_host(t) for t in recv]
+
+
+SIZES = [1, 7, 8, 64, 1000, 8192 * 3 + 17, 65536, 300_001]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 8])
+def test_allreduce_matches_oracle(dtype, R):
+    for n in SIZES:
+        xs = rand(R, n, dtype, 1000 * R + n, 1e-3 if dtype == "bf16" else 1.0)
+        ref = oracle.allreduce_fold(xs)
+        got = run_ar(xs)
+        for r in range(R):
+            assert np.array_equal(got[r], bits(ref[r])), f"n={n} rank={r}: {first_mismatch(got[r], bits(ref[r]))}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_allreduce_in_place_and_chunk_independent(dtype):
+    R, n = 8, 8 * 40000 + 24
+    xs = rand(R, n, dtype, 5)
+    ref = oracle.allreduce_fold(xs)
+    for kw in ({"inplace": True}, {"chunk_fraction": 0.001}, {"chunk_fraction": 0.37},
+               {"chunk_fraction": 1.0}, {"cu_budget": 8}, {"cu_budget": 32}):
+        got = run_ar(xs, **kw)
+        for r in range(R):
+            assert np.array_equal(got[r], bits(ref[r])), f"{kw} rank={r}: {first_mismatch(got[r], bits(ref[r]))}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("R", [1, 2, 3, 8])
+def test_reduce_scatter_matches_oracle(dtype, R):
+    for L in (1, 5, 1024, 33333):
+        n = L * R
+        xs = rand(R, n, dtype, 77 * R + L)
+        ref = oracle.reduce_scatter_ring(xs)
+        send = [to_dev(x) for x in xs]
+        recv = [torch.empty(L, dtype=send[0].dtype, device=send[0].device) for _ in range(R)]
+        ws = torch.empty(max(hc.hc_workspace_bytes(hc.HC_OP_REDUCE_SCATTER, n, R, hc._dtype(send[0])), 16),
+                         dtype=torch.uint8, device=send[0].device)
+        hc.hc_reduce_scatter(send, recv, L, ws)
+        torch.cuda.synchronize()
+        for r in range(R):
+            got = to_host(recv[r])
+            assert np.array_equal(got, bits(ref[r])), f"L={L} rank={r}: {first_mismatch(got, bits(ref[r]))}"
+        # in place: rank r's output is slice r of its own input
+        hc.hc_reduce_scatter(send, [s[r * L:(r + 1) * L] for r, s in enumerate(send)], L, ws)
+        torch.cuda.synchronize()
+        for r in range(R):
+            got = to_host(send[r][r * L:(r + 1) * L])
+            assert np.array_equal(got, bits(ref[r])), f"in-place L={L} rank={r}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("R", [1, 2, 5, 8])
+def test_all_gather_matches_oracle(dtype, R):
+    for L in (1, 3, 4096, 20001):
+        xs = rand(R, L, dtype, 3 * R + L)
+        ref = oracle.all_gather_ring(xs)
+        send = [to_dev(x) for x in xs]
+        recv = [torch.empty(L * R, dtype=send[0].dtype, device=send[0].device) for _ in range(R)]
+        hc.hc_all_gather(send, recv, L)
+        torch.cuda.synchronize()
+        for r in range(R):
+            assert np.array_equal(to_host(recv[r]), bits(ref[r])), f"L={L} rank={r}"
+        # in place: the send buffer is slice r of the output
+        outs = [to_dev(np.zeros(L * R, dtype=xs[0].dtype)) for _ in range(R)]
+        for r in range(R):
+            outs[r][r * L:(r + 1) * L].copy_(send[r])
+        hc.hc_all_gather([o[r * L:(r + 1) * L] for r, o in enumerate(outs)], outs, L)
+        torch.cuda.synchronize()
+        for r in range(R):
+            assert np.array_equal(to_host(outs[r]), bits(ref[r])), f"in-place L={L} rank={r}"
+
+
+def test_bf16_hop_every_a_against_sampled_b():
+    """R=2 allreduce: slice 0 computes hop(x1, x0), slice 1 hop(x0, x1), one fp32
+    add and one bf16 rounding each, over all 65,536 bf16 patterns of one operand."""
+    g = np.random.default_rng(21)
+    a = np.arange(1 << 16, dtype=np.uint16)
+    for bv in list(g.integers(0, 1 << 16, 24)) + [0x0000, 0x8000, 0x0001, 0x7F7F, 0x7F80, 0xFF80, 0x7FC0, 0xFFFF]:
+        b = np.full(a.size, bv, dtype=np.uint16)
+        got = run_ar([a, b])
+        want = oracle.hop_bf16_array(b, a)[: a.size // 2]
+        want = np.concatenate([want, oracle.hop_bf16_array(a, b)[a.size // 2:]])
+        assert np.array_equal(got[0], want), f"b=0x{int(bv):04x}: {first_mismatch(got[0], want)}"
+
+
+def test_fp32_hop_specials_and_subnormals():
+    g = np.random.default_rng(22)
+    a = g.integers(0, 1 << 32, 1 << 16, dtype=np.uint64).astype(np.uint32)
+    special = np.array([0, 0x80000000, 1, 0x80000001, 0x007FFFFF, 0x00800000, 0x7F7FFFFF, 0x7F800000,
+                        0xFF800000, 0x7FC00000, 0xFFC00001, 0x3F800000], dtype=np.uint32)
+    a[:special.size] = special
+    b = np.roll(a, 7)
+    got = run_ar([a.view(np.float32), b.view(np.float32)])
+    half = a.size // 2
+    want = np.concatenate([oracle.hop_f32_array(b, a)[:half], oracle.hop_f32_array(a, b)[half:]])
+    assert np.array_equal(got[0], want), first_mismatch(got[0], want)
+
+
+def test_ring_f32_workload_full_size():
+    """R=4 x 2^20 fp32 N(0,1), every rank's output equals the oracle's."""
+    xs = [inputs.host_bits(t) for t in inputs.ring_inputs_cuda("ring_f32", 4, 1 << 20)]
+    ref = oracle.allreduce_fold(xs)
+    got = run_ar(xs)
+    for r in range(4):
+        assert np.array_equal(got[r], bits(ref[r])), first_mismatch(got[r], bits(ref[r]))
+
+
+def test_ring_bf16_workload_full_size_sampled():
+    """R=8 x 2^26 bf16 N(0,1e-3) with 1% zeros: all ranks identical on the GPU,
+    and 2^20 sampled elements (plus every slice boundary) equal the oracle's fold."""
+    R, n = 8, 1 << 26
+    send = inputs.ring_inputs_cuda("ring_bf16", R, n)
+    xs = [inputs.host_bits(s) for s in send]
+    recv = [torch.empty_like(s) for s in send]
+    hc.hc_allreduce(send, recv)
+    torch.cuda.synchronize()
+    for r in range(1, R):
+        assert torch.equal(recv[r].view(torch.int16), recv[0].view(torch.int16)), f"rank {r} differs from rank 0"
+    g = np.random.default_rng(2)
+    L = n // R
+    idx = np.unique(np.concatenate([g.integers(0, n, 1 << 20),
+                                    np.arange(R) * L, np.arange(1, R + 1) * L - 1]).astype(np.uint64))
+    want = oracle.allreduce_fold_at(xs, idx)
+    got = to_host(recv[3])[idx.astype(np.int64)]
+    assert np.array_equal(got, want), first_mismatch(got, want)
+    del send, recv
+    torch.cuda.empty_cache()
