@@ -269,20 +269,25 @@ def bench_contention(args):
     A = torch.randn(8192, 8192, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
     Bm = torch.randn(8192, 8192, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
     C = torch.empty(8192, 8192, device="cuda", dtype=torch.bfloat16)
-    main = torch.cuda.current_stream()
+    # The GEMM runs on a non-blocking stream: a CU-masked HIP stream is a
+    # blocking stream, which the legacy default stream would serialize with.
+    main = torch.cuda.Stream()
     rs_bytes = 3 * 2 * n * (R - 1)
 
     def gemm_alone(iters):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(main)
-        for _ in range(iters):
-            torch.matmul(A, Bm, out=C)
+        with torch.cuda.stream(main):
+            for _ in range(iters):
+                torch.matmul(A, Bm, out=C)
         e1.record(main)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / iters
 
-    for _ in range(3):
-        torch.matmul(A, Bm, out=C)
+    with torch.cuda.stream(main):
+        for _ in range(3):
+            torch.matmul(A, Bm, out=C)
+    torch.cuda.synchronize()
     t_gemm = gemm_alone(10)
     rows = []
     for k in (8, 16, 32, 0):
@@ -311,9 +316,10 @@ def bench_contention(args):
         hc.hc_reduce_scatter(send, recv, L, ws, cu_budget=budget, stream=side)
         r1.record(side)
         ge[0].record(main)
-        for i in range(iters):
-            torch.matmul(A, Bm, out=C)
-            ge[i + 1].record(main)
+        with torch.cuda.stream(main):
+            for i in range(iters):
+                torch.matmul(A, Bm, out=C)
+                ge[i + 1].record(main)
         torch.cuda.synchronize()
         gt = [base.elapsed_time(e) for e in ge]
         rs_t0, rs_t1 = base.elapsed_time(r0), base.elapsed_time(r1)
@@ -354,8 +360,8 @@ def main():
     ap.add_argument("--workload", default="ring_bf16",
                     choices=["ring_bf16", "ring_f32", "codec", "compressed", "contention"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 24,
-                    help="elements per rank the oracle baseline runs on")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 26,
+                    help="elements per rank the oracle baseline runs on (default: the whole workload)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -14,10 +14,12 @@
 // exactly one byte of each code plane, which makes plane packing a bit-matrix
 // transpose inside one register pair.  The record is assembled in LDS
 // (<= 32784 bytes) and leaves with 16-byte stores.
-//   histogram : wave-level match loop (ballot of the lanes holding the
-//               leader's exponent, one LDS add per distinct exponent)
-//   ranking   : each thread ranks one exponent against all 256 keys
-//               (count desc, exponent asc), keys read from LDS as broadcasts
+//   histogram : LDS atomics into 32 replicated, bank-skewed sub-histograms
+//               (two 16-bit bins per word) held in the staging buffer, then
+//               one thread per exponent sums its 32 copies
+//   ranking   : occurring exponents are compacted (ballot + popcount) and
+//               each ranks itself against that short list of keys (count
+//               desc, exponent asc); absent exponents rank after them in order
 //   b choice  : wave 0 prefix-sums the ranked counts and takes the min of
 //               the seven candidate sizes (ties to the smaller b)
 //   escapes   : per-chunk counts, workgroup exclusive scan (wave shuffles +
@@ -48,8 +50,7 @@ struct Plan {
 
 struct Smem {
   uint4 stage[kStage16];         // the record being built or read
-  uint32_t hist[256];            // exponent histogram
-  uint32_t key[256];             // (count << 8) | (255 - exponent)
+  uint32_t key[256];             // (count << 8) | (255 - exponent) of occurring exponents
   uint32_t cbr[256];             // count by rank
   uint8_t code_of[256];          // exponent -> code
   uint32_t wsum[kWaves][4];      // per-wave escape-count totals (scan)
@@ -98,20 +99,13 @@ __device__ __forceinline__ uint32_t chunk_elem_word(const uint4& v, int i) {
   return (i & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
-// Adds the exponents of one element slot of the wave to the LDS histogram:
-// take the first unfinished lane's exponent, count the lanes that share it
-// with one ballot, add that count once, repeat for the remaining lanes.
-__device__ __forceinline__ void wave_hist_add(uint32_t e, uint32_t* hist) {
-  uint64_t todo = __ballot(1);
-  const uint32_t lane = __lane_id();
-  while (todo) {
-    const int leader = __ffsll((unsigned long long)todo) - 1;
-    const uint32_t ev = __builtin_amdgcn_readlane(e, leader);
-    const uint64_t same = __ballot(e == ev);
-    if (lane == (uint32_t)leader) atomicAdd(&hist[ev], (uint32_t)__popcll(same));
-    todo &= ~same;
-  }
-}
+// Exponent histogram layout during planning: kHistCopies sub-histograms in
+// the (not yet used) staging buffer, lane l of every wave adding into copy
+// l % 32, two 16-bit bins per 32-bit word.  The odd word stride puts the
+// copies of one bin in different LDS banks, so the lanes of a wave that hold
+// the same exponent (most of them, for trained-model data) do not collide.
+constexpr uint32_t kHistCopies = 32;
+constexpr uint32_t kHistStride = 129;   // words per copy (128 + 1)
 
 // Inclusive wave64 prefix sum of four packed counters.
 __device__ __forceinline__ uint4 wave_incl_scan4(uint4 v) {
@@ -206,28 +200,51 @@ __device__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, Smem& s) {
     p.mode = 0; p.b = 0; p.K = 0; p.n_esc = 0; p.rec_bytes = raw_bytes(m);
     return p;
   }
-  s.hist[t] = 0;
+  uint32_t* sub = reinterpret_cast<uint32_t*>(s.stage);
+  for (uint32_t i = t; i < kHistCopies * kHistStride; i += kThreads) sub[i] = 0;
   __syncthreads();
+  {
+    uint32_t* mine = sub + (__lane_id() & (kHistCopies - 1)) * kHistStride;
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+    for (int k = 0; k < kPer; ++k) {
+      const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      wave_hist_add(exp_lo(w4[q]), s.hist);
-      wave_hist_add(exp_hi(w4[q]), s.hist);
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t e0 = exp_lo(w4[q]), e1 = exp_hi(w4[q]);
+        atomicAdd(&mine[e0 >> 1], 1u << ((e0 & 1u) << 4));
+        atomicAdd(&mine[e1 >> 1], 1u << ((e1 & 1u) << 4));
+      }
     }
   }
   __syncthreads();
-  const uint32_t cnt = s.hist[t];
-  const uint32_t key = (cnt << 8) | (255u - (uint32_t)t);
-  s.key[t] = key;
-  __syncthreads();
-  uint32_t rank = 0;
-  const uint4* keys4 = reinterpret_cast<const uint4*>(s.key);
+  uint32_t cnt = 0;
 #pragma unroll 8
-  for (int i = 0; i < 64; ++i) {
-    const uint4 kk = keys4[i];
-    rank += (kk.x > key) + (kk.y > key) + (kk.z > key) + (kk.w > key);
+  for (uint32_t c = 0; c < kHistCopies; ++c) cnt += (sub[c * kHistStride + (t >> 1)] >> ((t & 1) << 4)) & 0xFFFFu;
+  // Rank = position in (count desc, exponent asc).  Only exponents that occur
+  // need comparisons: they are compacted into a short list of keys; an
+  // exponent that never occurs ranks after all that do, in exponent order.
+  const uint32_t key = (cnt << 8) | (255u - (uint32_t)t);
+  const uint64_t nzmask = __ballot(cnt > 0);
+  const uint32_t wave = (uint32_t)t >> 6;
+  const uint32_t below = (uint32_t)__popcll(nzmask & ((1ull << __lane_id()) - 1ull));
+  if (__lane_id() == 0) s.wsum[wave][0] = (uint32_t)__popcll(nzmask);
+  __syncthreads();
+  uint32_t before = 0, nz_total = 0;
+#pragma unroll
+  for (uint32_t w = 0; w < (uint32_t)kWaves; ++w) {
+    const uint32_t c = s.wsum[w][0];
+    before += w < wave ? c : 0;
+    nz_total += c;
+  }
+  const uint32_t nz_below = before + below;
+  if (cnt > 0) s.key[nz_below] = key;
+  __syncthreads();
+  uint32_t rank;
+  if (cnt > 0) {
+    rank = 0;
+    for (uint32_t i = 0; i < nz_total; ++i) rank += s.key[i] > key;
+  } else {
+    rank = nz_total + ((uint32_t)t - nz_below);
   }
   s.cbr[rank] = cnt;
   __syncthreads();

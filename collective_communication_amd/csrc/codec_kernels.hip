@@ -89,7 +89,7 @@ __global__ void empty_stream_kernel(uint8_t* out, uint64_t* out_bytes) {
   *out_bytes = 32;
 }
 
-__global__ __launch_bounds__(kThreads) void compress_kernel(const uint16_t* __restrict__ in, uint64_t n,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void compress_kernel(const uint16_t* __restrict__ in, uint64_t n,
                                                             uint8_t* __restrict__ out,
                                                             uint64_t* __restrict__ out_bytes,
                                                             CompressWs* __restrict__ ws, uint32_t nb) {
@@ -172,7 +172,7 @@ __device__ bool check_record(const uint8_t* in, uint64_t in_bytes, uint64_t n, u
   return true;
 }
 
-__global__ __launch_bounds__(kThreads) void decompress_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void decompress_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes,
                                                               uint16_t* __restrict__ out, uint64_t n,
                                                               int32_t* __restrict__ status, uint32_t nb) {
   __shared__ Smem s;
@@ -269,7 +269,7 @@ __device__ void read_slot(Smem& s, const uint8_t* src, uint32_t m, uint4 (&v)[kP
 }
 
 // Reduce-scatter step 0: every rank compresses the slice it sends first.
-__global__ __launch_bounds__(kThreads) void car_first_kernel(RingPtrs ptr, CarGeom g) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void car_first_kernel(RingPtrs ptr, CarGeom g) {
   __shared__ Smem s;
   const uint32_t p = blockIdx.x / g.nbs, blk = blockIdx.x % g.nbs;
   const uint32_t j = (p + g.R - 1) % g.R;  // sender p sends slice p-1
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void car_first_kernel(RingPtrs ptr, CarGe
 // Reduce-scatter step s: receiver q decompresses what q-1 sent, folds in its
 // own slice, writes the result if this is the last step, and compresses it
 // for the next hop.
-__global__ __launch_bounds__(kThreads) void car_rs_kernel(RingPtrs ptr, CarGeom g, uint32_t step) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void car_rs_kernel(RingPtrs ptr, CarGeom g, uint32_t step) {
   __shared__ Smem s;
   const uint32_t q = blockIdx.x / g.nbs, blk = blockIdx.x % g.nbs;
   const uint32_t p = (q + g.R - 1) % g.R;
@@ -294,12 +294,14 @@ __global__ __launch_bounds__(kThreads) void car_rs_kernel(RingPtrs ptr, CarGeom 
   const uint32_t m = block_elems(g, j, blk);
   if (m == 0) return;
   const uint64_t e0 = (uint64_t)j * g.L + (uint64_t)blk * kB;
-  uint4 own[kPer];
-  load_block(ptr.send[q] + e0, m, own);
   uint4 v[kPer];
   read_slot(s, slot(g, p, step & 1, blk), m, v);
+  {  // the receiver's own data, loaded once the decode state is dead
+    uint4 own[kPer];
+    load_block(ptr.send[q] + e0, m, own);
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) v[k] = hop_bf16x8(v[k], own[k]);
+    for (int k = 0; k < kPer; ++k) v[k] = hop_bf16x8(v[k], own[k]);
+  }
   if (step == g.R - 2) store_block(ptr.recv[q] + e0, m, v);
   const Plan pl = plan_block(v, m, s);
   write_block(v, pl, s);
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void car_rs_kernel(RingPtrs ptr, CarGeom 
 
 // All-gather step s: receiver q decompresses the finished slice from q-1 into
 // its output and, unless this is the last step, forwards the same bytes.
-__global__ __launch_bounds__(kThreads) void car_ag_kernel(RingPtrs ptr, CarGeom g, uint32_t step,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void car_ag_kernel(RingPtrs ptr, CarGeom g, uint32_t step,
                                                           uint32_t buf_in) {
   __shared__ Smem s;
   const uint32_t q = blockIdx.x / g.nbs, blk = blockIdx.x % g.nbs;
