@@ -11,19 +11,27 @@
 // gfx950 mapping.  Thread t of the workgroup owns the eight 16-byte chunks
 // c = t + 256k (k = 0..7) of the block, eight consecutive elements each, so
 // every global load and store of a wave is a contiguous 1 KB.  A chunk is
-// exactly one byte of each code plane, which makes plane packing a bit-matrix
-// transpose inside one register pair.  The record is assembled in LDS
-// (<= 32784 bytes) and leaves with 16-byte stores.
-//   histogram : LDS atomics into 32 replicated, bank-skewed sub-histograms
-//               (two 16-bit bins per word) held in the staging buffer, then
-//               one thread per exponent sums its 32 copies
+// exactly one byte of each code plane, which makes plane packing an 8x8
+// bit-matrix transpose inside one register pair; the four lanes of a quad
+// hold four consecutive chunks, so a byte transpose across the quad (two DPP
+// moves and two v_perm_b32) turns their plane bytes into one 32-bit LDS
+// store per plane.  The record is assembled in LDS (<= 32784 bytes) and
+// leaves with 16-byte stores.
+//   histogram : LDS atomics into 32 sub-histograms (lane l adds into copy
+//               l % 32, bin e at word e ^ copy so equal exponents of
+//               different lanes land in different banks), held in the
+//               staging buffer before the record needs it
 //   ranking   : occurring exponents are compacted (ballot + popcount) and
 //               each ranks itself against that short list of keys (count
 //               desc, exponent asc); absent exponents rank after them in order
-//   b choice  : wave 0 prefix-sums the ranked counts and takes the min of
-//               the seven candidate sizes (ties to the smaller b)
-//   escapes   : per-chunk counts, workgroup exclusive scan (wave shuffles +
-//               one LDS exchange), escaped exponent bytes written in order
+//   b choice  : a DPP prefix sum over the ranked counts gives the escape
+//               count of every b; each wave reads the seven candidates with
+//               readlane and keeps the smallest record (ties: smaller b)
+//   escapes   : an element is an escape exactly when all b of its plane bits
+//               are set, so the AND of the plane bytes is the escape mask;
+//               a workgroup scan (DPP rows + one LDS exchange) orders them
+//   decode    : for b <= 4 the dictionary sits in registers and v_perm_b32
+//               maps four codes to four exponents at once
 #pragma once
 
 #include "common.hpp"
@@ -38,6 +46,7 @@ constexpr uint32_t kPlaneBytes = kB / 8;        // one code plane
 constexpr uint32_t kRawFull = 16 + 2 * kB;      // raw record of a full block
 constexpr uint32_t kStage16 = kRawFull / 16;    // 2049 uint4 of LDS staging
 constexpr uint32_t kMagic = 0x315A4348u;
+constexpr uint32_t kHistCopies = 32;            // 32 x 256 words = 32 KB of staging
 
 struct Plan {
   uint32_t mode;       // 0 raw, 1 coded
@@ -53,70 +62,92 @@ struct Smem {
   uint32_t key[256];             // (count << 8) | (255 - exponent) of occurring exponents
   uint32_t cbr[256];             // count by rank
   uint8_t code_of[256];          // exponent -> code
-  uint32_t wsum[kWaves][4];      // per-wave escape-count totals (scan)
+  uint32_t wsum[kWaves][4];      // per-wave totals (scans)
   uint32_t plan[8];
   uint64_t misc[2];
 };
 
 __device__ __forceinline__ uint8_t* stage8(Smem& s) { return reinterpret_cast<uint8_t*>(s.stage); }
+__device__ __forceinline__ uint32_t* stage32(Smem& s) { return reinterpret_cast<uint32_t*>(s.stage); }
 
-__device__ __forceinline__ uint32_t dict_bytes(uint32_t b) { return (1u << b) < 16u ? 16u : (1u << b); }
-__device__ __forceinline__ uint32_t coded_bytes(uint32_t b, uint32_t n_esc) {
+__host__ __device__ constexpr uint32_t dict_bytes(uint32_t b) { return (1u << b) < 16u ? 16u : (1u << b); }
+__host__ __device__ constexpr uint32_t coded_bytes(uint32_t b, uint32_t n_esc) {
   return 16u + dict_bytes(b) + kPlaneBytes * b + kB + ((n_esc + 15u) & ~15u);
 }
-__device__ __forceinline__ uint32_t raw_bytes(uint32_t m) { return 16u + ((2u * m + 15u) & ~15u); }
-__device__ __forceinline__ uint32_t planes_off(uint32_t b) { return 16u + dict_bytes(b); }
-__device__ __forceinline__ uint32_t sm_off(uint32_t b) { return planes_off(b) + kPlaneBytes * b; }
-__device__ __forceinline__ uint32_t esc_off(uint32_t b) { return sm_off(b) + kB; }
+__host__ __device__ constexpr uint32_t raw_bytes(uint32_t m) { return 16u + ((2u * m + 15u) & ~15u); }
+__host__ __device__ constexpr uint32_t planes_off(uint32_t b) { return 16u + dict_bytes(b); }
+__host__ __device__ constexpr uint32_t sm_off(uint32_t b) { return planes_off(b) + kPlaneBytes * b; }
+__host__ __device__ constexpr uint32_t esc_off(uint32_t b) { return sm_off(b) + kB; }
 
-// 8x8 bit-matrix transpose of a 64-bit word (byte r, bit c) -> (byte c, bit
-// r), by three rounds of delta swaps over 1x1, 2x2 and 4x4 sub-blocks (the
-// recursive block transpose described in Hacker's Delight, section 7-3).
-// The transpose is its own inverse.
-__device__ __forceinline__ uint64_t transpose8(uint64_t x) {
-  uint64_t t;
-  t = (x ^ (x >> 7)) & 0x00AA00AA00AA00AAull;
-  x = x ^ t ^ (t << 7);
-  t = (x ^ (x >> 14)) & 0x0000CCCC0000CCCCull;
-  x = x ^ t ^ (t << 14);
-  t = (x ^ (x >> 28)) & 0x00000000F0F0F0F0ull;
-  x = x ^ t ^ (t << 28);
+// ---------------------------------------------------------------------------
+// cross-lane helpers
+// ---------------------------------------------------------------------------
+
+// DPP move: lanes whose source is outside the row read 0, rows outside
+// ROW_MASK read 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp0(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele steps
+// inside each 16-lane row, then the row totals carried by row broadcasts.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp0<0x111>(x);          // row_shr:1
+  x += dpp0<0x112>(x);          // row_shr:2
+  x += dpp0<0x114>(x);          // row_shr:4
+  x += dpp0<0x118>(x);          // row_shr:8
+  x += dpp0<0x142, 0xA>(x);     // row_bcast:15 into rows 1 and 3
+  x += dpp0<0x143, 0xC>(x);     // row_bcast:31 into rows 2 and 3
   return x;
 }
 
-// Sign and fraction of the two bf16 halves of w as two bytes:
-// byte = sign << 7 | fraction.
-__device__ __forceinline__ uint32_t sm_pair(uint32_t w) {
-  const uint32_t t = w & 0x807F807Fu;
-  return (t & 0x7Fu) | ((t >> 8) & 0x7F80u) | ((t >> 16) & 0x8000u);
+// 4x4 byte transpose across the four lanes of a quad: lane i of the quad
+// holds row i (bytes j = 0..3) and ends with column i.
+__device__ __forceinline__ uint32_t quad_byte_transpose(uint32_t x, uint32_t lane) {
+  const uint32_t p1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  x = __builtin_amdgcn_perm(p1, x, (lane & 1u) ? 0x03070105u : 0x06020400u);
+  const uint32_t p2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  return __builtin_amdgcn_perm(p2, x, (lane & 2u) ? 0x03020706u : 0x05040100u);
+}
+
+// 8x8 bit-matrix transpose of a 64-bit word held as (lo, hi): bit c of byte
+// r moves to bit r of byte c.  Three rounds of delta swaps over 1x1, 2x2
+// and 4x4 sub-blocks (the recursive block transpose of Hacker's Delight,
+// section 7-3); the first two rounds stay inside each 32-bit half.  The
+// transpose is its own inverse.
+__device__ __forceinline__ void transpose8(uint32_t& lo, uint32_t& hi) {
+  uint32_t t;
+  t = (lo ^ (lo >> 7)) & 0x00AA00AAu; lo = lo ^ t ^ (t << 7);
+  t = (hi ^ (hi >> 7)) & 0x00AA00AAu; hi = hi ^ t ^ (t << 7);
+  t = (lo ^ (lo >> 14)) & 0x0000CCCCu; lo = lo ^ t ^ (t << 14);
+  t = (hi ^ (hi >> 14)) & 0x0000CCCCu; hi = hi ^ t ^ (t << 14);
+  t = (lo ^ (hi << 4)) & 0xF0F0F0F0u;
+  lo ^= t;
+  hi ^= t >> 4;
 }
 
 __device__ __forceinline__ uint32_t exp_lo(uint32_t w) { return (w >> 7) & 0xFFu; }
 __device__ __forceinline__ uint32_t exp_hi(uint32_t w) { return (w >> 23) & 0xFFu; }
 
+// Sign/fraction bytes of four bf16 (two words): byte = sign << 7 | fraction.
+__device__ __forceinline__ uint32_t sm_quad(uint32_t w0, uint32_t w1) {
+  const uint32_t lows = __builtin_amdgcn_perm(w1, w0, 0x06040200u);   // low byte of each element
+  const uint32_t highs = __builtin_amdgcn_perm(w1, w0, 0x07050301u);  // high byte of each element
+  return (lows & 0x7F7F7F7Fu) | (highs & 0x80808080u);
+}
+
+// Four bf16 rebuilt from their sign/fraction bytes S and exponent bytes E,
+// as two words (elements 0,1 and 2,3).
+__device__ __forceinline__ uint2 rebuild_quad(uint32_t S, uint32_t E) {
+  const uint32_t H = (S & 0x80808080u) | ((E >> 1) & 0x7F7F7F7Fu);   // sign, exponent bits 7..1
+  const uint32_t L = (S & 0x7F7F7F7Fu) | ((E << 7) & 0x80808080u);   // exponent bit 0, fraction
+  return make_uint2(__builtin_amdgcn_perm(H, L, 0x05010400u), __builtin_amdgcn_perm(H, L, 0x07030602u));
+}
+
 __device__ __forceinline__ uint32_t chunk_elem_word(const uint4& v, int i) {
   const uint32_t w = (i < 2) ? v.x : (i < 4) ? v.y : (i < 6) ? v.z : v.w;
   return (i & 1) ? (w >> 16) : (w & 0xFFFFu);
-}
-
-// Exponent histogram layout during planning: kHistCopies sub-histograms in
-// the (not yet used) staging buffer, lane l of every wave adding into copy
-// l % 32, two 16-bit bins per 32-bit word.  The odd word stride puts the
-// copies of one bin in different LDS banks, so the lanes of a wave that hold
-// the same exponent (most of them, for trained-model data) do not collide.
-constexpr uint32_t kHistCopies = 32;
-constexpr uint32_t kHistStride = 129;   // words per copy (128 + 1)
-
-// Inclusive wave64 prefix sum of four packed counters.
-__device__ __forceinline__ uint4 wave_incl_scan4(uint4 v) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t x = __shfl_up(v.x, d, 64), y = __shfl_up(v.y, d, 64);
-    const uint32_t z = __shfl_up(v.z, d, 64), w = __shfl_up(v.w, d, 64);
-    if (lane >= d) { v.x += x; v.y += y; v.z += z; v.w += w; }
-  }
-  return v;
 }
 
 __device__ __forceinline__ uint32_t field16(const uint4& v, int k) {
@@ -126,13 +157,14 @@ __device__ __forceinline__ uint32_t field16(const uint4& v, int k) {
 
 // Workgroup exclusive scan of per-(thread, k) counts cnt[k] (each <= 8) in
 // element index order (chunk c = t + 256k, so k-major, then thread).  Returns
-// for each k the number of counted elements before this thread's chunk k.
-// Counters travel as 16-bit fields, two per 32-bit lane of a uint4.
-__device__ __forceinline__ void block_excl_scan8(const uint32_t (&cnt)[kPer], uint32_t (&excl)[kPer],
-                                                 Smem& s) {
-  const uint4 mine = make_uint4(cnt[0] | (cnt[1] << 16), cnt[2] | (cnt[3] << 16),
-                                cnt[4] | (cnt[5] << 16), cnt[6] | (cnt[7] << 16));
-  const uint4 incl = wave_incl_scan4(mine);
+// for each k the number of counted elements before this thread's chunk k,
+// and the total.  Counters travel as 16-bit fields, two per 32-bit word.
+__device__ __forceinline__ uint32_t block_excl_scan8(const uint32_t (&cnt)[kPer], uint32_t (&excl)[kPer],
+                                                     Smem& s) {
+  const uint32_t m0 = cnt[0] | (cnt[1] << 16), m1 = cnt[2] | (cnt[3] << 16);
+  const uint32_t m2 = cnt[4] | (cnt[5] << 16), m3 = cnt[6] | (cnt[7] << 16);
+  const uint4 incl = make_uint4(wave_incl_scan(m0), wave_incl_scan(m1), wave_incl_scan(m2), wave_incl_scan(m3));
+  const uint4 mine = make_uint4(m0, m1, m2, m3);
   const int wave = threadIdx.x >> 6;
   if (__lane_id() == 63) {
     s.wsum[wave][0] = incl.x; s.wsum[wave][1] = incl.y;
@@ -153,6 +185,7 @@ __device__ __forceinline__ void block_excl_scan8(const uint32_t (&cnt)[kPer], ui
     excl[k] = base + field16(before, k) + in_wave;
     base += field16(total, k);
   }
+  return base;
 }
 
 // Loads a block's elements: thread t gets chunks t + 256k.  Elements at or
@@ -190,44 +223,50 @@ __device__ __forceinline__ void store_block(uint16_t* dst, uint32_t m, const uin
   }
 }
 
+// ---------------------------------------------------------------------------
+// encoding
+// ---------------------------------------------------------------------------
+
 // Phase 1 of encoding: histogram, ranking, the choice of b and the record
-// size.  Leaves code_of[] and the plan in LDS; returns the plan (uniform).
+// size.  Leaves code_of[] and the dictionary in LDS; returns the plan
+// (uniform).  Ends with a barrier.
 __device__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, Smem& s) {
-  const int t = threadIdx.x;
+  const uint32_t t = threadIdx.x, lane = __lane_id();
   Plan p;
   p.m = m;
   if (m != kB) {  // partial blocks travel raw
     p.mode = 0; p.b = 0; p.K = 0; p.n_esc = 0; p.rec_bytes = raw_bytes(m);
     return p;
   }
-  uint32_t* sub = reinterpret_cast<uint32_t*>(s.stage);
-  for (uint32_t i = t; i < kHistCopies * kHistStride; i += kThreads) sub[i] = 0;
+  uint32_t* sub = stage32(s);
+#pragma unroll
+  for (int i = 0; i < (int)(kHistCopies * 256 / 4 / kThreads); ++i) s.stage[t + kThreads * i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
   {
-    uint32_t* mine = sub + (__lane_id() & (kHistCopies - 1)) * kHistStride;
+    const uint32_t copy = lane & (kHistCopies - 1);
+    uint32_t* mine = sub + copy * 256;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t e0 = exp_lo(w4[q]), e1 = exp_hi(w4[q]);
-        atomicAdd(&mine[e0 >> 1], 1u << ((e0 & 1u) << 4));
-        atomicAdd(&mine[e1 >> 1], 1u << ((e1 & 1u) << 4));
+        atomicAdd(&mine[exp_lo(w4[q]) ^ copy], 1u);
+        atomicAdd(&mine[exp_hi(w4[q]) ^ copy], 1u);
       }
     }
   }
   __syncthreads();
   uint32_t cnt = 0;
 #pragma unroll 8
-  for (uint32_t c = 0; c < kHistCopies; ++c) cnt += (sub[c * kHistStride + (t >> 1)] >> ((t & 1) << 4)) & 0xFFFFu;
+  for (uint32_t c = 0; c < kHistCopies; ++c) cnt += sub[c * 256 + (t ^ c)];
   // Rank = position in (count desc, exponent asc).  Only exponents that occur
   // need comparisons: they are compacted into a short list of keys; an
   // exponent that never occurs ranks after all that do, in exponent order.
-  const uint32_t key = (cnt << 8) | (255u - (uint32_t)t);
+  const uint32_t key = (cnt << 8) | (255u - t);
   const uint64_t nzmask = __ballot(cnt > 0);
-  const uint32_t wave = (uint32_t)t >> 6;
-  const uint32_t below = (uint32_t)__popcll(nzmask & ((1ull << __lane_id()) - 1ull));
-  if (__lane_id() == 0) s.wsum[wave][0] = (uint32_t)__popcll(nzmask);
+  const uint32_t wave = t >> 6;
+  const uint32_t below = (uint32_t)__popcll(nzmask & ((1ull << lane) - 1ull));
+  if (lane == 0) s.wsum[wave][0] = (uint32_t)__popcll(nzmask);
   __syncthreads();
   uint32_t before = 0, nz_total = 0;
 #pragma unroll
@@ -244,102 +283,71 @@ __device__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, Smem& s) {
     rank = 0;
     for (uint32_t i = 0; i < nz_total; ++i) rank += s.key[i] > key;
   } else {
-    rank = nz_total + ((uint32_t)t - nz_below);
+    rank = nz_total + (t - nz_below);
   }
   s.cbr[rank] = cnt;
   __syncthreads();
-  if (t < 64) {
-    // cover(K) = sum of the K largest counts, K = 2^b - 1.  Lane l holds
-    // ranks 2l and 2l+1; after the inclusive scan S_l covers ranks <= 2l+1,
-    // and cover(2^b - 1) = S_l - cbr[2l+1] at lane l = 2^(b-1) - 1.
-    const uint32_t a = s.cbr[2 * t], bb = s.cbr[2 * t + 1];
-    uint32_t S = a + bb;
+  // cover(K) = sum of the K largest counts, K = 2^b - 1.  Lane l holds ranks
+  // 2l and 2l+1; after the inclusive scan S_l covers ranks <= 2l+1, and
+  // cover(2^b - 1) = S_l - cbr[2l+1] at lane l = 2^(b-1) - 1.  Every wave
+  // computes the same plan.
+  {
+    const uint32_t a = s.cbr[2 * lane], bb = s.cbr[2 * lane + 1];
+    const uint32_t cover = wave_incl_scan(a + bb) - bb;
+    uint32_t best = 0xFFFFFFFFu;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t x = __shfl_up(S, d, 64);
-      if (t >= d) S += x;
+    for (uint32_t b = 1; b <= 7; ++b) {
+      const uint32_t cov = __builtin_amdgcn_readlane(cover, (1 << (b - 1)) - 1);
+      const uint32_t size = coded_bytes(b, kB - cov);
+      const uint32_t cand = (size << 3) | b;
+      best = cand < best ? cand : best;
     }
-    const uint32_t cover = S - bb;
-    // candidate key: size, then b (so the smaller b wins a tie), then n_esc
-    uint64_t cand = ~0ull;
-    const uint32_t l1 = (uint32_t)t + 1;
-    if ((l1 & (l1 - 1)) == 0) {  // t = 2^(b-1) - 1 for b = 1..7
-      const uint32_t b = 32 - __clz(l1);
-      const uint32_t n_esc = kB - cover;
-      cand = ((uint64_t)coded_bytes(b, n_esc) << 32) | ((uint64_t)b << 24) | n_esc;
-    }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const uint64_t o = __shfl_xor(cand, d, 64);
-      cand = o < cand ? o : cand;
-    }
-    if (t == 0) {
-      const uint32_t size = (uint32_t)(cand >> 32);
-      const uint32_t b = (uint32_t)(cand >> 24) & 0xFFu;
-      const uint32_t n_esc = (uint32_t)cand & 0xFFFFFFu;
-      if (size < kRawFull) {
-        s.plan[0] = 1; s.plan[1] = b; s.plan[2] = (1u << b) - 1; s.plan[3] = n_esc; s.plan[4] = size;
-      } else {
-        s.plan[0] = 0; s.plan[1] = 0; s.plan[2] = 0; s.plan[3] = 0; s.plan[4] = kRawFull;
-      }
+    const uint32_t b = best & 7u, size = best >> 3;
+    if (size < kRawFull) {
+      p.mode = 1; p.b = b; p.K = (1u << b) - 1u;
+      p.n_esc = kB - __builtin_amdgcn_readlane(cover, (1 << (b - 1)) - 1);
+      p.rec_bytes = size;
+    } else {
+      p.mode = 0; p.b = 0; p.K = 0; p.n_esc = 0; p.rec_bytes = kRawFull;
     }
   }
-  __syncthreads();
-  p.mode = s.plan[0]; p.b = s.plan[1]; p.K = s.plan[2]; p.n_esc = s.plan[3]; p.rec_bytes = s.plan[4];
   if (p.mode == 1) {
     s.code_of[t] = (uint8_t)(rank < p.K ? rank : p.K);
-    if (rank < p.K) stage8(s)[16 + rank] = (uint8_t)t;        // dictionary entry
-    else if (rank < dict_bytes(p.b)) stage8(s)[16 + rank] = 0;  // dictionary padding
+    if (rank < dict_bytes(p.b)) stage8(s)[16 + rank] = rank < p.K ? (uint8_t)t : (uint8_t)0;
   }
   __syncthreads();
   return p;
 }
 
-// Phase 2 of encoding: writes the record for plan p into the LDS staging
-// buffer.  Ends with a barrier.
-__device__ void write_block(const uint4 (&v)[kPer], const Plan& p, Smem& s) {
-  const int t = threadIdx.x;
+// Writes the coded record of a block with B-bit codes into the staging
+// buffer (everything after the 16-byte header and the dictionary).
+template <int B>
+__device__ void write_coded(const uint4 (&v)[kPer], const Plan& p, Smem& s) {
+  constexpr uint32_t poff = planes_off(B), soff = sm_off(B), eoff = esc_off(B);
+  const uint32_t t = threadIdx.x, lane = __lane_id(), qi = lane & 3u;
   uint8_t* st = stage8(s);
-  if (t == 0) {
-    uint32_t* h = reinterpret_cast<uint32_t*>(st);
-    h[0] = p.mode | (p.b << 8);
-    h[1] = p.m;
-    h[2] = p.n_esc;
-    h[3] = p.rec_bytes;
-  }
-  if (p.mode == 0) {
-    const uint32_t n16 = (p.rec_bytes - 16u) / 16u;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const uint32_t c = t + kThreads * k;
-      if (c < n16) s.stage[1 + c] = v[k];
-    }
-    __syncthreads();
-    return;
-  }
-  const uint32_t b = p.b, K = p.K;
-  const uint32_t poff = planes_off(b), soff = sm_off(b), eoff = esc_off(b);
+  uint32_t* st32 = stage32(s);
   uint32_t escmask[kPer], cnt[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const uint32_t c = t + kThreads * k;
-    const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-    uint32_t lo = 0, hi = 0, em = 0;
+    const uint32_t w0 = v[k].x, w1 = v[k].y, w2 = v[k].z, w3 = v[k].w;
+    uint32_t lo = (uint32_t)s.code_of[exp_lo(w0)] | ((uint32_t)s.code_of[exp_hi(w0)] << 8) |
+                  ((uint32_t)s.code_of[exp_lo(w1)] << 16) | ((uint32_t)s.code_of[exp_hi(w1)] << 24);
+    uint32_t hi = (uint32_t)s.code_of[exp_lo(w2)] | ((uint32_t)s.code_of[exp_hi(w2)] << 8) |
+                  ((uint32_t)s.code_of[exp_lo(w3)] << 16) | ((uint32_t)s.code_of[exp_hi(w3)] << 24);
+    transpose8(lo, hi);  // now byte j of (lo, hi) = plane j of this chunk
+    uint32_t em = lo;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t c0 = s.code_of[exp_lo(w4[q])];
-      const uint32_t c1 = s.code_of[exp_hi(w4[q])];
-      em |= (uint32_t)(c0 == K) << (2 * q);
-      em |= (uint32_t)(c1 == K) << (2 * q + 1);
-      const uint32_t pair = c0 | (c1 << 8);
-      if (q < 2) lo |= pair << (16 * q);
-      else hi |= pair << (16 * (q - 2));
+    for (int j = 1; j < B; ++j) em &= (j < 4 ? lo >> (8 * j) : hi >> (8 * (j - 4)));
+    em &= 0xFFu;
+    const uint32_t col_lo = quad_byte_transpose(lo, lane);
+    if (qi < (uint32_t)B) st32[(poff + qi * kPlaneBytes + (c - qi)) >> 2] = col_lo;
+    if constexpr (B > 4) {
+      const uint32_t col_hi = quad_byte_transpose(hi, lane);
+      if (qi < (uint32_t)(B - 4)) st32[(poff + (4 + qi) * kPlaneBytes + (c - qi)) >> 2] = col_hi;
     }
-    const uint64_t planes = transpose8(((uint64_t)hi << 32) | lo);
-    for (uint32_t j = 0; j < b; ++j) st[poff + j * kPlaneBytes + c] = (uint8_t)(planes >> (8 * j));
-    const uint32_t sm01 = sm_pair(w4[0]) | (sm_pair(w4[1]) << 16);
-    const uint32_t sm23 = sm_pair(w4[2]) | (sm_pair(w4[3]) << 16);
-    *reinterpret_cast<uint2*>(st + soff + 8 * c) = make_uint2(sm01, sm23);
+    *reinterpret_cast<uint2*>(st + soff + 8 * c) = make_uint2(sm_quad(w0, w1), sm_quad(w2, w3));
     escmask[k] = em;
     cnt[k] = __popc(em);
   }
@@ -358,7 +366,38 @@ __device__ void write_block(const uint4 (&v)[kPer], const Plan& p, Smem& s) {
       }
     }
     const uint32_t pad_end = (p.n_esc + 15u) & ~15u;
-    if ((uint32_t)t < pad_end - p.n_esc) st[eoff + p.n_esc + t] = 0;
+    if (t < pad_end - p.n_esc) st[eoff + p.n_esc + t] = 0;
+  }
+}
+
+// Phase 2 of encoding: writes the record for plan p into the LDS staging
+// buffer.  Ends with a barrier.
+__device__ void write_block(const uint4 (&v)[kPer], const Plan& p, Smem& s) {
+  const uint32_t t = threadIdx.x;
+  if (t == 0) {
+    uint32_t* h = stage32(s);
+    h[0] = p.mode | (p.b << 8);
+    h[1] = p.m;
+    h[2] = p.n_esc;
+    h[3] = p.rec_bytes;
+  }
+  if (p.mode == 0) {
+    const uint32_t n16 = (p.rec_bytes - 16u) / 16u;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const uint32_t c = t + kThreads * k;
+      if (c < n16) s.stage[1 + c] = v[k];
+    }
+  } else {
+    switch (p.b) {
+      case 1: write_coded<1>(v, p, s); break;
+      case 2: write_coded<2>(v, p, s); break;
+      case 3: write_coded<3>(v, p, s); break;
+      case 4: write_coded<4>(v, p, s); break;
+      case 5: write_coded<5>(v, p, s); break;
+      case 6: write_coded<6>(v, p, s); break;
+      default: write_coded<7>(v, p, s); break;
+    }
   }
   __syncthreads();
 }
@@ -373,6 +412,86 @@ __device__ __forceinline__ void copy_out(const Smem& s, uint8_t* dst, uint32_t r
 __device__ __forceinline__ void copy_in(Smem& s, const uint8_t* src, uint32_t rec_bytes) {
   const uint32_t n16 = rec_bytes / 16u;
   for (uint32_t i = threadIdx.x; i < n16; i += kThreads) s.stage[i] = ld16(src + 16 * i);
+}
+
+// ---------------------------------------------------------------------------
+// decoding
+// ---------------------------------------------------------------------------
+
+// Exponents of four elements from their codes (one byte each, < 2^B); d holds
+// the first 16 dictionary bytes.
+template <int B>
+__device__ __forceinline__ uint32_t lookup4(uint32_t codes, const uint32_t (&d)[4], const uint8_t* dict) {
+  if constexpr (B <= 3) {
+    return __builtin_amdgcn_perm(d[1], d[0], codes);
+  } else if constexpr (B == 4) {
+    const uint32_t c7 = codes & 0x07070707u;
+    const uint32_t a = __builtin_amdgcn_perm(d[1], d[0], c7);
+    const uint32_t b = __builtin_amdgcn_perm(d[3], d[2], c7);
+    const uint32_t sel = ((codes >> 3) & 0x01010101u) * 0xFFu;
+    return (b & sel) | (a & ~sel);
+  } else {
+    return (uint32_t)dict[codes & 0xFFu] | ((uint32_t)dict[(codes >> 8) & 0xFFu] << 8) |
+           ((uint32_t)dict[(codes >> 16) & 0xFFu] << 16) | ((uint32_t)dict[codes >> 24] << 24);
+  }
+}
+
+template <int B>
+__device__ bool read_coded(Smem& s, uint32_t n_esc, uint4 (&v)[kPer]) {
+  constexpr uint32_t K = (1u << B) - 1u;
+  constexpr uint32_t poff = planes_off(B), soff = sm_off(B), eoff = esc_off(B);
+  const uint32_t t = threadIdx.x;
+  const uint8_t* st = stage8(s);
+  const uint32_t* st32 = stage32(s);
+  bool bad = false;
+  if (t >= K && t < dict_bytes(B)) bad |= st[16 + t] != 0;  // dictionary padding must be zero
+  const uint32_t d[4] = {st32[4], st32[5], st32[6], st32[7]};
+  uint32_t clo[kPer], chi[kPer], escmask[kPer], cnt[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const uint32_t c = t + kThreads * k;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const uint32_t byte = st[poff + j * kPlaneBytes + c];
+      if (j < 4) lo |= byte << (8 * j);
+      else hi |= byte << (8 * (j - 4));
+    }
+    uint32_t em = lo;
+#pragma unroll
+    for (int j = 1; j < B; ++j) em &= (j < 4 ? lo >> (8 * j) : hi >> (8 * (j - 4)));
+    em &= 0xFFu;
+    transpose8(lo, hi);  // now byte i of (lo, hi) = code of element i
+    clo[k] = lo;
+    chi[k] = hi;
+    escmask[k] = em;
+    cnt[k] = __popc(em);
+  }
+  uint32_t excl[kPer];
+  const uint32_t total = block_excl_scan8(cnt, excl, s);
+  const bool count_ok = total == n_esc;
+  const uint32_t pad_end = (n_esc + 15u) & ~15u;
+  if (t < pad_end - n_esc) bad |= st[eoff + n_esc + t] != 0;  // escape padding must be zero
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const uint32_t c = t + kThreads * k;
+    uint32_t E0 = lookup4<B>(clo[k], d, st + 16);
+    uint32_t E1 = lookup4<B>(chi[k], d, st + 16);
+    uint32_t em = escmask[k], pos = excl[k];
+    while (em) {  // escaped elements take their exponent from the escape plane
+      const int i = __ffs(em) - 1;
+      em &= em - 1;
+      const uint32_t e = (count_ok && pos < n_esc) ? st[eoff + pos] : 0u;
+      ++pos;
+      const uint32_t sh = 8u * (i & 3);
+      if (i < 4) E0 = (E0 & ~(0xFFu << sh)) | (e << sh);
+      else E1 = (E1 & ~(0xFFu << sh)) | (e << sh);
+    }
+    const uint2 smv = *reinterpret_cast<const uint2*>(st + soff + 8 * c);
+    const uint2 a = rebuild_quad(smv.x, E0), b = rebuild_quad(smv.y, E1);
+    v[k] = make_uint4(a.x, a.y, b.x, b.y);
+  }
+  return !__syncthreads_or(bad || !count_ok);
 }
 
 // Decodes the staged record (header already validated for mode, b, m,
@@ -405,65 +524,15 @@ __device__ bool read_block(Smem& s, uint32_t mode, uint32_t b, uint32_t m, uint3
     }
     return !any_bad;
   }
-  const uint32_t K = (1u << b) - 1u;
-  const uint32_t poff = planes_off(b), soff = sm_off(b), eoff = esc_off(b);
-  bool bad = false;
-  // dictionary padding must be zero
-  if ((uint32_t)t >= K && (uint32_t)t < dict_bytes(b)) bad |= st[16 + t] != 0;
-  uint32_t codes_lo[kPer], codes_hi[kPer], cnt[kPer];
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const uint32_t c = t + kThreads * k;
-    uint64_t x = 0;
-    for (uint32_t j = 0; j < b; ++j) x |= (uint64_t)st[poff + j * kPlaneBytes + c] << (8 * j);
-    const uint64_t codes = transpose8(x);
-    codes_lo[k] = (uint32_t)codes;
-    codes_hi[k] = (uint32_t)(codes >> 32);
-    uint32_t n = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      n += ((codes_lo[k] >> (8 * i)) & 0xFFu) == K;
-      n += ((codes_hi[k] >> (8 * i)) & 0xFFu) == K;
-    }
-    cnt[k] = n;
+  switch (b) {
+    case 1: return read_coded<1>(s, n_esc, v);
+    case 2: return read_coded<2>(s, n_esc, v);
+    case 3: return read_coded<3>(s, n_esc, v);
+    case 4: return read_coded<4>(s, n_esc, v);
+    case 5: return read_coded<5>(s, n_esc, v);
+    case 6: return read_coded<6>(s, n_esc, v);
+    default: return read_coded<7>(s, n_esc, v);
   }
-  uint32_t excl[kPer];
-  block_excl_scan8(cnt, excl, s);
-  // total escapes = excl of the last chunk of the last thread + its count
-  uint32_t total = 0;
-  if (t == kThreads - 1) total = excl[kPer - 1] + cnt[kPer - 1];
-  if (t == kThreads - 1) s.plan[7] = total;
-  // escape padding must be zero
-  const uint32_t pad_end = (n_esc + 15u) & ~15u;
-  if ((uint32_t)t < pad_end - n_esc) bad |= st[eoff + n_esc + t] != 0;
-  __syncthreads();
-  const bool count_ok = s.plan[7] == n_esc;
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const uint32_t c = t + kThreads * k;
-    const uint2 smv = *reinterpret_cast<const uint2*>(st + soff + 8 * c);
-    uint32_t pos = excl[k];
-    uint32_t w4[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t cw = q < 2 ? codes_lo[k] : codes_hi[k];
-      const uint32_t code0 = (cw >> (16 * (q & 1))) & 0xFFu;
-      const uint32_t code1 = (cw >> (16 * (q & 1) + 8)) & 0xFFu;
-      uint32_t e0, e1;
-      if (code0 == K) { e0 = (count_ok && pos < n_esc) ? st[eoff + pos] : 0; ++pos; }
-      else e0 = st[16 + code0];
-      if (code1 == K) { e1 = (count_ok && pos < n_esc) ? st[eoff + pos] : 0; ++pos; }
-      else e1 = st[16 + code1];
-      const uint32_t smw = (q < 2 ? smv.x : smv.y) >> (16 * (q & 1));
-      const uint32_t s0 = smw & 0xFFu, s1 = (smw >> 8) & 0xFFu;
-      const uint32_t lo = ((s0 & 0x80u) << 8) | (e0 << 7) | (s0 & 0x7Fu);
-      const uint32_t hi = ((s1 & 0x80u) << 8) | (e1 << 7) | (s1 & 0x7Fu);
-      w4[q] = lo | (hi << 16);
-    }
-    v[k] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-  }
-  const bool any_bad = __syncthreads_or(bad || !count_ok);
-  return !any_bad;
 }
 
 }  // namespace codec

@@ -105,25 +105,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const Plan p = plan_block(v, m, s);
   if (t == 0) publish(&ws->desc[bid], (bid == 0 ? kFlagIncl : kFlagAgg) | p.rec_bytes);
   write_block(v, p, s);
-  if (t == 0) {
+  if (t < 64) {
+    // Decoupled look-back, one wave wide: lane l reads the descriptor of block
+    // bid-1-l.  The nearest predecessor with an inclusive prefix ends the walk;
+    // the aggregates of the blocks between add to it.  A window with an
+    // unpublished descriptor before that point is read again (bounded).
+    const uint32_t lane = t;
     uint64_t excl = 0;
-    for (int64_t j = (int64_t)bid - 1; j >= 0; --j) {
-      uint64_t d = peek(&ws->desc[j]);
-      uint32_t spins = 0;
-      while ((d >> 62) == 0 && spins < kSpinLimit) {
+    int64_t base = (int64_t)bid - 1;
+    uint32_t spins = 0;
+    while (base >= 0) {
+      const int64_t j = base - (int64_t)lane;
+      const uint64_t d = j >= 0 ? peek(&ws->desc[j]) : kFlagIncl;
+      const uint64_t incl_mask = __ballot((d >> 62) == 2);
+      const uint64_t zero_mask = __ballot((d >> 62) == 0);
+      const int first = incl_mask ? __ffsll((unsigned long long)incl_mask) - 1 : 64;
+      const uint64_t need = first == 64 ? ~0ull : ((2ull << first) - 1ull);
+      if (zero_mask & need) {
+        if (++spins >= kSpinLimit) {  // a predecessor never published: give up, flag it
+          if (lane == 0) atomicExch(&ws->error, 1u);
+          break;
+        }
         __builtin_amdgcn_s_sleep(1);
-        d = peek(&ws->desc[j]);
-        ++spins;
+        continue;
       }
-      if ((d >> 62) == 0) {  // a predecessor never published: give up, flag it
-        atomicExch(&ws->error, 1u);
+      uint32_t agg = (int)lane < first ? (uint32_t)(d & kValueMask) : 0u;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) agg += __shfl_xor(agg, o, 64);
+      excl += agg;
+      if (first < 64) {
+        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)d, first);
+        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(d >> 32), first);
+        excl += (((uint64_t)hi << 32) | lo) & kValueMask;
         break;
       }
-      excl += d & kValueMask;
-      if ((d >> 62) == 2) break;
+      base -= 64;
     }
-    if (bid != 0) publish(&ws->desc[bid], kFlagIncl | (excl + p.rec_bytes));
-    s.misc[0] = excl;
+    if (lane == 0) {
+      if (bid != 0) publish(&ws->desc[bid], kFlagIncl | (excl + p.rec_bytes));
+      s.misc[0] = excl;
+    }
   }
   __syncthreads();
   const uint64_t off = header_bytes(nb) + s.misc[0];
@@ -139,35 +160,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 }
 
 // Validates the stream header and the record of block bid; on success fills
-// the record fields.  Thread 0 only.
+// the record fields.  Thread 0 only.  The header, both offsets and the record
+// header are fetched with two rounds of independent loads.
 __device__ bool check_record(const uint8_t* in, uint64_t in_bytes, uint64_t n, uint32_t nb, uint32_t bid,
                              uint32_t* mode, uint32_t* b, uint32_t* n_esc, uint32_t* rec_bytes,
                              uint64_t* off_out) {
   const uint64_t hdr = header_bytes(nb);
   if (in_bytes < hdr) return false;
-  const uint32_t* h = reinterpret_cast<const uint32_t*>(in);
-  if (h[0] != kMagic || h[1] != kB || *reinterpret_cast<const uint64_t*>(in + 8) != n || h[4] != nb || h[5] != 0)
-    return false;
-  const uint64_t total = *reinterpret_cast<const uint64_t*>(in + 24);
-  if (total > in_bytes || total < hdr) return false;
-  if (bid == 0 && (nb & 1u) && *reinterpret_cast<const uint64_t*>(in + 32 + 8ull * nb) != 0) return false;
   const uint64_t* offs = reinterpret_cast<const uint64_t*>(in + 32);
+  const uint4 h0 = ld16(in), h1 = ld16(in + 16);
   const uint64_t off = offs[bid];
-  const uint64_t next = bid + 1 < nb ? offs[bid + 1] : total;
-  if (bid == 0 && off != hdr) return false;
-  if ((off & 15u) || off < hdr || off + 16 > total || next > total || next < off) return false;
-  const uint8_t* rec = in + off;
-  const uint32_t* r = reinterpret_cast<const uint32_t*>(rec);
-  const uint32_t md = rec[0], bb = rec[1], reserved = r[0] >> 16, rm = r[1], ne = r[2], rb = r[3];
+  const uint64_t next_off = bid + 1 < nb ? offs[bid + 1] : 0;
+  const uint64_t pad = (bid == 0 && (nb & 1u)) ? offs[nb] : 0;
+  const uint64_t hn = ((uint64_t)h0.w << 32) | h0.z;
+  const uint64_t total = ((uint64_t)h1.w << 32) | h1.z;
+  const uint64_t next = bid + 1 < nb ? next_off : total;
+  bool ok = h0.x == kMagic && h0.y == kB && hn == n && h1.x == nb && h1.y == 0 && total <= in_bytes &&
+            total >= hdr && pad == 0 && (bid != 0 || off == hdr) && (off & 15u) == 0 && off >= hdr &&
+            off + 16 <= total && next <= total && next >= off;
+  if (!ok) return false;
+  const uint4 r = ld16(in + off);
+  const uint32_t md = r.x & 0xFFu, bb = (r.x >> 8) & 0xFFu, reserved = r.x >> 16, rm = r.y, ne = r.z, rb = r.w;
   const uint32_t m = (uint32_t)(((uint64_t)bid + 1) * kB <= n ? kB : n - (uint64_t)bid * kB);
-  if (reserved != 0 || rm != m || off + rb != next) return false;
-  if (md == 0) {
-    if (bb != 0 || ne != 0 || rb != raw_bytes(m)) return false;
-  } else if (md == 1) {
-    if (m != kB || bb < 1 || bb > 7 || ne > kB || rb != coded_bytes(bb, ne)) return false;
-  } else {
-    return false;
-  }
+  ok = reserved == 0 && rm == m && off + rb == next &&
+       ((md == 0 && bb == 0 && ne == 0 && rb == raw_bytes(m)) ||
+        (md == 1 && m == kB && bb >= 1 && bb <= 7 && ne <= kB && rb == coded_bytes(bb, ne)));
+  if (!ok) return false;
   *mode = md; *b = bb; *n_esc = ne; *rec_bytes = rb; *off_out = off;
   return true;
 }
