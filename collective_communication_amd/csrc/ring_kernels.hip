@@ -7,12 +7,12 @@
 // it (recv) during all-gather.  "CCCL: In-GPU Compression-Coupled
 // Collective Communication" (Figure 2, section 5) shows NCCL's version moving
 // 16-byte packs; here every lane moves 16-byte vectors too (4 fp32 or 8
-// bf16), four of them per operand in flight, so a wave64 issues fully
-// coalesced 1 KB loads.  Both kernels are HBM bound: a reduce hop reads 2
+// bf16), two of them per operand in flight, so a wave64 issues fully
+// coalesced 1 KB loads, marked non-temporal.  Both kernels are HBM bound: a reduce hop reads 2
 // and writes 1 element per element of the step, a copy hop reads 1, writes 1.
 //
 // One launch covers one whole ring step: up to 64 segments (one per
-// receiver), cut into 8192-element (bf16) / 4096-element (fp32) tiles, one
+// receiver), cut into 4096-element (bf16) / 2048-element (fp32) tiles, one
 // tile per workgroup, or a persistent grid-stride loop when the caller gives
 // a CU budget.
 #include "common.hpp"
@@ -21,7 +21,48 @@
 namespace hc {
 namespace {
 
-constexpr int kUnroll = 4;
+// Tuning knobs (compile-time).  Measured on MI355X for R=8 x 2^26 bf16: two
+// 16-byte vectors per operand per lane and non-temporal loads give the
+// fastest hops; the non-temporal hint matters on the received operand,
+// whose lines would otherwise push the partials that the next step reads
+// out of the caches.  Non-temporal stores are slower (the next hop reads
+// what this one writes).
+#ifndef HC_RING_UNROLL
+#define HC_RING_UNROLL 2
+#endif
+#ifndef HC_RING_NT_LOAD
+#define HC_RING_NT_LOAD 1
+#endif
+#ifndef HC_RING_NT_A
+#define HC_RING_NT_A HC_RING_NT_LOAD
+#endif
+#ifndef HC_RING_NT_B
+#define HC_RING_NT_B HC_RING_NT_LOAD
+#endif
+#ifndef HC_RING_NT_STORE
+#define HC_RING_NT_STORE 0
+#endif
+constexpr int kUnroll = HC_RING_UNROLL;  // 16-byte vectors per operand in flight per lane
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ uint4 ld_stream(const char* p) {
+  if constexpr (NT) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return ld16(p);
+  }
+}
+__device__ __forceinline__ void st_stream(char* p, uint4 v) {
+  if constexpr (HC_RING_NT_STORE) {
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+  } else {
+    st16(p, v);
+  }
+}
 
 struct SegArgs {
   const void* a[kMaxSegs];
@@ -85,14 +126,14 @@ __global__ __launch_bounds__(kThreads) void step_kernel(SegArgs args) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const uint64_t off = (base + (uint64_t)(u * kThreads + tid) * V) * ES;
-        va[u] = ld16(pa + off);
-        if constexpr (REDUCE) vb[u] = ld16(pb + off);
+        va[u] = ld_stream<HC_RING_NT_A>(pa + off);
+        if constexpr (REDUCE) vb[u] = ld_stream<HC_RING_NT_B>(pb + off);
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const uint64_t off = (base + (uint64_t)(u * kThreads + tid) * V) * ES;
-        if constexpr (REDUCE) st16(pd + off, vec_hop<ES>(va[u], vb[u]));
-        else st16(pd + off, va[u]);
+        if constexpr (REDUCE) st_stream(pd + off, vec_hop<ES>(va[u], vb[u]));
+        else st_stream(pd + off, va[u]);
       }
     } else {
       const uint64_t end = base + kTile < len ? base + kTile : len;
