@@ -278,13 +278,15 @@ __device__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, Smem& s) {
   const uint32_t nz_below = before + below;
   if (cnt > 0) s.key[nz_below] = key;
   __syncthreads();
-  uint32_t rank;
-  if (cnt > 0) {
-    rank = 0;
-    for (uint32_t i = 0; i < nz_total; ++i) rank += s.key[i] > key;
-  } else {
-    rank = nz_total + (t - nz_below);
+  // Each wave holds up to 64 of the compacted keys in registers and walks
+  // them with readlane, so the comparisons wait on no memory.
+  uint32_t rank = 0;
+  for (uint32_t base = 0; base < nz_total; base += 64) {
+    const uint32_t kr = base + lane < nz_total ? s.key[base + lane] : 0u;
+    const uint32_t lim = nz_total - base < 64u ? nz_total - base : 64u;
+    for (uint32_t j = 0; j < lim; ++j) rank += __builtin_amdgcn_readlane(kr, j) > key;
   }
+  if (cnt == 0) rank = nz_total + (t - nz_below);
   s.cbr[rank] = cnt;
   __syncthreads();
   // cover(K) = sum of the K largest counts, K = 2^b - 1.  Lane l holds ranks

@@ -159,12 +159,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   }
 }
 
-// Validates the stream header and the record of block bid; on success fills
-// the record fields.  Thread 0 only.  The header, both offsets and the record
-// header are fetched with two rounds of independent loads.
-__device__ bool check_record(const uint8_t* in, uint64_t in_bytes, uint64_t n, uint32_t nb, uint32_t bid,
-                             uint32_t* mode, uint32_t* b, uint32_t* n_esc, uint32_t* rec_bytes,
-                             uint64_t* off_out) {
+// Validates the stream header and the offsets of block bid; on success
+// returns the record's offset and length (next offset minus this one).
+// Thread 0 only; all loads are independent, one round trip.
+__device__ bool check_stream(const uint8_t* in, uint64_t in_bytes, uint64_t n, uint32_t nb, uint32_t bid,
+                             uint64_t* off_out, uint32_t* len_out) {
   const uint64_t hdr = header_bytes(nb);
   if (in_bytes < hdr) return false;
   const uint64_t* offs = reinterpret_cast<const uint64_t*>(in + 32);
@@ -175,32 +174,40 @@ __device__ bool check_record(const uint8_t* in, uint64_t in_bytes, uint64_t n, u
   const uint64_t hn = ((uint64_t)h0.w << 32) | h0.z;
   const uint64_t total = ((uint64_t)h1.w << 32) | h1.z;
   const uint64_t next = bid + 1 < nb ? next_off : total;
-  bool ok = h0.x == kMagic && h0.y == kB && hn == n && h1.x == nb && h1.y == 0 && total <= in_bytes &&
-            total >= hdr && pad == 0 && (bid != 0 || off == hdr) && (off & 15u) == 0 && off >= hdr &&
-            off + 16 <= total && next <= total && next >= off;
-  if (!ok) return false;
-  const uint4 r = ld16(in + off);
-  const uint32_t md = r.x & 0xFFu, bb = (r.x >> 8) & 0xFFu, reserved = r.x >> 16, rm = r.y, ne = r.z, rb = r.w;
-  const uint32_t m = (uint32_t)(((uint64_t)bid + 1) * kB <= n ? kB : n - (uint64_t)bid * kB);
-  ok = reserved == 0 && rm == m && off + rb == next &&
-       ((md == 0 && bb == 0 && ne == 0 && rb == raw_bytes(m)) ||
-        (md == 1 && m == kB && bb >= 1 && bb <= 7 && ne <= kB && rb == coded_bytes(bb, ne)));
-  if (!ok) return false;
-  *mode = md; *b = bb; *n_esc = ne; *rec_bytes = rb; *off_out = off;
-  return true;
+  const bool ok = h0.x == kMagic && h0.y == kB && hn == n && h1.x == nb && h1.y == 0 && total <= in_bytes &&
+                  total >= hdr && pad == 0 && (bid != 0 || off == hdr) && (off & 15u) == 0 && off >= hdr &&
+                  next <= total && next >= off + 16 && next - off <= kRawFull && ((next - off) & 15u) == 0;
+  *off_out = off;
+  *len_out = ok ? (uint32_t)(next - off) : 0u;
+  return ok;
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void decompress_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes,
-                                                              uint16_t* __restrict__ out, uint64_t n,
-                                                              int32_t* __restrict__ status, uint32_t nb) {
+// Validates a staged record header against the format for a block of m
+// elements and the record length len.  Thread 0 only.
+__device__ bool check_record_header(const Smem& s, uint32_t m, uint32_t len, uint32_t* mode, uint32_t* b,
+                                    uint32_t* n_esc) {
+  const uint4 r = s.stage[0];
+  const uint32_t md = r.x & 0xFFu, bb = (r.x >> 8) & 0xFFu, reserved = r.x >> 16, rm = r.y, ne = r.z, rb = r.w;
+  const bool ok = reserved == 0 && rm == m && rb == len &&
+                  ((md == 0 && bb == 0 && ne == 0 && rb == raw_bytes(m)) ||
+                   (md == 1 && m == kB && bb >= 1 && bb <= 7 && ne <= kB && rb == coded_bytes(bb, ne)));
+  *mode = md; *b = bb; *n_esc = ne;
+  return ok;
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void decompress_kernel(
+    const uint8_t* __restrict__ in, uint64_t in_bytes, uint16_t* __restrict__ out, uint64_t n,
+    int32_t* __restrict__ status, uint32_t nb) {
   __shared__ Smem s;
   const int t = threadIdx.x;
   const uint32_t bid = blockIdx.x;
+  const uint64_t first = (uint64_t)bid * kB;
+  const uint32_t m = (uint32_t)((n - first) < kB ? (n - first) : kB);
   if (t == 0) {
-    uint32_t mode = 0, b = 0, n_esc = 0, rb = 0;
     uint64_t off = 0;
-    const bool ok = check_record(in, in_bytes, n, nb, bid, &mode, &b, &n_esc, &rb, &off);
-    s.plan[0] = ok; s.plan[1] = mode; s.plan[2] = b; s.plan[3] = n_esc; s.plan[4] = rb;
+    uint32_t len = 0;
+    s.plan[0] = check_stream(in, in_bytes, n, nb, bid, &off, &len);
+    s.plan[4] = len;
     s.misc[0] = off;
   }
   __syncthreads();
@@ -208,13 +215,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (t == 0) atomicExch(status, (int32_t)HC_ERR_CORRUPT_STREAM);
     return;
   }
-  const uint32_t mode = s.plan[1], b = s.plan[2], n_esc = s.plan[3], rb = s.plan[4];
-  const uint64_t first = (uint64_t)bid * kB;
-  const uint32_t m = (uint32_t)((n - first) < kB ? (n - first) : kB);
-  copy_in(s, in + s.misc[0], rb);
+  const uint32_t len = s.plan[4];
+  copy_in(s, in + s.misc[0], len);  // the whole record, its header included
   __syncthreads();
+  if (t == 0) {
+    uint32_t mode = 0, b = 0, n_esc = 0;
+    s.plan[0] = check_record_header(s, m, len, &mode, &b, &n_esc);
+    s.plan[1] = mode; s.plan[2] = b; s.plan[3] = n_esc;
+  }
+  __syncthreads();
+  if (!s.plan[0]) {
+    if (t == 0) atomicExch(status, (int32_t)HC_ERR_CORRUPT_STREAM);
+    return;
+  }
   uint4 v[kPer];
-  const bool ok = read_block(s, mode, b, m, n_esc, rb, v);
+  const bool ok = read_block(s, s.plan[1], s.plan[2], m, s.plan[3], len, v);
   if (!ok) {
     if (t == 0) atomicExch(status, (int32_t)HC_ERR_CORRUPT_STREAM);
     return;
