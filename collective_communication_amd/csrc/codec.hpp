@@ -17,9 +17,10 @@
 // moves and two v_perm_b32) turns their plane bytes into one 32-bit LDS
 // store per plane.  The record is assembled in LDS (<= 32784 bytes) and
 // leaves with 16-byte stores.
-//   histogram : LDS atomics into 32 sub-histograms (lane l adds into copy
-//               l % 32, bin e at word e ^ copy so equal exponents of
-//               different lanes land in different banks), held in the
+//   histogram : LDS atomics into 32 sub-histograms laid out bin-major
+//               (lane l adds into copy l % 32, word 32e + copy, so the lanes
+//               of a half-wave never share a bank and the address comes
+//               straight out of the bf16 word with one AND-OR), held in the
 //               staging buffer before the record needs it
 //   ranking   : occurring exponents are compacted (ballot + popcount) and
 //               each ranks itself against that short list of keys (count
@@ -46,7 +47,7 @@ constexpr uint32_t kPlaneBytes = kB / 8;        // one code plane
 constexpr uint32_t kRawFull = 16 + 2 * kB;      // raw record of a full block
 constexpr uint32_t kStage16 = kRawFull / 16;    // 2049 uint4 of LDS staging
 constexpr uint32_t kMagic = 0x315A4348u;
-constexpr uint32_t kHistCopies = 32;            // 32 x 256 words = 32 KB of staging
+constexpr uint32_t kHistCopies = 32;            // 256 bins x 32 words = 32 KB of staging
 
 struct Plan {
   uint32_t mode;       // 0 raw, 1 coded
@@ -58,7 +59,8 @@ struct Plan {
 };
 
 struct Smem {
-  uint4 stage[kStage16];         // the record being built or read
+  uint4 stage[kStage16 + 1];     // the record being built or read, plus a spare vector that
+                                 // the decoder's 12-byte escape window may touch
   uint32_t key[256];             // (count << 8) | (255 - exponent) of occurring exponents
   uint32_t cbr[256];             // count by rank
   uint8_t code_of[256];          // exponent -> code
@@ -130,6 +132,13 @@ __device__ __forceinline__ void transpose8(uint32_t& lo, uint32_t& hi) {
 __device__ __forceinline__ uint32_t exp_lo(uint32_t w) { return (w >> 7) & 0xFFu; }
 __device__ __forceinline__ uint32_t exp_hi(uint32_t w) { return (w >> 23) & 0xFFu; }
 
+// Exponent bytes of four bf16 (two words), in element order.  Shifting a
+// word left by one puts the exponent of its low element in byte 1 and that
+// of its high element in byte 3.
+__device__ __forceinline__ uint32_t exps4(uint32_t w0, uint32_t w1) {
+  return __builtin_amdgcn_perm(w1 << 1, w0 << 1, 0x07050301u);
+}
+
 // Sign/fraction bytes of four bf16 (two words): byte = sign << 7 | fraction.
 __device__ __forceinline__ uint32_t sm_quad(uint32_t w0, uint32_t w1) {
   const uint32_t lows = __builtin_amdgcn_perm(w1, w0, 0x06040200u);   // low byte of each element
@@ -155,12 +164,21 @@ __device__ __forceinline__ uint32_t field16(const uint4& v, int k) {
   return (k & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
-// Workgroup exclusive scan of per-(thread, k) counts cnt[k] (each <= 8) in
-// element index order (chunk c = t + 256k, so k-major, then thread).  Returns
-// for each k the number of counted elements before this thread's chunk k,
+// Escape masks of a thread's eight chunks, one byte each, packed in two
+// words: chunk k in byte k % 4 of word k / 4.
+__device__ __forceinline__ uint32_t mask_of(const uint32_t (&em)[2], int k) {
+  return (em[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+}
+
+// Workgroup exclusive scan of the escape counts popc(mask k) (each <= 8) in
+// element index order (chunk c = t + 256k, so k-major, then thread).
+// Returns for each k the number of escapes before this thread's chunk k,
 // and the total.  Counters travel as 16-bit fields, two per 32-bit word.
-__device__ __forceinline__ uint32_t block_excl_scan8(const uint32_t (&cnt)[kPer], uint32_t (&excl)[kPer],
+__device__ __forceinline__ uint32_t block_excl_scan8(const uint32_t (&em)[2], uint32_t (&excl)[kPer],
                                                      Smem& s) {
+  uint32_t cnt[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) cnt[k] = __popc(mask_of(em, k));
   const uint32_t m0 = cnt[0] | (cnt[1] << 16), m1 = cnt[2] | (cnt[3] << 16);
   const uint32_t m2 = cnt[4] | (cnt[5] << 16), m3 = cnt[6] | (cnt[7] << 16);
   const uint4 incl = make_uint4(wave_incl_scan(m0), wave_incl_scan(m1), wave_incl_scan(m2), wave_incl_scan(m3));
@@ -201,10 +219,43 @@ __device__ __forceinline__ void load_block(const uint16_t* src, uint32_t m, uint
   for (int k = 0; k < kPer; ++k) {
     const uint32_t e0 = 8u * (t + kThreads * k);
     uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
     for (uint32_t i = 0; i < 8; ++i)
       if (e0 + i < m) w[i >> 1] |= (uint32_t)src[e0 + i] << (16 * (i & 1));
     v[k] = make_uint4(w[0], w[1], w[2], w[3]);
   }
+}
+
+// Loads a block's elements into the staging buffer, chunk c at stage[c]: a
+// full block with direct global->LDS 16-byte loads (each wave instruction
+// fills 1 KB of LDS from 64 consecutive chunks and holds no registers), a
+// partial one element by element with zeros past m.  Ends with a barrier.
+__device__ __forceinline__ void load_block_lds(const uint16_t* src, uint32_t m, Smem& s) {
+  const uint32_t t = threadIdx.x;
+  if (m == kB) {
+    const uint32_t lane = __lane_id(), wave = t >> 6;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const uint32_t c0 = kThreads * k + 64u * wave;  // first chunk of this wave's 1 KB
+      __builtin_amdgcn_global_load_lds(src + 8 * (c0 + lane),
+                                       (__attribute__((address_space(3))) void*)&s.stage[c0], 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // LDS DMA completes on the vector memory counter
+  } else {
+    uint4 one[1];
+#pragma unroll 1
+    for (int k = 0; k < kPer; ++k) {
+      const uint32_t c = t + kThreads * k;
+      const uint32_t e0 = 8u * c;
+      uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (uint32_t i = 0; i < 8; ++i)
+        if (e0 + i < m) w[i >> 1] |= (uint32_t)src[e0 + i] << (16 * (i & 1));
+      one[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      s.stage[c] = one[0];
+    }
+  }
+  __syncthreads();
 }
 
 // Stores a block's elements (first m only).
@@ -218,6 +269,7 @@ __device__ __forceinline__ void store_block(uint16_t* dst, uint32_t m, const uin
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const uint32_t e0 = 8u * (t + kThreads * k);
+#pragma unroll
     for (uint32_t i = 0; i < 8; ++i)
       if (e0 + i < m) dst[e0 + i] = (uint16_t)chunk_elem_word(v[k], (int)i);
   }
@@ -230,7 +282,7 @@ __device__ __forceinline__ void store_block(uint16_t* dst, uint32_t m, const uin
 // Phase 1 of encoding: histogram, ranking, the choice of b and the record
 // size.  Leaves code_of[] and the dictionary in LDS; returns the plan
 // (uniform).  Ends with a barrier.
-__device__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, Smem& s) {
+__device__ __forceinline__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, Smem& s) {
   const uint32_t t = threadIdx.x, lane = __lane_id();
   Plan p;
   p.m = m;
@@ -238,27 +290,36 @@ __device__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, Smem& s) {
     p.mode = 0; p.b = 0; p.K = 0; p.n_esc = 0; p.rec_bytes = raw_bytes(m);
     return p;
   }
-  uint32_t* sub = stage32(s);
+  // 32 sub-histograms, bin-major: the count of exponent e in copy c is word
+  // 32e + c.  Lane l adds into copy l % 32, so the 32 lanes of a half-wave
+  // always hit 32 different banks, and the byte address of bin e is e << 7
+  // OR c << 2: for the low element of a word that is the word ANDed with
+  // 0x7F80 (its exponent field already sits at bit 7).
+  uint8_t* sub8 = stage8(s);
 #pragma unroll
   for (int i = 0; i < (int)(kHistCopies * 256 / 4 / kThreads); ++i) s.stage[t + kThreads * i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
   {
-    const uint32_t copy = lane & (kHistCopies - 1);
-    uint32_t* mine = sub + copy * 256;
+    const uint32_t c4 = (lane & (kHistCopies - 1)) << 2;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        atomicAdd(&mine[exp_lo(w4[q]) ^ copy], 1u);
-        atomicAdd(&mine[exp_hi(w4[q]) ^ copy], 1u);
+        atomicAdd(reinterpret_cast<uint32_t*>(sub8 + ((w4[q] & 0x7F80u) | c4)), 1u);
+        atomicAdd(reinterpret_cast<uint32_t*>(sub8 + (((w4[q] >> 16) & 0x7F80u) | c4)), 1u);
       }
     }
   }
   __syncthreads();
+  // Thread t sums the 32 copies of bin t: eight 16-byte reads, started at a
+  // different quad in each group of eight lanes to spread the banks.
   uint32_t cnt = 0;
-#pragma unroll 8
-  for (uint32_t c = 0; c < kHistCopies; ++c) cnt += sub[c * 256 + (t ^ c)];
+#pragma unroll
+  for (uint32_t i = 0; i < 8; ++i) {
+    const uint4 q = s.stage[t * 8 + ((i + t) & 7u)];
+    cnt += q.x + q.y + q.z + q.w;
+  }
   // Rank = position in (count desc, exponent asc).  Only exponents that occur
   // need comparisons: they are compacted into a short list of keys; an
   // exponent that never occurs ranks after all that do, in exponent order.
@@ -279,9 +340,10 @@ __device__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, Smem& s) {
   if (cnt > 0) s.key[nz_below] = key;
   __syncthreads();
   // Each wave holds up to 64 of the compacted keys in registers and walks
-  // them with readlane, so the comparisons wait on no memory.
+  // them with readlane, so the comparisons wait on no memory.  A wave whose
+  // exponents all have count 0 needs no comparison.
   uint32_t rank = 0;
-  for (uint32_t base = 0; base < nz_total; base += 64) {
+  for (uint32_t base = 0; nzmask != 0 && base < nz_total; base += 64) {  // waves without one skip
     const uint32_t kr = base + lane < nz_total ? s.key[base + lane] : 0u;
     const uint32_t lim = nz_total - base < 64u ? nz_total - base : 64u;
     for (uint32_t j = 0; j < lim; ++j) rank += __builtin_amdgcn_readlane(kr, j) > key;
@@ -324,12 +386,12 @@ __device__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, Smem& s) {
 // Writes the coded record of a block with B-bit codes into the staging
 // buffer (everything after the 16-byte header and the dictionary).
 template <int B>
-__device__ void write_coded(const uint4 (&v)[kPer], const Plan& p, Smem& s) {
+__device__ __forceinline__ void write_coded(const uint4 (&v)[kPer], const Plan& p, Smem& s) {
   constexpr uint32_t poff = planes_off(B), soff = sm_off(B), eoff = esc_off(B);
   const uint32_t t = threadIdx.x, lane = __lane_id(), qi = lane & 3u;
   uint8_t* st = stage8(s);
   uint32_t* st32 = stage32(s);
-  uint32_t escmask[kPer], cnt[kPer];
+  uint32_t escmask[2] = {0, 0};
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const uint32_t c = t + kThreads * k;
@@ -350,21 +412,21 @@ __device__ void write_coded(const uint4 (&v)[kPer], const Plan& p, Smem& s) {
       if (qi < (uint32_t)(B - 4)) st32[(poff + (4 + qi) * kPlaneBytes + (c - qi)) >> 2] = col_hi;
     }
     *reinterpret_cast<uint2*>(st + soff + 8 * c) = make_uint2(sm_quad(w0, w1), sm_quad(w2, w3));
-    escmask[k] = em;
-    cnt[k] = __popc(em);
+    escmask[k >> 2] |= em << (8 * (k & 3));
   }
   if (p.n_esc) {
     uint32_t excl[kPer];
-    block_excl_scan8(cnt, excl, s);
+    block_excl_scan8(escmask, excl, s);
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-      uint32_t em = escmask[k], pos = excl[k];
-      const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-      while (em) {
-        const int i = __ffs(em) - 1;
-        em &= em - 1;
-        const uint32_t w = w4[i >> 1];
-        st[eoff + pos++] = (uint8_t)((i & 1) ? exp_hi(w) : exp_lo(w));
+      uint32_t em = mask_of(escmask, k), pos = excl[k];
+      if (em) {
+        const uint32_t e03 = exps4(v[k].x, v[k].y), e47 = exps4(v[k].z, v[k].w);
+        while (em) {
+          const uint32_t i = (uint32_t)__builtin_ctz(em);
+          em &= em - 1;
+          st[eoff + pos++] = (uint8_t)__builtin_amdgcn_perm(e47, e03, 0x0C0C0C00u | i);
+        }
       }
     }
     const uint32_t pad_end = (p.n_esc + 15u) & ~15u;
@@ -374,7 +436,7 @@ __device__ void write_coded(const uint4 (&v)[kPer], const Plan& p, Smem& s) {
 
 // Phase 2 of encoding: writes the record for plan p into the LDS staging
 // buffer.  Ends with a barrier.
-__device__ void write_block(const uint4 (&v)[kPer], const Plan& p, Smem& s) {
+__device__ __forceinline__ void write_block(const uint4 (&v)[kPer], const Plan& p, Smem& s) {
   const uint32_t t = threadIdx.x;
   if (t == 0) {
     uint32_t* h = stage32(s);
@@ -439,7 +501,7 @@ __device__ __forceinline__ uint32_t lookup4(uint32_t codes, const uint32_t (&d)[
 }
 
 template <int B>
-__device__ bool read_coded(Smem& s, uint32_t n_esc, uint4 (&v)[kPer]) {
+__device__ __forceinline__ bool read_coded(Smem& s, uint32_t n_esc, uint4 (&v)[kPer]) {
   constexpr uint32_t K = (1u << B) - 1u;
   constexpr uint32_t poff = planes_off(B), soff = sm_off(B), eoff = esc_off(B);
   const uint32_t t = threadIdx.x;
@@ -448,7 +510,7 @@ __device__ bool read_coded(Smem& s, uint32_t n_esc, uint4 (&v)[kPer]) {
   bool bad = false;
   if (t >= K && t < dict_bytes(B)) bad |= st[16 + t] != 0;  // dictionary padding must be zero
   const uint32_t d[4] = {st32[4], st32[5], st32[6], st32[7]};
-  uint32_t clo[kPer], chi[kPer], escmask[kPer], cnt[kPer];
+  uint32_t clo[kPer], chi[kPer], escmask[2] = {0, 0};
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const uint32_t c = t + kThreads * k;
@@ -466,11 +528,10 @@ __device__ bool read_coded(Smem& s, uint32_t n_esc, uint4 (&v)[kPer]) {
     transpose8(lo, hi);  // now byte i of (lo, hi) = code of element i
     clo[k] = lo;
     chi[k] = hi;
-    escmask[k] = em;
-    cnt[k] = __popc(em);
+    escmask[k >> 2] |= em << (8 * (k & 3));
   }
   uint32_t excl[kPer];
-  const uint32_t total = block_excl_scan8(cnt, excl, s);
+  const uint32_t total = block_excl_scan8(escmask, excl, s);
   const bool count_ok = total == n_esc;
   const uint32_t pad_end = (n_esc + 15u) & ~15u;
   if (t < pad_end - n_esc) bad |= st[eoff + n_esc + t] != 0;  // escape padding must be zero
@@ -479,15 +540,25 @@ __device__ bool read_coded(Smem& s, uint32_t n_esc, uint4 (&v)[kPer]) {
     const uint32_t c = t + kThreads * k;
     uint32_t E0 = lookup4<B>(clo[k], d, st + 16);
     uint32_t E1 = lookup4<B>(chi[k], d, st + 16);
-    uint32_t em = escmask[k], pos = excl[k];
-    while (em) {  // escaped elements take their exponent from the escape plane
-      const int i = __ffs(em) - 1;
-      em &= em - 1;
-      const uint32_t e = (count_ok && pos < n_esc) ? st[eoff + pos] : 0u;
-      ++pos;
-      const uint32_t sh = 8u * (i & 3);
-      if (i < 4) E0 = (E0 & ~(0xFFu << sh)) | (e << sh);
-      else E1 = (E1 & ~(0xFFu << sh)) | (e << sh);
+    uint32_t em = mask_of(escmask, k);
+    if (em && count_ok) {
+      // Escaped elements take their exponents, in order, from the escape
+      // plane bytes excl[k] .. excl[k] + popc - 1 (at most 8): three aligned
+      // words cover them, and the lookup left a zero byte at every escaped
+      // position (the dictionary entry of code K is zero padding).
+      const uint32_t a = eoff + excl[k];  // + popc <= rec_bytes <= kRawFull: the spare vector covers the rest
+      const uint32_t* w = st32 + (a >> 2);
+      const uint32_t d0 = w[0], d1 = w[1], d2 = w[2];
+      const uint32_t x0 = __builtin_amdgcn_alignbyte(d1, d0, a & 3u), x1 = __builtin_amdgcn_alignbyte(d2, d1, a & 3u);
+      uint32_t j = 0;
+      while (em) {
+        const uint32_t i = (uint32_t)__builtin_ctz(em);
+        em &= em - 1;
+        const uint32_t e = __builtin_amdgcn_perm(x1, x0, 0x0C0C0C00u | j);
+        ++j;
+        if (i < 4) E0 |= e << (8u * i);
+        else E1 |= e << (8u * (i - 4u));
+      }
     }
     const uint2 smv = *reinterpret_cast<const uint2*>(st + soff + 8 * c);
     const uint2 a = rebuild_quad(smv.x, E0), b = rebuild_quad(smv.y, E1);
@@ -499,7 +570,7 @@ __device__ bool read_coded(Smem& s, uint32_t n_esc, uint4 (&v)[kPer]) {
 // Decodes the staged record (header already validated for mode, b, m,
 // rec_bytes) into v.  Returns false (uniform) when the escape count or a
 // padding byte disagrees with the format.  Ends with a barrier.
-__device__ bool read_block(Smem& s, uint32_t mode, uint32_t b, uint32_t m, uint32_t n_esc,
+__device__ __forceinline__ bool read_block(Smem& s, uint32_t mode, uint32_t b, uint32_t m, uint32_t n_esc,
                            uint32_t rec_bytes, uint4 (&v)[kPer]) {
   const int t = threadIdx.x;
   const uint8_t* st = stage8(s);
@@ -519,6 +590,7 @@ __device__ bool read_block(Smem& s, uint32_t mode, uint32_t b, uint32_t m, uint3
       for (int k = 0; k < kPer; ++k) {
         const uint32_t e0 = 8u * (t + kThreads * k);
         uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+    #pragma unroll
         for (uint32_t i = 0; i < 8; ++i)
           if (e0 + i >= m) w4[i >> 1] &= (i & 1) ? 0x0000FFFFu : 0xFFFF0000u;
         v[k] = make_uint4(w4[0], w4[1], w4[2], w4[3]);

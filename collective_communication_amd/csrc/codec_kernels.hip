@@ -285,12 +285,13 @@ __device__ __forceinline__ void count_wire(const CarGeom& g, uint32_t rec_bytes)
 // Reads a wire record produced by this library from a slot into LDS and
 // decodes it.  The record header is clamped to the slot so that a damaged
 // slot can never send a read out of bounds.
-__device__ void read_slot(Smem& s, const uint8_t* src, uint32_t m, uint4 (&v)[kPer]) {
+__device__ __forceinline__ void read_slot(Smem& s, const uint8_t* src, uint32_t m, uint4 (&v)[kPer]) {
   if (threadIdx.x == 0) {
     const uint32_t* r = reinterpret_cast<const uint32_t*>(src);
     uint32_t mode = src[0], b = src[1], ne = r[2], rb = r[3];
     const bool ok = (mode == 0 && rb == raw_bytes(m)) ||
-                    (mode == 1 && m == kB && b >= 1 && b <= 7 && ne <= kB && rb == coded_bytes(b, ne));
+                    (mode == 1 && m == kB && b >= 1 && b <= 7 && ne <= kB && rb == coded_bytes(b, ne) &&
+                     rb < kRawFull);
     if (!ok) { mode = 0; b = 0; ne = 0; rb = raw_bytes(m); }
     s.plan[1] = mode; s.plan[2] = b; s.plan[3] = ne; s.plan[4] = rb;
   }
@@ -329,12 +330,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const uint64_t e0 = (uint64_t)j * g.L + (uint64_t)blk * kB;
   uint4 v[kPer];
   read_slot(s, slot(g, p, step & 1, blk), m, v);
-  {  // the receiver's own data, loaded once the decode state is dead
-    uint4 own[kPer];
-    load_block(ptr.send[q] + e0, m, own);
+  // The receiver's own data goes through the staging buffer, which the decode
+  // has finished with: it costs no registers while the decoded block is live.
+  load_block_lds(ptr.send[q] + e0, m, s);
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) v[k] = hop_bf16x8(v[k], own[k]);
+  for (int k = 0; k < kPer; ++k) {
+    v[k] = hop_bf16x8(v[k], s.stage[threadIdx.x + kThreads * k]);
+    // Pin each packed word: left alone, the compiler carries the two unpacked
+    // halves of every sum into the encoder and runs out of registers there.
+    asm volatile("" : "+v"(v[k].x), "+v"(v[k].y), "+v"(v[k].z), "+v"(v[k].w));
   }
+  __syncthreads();  // the staging buffer is the histogram's next
   if (step == g.R - 2) store_block(ptr.recv[q] + e0, m, v);
   const Plan pl = plan_block(v, m, s);
   write_block(v, pl, s);
