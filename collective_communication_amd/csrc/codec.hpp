@@ -1,4 +1,4 @@
-// codec.hpp -- one HCZ1 block (16384 bf16 = 32 KB) per 256-thread workgroup.
+// codec.hpp -- one HCZ1 block (16384 bf16 = 32 KB) per 512-thread workgroup.
 //
 // The method is the exponent coder of "CCCL: In-GPU Compression-Coupled
 // Collective Communication": section 4.1 (a bf16 word splits into sign,
@@ -8,9 +8,12 @@
 // 4.4 (the block writes its output in one pass, no temporary buffers).  Byte
 // format: see include/hc.h.
 //
-// gfx950 mapping.  Thread t of the workgroup owns the eight 16-byte chunks
-// c = t + 256k (k = 0..7) of the block, eight consecutive elements each, so
-// every global load and store of a wave is a contiguous 1 KB.  A chunk is
+// gfx950 mapping.  Thread t of the workgroup owns the four 16-byte chunks
+// c = t + 512k (k = 0..3) of the block, eight consecutive elements each, so
+// every global load and store of a wave is a contiguous 1 KB.  Eight waves
+// per block at no more than 64 VGPRs keep eight waves on every SIMD (LDS
+// holds four blocks per CU): each wave's share of a block's serial latency
+// chain is half what four waves of eight chunks would carry.  A chunk is
 // exactly one byte of each code plane, which makes plane packing an 8x8
 // bit-matrix transpose inside one register pair; the four lanes of a quad
 // hold four consecutive chunks, so a byte transpose across the quad (two DPP
@@ -22,9 +25,10 @@
 //               of a half-wave never share a bank and the address comes
 //               straight out of the bf16 word with one AND-OR), held in the
 //               staging buffer before the record needs it
-//   ranking   : occurring exponents are compacted (ballot + popcount) and
-//               each ranks itself against that short list of keys (count
-//               desc, exponent asc); absent exponents rank after them in order
+//   ranking   : occurring exponents are compacted (ballot + popcount) into
+//               a short list of keys (count desc, exponent asc); eight lanes
+//               rank one key by counting the larger ones, one LDS round trip
+//               per 64 keys; absent exponents rank after them in order
 //   b choice  : a DPP prefix sum over the ranked counts gives the escape
 //               count of every b; each wave reads the seven candidates with
 //               readlane and keeps the smallest record (ties: smaller b)
@@ -42,7 +46,11 @@ namespace codec {
 
 constexpr uint32_t kB = 16384;                  // elements per block
 constexpr uint32_t kChunks = kB / 8;            // 16-byte chunks per block
-constexpr int kPer = kChunks / kThreads;        // chunks per thread (8)
+constexpr int kCT = 512;                        // threads of a codec workgroup
+constexpr int kCW = kCT / 64;                   // its waves
+constexpr int kPer = kChunks / kCT;             // chunks per thread (4)
+constexpr int kEmWords = (kPer + 3) / 4;        // words of packed per-chunk escape masks
+static_assert(kPer % 2 == 0 && kPer <= 8 && kCT >= 256, "codec thread layout");
 constexpr uint32_t kPlaneBytes = kB / 8;        // one code plane
 constexpr uint32_t kRawFull = 16 + 2 * kB;      // raw record of a full block
 constexpr uint32_t kStage16 = kRawFull / 16;    // 2049 uint4 of LDS staging
@@ -64,7 +72,8 @@ struct Smem {
   uint32_t key[256];             // (count << 8) | (255 - exponent) of occurring exponents
   uint32_t cbr[256];             // count by rank
   uint8_t code_of[256];          // exponent -> code
-  uint32_t wsum[kWaves][4];      // per-wave totals (scans)
+  uint8_t rank_of[256];          // exponent -> rank by (count desc, exponent asc)
+  uint32_t wsum[kCW][4];         // per-wave totals (scans)
   uint32_t plan[8];
   uint64_t misc[2];
 };
@@ -159,65 +168,70 @@ __device__ __forceinline__ uint32_t chunk_elem_word(const uint4& v, int i) {
   return (i & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
-__device__ __forceinline__ uint32_t field16(const uint4& v, int k) {
-  const uint32_t w = (k < 2) ? v.x : (k < 4) ? v.y : (k < 6) ? v.z : v.w;
-  return (k & 1) ? (w >> 16) : (w & 0xFFFFu);
-}
 
-// Escape masks of a thread's eight chunks, one byte each, packed in two
-// words: chunk k in byte k % 4 of word k / 4.
-__device__ __forceinline__ uint32_t mask_of(const uint32_t (&em)[2], int k) {
+// Escape masks of a thread's chunks, one byte each, packed four to a word:
+// chunk k in byte k % 4 of word k / 4.
+__device__ __forceinline__ uint32_t mask_of(const uint32_t (&em)[kEmWords], int k) {
   return (em[k >> 2] >> (8 * (k & 3))) & 0xFFu;
 }
 
+__device__ __forceinline__ uint32_t field16(const uint32_t* w, int k) {
+  return (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+}
+
 // Workgroup exclusive scan of the escape counts popc(mask k) (each <= 8) in
-// element index order (chunk c = t + 256k, so k-major, then thread).
+// element index order (chunk c = t + kCT * k, so k-major, then thread).
 // Returns for each k the number of escapes before this thread's chunk k,
-// and the total.  Counters travel as 16-bit fields, two per 32-bit word.
-__device__ __forceinline__ uint32_t block_excl_scan8(const uint32_t (&em)[2], uint32_t (&excl)[kPer],
-                                                     Smem& s) {
-  uint32_t cnt[kPer];
+// and the total.  Counters travel as 16-bit fields, two per 32-bit word
+// (a field never exceeds 8 * kCT).
+__device__ __forceinline__ uint32_t block_excl_scan(const uint32_t (&em)[kEmWords], uint32_t (&excl)[kPer],
+                                                    Smem& s) {
+  constexpr int kW = kPer / 2;
+  uint32_t mine[kW], incl[kW];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) cnt[k] = __popc(mask_of(em, k));
-  const uint32_t m0 = cnt[0] | (cnt[1] << 16), m1 = cnt[2] | (cnt[3] << 16);
-  const uint32_t m2 = cnt[4] | (cnt[5] << 16), m3 = cnt[6] | (cnt[7] << 16);
-  const uint4 incl = make_uint4(wave_incl_scan(m0), wave_incl_scan(m1), wave_incl_scan(m2), wave_incl_scan(m3));
-  const uint4 mine = make_uint4(m0, m1, m2, m3);
+  for (int i = 0; i < kW; ++i) {
+    mine[i] = __popc(mask_of(em, 2 * i)) | (__popc(mask_of(em, 2 * i + 1)) << 16);
+    incl[i] = wave_incl_scan(mine[i]);
+  }
   const int wave = threadIdx.x >> 6;
   if (__lane_id() == 63) {
-    s.wsum[wave][0] = incl.x; s.wsum[wave][1] = incl.y;
-    s.wsum[wave][2] = incl.z; s.wsum[wave][3] = incl.w;
+#pragma unroll
+    for (int i = 0; i < kW; ++i) s.wsum[wave][i] = incl[i];
   }
   __syncthreads();
-  uint4 before = make_uint4(0, 0, 0, 0), total = make_uint4(0, 0, 0, 0);
+  uint32_t before[kW], total[kW];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const uint4 t = make_uint4(s.wsum[w][0], s.wsum[w][1], s.wsum[w][2], s.wsum[w][3]);
-    if (w < wave) { before.x += t.x; before.y += t.y; before.z += t.z; before.w += t.w; }
-    total.x += t.x; total.y += t.y; total.z += t.z; total.w += t.w;
+  for (int i = 0; i < kW; ++i) before[i] = total[i] = 0;
+#pragma unroll
+  for (int w = 0; w < kCW; ++w) {
+#pragma unroll
+    for (int i = 0; i < kW; ++i) {
+      const uint32_t x = s.wsum[w][i];
+      before[i] += w < wave ? x : 0u;
+      total[i] += x;
+    }
   }
   uint32_t base = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const uint32_t in_wave = field16(incl, k) - field16(mine, k);
-    excl[k] = base + field16(before, k) + in_wave;
+    excl[k] = base + field16(before, k) + field16(incl, k) - field16(mine, k);
     base += field16(total, k);
   }
   return base;
 }
 
-// Loads a block's elements: thread t gets chunks t + 256k.  Elements at or
+// Loads a block's elements: thread t gets chunks t + 512k.  Elements at or
 // past m read as zero.
 __device__ __forceinline__ void load_block(const uint16_t* src, uint32_t m, uint4 (&v)[kPer]) {
   const int t = threadIdx.x;
   if (m == kB) {
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) v[k] = ld16(src + 8 * (t + kThreads * k));
+    for (int k = 0; k < kPer; ++k) v[k] = ld16(src + 8 * (t + kCT * k));
     return;
   }
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const uint32_t e0 = 8u * (t + kThreads * k);
+    const uint32_t e0 = 8u * (t + kCT * k);
     uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
     for (uint32_t i = 0; i < 8; ++i)
@@ -236,7 +250,7 @@ __device__ __forceinline__ void load_block_lds(const uint16_t* src, uint32_t m, 
     const uint32_t lane = __lane_id(), wave = t >> 6;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-      const uint32_t c0 = kThreads * k + 64u * wave;  // first chunk of this wave's 1 KB
+      const uint32_t c0 = kCT * k + 64u * wave;  // first chunk of this wave's 1 KB
       __builtin_amdgcn_global_load_lds(src + 8 * (c0 + lane),
                                        (__attribute__((address_space(3))) void*)&s.stage[c0], 16, 0, 0);
     }
@@ -245,7 +259,7 @@ __device__ __forceinline__ void load_block_lds(const uint16_t* src, uint32_t m, 
     uint4 one[1];
 #pragma unroll 1
     for (int k = 0; k < kPer; ++k) {
-      const uint32_t c = t + kThreads * k;
+      const uint32_t c = t + kCT * k;
       const uint32_t e0 = 8u * c;
       uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -263,12 +277,12 @@ __device__ __forceinline__ void store_block(uint16_t* dst, uint32_t m, const uin
   const int t = threadIdx.x;
   if (m == kB) {
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) st16(dst + 8 * (t + kThreads * k), v[k]);
+    for (int k = 0; k < kPer; ++k) st16(dst + 8 * (t + kCT * k), v[k]);
     return;
   }
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const uint32_t e0 = 8u * (t + kThreads * k);
+    const uint32_t e0 = 8u * (t + kCT * k);
 #pragma unroll
     for (uint32_t i = 0; i < 8; ++i)
       if (e0 + i < m) dst[e0 + i] = (uint16_t)chunk_elem_word(v[k], (int)i);
@@ -297,7 +311,7 @@ __device__ __forceinline__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, S
   // 0x7F80 (its exponent field already sits at bit 7).
   uint8_t* sub8 = stage8(s);
 #pragma unroll
-  for (int i = 0; i < (int)(kHistCopies * 256 / 4 / kThreads); ++i) s.stage[t + kThreads * i] = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < (int)(kHistCopies * 256 / 4 / kCT); ++i) s.stage[t + kCT * i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
   {
     const uint32_t c4 = (lane & (kHistCopies - 1)) << 2;
@@ -312,44 +326,69 @@ __device__ __forceinline__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, S
     }
   }
   __syncthreads();
-  // Thread t sums the 32 copies of bin t: eight 16-byte reads, started at a
-  // different quad in each group of eight lanes to spread the banks.
+  // Threads 0..255 (the first four waves) own one exponent bin each from here
+  // to the code table.  Thread t sums the 32 copies of bin t: eight 16-byte
+  // reads, started at a different quad in each group of eight lanes to
+  // spread the banks.  Other threads hold count 0 and write nothing.
+  const bool owner = t < 256u;
   uint32_t cnt = 0;
+  if (owner) {
 #pragma unroll
-  for (uint32_t i = 0; i < 8; ++i) {
-    const uint4 q = s.stage[t * 8 + ((i + t) & 7u)];
-    cnt += q.x + q.y + q.z + q.w;
+    for (uint32_t i = 0; i < 8; ++i) {
+      const uint4 q = s.stage[t * 8 + ((i + t) & 7u)];
+      cnt += q.x + q.y + q.z + q.w;
+    }
   }
-  // Rank = position in (count desc, exponent asc).  Only exponents that occur
-  // need comparisons: they are compacted into a short list of keys; an
-  // exponent that never occurs ranks after all that do, in exponent order.
+  // Rank = position in (count desc, exponent asc); key order is that order.
   const uint32_t key = (cnt << 8) | (255u - t);
   const uint64_t nzmask = __ballot(cnt > 0);
   const uint32_t wave = t >> 6;
   const uint32_t below = (uint32_t)__popcll(nzmask & ((1ull << lane) - 1ull));
-  if (lane == 0) s.wsum[wave][0] = (uint32_t)__popcll(nzmask);
+  if (owner && lane == 0) s.wsum[wave][0] = (uint32_t)__popcll(nzmask);
   __syncthreads();
   uint32_t before = 0, nz_total = 0;
 #pragma unroll
-  for (uint32_t w = 0; w < (uint32_t)kWaves; ++w) {
+  for (uint32_t w = 0; w < 4u; ++w) {  // the owner waves
     const uint32_t c = s.wsum[w][0];
     before += w < wave ? c : 0;
     nz_total += c;
   }
   const uint32_t nz_below = before + below;
-  if (cnt > 0) s.key[nz_below] = key;
-  __syncthreads();
-  // Each wave holds up to 64 of the compacted keys in registers and walks
-  // them with readlane, so the comparisons wait on no memory.  A wave whose
-  // exponents all have count 0 needs no comparison.
-  uint32_t rank = 0;
-  for (uint32_t base = 0; nzmask != 0 && base < nz_total; base += 64) {  // waves without one skip
-    const uint32_t kr = base + lane < nz_total ? s.key[base + lane] : 0u;
-    const uint32_t lim = nz_total - base < 64u ? nz_total - base : 64u;
-    for (uint32_t j = 0; j < lim; ++j) rank += __builtin_amdgcn_readlane(kr, j) > key;
+  // An exponent that never occurs ranks after all that do, in exponent order;
+  // the occurring ones are compacted into a short list of keys.
+  if (owner) {
+    if (cnt > 0) {
+      s.key[nz_below] = key;
+    } else {
+      const uint32_t r = nz_total + (t - nz_below);
+      s.cbr[r] = 0;
+      s.rank_of[t] = (uint8_t)r;
+    }
   }
-  if (cnt == 0) rank = nz_total + (t - nz_below);
-  s.cbr[rank] = cnt;
+  __syncthreads();
+  // rank(key i) = #{keys j > key i} (keys are distinct).  Eight lanes rank
+  // one key: lane g of the group compares it with keys g, g+8, g+16, ...,
+  // eight independent LDS reads per 64 keys, and three shuffles add the
+  // eight partial counts.  64 keys per pass over the workgroup's 512 lanes.
+  for (uint32_t i0 = 0; i0 < nz_total; i0 += kCT / 8) {
+    const uint32_t i = i0 + (t >> 3), g = t & 7u;
+    const uint32_t ki = i < nz_total ? s.key[i] : 0xFFFFFFFFu;
+    uint32_t c = 0;
+    for (uint32_t j0 = 0; j0 < nz_total; j0 += 64) {
+#pragma unroll
+      for (uint32_t u = 0; u < 8; ++u) {
+        const uint32_t j = j0 + g + 8u * u;
+        c += (j < nz_total ? s.key[j] : 0u) > ki;
+      }
+    }
+    c += __shfl_xor(c, 1, 8);
+    c += __shfl_xor(c, 2, 8);
+    c += __shfl_xor(c, 4, 8);
+    if (g == 0 && i < nz_total) {
+      s.cbr[c] = ki >> 8;
+      s.rank_of[255u - (ki & 0xFFu)] = (uint8_t)c;
+    }
+  }
   __syncthreads();
   // cover(K) = sum of the K largest counts, K = 2^b - 1.  Lane l holds ranks
   // 2l and 2l+1; after the inclusive scan S_l covers ranks <= 2l+1, and
@@ -375,7 +414,8 @@ __device__ __forceinline__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, S
       p.mode = 0; p.b = 0; p.K = 0; p.n_esc = 0; p.rec_bytes = kRawFull;
     }
   }
-  if (p.mode == 1) {
+  if (p.mode == 1 && owner) {
+    const uint32_t rank = s.rank_of[t];
     s.code_of[t] = (uint8_t)(rank < p.K ? rank : p.K);
     if (rank < dict_bytes(p.b)) stage8(s)[16 + rank] = rank < p.K ? (uint8_t)t : (uint8_t)0;
   }
@@ -391,10 +431,10 @@ __device__ __forceinline__ void write_coded(const uint4 (&v)[kPer], const Plan& 
   const uint32_t t = threadIdx.x, lane = __lane_id(), qi = lane & 3u;
   uint8_t* st = stage8(s);
   uint32_t* st32 = stage32(s);
-  uint32_t escmask[2] = {0, 0};
+  uint32_t escmask[kEmWords] = {};
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const uint32_t c = t + kThreads * k;
+    const uint32_t c = t + kCT * k;
     const uint32_t w0 = v[k].x, w1 = v[k].y, w2 = v[k].z, w3 = v[k].w;
     uint32_t lo = (uint32_t)s.code_of[exp_lo(w0)] | ((uint32_t)s.code_of[exp_hi(w0)] << 8) |
                   ((uint32_t)s.code_of[exp_lo(w1)] << 16) | ((uint32_t)s.code_of[exp_hi(w1)] << 24);
@@ -416,7 +456,7 @@ __device__ __forceinline__ void write_coded(const uint4 (&v)[kPer], const Plan& 
   }
   if (p.n_esc) {
     uint32_t excl[kPer];
-    block_excl_scan8(escmask, excl, s);
+    block_excl_scan(escmask, excl, s);
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       uint32_t em = mask_of(escmask, k), pos = excl[k];
@@ -449,7 +489,7 @@ __device__ __forceinline__ void write_block(const uint4 (&v)[kPer], const Plan& 
     const uint32_t n16 = (p.rec_bytes - 16u) / 16u;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-      const uint32_t c = t + kThreads * k;
+      const uint32_t c = t + kCT * k;
       if (c < n16) s.stage[1 + c] = v[k];
     }
   } else {
@@ -469,13 +509,13 @@ __device__ __forceinline__ void write_block(const uint4 (&v)[kPer], const Plan& 
 // Copies a staged record (rec_bytes, a multiple of 16) to global memory.
 __device__ __forceinline__ void copy_out(const Smem& s, uint8_t* dst, uint32_t rec_bytes) {
   const uint32_t n16 = rec_bytes / 16u;
-  for (uint32_t i = threadIdx.x; i < n16; i += kThreads) st16(dst + 16 * i, s.stage[i]);
+  for (uint32_t i = threadIdx.x; i < n16; i += kCT) st16(dst + 16 * i, s.stage[i]);
 }
 
 // Copies a record from global memory into the staging buffer.
 __device__ __forceinline__ void copy_in(Smem& s, const uint8_t* src, uint32_t rec_bytes) {
   const uint32_t n16 = rec_bytes / 16u;
-  for (uint32_t i = threadIdx.x; i < n16; i += kThreads) s.stage[i] = ld16(src + 16 * i);
+  for (uint32_t i = threadIdx.x; i < n16; i += kCT) s.stage[i] = ld16(src + 16 * i);
 }
 
 // ---------------------------------------------------------------------------
@@ -510,10 +550,10 @@ __device__ __forceinline__ bool read_coded(Smem& s, uint32_t n_esc, uint4 (&v)[k
   bool bad = false;
   if (t >= K && t < dict_bytes(B)) bad |= st[16 + t] != 0;  // dictionary padding must be zero
   const uint32_t d[4] = {st32[4], st32[5], st32[6], st32[7]};
-  uint32_t clo[kPer], chi[kPer], escmask[2] = {0, 0};
+  uint32_t clo[kPer], chi[kPer], escmask[kEmWords] = {};
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const uint32_t c = t + kThreads * k;
+    const uint32_t c = t + kCT * k;
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int j = 0; j < B; ++j) {
@@ -531,13 +571,13 @@ __device__ __forceinline__ bool read_coded(Smem& s, uint32_t n_esc, uint4 (&v)[k
     escmask[k >> 2] |= em << (8 * (k & 3));
   }
   uint32_t excl[kPer];
-  const uint32_t total = block_excl_scan8(escmask, excl, s);
+  const uint32_t total = block_excl_scan(escmask, excl, s);
   const bool count_ok = total == n_esc;
   const uint32_t pad_end = (n_esc + 15u) & ~15u;
   if (t < pad_end - n_esc) bad |= st[eoff + n_esc + t] != 0;  // escape padding must be zero
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const uint32_t c = t + kThreads * k;
+    const uint32_t c = t + kCT * k;
     uint32_t E0 = lookup4<B>(clo[k], d, st + 16);
     uint32_t E1 = lookup4<B>(chi[k], d, st + 16);
     uint32_t em = mask_of(escmask, k);
@@ -578,17 +618,17 @@ __device__ __forceinline__ bool read_block(Smem& s, uint32_t mode, uint32_t b, u
     const uint32_t n16 = (rec_bytes - 16u) / 16u;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-      const uint32_t c = t + kThreads * k;
+      const uint32_t c = t + kCT * k;
       v[k] = c < n16 ? s.stage[1 + c] : make_uint4(0, 0, 0, 0);
     }
     // padding after the m words must be zero
     bool bad = false;
-    for (uint32_t i = 16u + 2u * m + t; i < rec_bytes; i += kThreads) bad |= st[i] != 0;
+    for (uint32_t i = 16u + 2u * m + t; i < rec_bytes; i += kCT) bad |= st[i] != 0;
     const bool any_bad = __syncthreads_or(bad);
     if (!any_bad && m != kB) {  // clear lanes past m so callers see zeros there
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
-        const uint32_t e0 = 8u * (t + kThreads * k);
+        const uint32_t e0 = 8u * (t + kCT * k);
         uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
     #pragma unroll
         for (uint32_t i = 0; i < 8; ++i)

@@ -89,7 +89,7 @@ __global__ void empty_stream_kernel(uint8_t* out, uint64_t* out_bytes) {
   *out_bytes = 32;
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void compress_kernel(const uint16_t* __restrict__ in, uint64_t n,
+__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void compress_kernel(const uint16_t* __restrict__ in, uint64_t n,
                                                             uint8_t* __restrict__ out,
                                                             uint64_t* __restrict__ out_bytes,
                                                             CompressWs* __restrict__ ws, uint32_t nb) {
@@ -195,7 +195,7 @@ __device__ bool check_record_header(const Smem& s, uint32_t m, uint32_t len, uin
   return ok;
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void decompress_kernel(
+__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void decompress_kernel(
     const uint8_t* __restrict__ in, uint64_t in_bytes, uint16_t* __restrict__ out, uint64_t n,
     int32_t* __restrict__ status, uint32_t nb) {
   __shared__ Smem s;
@@ -303,7 +303,7 @@ __device__ __forceinline__ void read_slot(Smem& s, const uint8_t* src, uint32_t 
 }
 
 // Reduce-scatter step 0: every rank compresses the slice it sends first.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void car_first_kernel(RingPtrs ptr, CarGeom g) {
+__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void car_first_kernel(RingPtrs ptr, CarGeom g) {
   __shared__ Smem s;
   const uint32_t p = blockIdx.x / g.nbs, blk = blockIdx.x % g.nbs;
   const uint32_t j = (p + g.R - 1) % g.R;  // sender p sends slice p-1
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 // Reduce-scatter step s: receiver q decompresses what q-1 sent, folds in its
 // own slice, writes the result if this is the last step, and compresses it
 // for the next hop.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void car_rs_kernel(RingPtrs ptr, CarGeom g, uint32_t step) {
+__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void car_rs_kernel(RingPtrs ptr, CarGeom g, uint32_t step) {
   __shared__ Smem s;
   const uint32_t q = blockIdx.x / g.nbs, blk = blockIdx.x % g.nbs;
   const uint32_t p = (q + g.R - 1) % g.R;
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   load_block_lds(ptr.send[q] + e0, m, s);
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    v[k] = hop_bf16x8(v[k], s.stage[threadIdx.x + kThreads * k]);
+    v[k] = hop_bf16x8(v[k], s.stage[threadIdx.x + kCT * k]);
     // Pin each packed word: left alone, the compiler carries the two unpacked
     // halves of every sum into the encoder and runs out of registers there.
     asm volatile("" : "+v"(v[k].x), "+v"(v[k].y), "+v"(v[k].z), "+v"(v[k].w));
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 
 // All-gather step s: receiver q decompresses the finished slice from q-1 into
 // its output and, unless this is the last step, forwards the same bytes.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void car_ag_kernel(RingPtrs ptr, CarGeom g, uint32_t step,
+__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void car_ag_kernel(RingPtrs ptr, CarGeom g, uint32_t step,
                                                           uint32_t buf_in) {
   __shared__ Smem s;
   const uint32_t q = blockIdx.x / g.nbs, blk = blockIdx.x % g.nbs;
@@ -392,7 +392,7 @@ hipError_t launch_compress(const uint16_t* in, size_t n, void* out, uint64_t* ou
   if (nb >= (1ull << 31)) return hipErrorInvalidValue;
   hipError_t e = launch_fill_u32(ws, 0u, compress_ws_bytes(n) / 4, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(compress_kernel, dim3((uint32_t)nb), dim3(kThreads), 0, stream, in, (uint64_t)n,
+  hipLaunchKernelGGL(compress_kernel, dim3((uint32_t)nb), dim3(kCT), 0, stream, in, (uint64_t)n,
                      static_cast<uint8_t*>(out), out_bytes, static_cast<CompressWs*>(ws), (uint32_t)nb);
   return hipGetLastError();
 }
@@ -408,7 +408,7 @@ hipError_t launch_decompress(const void* in, size_t in_bytes, uint16_t* out, siz
                        (uint64_t)in_bytes, status);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(decompress_kernel, dim3((uint32_t)nb), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL(decompress_kernel, dim3((uint32_t)nb), dim3(kCT), 0, stream,
                      static_cast<const uint8_t*>(in), (uint64_t)in_bytes, out, (uint64_t)n, status, (uint32_t)nb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -486,7 +486,7 @@ hipError_t launch_compressed_allreduce(void* const* send, void* const* recv, siz
   g.nbs = (uint32_t)nbs;
   g.wire = static_cast<uint8_t*>(ws);
   g.wire_bytes = wire_bytes;
-  const dim3 grid((uint32_t)(R * nbs)), block(kThreads);
+  const dim3 grid((uint32_t)(R * nbs)), block(kCT);
   hipError_t e = mark();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(car_first_kernel, grid, block, 0, stream, ptr, g);
