@@ -283,21 +283,37 @@ __device__ __forceinline__ void count_wire(const CarGeom& g, uint32_t rec_bytes)
 }
 
 // Reads a wire record produced by this library from a slot into LDS and
-// decodes it.  The record header is clamped to the slot so that a damaged
-// slot can never send a read out of bounds.
+// decodes it.  The first kSpecVecs vectors of the slot are loaded with the
+// record header, before its length is known (they lie inside the slot
+// whatever the record is), so a record of up to kSpecVecs * 16 bytes takes
+// one round trip.  The record header is clamped to the slot so that a
+// damaged slot can never send a read out of bounds.
+constexpr uint32_t kSpecPer = 3;                    // vectors per thread read ahead
+constexpr uint32_t kSpecVecs = kSpecPer * kCT;      // 1536 vectors = 24 KB
+static_assert(kSpecVecs <= kStage16, "read-ahead stays inside a slot");
+
 __device__ __forceinline__ void read_slot(Smem& s, const uint8_t* src, uint32_t m, uint4 (&v)[kPer]) {
-  if (threadIdx.x == 0) {
-    const uint32_t* r = reinterpret_cast<const uint32_t*>(src);
-    uint32_t mode = src[0], b = src[1], ne = r[2], rb = r[3];
+  const uint32_t t = threadIdx.x;
+  uint4 pre[kSpecPer];
+#pragma unroll
+  for (uint32_t i = 0; i < kSpecPer; ++i) pre[i] = ld16(src + 16 * (t + kCT * i));
+  if (t == 0) {
+    const uint32_t mode = pre[0].x & 0xFFu, b = (pre[0].x >> 8) & 0xFFu, ne = pre[0].z, rb = pre[0].w;
     const bool ok = (mode == 0 && rb == raw_bytes(m)) ||
                     (mode == 1 && m == kB && b >= 1 && b <= 7 && ne <= kB && rb == coded_bytes(b, ne) &&
                      rb < kRawFull);
-    if (!ok) { mode = 0; b = 0; ne = 0; rb = raw_bytes(m); }
-    s.plan[1] = mode; s.plan[2] = b; s.plan[3] = ne; s.plan[4] = rb;
+    s.plan[1] = ok ? mode : 0u;
+    s.plan[2] = ok ? b : 0u;
+    s.plan[3] = ok ? ne : 0u;
+    s.plan[4] = ok ? rb : raw_bytes(m);
   }
   __syncthreads();
   const uint32_t mode = s.plan[1], b = s.plan[2], ne = s.plan[3], rb = s.plan[4];
-  copy_in(s, src, rb);
+  const uint32_t n16 = rb / 16u;
+#pragma unroll
+  for (uint32_t i = 0; i < kSpecPer; ++i)
+    if (t + kCT * i < n16) s.stage[t + kCT * i] = pre[i];
+  for (uint32_t i = kSpecVecs + t; i < n16; i += kCT) s.stage[i] = ld16(src + 16 * i);
   __syncthreads();
   read_block(s, mode, b, m, ne, rb, v);
 }
@@ -331,7 +347,8 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
   uint4 v[kPer];
   read_slot(s, slot(g, p, step & 1, blk), m, v);
   // The receiver's own data goes through the staging buffer, which the decode
-  // has finished with: it costs no registers while the decoded block is live.
+  // has finished with: it costs no registers while the decoded block is live
+  // (loaded into registers during the decode instead, it spills).
   load_block_lds(ptr.send[q] + e0, m, s);
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
