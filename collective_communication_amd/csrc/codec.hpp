@@ -296,6 +296,16 @@ __device__ __forceinline__ void store_block(uint16_t* dst, uint32_t m, const uin
 // Phase 1 of encoding: histogram, ranking, the choice of b and the record
 // size.  Leaves code_of[] and the dictionary in LDS; returns the plan
 // (uniform).  Ends with a barrier.
+// Clears the sub-histograms (the first 32 KB of the staging buffer).  The
+// caller puts a barrier between this and plan_block<true>.
+__device__ __forceinline__ void zero_hist(Smem& s) {
+#pragma unroll
+  for (int i = 0; i < (int)(kHistCopies * 256 / 4 / kCT); ++i) s.stage[threadIdx.x + kCT * i] = make_uint4(0, 0, 0, 0);
+}
+
+// ZEROED: the caller has already cleared the sub-histograms (zero_hist) and
+// passed a barrier since.
+template <bool ZEROED = false>
 __device__ __forceinline__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, Smem& s) {
   const uint32_t t = threadIdx.x, lane = __lane_id();
   Plan p;
@@ -310,9 +320,10 @@ __device__ __forceinline__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, S
   // OR c << 2: for the low element of a word that is the word ANDed with
   // 0x7F80 (its exponent field already sits at bit 7).
   uint8_t* sub8 = stage8(s);
-#pragma unroll
-  for (int i = 0; i < (int)(kHistCopies * 256 / 4 / kCT); ++i) s.stage[t + kCT * i] = make_uint4(0, 0, 0, 0);
-  __syncthreads();
+  if constexpr (!ZEROED) {
+    zero_hist(s);
+    __syncthreads();
+  }
   {
     const uint32_t c4 = (lane & (kHistCopies - 1)) << 2;
 #pragma unroll

@@ -96,13 +96,14 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
   __shared__ Smem s;
   const int t = threadIdx.x;
   if (t == 0) s.plan[6] = atomicAdd(&ws->ticket, 1u);
+  zero_hist(s);  // while the ticket is on its way
   __syncthreads();
   const uint32_t bid = s.plan[6];
   const uint64_t first = (uint64_t)bid * kB;
   const uint32_t m = (uint32_t)((n - first) < kB ? (n - first) : kB);
   uint4 v[kPer];
   load_block(in + first, m, v);
-  const Plan p = plan_block(v, m, s);
+  const Plan p = plan_block<true>(v, m, s);
   if (t == 0) publish(&ws->desc[bid], (bid == 0 ? kFlagIncl : kFlagAgg) | p.rec_bytes);
   write_block(v, p, s);
   if (t < 64) {
