@@ -1,11 +1,16 @@
 """Pins of the oracle's scalar rules (bf16 rounding, the fp32 and bf16 hops)
 against routes that share nothing with it: PyTorch's fp32->bf16 conversion and
 exact fp64 sums.  CPU only."""
+import os
+import subprocess
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def torch_bf16(bits_u32: np.ndarray) -> np.ndarray:
@@ -134,3 +139,18 @@ def test_f32_hop_keeps_subnormals_and_signed_zero():
 ])
 def test_bf16_hop_hand_cases(a, b, expect):
     assert oracle.hop_bf16(a, b) == expect
+
+
+@pytest.mark.slow
+def test_bf16_hop_exhaustive_all_pairs(tmp_path):
+    """All 2^32 bf16 (a, b) pairs against an fp64 -> fp32 -> integer-carry
+    route (tests/pins/hop_bf16_exhaustive.c), on 8 threads."""
+    oracle.lib()  # builds liboracle_hc.so if needed
+    so_dir = os.path.dirname(oracle._LIB_PATH)
+    exe = tmp_path / "hop_bf16_exhaustive"
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-pthread",
+                    os.path.join(HERE, "pins", "hop_bf16_exhaustive.c"), "-o", str(exe),
+                    f"-L{so_dir}", "-loracle_hc", f"-Wl,-rpath,{so_dir}", "-lm"], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "mismatches=0" in r.stdout
