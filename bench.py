@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -304,23 +305,20 @@ def bench_contention(args):
             torch.matmul(A, Bm, out=C)
     torch.cuda.synchronize()
     t_gemm = gemm_alone(10)
-    rows = []
-    for k in (8, 16, 32, 0):
-        handle = hc.hc_stream_create_cu_budget(k) if k else None
-        side = torch.cuda.ExternalStream(handle) if k else torch.cuda.Stream()
-        budget = k
-        # reduce-scatter alone on the side stream
+
+    def measure(op, side, cu_used, nbytes, prefix):
+        """`op(stream)` alone on `side`, then again while the GEMM loops on the
+        main stream for as long as it runs."""
         for _ in range(2):
-            hc.hc_reduce_scatter(send, recv, L, ws, cu_budget=budget, stream=side)
+            op(side)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(side)
-        hc.hc_reduce_scatter(send, recv, L, ws, cu_budget=budget, stream=side)
+        op(side)
         e1.record(side)
         torch.cuda.synchronize()
-        t_rs_alone = e0.elapsed_time(e1)
-        # concurrent: the GEMM loop on the main stream for as long as the reduce runs
-        iters = max(4, int(t_rs_alone / t_gemm) + 2)
+        t_alone = e0.elapsed_time(e1)
+        iters = max(4, int(t_alone / t_gemm) + 2)
         base = torch.cuda.Event(enable_timing=True)
         ge = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
         r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -328,7 +326,7 @@ def bench_contention(args):
         base.record(main)
         side.wait_event(base)
         r0.record(side)
-        hc.hc_reduce_scatter(send, recv, L, ws, cu_budget=budget, stream=side)
+        op(side)
         r1.record(side)
         ge[0].record(main)
         with torch.cuda.stream(main):
@@ -337,34 +335,56 @@ def bench_contention(args):
                 ge[i + 1].record(main)
         torch.cuda.synchronize()
         gt = [base.elapsed_time(e) for e in ge]
-        rs_t0, rs_t1 = base.elapsed_time(r0), base.elapsed_time(r1)
-        overl = [gt[i + 1] - gt[i] for i in range(iters) if gt[i] < rs_t1 and gt[i + 1] > rs_t0]
+        t0, t1 = base.elapsed_time(r0), base.elapsed_time(r1)
+        overl = [gt[i + 1] - gt[i] for i in range(iters) if gt[i] < t1 and gt[i + 1] > t0]
         t_gemm_conc = median(overl) if overl else float("nan")
-        cu_used = k if k else N_CU
-        # contention rate: share of CUs held by the reduce while the GEMM runs
-        comp = [(gt[i], gt[i + 1]) for i in range(iters)]
+        # contention rate: share of CUs held by the collective while the GEMM runs
         num = den = 0.0
-        for a, b in comp:
-            lo, hi = max(a, rs_t0), min(b, rs_t1)
-            den += b - a
+        for i in range(iters):
+            a_, b_ = gt[i], gt[i + 1]
+            lo, hi = max(a_, t0), min(b_, t1)
+            den += b_ - a_
             if hi > lo:
                 num += (hi - lo) * cu_used / N_CU
-        rows.append({"cu_budget": k if k else "all", "rs_alone_ms": round(t_rs_alone, 4),
-                     "rs_concurrent_ms": round(rs_t1 - rs_t0, 4),
-                     "rs_alone_gbps": round(rs_bytes / t_rs_alone / 1e6, 1),
-                     "rs_concurrent_gbps": round(rs_bytes / (rs_t1 - rs_t0) / 1e6, 1),
-                     "gemm_alone_ms": round(t_gemm, 4), "gemm_concurrent_ms": round(t_gemm_conc, 4),
-                     "gemm_slowdown": round(t_gemm_conc / t_gemm - 1, 4),
-                     "contention_rate": round(num / den, 5) if den else None})
+        return {f"{prefix}_alone_ms": round(t_alone, 4), f"{prefix}_concurrent_ms": round(t1 - t0, 4),
+                f"{prefix}_alone_gbps": round(nbytes / t_alone / 1e6, 1),
+                f"{prefix}_concurrent_gbps": round(nbytes / (t1 - t0) / 1e6, 1),
+                "gemm_alone_ms": round(t_gemm, 4), "gemm_concurrent_ms": round(t_gemm_conc, 4),
+                "gemm_slowdown": round(t_gemm_conc / t_gemm - 1, 4),
+                "contention_rate": round(num / den, 5) if den else None}
+
+    rows = []
+    for k in (8, 16, 32, 0):
+        handle = hc.hc_stream_create_cu_budget(k) if k else None
+        side = torch.cuda.ExternalStream(handle) if k else torch.cuda.Stream()
+        row = {"op": "reduce_scatter", "cu_budget": k if k else "all"}
+        row.update(measure(lambda st: hc.hc_reduce_scatter(send, recv, L, ws, cu_budget=k, stream=st), side,
+                           k if k else N_CU, rs_bytes, "rs"))
+        rows.append(row)
         if k:
             del side
             hc.hc_stream_destroy(handle)
+    # The all-gather that follows this reduce-scatter (R slices of L -> R
+    # outputs of n), on copy kernels and on the DMA copy engines (the offload
+    # of "HOCCL ...", section 2), measured by dma_contention in a process of
+    # its own: inside this torch process the HIP runtime bundled with the
+    # wheel serves hipMemcpyDeviceToDeviceNoCU with blit kernels on the CUs.
+    del send, recv, ws
+    torch.cuda.empty_cache()
+    tool = os.path.join(os.path.dirname(hc.LIB_PATH), "dma_contention")
+    try:
+        r = subprocess.run([tool, "bench"], capture_output=True, text=True, timeout=600)
+        ag = json.loads(r.stdout.strip().splitlines()[-1]) if r.returncode == 0 else {"error": r.stderr[-2000:]}
+    except (OSError, ValueError, subprocess.TimeoutExpired) as exc:
+        ag = {"error": repr(exc)}
     return {"metric": "Reduce-scatter under a CU budget beside a bf16 GEMM: contention rate, GEMM slowdown, RS GB/s",
             "value": rows[0]["rs_concurrent_gbps"], "unit": "GB/s", "n_gpus": 1, "steps": 1, "warmup": 2,
             "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": f"R={R} reduce-scatter of {R} x {n} bf16 N(0,1e-3) on a CU-masked side stream, "
-                                   "main stream torch.matmul 8192^3 bf16"},
-            "gemm_tflops_alone": round(2 * 8192 ** 3 / (t_gemm / 1e3) / 1e12, 1), "rows": rows}
+                                   "main stream torch.matmul 8192^3 bf16; then the matching all-gather "
+                                   f"({R} x {L} -> {R} x {n}) on CU copy kernels and on the DMA copy engines"},
+            "gemm_tflops_alone": round(2 * 8192 ** 3 / (t_gemm / 1e3) / 1e12, 1), "rows": rows,
+            "all_gather": ag}
 
 
 def main():

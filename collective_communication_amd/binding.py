@@ -50,7 +50,8 @@ class HcError(RuntimeError):
 
 class hc_opts_t(ctypes.Structure):
     _fields_ = [("chunk_fraction", ctypes.c_double), ("cu_budget", ctypes.c_int32),
-                ("n_step_events", ctypes.c_int32), ("step_events", ctypes.c_void_p)]
+                ("n_step_events", ctypes.c_int32), ("step_events", ctypes.c_void_p),
+                ("copy_engine", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class hc_task_t(ctypes.Structure):
@@ -142,10 +143,11 @@ class StepEvents:
         return [self.events[k].elapsed_time(self.events[k + 1]) for k in range(len(self.events) - 1)]
 
 
-def _opts(chunk_fraction: float = 0.0, cu_budget: int = 0, step_events: StepEvents | None = None):
-    if chunk_fraction == 0.0 and cu_budget == 0 and step_events is None:
+def _opts(chunk_fraction: float = 0.0, cu_budget: int = 0, step_events: StepEvents | None = None,
+          copy_engine: int = 0):
+    if chunk_fraction == 0.0 and cu_budget == 0 and step_events is None and copy_engine == 0:
         return None
-    o = hc_opts_t(chunk_fraction, cu_budget, 0, None)
+    o = hc_opts_t(chunk_fraction, cu_budget, 0, None, int(copy_engine), 0)
     if step_events is not None:
         o.n_step_events = len(step_events.events)
         o.step_events = ctypes.cast(step_events._arr, ctypes.c_void_p)
@@ -177,7 +179,8 @@ def _dptr(t: torch.Tensor | None, need_bytes: int, name: str) -> int | None:
 # ----------------------------------------------------------------------------- ring
 
 def hc_allreduce(sendbufs, recvbufs, count: int | None = None, *, chunk_fraction: float = 0.0,
-                 cu_budget: int = 0, step_events: StepEvents | None = None, stream=None):
+                 cu_budget: int = 0, step_events: StepEvents | None = None, copy_engine: int = 0,
+                 stream=None):
     L = load()
     R = len(sendbufs)
     if count is None:
@@ -189,13 +192,13 @@ def hc_allreduce(sendbufs, recvbufs, count: int | None = None, *, chunk_fraction
         raise TypeError("all buffers need one dtype")
     sp, _k1 = _ptr_array(sendbufs, count, "sendbufs")
     rp, _k2 = _ptr_array(recvbufs, count, "recvbufs")
-    _check(L.hc_allreduce(sp, rp, count, dt, R, _opts(chunk_fraction, cu_budget, step_events),
+    _check(L.hc_allreduce(sp, rp, count, dt, R, _opts(chunk_fraction, cu_budget, step_events, copy_engine),
                           _stream_handle(stream)))
 
 
 def hc_reduce_scatter(sendbufs, recvbufs, recvcount: int | None = None, ws=None, *,
                       chunk_fraction: float = 0.0, cu_budget: int = 0,
-                      step_events: StepEvents | None = None, stream=None):
+                      step_events: StepEvents | None = None, copy_engine: int = 0, stream=None):
     L = load()
     R = len(sendbufs)
     if recvcount is None:
@@ -209,11 +212,12 @@ def hc_reduce_scatter(sendbufs, recvbufs, recvcount: int | None = None, ws=None,
     wsp = _dptr(ws, need, "ws") if ws is not None else None
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(L.hc_reduce_scatter(sp, rp, recvcount, dt, R, wsp, ws_bytes,
-                               _opts(chunk_fraction, cu_budget, step_events), _stream_handle(stream)))
+                               _opts(chunk_fraction, cu_budget, step_events, copy_engine), _stream_handle(stream)))
 
 
 def hc_all_gather(sendbufs, recvbufs, sendcount: int | None = None, *, chunk_fraction: float = 0.0,
-                  cu_budget: int = 0, step_events: StepEvents | None = None, stream=None):
+                  cu_budget: int = 0, step_events: StepEvents | None = None, copy_engine: int = 0,
+                  stream=None):
     L = load()
     R = len(sendbufs)
     if sendcount is None:
@@ -223,7 +227,7 @@ def hc_all_gather(sendbufs, recvbufs, sendcount: int | None = None, *, chunk_fra
         raise TypeError("all buffers need one dtype")
     sp, _k1 = _ptr_array(sendbufs, sendcount, "sendbufs")
     rp, _k2 = _ptr_array(recvbufs, sendcount * R, "recvbufs")
-    _check(L.hc_all_gather(sp, rp, sendcount, dt, R, _opts(chunk_fraction, cu_budget, step_events),
+    _check(L.hc_all_gather(sp, rp, sendcount, dt, R, _opts(chunk_fraction, cu_budget, step_events, copy_engine),
                            _stream_handle(stream)))
 
 

@@ -56,6 +56,9 @@ hc_status_t check_common(int nranks, hc_dtype_t dtype, const hc_opts_t* opts) {
     if (opts->cu_budget < 0 || opts->cu_budget > 4096)
       return fail(HC_ERR_INVALID_ARGUMENT, "cu_budget %d outside 0..4096", opts->cu_budget);
     if (opts->n_step_events < 0) return fail(HC_ERR_INVALID_ARGUMENT, "n_step_events < 0");
+    if (opts->copy_engine != 0 && opts->copy_engine != 1)
+      return fail(HC_ERR_INVALID_ARGUMENT, "copy_engine %d is neither 0 nor 1", opts->copy_engine);
+    if (opts->reserved != 0) return fail(HC_ERR_INVALID_ARGUMENT, "reserved option field is not 0");
   }
   return HC_SUCCESS;
 }
@@ -84,6 +87,19 @@ double chunk_fraction(const hc_opts_t* o) {
   return (o && o->chunk_fraction != 0.0) ? o->chunk_fraction : 0.01;
 }
 int cu_budget(const hc_opts_t* o) { return o ? o->cu_budget : 0; }
+bool copy_engine(const hc_opts_t* o) { return o && o->copy_engine == 1; }
+
+// One copy step: the segments as one copy kernel on the compute units, or as
+// one DMA copy per segment on the copy engines (stream ordered).
+hipError_t copy_step(const hc::Seg* segs, int nseg, size_t es, int budget, bool dma, hipStream_t stream) {
+  if (!dma) return hc::launch_copy_step(segs, nseg, es, budget, stream);
+  for (int i = 0; i < nseg; ++i) {
+    if (segs[i].len == 0) continue;
+    hipError_t e = hipMemcpyAsync(segs[i].dst, segs[i].a, segs[i].len * es, hipMemcpyDeviceToDeviceNoCU, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 // Checks a pointer array: non-NULL and aligned to `align` bytes.
 hc_status_t check_ptrs(void* const* bufs, int R, const char* name, size_t align) {
@@ -120,7 +136,7 @@ char* mp(void* p, size_t bytes) { return static_cast<char*>(p) + bytes; }
 // Runs the allreduce task list one ring step per launch: all receivers of a
 // step in one kernel, their chunks merged into one segment per receiver.
 hc_status_t run_allreduce(void* const* send, void* const* recv, size_t count, hc_dtype_t dtype,
-                          int R, size_t chunk, int budget, Tap& tap, hipStream_t stream) {
+                          int R, size_t chunk, int budget, bool dma, Tap& tap, hipStream_t stream) {
   const size_t es = esize(dtype);
   std::vector<hc_task_t> tasks = hc::ring_tasks(R, count, chunk);
   size_t k = 0;
@@ -148,7 +164,7 @@ hc_status_t run_allreduce(void* const* send, void* const* recv, size_t count, hc
     hipError_t e = tap.mark(stream);
     if (e != hipSuccess) return device_fail(e, "hipEventRecord");
     e = op == 1 ? hc::launch_reduce_step(segs, nseg, dtype, budget, stream)
-                : hc::launch_copy_step(segs, nseg, es, budget, stream);
+                : copy_step(segs, nseg, es, budget, dma, stream);
     if (e != hipSuccess) return device_fail(e, op == 1 ? "reduce step launch" : "copy step launch");
   }
   hipError_t e = tap.mark(stream);
@@ -156,12 +172,12 @@ hc_status_t run_allreduce(void* const* send, void* const* recv, size_t count, hc
 }
 
 // One-rank operations: a single step that copies (or nothing in place).
-hc_status_t run_single(const void* src, void* dst, size_t count, size_t es, int budget, Tap& tap,
+hc_status_t run_single(const void* src, void* dst, size_t count, size_t es, int budget, bool dma, Tap& tap,
                        hipStream_t stream) {
   hipError_t e = tap.mark(stream);
   if (e == hipSuccess && src != dst) {
     hc::Seg seg{src, nullptr, dst, count};
-    e = hc::launch_copy_step(&seg, 1, es, budget, stream);
+    e = copy_step(&seg, 1, es, budget, dma, stream);
   }
   if (e == hipSuccess) e = tap.mark(stream);
   return e == hipSuccess ? HC_SUCCESS : device_fail(e, "copy launch");
@@ -231,8 +247,10 @@ hc_status_t hc_allreduce(void* const* sendbufs, void* const* recvbufs, size_t co
   Tap tap;
   if ((st = make_tap(opts, HC_OP_ALLREDUCE, nranks, &tap))) return st;
   const size_t chunk = hc::chunk_elems(count, chunk_fraction(opts), 1024);
-  if (nranks == 1) return run_single(sendbufs[0], recvbufs[0], count, es, cu_budget(opts), tap, stream);
-  return run_allreduce(sendbufs, recvbufs, count, dtype, nranks, chunk, cu_budget(opts), tap, stream);
+  if (nranks == 1)
+    return run_single(sendbufs[0], recvbufs[0], count, es, cu_budget(opts), copy_engine(opts), tap, stream);
+  return run_allreduce(sendbufs, recvbufs, count, dtype, nranks, chunk, cu_budget(opts), copy_engine(opts), tap,
+                       stream);
 }
 
 size_t hc_workspace_bytes(hc_op_t op, size_t count, int nranks, hc_dtype_t dtype) {
@@ -276,7 +294,7 @@ hc_status_t hc_reduce_scatter(void* const* sendbufs, void* const* recvbufs, size
   if ((st = check_disjoint(in, out, ok))) return st;
   Tap tap;
   if ((st = make_tap(opts, HC_OP_REDUCE_SCATTER, R, &tap))) return st;
-  if (R == 1) return run_single(sendbufs[0], recvbufs[0], L, es, cu_budget(opts), tap, stream);
+  if (R == 1) return run_single(sendbufs[0], recvbufs[0], L, es, cu_budget(opts), copy_engine(opts), tap, stream);
   const size_t need = 2 * n * es;
   if (!d_ws) return fail(HC_ERR_INVALID_ARGUMENT, "d_ws is NULL");
   if (!aligned16(d_ws)) return fail(HC_ERR_INVALID_ARGUMENT, "d_ws is not 16-byte aligned");
@@ -338,7 +356,7 @@ hc_status_t hc_all_gather(void* const* sendbufs, void* const* recvbufs, size_t s
     int nseg = 0;
     for (int r = 0; r < R; ++r)
       if (!ok[r]) segs[nseg++] = hc::Seg{sendbufs[r], nullptr, mp(recvbufs[r], (size_t)r * L * es), L};
-    hipError_t e = hc::launch_copy_step(segs, nseg, es, budget, stream);
+    hipError_t e = copy_step(segs, nseg, es, budget, copy_engine(opts), stream);
     if (e != hipSuccess) return device_fail(e, "local copy launch");
   }
   for (int s = 0; s + 1 < R; ++s) {
@@ -350,7 +368,7 @@ hc_status_t hc_all_gather(void* const* sendbufs, void* const* recvbufs, size_t s
       segs[q] = hc::Seg{a, nullptr, mp(recvbufs[q], (size_t)j * L * es), L};
     }
     hipError_t e = s > 0 ? tap.mark(stream) : hipSuccess;  // step 0 began before the local copies
-    if (e == hipSuccess) e = hc::launch_copy_step(segs, R, es, budget, stream);
+    if (e == hipSuccess) e = copy_step(segs, R, es, budget, copy_engine(opts), stream);
     if (e != hipSuccess) return device_fail(e, "copy step launch");
   }
   hipError_t e = tap.mark(stream);
@@ -409,6 +427,8 @@ hc_status_t hc_compressed_allreduce(void* const* sendbufs, void* const* recvbufs
   if (st) return st;
   if (opts && opts->cu_budget != 0)
     return fail(HC_ERR_UNSUPPORTED, "cu_budget is not supported by the compressed allreduce");
+  if (copy_engine(opts))
+    return fail(HC_ERR_UNSUPPORTED, "the compressed allreduce decodes during its all-gather: no copy_engine");
   if (d_wire_bytes && ((uintptr_t)d_wire_bytes & 7u))
     return fail(HC_ERR_INVALID_ARGUMENT, "d_wire_bytes is not 8-byte aligned");
   if ((st = check_ptrs(sendbufs, nranks, "sendbufs", 16))) return st;

@@ -74,12 +74,31 @@ typedef enum { HC_F32 = 0, HC_BF16 = 1 } hc_dtype_t;
  *     records step_events[k] on its stream right before ring step k and
  *     step_events[steps] after the last step, where steps =
  *     hc_step_count(op, nranks).  n_step_events < steps + 1 is
- *     HC_ERR_INVALID_ARGUMENT.  NULL records nothing. */
+ *     HC_ERR_INVALID_ARGUMENT.  NULL records nothing.
+ *   copy_engine: 0 = all-gather copy steps run as copy kernels on the
+ *     compute units; 1 = they run on the GPU's DMA copy engines
+ *     (hipMemcpyAsync of kind hipMemcpyDeviceToDeviceNoCU, stream ordered,
+ *     one copy per receiver and step), holding no compute unit at all.  This
+ *     is the offload of "HOCCL: Offloading Collective Communication from GPU
+ *     Cores to Accelerate Distributed Training" (section 2): a copy can leave
+ *     the cores, a reduction cannot, so reduce-scatter steps always run on
+ *     the compute units.  Applies to hc_all_gather, to the all-gather half of
+ *     hc_allreduce and to one-rank copies; hc_compressed_allreduce decodes
+ *     during its all-gather and rejects it (HC_ERR_UNSUPPORTED).  Other
+ *     values are HC_ERR_INVALID_ARGUMENT.  Which engine serves such a copy
+ *     is the HIP runtime's choice: measured on MI355X, the ROCm 7.2 runtime
+ *     in /opt/rocm uses the DMA engines (about 60 GB/s per copy, one copy at
+ *     a time per stream), while the runtime bundled with the PyTorch 2.10
+ *     wheel runs the same calls as blit kernels on the compute units.  The
+ *     values are identical either way.
+ *   reserved: must be 0. */
 typedef struct {
     double chunk_fraction;
     int32_t cu_budget;
     int32_t n_step_events;
     hipEvent_t *step_events;
+    int32_t copy_engine;
+    int32_t reserved;
 } hc_opts_t;
 
 /*
