@@ -88,6 +88,12 @@ def lib():
         L.or_hop_f32.restype = ctypes.c_uint32
         L.or_hop_bf16.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
         L.or_hop_bf16.restype = ctypes.c_uint16
+        L.or_sgd_f32.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_float]
+        L.or_sgd_f32.restype = ctypes.c_uint32
+        L.or_sgd_bf16.argtypes = [ctypes.c_uint16, ctypes.c_uint16, ctypes.c_float]
+        L.or_sgd_bf16.restype = ctypes.c_uint16
+        L.or_allreduce_sgd.argtypes = [PP, PP, PP, S, ctypes.c_int, ctypes.c_int, ctypes.c_float]
+        L.or_allreduce_sgd.restype = ctypes.c_int
         L.or_slice_len.argtypes = [S, ctypes.c_int]
         L.or_slice_len.restype = S
         L.or_chunk_elems.argtypes = [S, S]
@@ -224,6 +230,33 @@ def allreduce_fold(xs):
     rc = lib().or_allreduce_fold(xp, op, n, _dtype_code(xs[0]), R)
     if rc != OK:
         raise ValueError(f"or_allreduce_fold status {rc}")
+    return outs
+
+
+def sgd_f32(w: int, g: int, lr: float) -> int:
+    return int(lib().or_sgd_f32(w, g, lr))
+
+
+def sgd_bf16(w: int, g: int, lr: float) -> int:
+    return int(lib().or_sgd_bf16(w, g, lr))
+
+
+def allreduce_sgd(grads, weights, lr: float):
+    """Allreduce of the gradients fused with the update w - lr*g on each
+    slice owner's weights; returns the R weight buffers after the call (all
+    equal).  lr is taken as an fp32 value."""
+    grads = _check_same(grads)
+    weights = _check_same(weights)
+    if weights[0].dtype != grads[0].dtype or weights[0].size != grads[0].size or len(weights) != len(grads):
+        raise ValueError("grads and weights need one dtype, size and rank count")
+    R, n = len(grads), grads[0].size
+    outs = [np.empty_like(grads[0]) for _ in range(R)]
+    gp, _k1 = _ptrs(grads)
+    wp, _k2 = _ptrs(weights)
+    op, _k3 = _ptrs(outs)
+    rc = lib().or_allreduce_sgd(gp, wp, op, n, _dtype_code(grads[0]), R, lr)
+    if rc != OK:
+        raise ValueError(f"or_allreduce_sgd status {rc}")
     return outs
 
 

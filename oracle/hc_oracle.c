@@ -26,6 +26,10 @@
  *             is one execution of the algorithm) and section 3 (Transfer(src,
  *             dst, step, chunkId, opType) tasks; data dependencies exist only
  *             within one chunk).
+ *             The same section's fusion example: an AllReduce of gradients
+ *             followed by an elementwise optimizer update becomes a
+ *             ReduceScatter, the update on each rank's slice, and an
+ *             AllGather of the updated slices.
  *  [CCCL]     "CCCL: In-GPU Compression-Coupled Collective Communication",
  *             section 4.1 (sign and fraction sent raw, the 8-bit bf16 exponent
  *             coded from a frequency table), 4.3 (a local table per thread
@@ -50,6 +54,13 @@
  *    payload of a NaN result, so both sides agree on one.
  *  - Chunk = round_up(ceil(N/100), A) elements, A = 1024 (uncompressed) or
  *    16384 (compressed, one codec block).  Chunking never changes a value.
+ *  - Fused SGD update: with g the allreduce sum of the gradients (the fold
+ *    above) and w the owner's weight, the new weight is w - lr*g with the
+ *    product and the difference each rounded once in fp32 (no fused
+ *    multiply-add); in bf16 w and g are widened exactly and the difference is
+ *    rounded to bf16 nearest-even; a NaN result is the canonical quiet NaN.
+ *    The slice owner is rank j for slice j (where the reduce-scatter leaves
+ *    the sum); every rank ends with the owners' updated slices.
  *  - The codec byte format "HCZ1" (fixed-length dictionary codes plus an
  *    escape for the exponent, raw sign/mantissa byte) is defined in full
  *    above or_compress below.
@@ -115,6 +126,25 @@ uint16_t or_hop_bf16(uint16_t a, uint16_t b)
 {
     float s = or_bf16_to_f32(a) + or_bf16_to_f32(b);
     return or_f32_to_bf16(bits_of_f32(s));
+}
+
+/* Fused SGD update of one weight: w - lr*g, product and difference rounded
+ * once each in fp32. */
+uint32_t or_sgd_f32(uint32_t w, uint32_t g, float lr)
+{
+    float t = lr * f32_of_bits(g);
+    float r = f32_of_bits(w) - t;
+    if (r != r) return 0x7FC00000u;
+    return bits_of_f32(r);
+}
+
+/* The same on bf16 words: widen w and g, the fp32 steps above, round the
+ * result to bf16. */
+uint16_t or_sgd_bf16(uint16_t w, uint16_t g, float lr)
+{
+    float t = lr * or_bf16_to_f32(g);
+    float r = or_bf16_to_f32(w) - t;
+    return or_f32_to_bf16(bits_of_f32(r));
 }
 
 static size_t elem_size(int dtype) { return dtype == OR_F32 ? 4 : 2; }
@@ -218,6 +248,29 @@ int or_allreduce_fold(const void *const *x, void *const *out, size_t n, int dtyp
         for (int k = 2; k <= R; ++k)
             acc = hop(acc, load_elem(x[mod(j + k, R)], i, dtype), dtype);
         for (int r = 0; r < R; ++r) store_elem(out[r], i, dtype, acc);
+    }
+    return OR_OK;
+}
+
+/*
+ * Allreduce of gradients fused with an SGD update (CoCoNet's fusion): g is the
+ * fold above; the owner of slice j (rank j) updates its weights there, and
+ * every rank's output holds the updated weights.  w_in[r] are the ranks'
+ * weights before the call; only the owner's copy of a slice is read.
+ */
+int or_allreduce_sgd(const void *const *grads, const void *const *w_in, void *const *w_out, size_t n,
+                     int dtype, int R, float lr)
+{
+    if (R < 1 || (dtype != OR_F32 && dtype != OR_BF16)) return OR_INVALID;
+    size_t L = or_slice_len(n, R);
+    for (size_t i = 0; i < n; ++i) {
+        int j = (int)(i / L);
+        uint32_t g = load_elem(grads[mod(j + 1, R)], i, dtype);
+        for (int k = 2; k <= R; ++k)
+            g = hop(g, load_elem(grads[mod(j + k, R)], i, dtype), dtype);
+        uint32_t w = load_elem(w_in[j], i, dtype);
+        uint32_t nw = dtype == OR_F32 ? or_sgd_f32(w, g, lr) : or_sgd_bf16((uint16_t)w, (uint16_t)g, lr);
+        for (int r = 0; r < R; ++r) store_elem(w_out[r], i, dtype, nw);
     }
     return OR_OK;
 }
