@@ -10,8 +10,10 @@ allreduce (14 ring steps) over inputs already resident in HBM.
 Other workloads (--workload): ring_f32 (R=4 x 2^20 fp32), codec (2^28 bf16
 compress/decompress of weights, activations, gradients), compressed (the
 fused compressed ring, R=8 x 2^25 bf16), contention (R=8 reduce-scatter of
-2^28 bf16 on a CU-budget stream next to a bf16 8192^3 GEMM).  Each prints one
-JSON line of its own.
+2^28 bf16 on a CU-budget stream next to a bf16 8192^3 GEMM, plus the matching
+all-gather on CU copy kernels and on the DMA engines), fused_sgd (the allreduce
+of R=8 x 2^26 bf16 gradients fused with an SGD update of the weights).  Each
+prints one JSON line of its own.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 The headline time is K back-to-back calls with nothing else on the stream.
@@ -268,6 +270,60 @@ def bench_compressed(args):
             "ag_step_ms": round(sum(parts["ag"]) / len(parts["ag"]), 5)}
 
 
+def bench_fused_sgd(args):
+    """The allreduce of R=8 x 2^26 bf16 gradients fused with an SGD update of
+    replicated bf16 weights (hc_allreduce_sgd), next to the unfused sequence:
+    hc_allreduce of the gradients, then every rank updating its whole buffer
+    (torch's w.sub_(g, alpha=lr); rounding aside, the same arithmetic)."""
+    import torch
+
+    from collective_communication_amd import binding as hc
+    from collective_communication_amd import inputs
+
+    R, n, lr = 8, 1 << 26, 0.01
+    grads = inputs.ring_inputs_cuda("ring_bf16", R, n)
+    w0 = inputs.normal_bf16_cuda("fused_sgd", 0, n, 1.0)
+    weights = [w0.clone() for _ in range(R)]
+    sums = [torch.empty_like(g) for g in grads]
+
+    def fused():
+        hc.hc_allreduce_sgd(grads, weights, lr)
+
+    def unfused():
+        hc.hc_allreduce(grads, sums)
+        for w, g in zip(weights, sums):
+            w.sub_(g, alpha=lr)
+
+    for _ in range(args.warmup):
+        fused()
+        unfused()
+    ms = timed_ms(fused, args.steps)
+    ms_unfused = timed_ms(unfused, args.steps)
+    steps = hc.hc_step_count(hc.HC_OP_ALLREDUCE, R)
+    evsets = [hc.StepEvents([torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)])
+              for _ in range(args.steps)]
+    for k in range(args.steps):
+        hc.hc_allreduce_sgd(grads, weights, lr, step_events=evsets[k])
+    torch.cuda.synchronize()
+    last = [ev.elapsed_ms()[R - 2] for ev in evsets]
+    # bytes: R-2 plain reduce steps (read 2, write 1), the fused step (read 3,
+    # write 1), R-1 copy steps (read 1, write 1), every one over n elements
+    alg = 2 * n * (3 * (R - 2) + 4 + 2 * (R - 1))
+    alg_unfused = 2 * n * (3 * (R - 1) + 2 * (R - 1)) + 2 * n * R * 3
+    return {"metric": "Allreduce fused with an SGD update: algbw and achieved HBM GB/s, R=8, 2^26 bf16",
+            "value": round(n * 2 / (ms / 1e3) / 1e9, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": f"hc_allreduce_sgd, R={R} x {n} bf16 gradients N(0,1e-3) with 1% zeros, "
+                                   f"replicated bf16 weights N(0,1), lr={lr}"},
+            "hbm_gbps": round(alg / (ms / 1e3) / 1e9, 1),
+            "hbm_frac_of_peak": round(alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4), "alg_bytes": alg,
+            "fused_step_ms": round(sum(last) / len(last), 5),
+            "fused_step_gbps": round(8 * n / (sum(last) / len(last) / 1e3) / 1e9, 1),
+            "unfused_ms": round(ms_unfused, 5), "unfused_alg_bytes": alg_unfused,
+            "speedup_vs_unfused": round(ms_unfused / ms, 3)}
+
+
 def bench_contention(args):
     import torch
 
@@ -393,7 +449,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ring_bf16",
-                    choices=["ring_bf16", "ring_f32", "codec", "compressed", "contention"])
+                    choices=["ring_bf16", "ring_f32", "codec", "compressed", "contention", "fused_sgd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 26,
                     help="elements per rank the oracle baseline runs on (default: the whole workload)")
@@ -415,6 +471,8 @@ def main():
         line = bench_codec(args)
     elif args.workload == "compressed":
         line = bench_compressed(args)
+    elif args.workload == "fused_sgd":
+        line = bench_fused_sgd(args)
     else:
         line = bench_contention(args)
     print(json.dumps(line), flush=True)

@@ -38,7 +38,7 @@ EXPORTED = [
     "hc_allreduce", "hc_reduce_scatter", "hc_all_gather", "hc_compress_bound_bf16",
     "hc_compress_bf16", "hc_decompress_bf16", "hc_compressed_allreduce", "hc_workspace_bytes",
     "hc_stream_create_cu_budget", "hc_stream_destroy", "hc_chunk_elems", "hc_ring_tasks",
-    "hc_status_string", "hc_last_error", "hc_version", "hc_step_count",
+    "hc_status_string", "hc_last_error", "hc_version", "hc_step_count", "hc_allreduce_sgd",
 ]
 
 
@@ -78,6 +78,7 @@ def load(path: str = LIB_PATH):
     L.hc_allreduce.argtypes = [PP, PP, S, I, I, O, P]
     L.hc_reduce_scatter.argtypes = [PP, PP, S, I, I, P, S, O, P]
     L.hc_all_gather.argtypes = [PP, PP, S, I, I, O, P]
+    L.hc_allreduce_sgd.argtypes = [PP, PP, S, I, I, ctypes.c_float, O, P]
     L.hc_compress_bound_bf16.argtypes = [S]
     L.hc_compress_bound_bf16.restype = S
     L.hc_compress_bf16.argtypes = [P, S, P, S, P, P, S, P]
@@ -93,7 +94,7 @@ def load(path: str = LIB_PATH):
     L.hc_step_count.argtypes = [I, I]
     L.hc_step_count.restype = I
     L.hc_ring_tasks.restype = S
-    for name in ("hc_allreduce", "hc_reduce_scatter", "hc_all_gather", "hc_compress_bf16",
+    for name in ("hc_allreduce", "hc_reduce_scatter", "hc_all_gather", "hc_allreduce_sgd", "hc_compress_bf16",
                  "hc_decompress_bf16", "hc_compressed_allreduce", "hc_stream_create_cu_budget",
                  "hc_stream_destroy"):
         getattr(L, name).restype = I
@@ -194,6 +195,26 @@ def hc_allreduce(sendbufs, recvbufs, count: int | None = None, *, chunk_fraction
     rp, _k2 = _ptr_array(recvbufs, count, "recvbufs")
     _check(L.hc_allreduce(sp, rp, count, dt, R, _opts(chunk_fraction, cu_budget, step_events, copy_engine),
                           _stream_handle(stream)))
+
+
+def hc_allreduce_sgd(grads, weights, lr: float, count: int | None = None, *, chunk_fraction: float = 0.0,
+                     cu_budget: int = 0, step_events: StepEvents | None = None, copy_engine: int = 0,
+                     stream=None):
+    """Allreduce of grads fused with weights <- weights - lr * sum (see
+    include/hc.h); grads are overwritten with partial sums."""
+    L = load()
+    R = len(grads)
+    if len(weights) != R:
+        raise ValueError("one weight buffer per rank")
+    if count is None:
+        count = grads[0].numel()
+    dt = _dtype(grads[0])
+    if any(t.dtype != grads[0].dtype for t in list(grads) + list(weights)):
+        raise TypeError("all buffers need one dtype")
+    gp, _k1 = _ptr_array(grads, count, "grads")
+    wp, _k2 = _ptr_array(weights, count, "weights")
+    _check(L.hc_allreduce_sgd(gp, wp, count, dt, R, float(lr),
+                              _opts(chunk_fraction, cu_budget, step_events, copy_engine), _stream_handle(stream)))
 
 
 def hc_reduce_scatter(sendbufs, recvbufs, recvcount: int | None = None, ws=None, *,

@@ -6,6 +6,9 @@
 //  * bf16 hop: widen both operands exactly (bf16 is the top half of an fp32
 //    word), one fp32 add, round the sum to bf16 nearest-even.
 //  * a NaN sum becomes the canonical quiet NaN (0x7FC00000 / 0x7FC0).
+//  * SGD update (the fused allreduce + update): w - lr*g with the product and
+//    the difference rounded once each in fp32 (no fused multiply-add); bf16
+//    operands are widened exactly and the result rounded to bf16 as above.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -49,6 +52,28 @@ __device__ __forceinline__ uint4 hop_bf16x8(uint4 a, uint4 b) {
 
 __device__ __forceinline__ uint4 hop_f32x4(uint4 a, uint4 b) {
   return make_uint4(hop_f32(a.x, b.x), hop_f32(a.y, b.y), hop_f32(a.z, b.z), hop_f32(a.w, b.w));
+}
+
+__device__ __forceinline__ uint32_t sgd_f32(uint32_t w, uint32_t g, float lr) {
+  const float t = lr * bits_f32(g);
+  const float r = bits_f32(w) - t;
+  return (r != r) ? 0x7FC00000u : f32_bits(r);
+}
+
+// Two bf16 updates on packed pairs of weights and gradients.
+__device__ __forceinline__ uint32_t sgd_bf16x2(uint32_t w, uint32_t g, float lr) {
+  const float lo = bits_f32(w << 16) - lr * bits_f32(g << 16);
+  const float hi = bits_f32(w & 0xFFFF0000u) - lr * bits_f32(g & 0xFFFF0000u);
+  return bf16_rne(f32_bits(lo)) | (bf16_rne(f32_bits(hi)) << 16);
+}
+
+__device__ __forceinline__ uint4 sgd_bf16x8(uint4 w, uint4 g, float lr) {
+  return make_uint4(sgd_bf16x2(w.x, g.x, lr), sgd_bf16x2(w.y, g.y, lr), sgd_bf16x2(w.z, g.z, lr),
+                    sgd_bf16x2(w.w, g.w, lr));
+}
+
+__device__ __forceinline__ uint4 sgd_f32x4(uint4 w, uint4 g, float lr) {
+  return make_uint4(sgd_f32(w.x, g.x, lr), sgd_f32(w.y, g.y, lr), sgd_f32(w.z, g.z, lr), sgd_f32(w.w, g.w, lr));
 }
 
 // Streaming 16-byte global accesses.

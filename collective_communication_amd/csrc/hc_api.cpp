@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <string>
+#include <cmath>
 #include <vector>
 
 #include "hc.h"
@@ -171,6 +172,53 @@ hc_status_t run_allreduce(void* const* send, void* const* recv, size_t count, hc
   return e == hipSuccess ? HC_SUCCESS : device_fail(e, "hipEventRecord");
 }
 
+// The allreduce task list with the reduce-scatter run in place on the
+// gradients and its last step fused with the update of the owner's weights;
+// the all-gather then spreads the updated weight slices.
+hc_status_t run_allreduce_sgd(void* const* grads, void* const* weights, size_t count, hc_dtype_t dtype, int R,
+                              size_t chunk, float lr, int budget, bool dma, Tap& tap, hipStream_t stream) {
+  const size_t es = esize(dtype);
+  std::vector<hc_task_t> tasks = hc::ring_tasks(R, count, chunk);
+  size_t k = 0;
+  while (k < tasks.size()) {
+    const int op = tasks[k].op, step = tasks[k].step;
+    const bool last_rs = op == 1 && step == R - 2;
+    hc::Seg segs[hc::kMaxSegs];
+    int nseg = 0, last_dst = -1;
+    uint64_t last_end = 0;
+    while (k < tasks.size() && tasks[k].op == op && tasks[k].step == step) {
+      const hc_task_t& t = tasks[k];
+      const size_t off = t.off * es;
+      if (t.dst == last_dst && t.off == last_end) {
+        segs[nseg - 1].len += t.len;
+      } else {
+        if (op == 1) {  // partials stay in the gradients; the last step writes weights
+          segs[nseg].a = cp(grads[t.src], off);
+          segs[nseg].b = cp(grads[t.dst], off);
+          segs[nseg].dst = last_rs ? mp(weights[t.dst], off) : mp(grads[t.dst], off);
+        } else {
+          segs[nseg].a = cp(weights[t.src], off);
+          segs[nseg].b = nullptr;
+          segs[nseg].dst = mp(weights[t.dst], off);
+        }
+        segs[nseg].len = t.len;
+        ++nseg;
+      }
+      last_dst = t.dst;
+      last_end = t.off + t.len;
+      ++k;
+    }
+    hipError_t e = tap.mark(stream);
+    if (e != hipSuccess) return device_fail(e, "hipEventRecord");
+    if (op == 1) e = last_rs ? hc::launch_sgd_step(segs, nseg, dtype, lr, budget, stream)
+                             : hc::launch_reduce_step(segs, nseg, dtype, budget, stream);
+    else e = copy_step(segs, nseg, es, budget, dma, stream);
+    if (e != hipSuccess) return device_fail(e, op == 1 ? "reduce step launch" : "copy step launch");
+  }
+  hipError_t e = tap.mark(stream);
+  return e == hipSuccess ? HC_SUCCESS : device_fail(e, "hipEventRecord");
+}
+
 // One-rank operations: a single step that copies (or nothing in place).
 hc_status_t run_single(const void* src, void* dst, size_t count, size_t es, int budget, bool dma, Tap& tap,
                        hipStream_t stream) {
@@ -251,6 +299,40 @@ hc_status_t hc_allreduce(void* const* sendbufs, void* const* recvbufs, size_t co
     return run_single(sendbufs[0], recvbufs[0], count, es, cu_budget(opts), copy_engine(opts), tap, stream);
   return run_allreduce(sendbufs, recvbufs, count, dtype, nranks, chunk, cu_budget(opts), copy_engine(opts), tap,
                        stream);
+}
+
+hc_status_t hc_allreduce_sgd(void* const* grads, void* const* weights, size_t count, hc_dtype_t dtype,
+                             int nranks, float lr, const hc_opts_t* opts, hipStream_t stream) {
+  g_last_error.clear();
+  hc_status_t st = check_common(nranks, dtype, opts);
+  if (st) return st;
+  if (!(lr == lr) || lr == INFINITY || lr == -INFINITY)
+    return fail(HC_ERR_INVALID_ARGUMENT, "lr is not finite");
+  if (count == 0) return HC_SUCCESS;
+  if ((st = check_ptrs(grads, nranks, "grads", esize(dtype)))) return st;
+  if ((st = check_ptrs(weights, nranks, "weights", esize(dtype)))) return st;
+  if (count > ((size_t)1 << 40)) return fail(HC_ERR_INVALID_ARGUMENT, "count %zu too large", count);
+  const size_t es = esize(dtype);
+  // Every buffer is written: all 2R ranges must be pairwise disjoint.
+  std::vector<Range> all;
+  for (int r = 0; r < nranks; ++r) all.push_back({(uintptr_t)grads[r], (uintptr_t)grads[r] + count * es});
+  for (int r = 0; r < nranks; ++r) all.push_back({(uintptr_t)weights[r], (uintptr_t)weights[r] + count * es});
+  for (size_t i = 0; i < all.size(); ++i)
+    for (size_t j = i + 1; j < all.size(); ++j)
+      if (overlap(all[i], all[j]))
+        return fail(HC_ERR_INVALID_ARGUMENT, "buffers %zu and %zu overlap (grads 0..R-1, then weights)", i, j);
+  Tap tap;
+  if ((st = make_tap(opts, HC_OP_ALLREDUCE, nranks, &tap))) return st;
+  if (nranks == 1) {  // the sum is the one gradient: one update step
+    hipError_t e = tap.mark(stream);
+    hc::Seg seg{grads[0], nullptr, weights[0], count};
+    if (e == hipSuccess) e = hc::launch_sgd_step(&seg, 1, dtype, lr, cu_budget(opts), stream);
+    if (e == hipSuccess) e = tap.mark(stream);
+    return e == hipSuccess ? HC_SUCCESS : device_fail(e, "update launch");
+  }
+  const size_t chunk = hc::chunk_elems(count, chunk_fraction(opts), 1024);
+  return run_allreduce_sgd(grads, weights, count, dtype, nranks, chunk, lr, cu_budget(opts), copy_engine(opts),
+                           tap, stream);
 }
 
 size_t hc_workspace_bytes(hc_op_t op, size_t count, int nranks, hc_dtype_t dtype) {

@@ -26,6 +26,11 @@ hipError_t launch_reduce_step(const Seg* segs, int nseg, hc_dtype_t dtype, int c
                               hipStream_t stream);
 hipError_t launch_copy_step(const Seg* segs, int nseg, size_t elem_bytes, int cu_budget,
                             hipStream_t stream);
+// The last reduce-scatter step fused with an SGD update: g = hop(a, b) (or
+// g = a when b is NULL, a one-rank "sum"), then dst = dst - lr*g in place
+// (dst holds the owner's weights).
+hipError_t launch_sgd_step(const Seg* segs, int nseg, hc_dtype_t dtype, float lr, int cu_budget,
+                           hipStream_t stream);
 
 // Codec.
 hipError_t launch_fill_u32(void* dst, uint32_t value, size_t words, hipStream_t stream);

@@ -11,6 +11,13 @@
 // coalesced 1 KB loads, marked non-temporal.  Both kernels are HBM bound: a reduce hop reads 2
 // and writes 1 element per element of the step, a copy hop reads 1, writes 1.
 //
+// The last reduce-scatter step of the fused allreduce + SGD update
+// ("Breaking the computation and communication abstraction barrier in
+// distributed machine learning workloads", "The idea": the optimizer update
+// moves between the ReduceScatter and the AllGather) reads the owner's weight
+// from the destination and writes the updated weight there: 3 reads, 1 write
+// per element.
+//
 // One launch covers one whole ring step: up to 64 segments (one per
 // receiver), cut into 4096-element (bf16) / 2048-element (fp32) tiles, one
 // tile per workgroup, or a persistent grid-stride loop when the caller gives
@@ -64,6 +71,12 @@ __device__ __forceinline__ void st_stream(char* p, uint4 v) {
   }
 }
 
+// Step operations.
+constexpr int kCopy = 0;     // dst = a
+constexpr int kReduce = 1;   // dst = hop(a, b)
+constexpr int kSgd = 2;      // dst = dst - lr * hop(a, b)
+constexpr int kSgdOne = 3;   // dst = dst - lr * a (one rank: the sum is a)
+
 struct SegArgs {
   const void* a[kMaxSegs];
   const void* b[kMaxSegs];
@@ -71,6 +84,7 @@ struct SegArgs {
   uint64_t len[kMaxSegs];
   uint32_t tile0[kMaxSegs + 1];  // first tile of each segment; tile0[nseg] = total
   int32_t nseg;
+  float lr;
 };
 
 template <int ES>
@@ -80,6 +94,21 @@ __device__ __forceinline__ uint32_t scalar_hop(uint32_t a, uint32_t b) {
   } else {
     return bf16_rne(f32_bits(bits_f32(a << 16) + bits_f32(b << 16)));
   }
+}
+
+template <int ES>
+__device__ __forceinline__ uint32_t scalar_sgd(uint32_t w, uint32_t g, float lr) {
+  if constexpr (ES == 4) {
+    return sgd_f32(w, g, lr);
+  } else {
+    return bf16_rne(f32_bits(bits_f32(w << 16) - lr * bits_f32(g << 16)));
+  }
+}
+
+template <int ES>
+__device__ __forceinline__ uint4 vec_sgd(uint4 w, uint4 g, float lr) {
+  if constexpr (ES == 4) return sgd_f32x4(w, g, lr);
+  else return sgd_bf16x8(w, g, lr);
 }
 
 template <int ES>
@@ -100,11 +129,14 @@ __device__ __forceinline__ uint4 vec_hop(uint4 a, uint4 b) {
   else return hop_bf16x8(a, b);
 }
 
-// ES: element bytes (4 fp32, 2 bf16).  REDUCE: recvReduceCopy, else copy.
-// VEC: every segment pointer is 16-byte aligned, so whole tiles move as
-// 16-byte vectors; otherwise (odd slice offsets) each lane moves elements.
-template <int ES, bool REDUCE, bool VEC>
+// ES: element bytes (4 fp32, 2 bf16).  OP: kCopy, kReduce (recvReduceCopy),
+// kSgd, kSgdOne.  VEC: every segment pointer is 16-byte aligned, so whole
+// tiles move as 16-byte vectors; otherwise (odd slice offsets) each lane
+// moves elements.
+template <int ES, int OP, bool VEC>
 __global__ __launch_bounds__(kThreads) void step_kernel(SegArgs args) {
+  constexpr bool kUsesB = OP == kReduce || OP == kSgd;
+  constexpr bool kUpdates = OP == kSgd || OP == kSgdOne;
   constexpr int V = 16 / ES;
   constexpr uint64_t kTile = (uint64_t)kThreads * V * kUnroll;
   const uint32_t total = args.tile0[args.nseg];
@@ -122,25 +154,31 @@ __global__ __launch_bounds__(kThreads) void step_kernel(SegArgs args) {
     const char* pb = static_cast<const char*>(args.b[s]);
     char* pd = static_cast<char*>(args.dst[s]);
     if (VEC && base + kTile <= len) {
-      uint4 va[kUnroll], vb[kUnroll];
+      uint4 va[kUnroll], vb[kUnroll], vw[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const uint64_t off = (base + (uint64_t)(u * kThreads + tid) * V) * ES;
         va[u] = ld_stream<HC_RING_NT_A>(pa + off);
-        if constexpr (REDUCE) vb[u] = ld_stream<HC_RING_NT_B>(pb + off);
+        if constexpr (kUsesB) vb[u] = ld_stream<HC_RING_NT_B>(pb + off);
+        if constexpr (kUpdates) vw[u] = ld16(pd + off);
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const uint64_t off = (base + (uint64_t)(u * kThreads + tid) * V) * ES;
-        if constexpr (REDUCE) st_stream(pd + off, vec_hop<ES>(va[u], vb[u]));
-        else st_stream(pd + off, va[u]);
+        if constexpr (OP == kCopy) st_stream(pd + off, va[u]);
+        else if constexpr (OP == kReduce) st_stream(pd + off, vec_hop<ES>(va[u], vb[u]));
+        else if constexpr (OP == kSgd) st_stream(pd + off, vec_sgd<ES>(vw[u], vec_hop<ES>(va[u], vb[u]), args.lr));
+        else st_stream(pd + off, vec_sgd<ES>(vw[u], va[u], args.lr));
       }
     } else {
       const uint64_t end = base + kTile < len ? base + kTile : len;
       for (uint64_t i = base + tid; i < end; i += kThreads) {
         const uint32_t x = ld_elem<ES>(pa, i);
-        if constexpr (REDUCE) st_elem<ES>(pd, i, scalar_hop<ES>(x, ld_elem<ES>(pb, i)));
-        else st_elem<ES>(pd, i, x);
+        if constexpr (OP == kCopy) st_elem<ES>(pd, i, x);
+        else if constexpr (OP == kReduce) st_elem<ES>(pd, i, scalar_hop<ES>(x, ld_elem<ES>(pb, i)));
+        else if constexpr (OP == kSgd)
+          st_elem<ES>(pd, i, scalar_sgd<ES>(ld_elem<ES>(pd, i), scalar_hop<ES>(x, ld_elem<ES>(pb, i)), args.lr));
+        else st_elem<ES>(pd, i, scalar_sgd<ES>(ld_elem<ES>(pd, i), x, args.lr));
       }
     }
   }
@@ -148,8 +186,9 @@ __global__ __launch_bounds__(kThreads) void step_kernel(SegArgs args) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-template <int ES, bool REDUCE>
-hipError_t launch_step(const Seg* segs, int nseg, int cu_budget, hipStream_t stream) {
+template <int ES, int OP>
+hipError_t launch_step(const Seg* segs, int nseg, int cu_budget, hipStream_t stream, float lr = 0.0f) {
+  constexpr bool kUsesB = OP == kReduce || OP == kSgd;
   constexpr uint64_t kTile = (uint64_t)kThreads * (16 / ES) * kUnroll;
   if (nseg <= 0) return hipSuccess;
   if (nseg > kMaxSegs) return hipErrorInvalidValue;
@@ -160,26 +199,26 @@ hipError_t launch_step(const Seg* segs, int nseg, int cu_budget, hipStream_t str
   for (int i = 0; i < nseg; ++i) {
     if (segs[i].len == 0) continue;
     args.a[k] = segs[i].a;
-    args.b[k] = REDUCE ? segs[i].b : segs[i].a;
+    args.b[k] = kUsesB ? segs[i].b : segs[i].a;
     args.dst[k] = segs[i].dst;
     args.len[k] = segs[i].len;
     args.tile0[k] = (uint32_t)tiles;
     tiles += (segs[i].len + kTile - 1) / kTile;
-    vec = vec && aligned16(segs[i].a) && aligned16(segs[i].dst) &&
-          (!REDUCE || aligned16(segs[i].b));
+    vec = vec && aligned16(segs[i].a) && aligned16(segs[i].dst) && (!kUsesB || aligned16(segs[i].b));
     ++k;
   }
   if (k == 0) return hipSuccess;
   if (tiles >= 0xFFFFFFFFull) return hipErrorInvalidValue;
   args.nseg = k;
   args.tile0[k] = (uint32_t)tiles;
+  args.lr = lr;
   uint32_t grid = (uint32_t)tiles;
   if (cu_budget > 0) {
     const uint64_t cap = (uint64_t)cu_budget * kWgPerCuBudget;
     if (grid > cap) grid = (uint32_t)cap;
   }
-  if (vec) hipLaunchKernelGGL((step_kernel<ES, REDUCE, true>), dim3(grid), dim3(kThreads), 0, stream, args);
-  else hipLaunchKernelGGL((step_kernel<ES, REDUCE, false>), dim3(grid), dim3(kThreads), 0, stream, args);
+  if (vec) hipLaunchKernelGGL((step_kernel<ES, OP, true>), dim3(grid), dim3(kThreads), 0, stream, args);
+  else hipLaunchKernelGGL((step_kernel<ES, OP, false>), dim3(grid), dim3(kThreads), 0, stream, args);
   return hipGetLastError();
 }
 
@@ -187,14 +226,24 @@ hipError_t launch_step(const Seg* segs, int nseg, int cu_budget, hipStream_t str
 
 hipError_t launch_reduce_step(const Seg* segs, int nseg, hc_dtype_t dtype, int cu_budget,
                               hipStream_t stream) {
-  if (dtype == HC_F32) return launch_step<4, true>(segs, nseg, cu_budget, stream);
-  return launch_step<2, true>(segs, nseg, cu_budget, stream);
+  if (dtype == HC_F32) return launch_step<4, kReduce>(segs, nseg, cu_budget, stream);
+  return launch_step<2, kReduce>(segs, nseg, cu_budget, stream);
+}
+
+hipError_t launch_sgd_step(const Seg* segs, int nseg, hc_dtype_t dtype, float lr, int cu_budget,
+                           hipStream_t stream) {
+  const bool one = nseg > 0 && segs[0].b == nullptr;
+  if (dtype == HC_F32)
+    return one ? launch_step<4, kSgdOne>(segs, nseg, cu_budget, stream, lr)
+               : launch_step<4, kSgd>(segs, nseg, cu_budget, stream, lr);
+  return one ? launch_step<2, kSgdOne>(segs, nseg, cu_budget, stream, lr)
+             : launch_step<2, kSgd>(segs, nseg, cu_budget, stream, lr);
 }
 
 hipError_t launch_copy_step(const Seg* segs, int nseg, size_t elem_bytes, int cu_budget,
                             hipStream_t stream) {
-  if (elem_bytes == 4) return launch_step<4, false>(segs, nseg, cu_budget, stream);
-  return launch_step<2, false>(segs, nseg, cu_budget, stream);
+  if (elem_bytes == 4) return launch_step<4, kCopy>(segs, nseg, cu_budget, stream);
+  return launch_step<2, kCopy>(segs, nseg, cu_budget, stream);
 }
 
 }  // namespace hc

@@ -30,7 +30,7 @@ import numpy as np
 ROOT_SEED = 20261202
 
 WORKLOAD_IDS = {"ring_f32": 1, "ring_bf16": 2, "codec": 3, "compressed": 4, "contention": 5,
-                "test": 99}
+                "fused_sgd": 6, "test": 99}
 
 
 def rng_for(workload: str | int, index: int) -> np.random.Generator:

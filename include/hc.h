@@ -148,6 +148,34 @@ hc_status_t hc_all_gather(void *const *sendbufs, void *const *recvbufs, size_t s
                           hc_dtype_t dtype, int nranks, const hc_opts_t *opts,
                           hipStream_t stream);
 
+/*
+ * hc_allreduce_sgd -- the allreduce of gradients fused with an SGD update of
+ * the weights: "Breaking the computation and communication abstraction
+ * barrier in distributed machine learning workloads" ("The idea") moves an
+ * elementwise optimizer update between the ReduceScatter and the AllGather,
+ * so that each rank updates only the slice whose sum it holds and the
+ * AllGather spreads updated weights instead of summed gradients.
+ *   grads[r], weights[r]: count elements each, dtype HC_F32 or HC_BF16,
+ *     element-aligned; all 2*nranks buffers pairwise disjoint.
+ *   g = the ring allreduce sum of the grads, exactly as hc_allreduce computes
+ *     it (same fold order, same per-hop rounding).  For slice j (the
+ *     hc_allreduce slicing) the new weight is weights[j] - lr*g, the product
+ *     and the difference rounded once each in fp32 (bf16: operands widened
+ *     exactly, result rounded to nearest even; a NaN result is the canonical
+ *     quiet NaN).  On return every weights[r] holds the new weights; slice j
+ *     comes from rank j's weights before the call (when every rank holds the
+ *     same weights, as in data-parallel training, that is simply w - lr*g).
+ *   grads are the reduction's scratch: their contents after the call are
+ *     partial sums, unspecified.
+ *   lr: any finite float (not finite: HC_ERR_INVALID_ARGUMENT).
+ *   opts: chunk_fraction, cu_budget, step_events (2*(nranks-1) steps, 1 for
+ *     one rank) and copy_engine (the all-gather copies) as for hc_allreduce.
+ * Asynchronous on stream; argument errors are detected before anything is
+ * enqueued.
+ */
+hc_status_t hc_allreduce_sgd(void *const *grads, void *const *weights, size_t count, hc_dtype_t dtype,
+                             int nranks, float lr, const hc_opts_t *opts, hipStream_t stream);
+
 /* Largest HCZ1 stream for n bf16 elements (every block stored raw):
  * 32 + round_up(8*n_blocks, 16) + sum over blocks of 16 + round_up(2*m, 16). */
 size_t hc_compress_bound_bf16(size_t n);

@@ -119,6 +119,13 @@ def test_argument_errors_before_any_launch(hc):
     o = hc.hc_opts_t(0.0, 0, 0, None, 1, 0)
     assert L.hc_compressed_allreduce(good, good2, 1 << 16, 2, 0x900000, 1 << 30, None, ctypes.byref(o),
                                      None) == hc.HC_ERR_UNSUPPORTED
+    # fused allreduce + SGD: lr must be finite; grads and weights may not overlap
+    assert L.hc_allreduce_sgd(good, good2, 16, hc.HC_F32, 2, float("nan"), None, None) == E
+    assert L.hc_allreduce_sgd(good, good2, 16, hc.HC_F32, 2, float("inf"), None, None) == E
+    assert L.hc_allreduce_sgd(good, good, 16, hc.HC_F32, 2, 0.1, None, None) == E
+    assert b"overlap" in L.hc_last_error()
+    assert L.hc_allreduce_sgd(null, good2, 16, hc.HC_F32, 2, 0.1, None, None) == E
+    assert L.hc_allreduce_sgd(good, good2, 0, hc.HC_F32, 2, 0.1, None, None) == hc.HC_SUCCESS
     # count 0 is a no-op success
     assert L.hc_allreduce(good, good2, 0, hc.HC_F32, 2, None, None) == hc.HC_SUCCESS
     # reduce-scatter: missing / small / misaligned workspace
