@@ -114,6 +114,8 @@ def lib():
         L.or_plan_block.restype = ctypes.c_int
         L.or_compress.argtypes = [P, S, P, S]
         L.or_compress.restype = S
+        L.or_compress_scoped.argtypes = [P, S, P, S, S]
+        L.or_compress_scoped.restype = S
         L.or_decompress.argtypes = [P, S, P, S]
         L.or_decompress.restype = ctypes.c_int
         L.or_compressed_allreduce.argtypes = [PP, PP, S, ctypes.c_int, S,
@@ -342,6 +344,18 @@ def compress(v: np.ndarray) -> bytes:
     sz = int(lib().or_compress(v.ctypes.data, v.size, out.ctypes.data, cap))
     if sz == 0:
         raise RuntimeError("oracle compress: capacity")
+    return out[:sz].tobytes()
+
+
+def compress_scoped(v: np.ndarray, group: int) -> bytes:
+    """HCZ1 stream whose code tables are shared by groups of `group` full
+    blocks (0: one table for the whole stream); group 1 is compress()."""
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    cap = compress_bound(v.size)
+    out = np.zeros(cap, dtype=np.uint8)
+    sz = int(lib().or_compress_scoped(v.ctypes.data, v.size, out.ctypes.data, cap, group))
+    if sz == 0:
+        raise RuntimeError("oracle compress_scoped: capacity")
     return out[:sz].tobytes()
 
 

@@ -503,12 +503,11 @@ int or_plan_block(const uint16_t *v, size_t m, or_block_plan_t *plan)
     return OR_OK;
 }
 
-/* Encode one block into rec (which has room for plan->rec_bytes). */
-static void encode_block(const uint16_t *v, size_t m, uint8_t *rec)
+/* Write one block's record for a decided plan and symbol order into rec
+ * (which has room for plan.rec_bytes). */
+static void write_record(const uint16_t *v, size_t m, const or_block_plan_t plan, const int order[256],
+                         uint8_t *rec)
 {
-    or_block_plan_t plan;
-    int order[256];
-    plan_block(v, m, &plan, order);
     memset(rec, 0, plan.rec_bytes);
     rec[0] = (uint8_t)plan.mode;
     rec[1] = (uint8_t)plan.b;
@@ -538,6 +537,15 @@ static void encode_block(const uint16_t *v, size_t m, uint8_t *rec)
         sm[i] = (uint8_t)(((v[i] >> 8) & 0x80) | (v[i] & 0x7F));
         if (code == K) esc[ne++] = (uint8_t)e;
     }
+}
+
+/* Encode one block into rec with its own table (the HCZ1 rule). */
+static void encode_block(const uint16_t *v, size_t m, uint8_t *rec)
+{
+    or_block_plan_t plan;
+    int order[256];
+    plan_block(v, m, &plan, order);
+    write_record(v, m, plan, order, rec);
 }
 
 /*
@@ -570,6 +578,92 @@ size_t or_compress(const uint16_t *in, size_t n, uint8_t *out, size_t cap)
         encode_block(in + k * HCZ_B, m, out + off);
         off += get_u32(out + off + 12);
     }
+    return total;
+}
+
+/*
+ * Table-scope variant (the sample-size question of CCCL section 4.3, and the
+ * global-table baseline of section 4.2): one symbol order and one code length
+ * b for each group of `group` consecutive full blocks (group = 0: all full
+ * blocks of the stream share one table).  The order is (count desc, symbol
+ * asc) over the group's summed histogram; b minimizes the sum over the
+ * group's full blocks of their coded record sizes (ties: smaller b); a block
+ * whose coded record would not be smaller than its raw record is raw, and
+ * partial blocks are raw.  Every record still carries its dictionary, so the
+ * stream is an ordinary HCZ1 stream.  group = 1 is or_compress exactly.
+ * Returns the stream size, or 0 when cap is too small.
+ */
+size_t or_compress_scoped(const uint16_t *in, size_t n, uint8_t *out, size_t cap, size_t group)
+{
+    size_t nb = ceil_div(n, HCZ_B), nfull = n / HCZ_B;
+    size_t G = group == 0 ? (nfull ? nfull : 1) : group;
+    size_t ngroups = nfull ? ceil_div(nfull, G) : 0;
+    int (*orders)[256] = (int (*)[256])malloc(sizeof(int[256]) * (ngroups ? ngroups : 1));
+    int *bs = (int *)malloc(sizeof(int) * (ngroups ? ngroups : 1));
+    or_block_plan_t *plans = (or_block_plan_t *)malloc(sizeof(or_block_plan_t) * (nb ? nb : 1));
+    if (!orders || !bs || !plans) { free(orders); free(bs); free(plans); return 0; }
+    for (size_t g = 0; g < ngroups; ++g) {
+        size_t k0 = g * G, k1 = k0 + G < nfull ? k0 + G : nfull;
+        uint32_t hist[256] = {0};
+        for (size_t k = k0; k < k1; ++k)
+            for (size_t i = 0; i < HCZ_B; ++i) hist[(in[k * HCZ_B + i] >> 7) & 0xFF]++;
+        for (int t = 0; t < 256; ++t) orders[g][t] = t;
+        g_sort_counts = hist;
+        qsort(orders[g], 256, sizeof(int), by_count_then_symbol);
+        size_t best = 0;
+        int best_b = 0;
+        for (int b = 1; b <= 7; ++b) {
+            size_t K = ((size_t)1 << b) - 1, sum = 0;
+            for (size_t k = k0; k < k1; ++k) {
+                uint32_t bh[256] = {0};
+                for (size_t i = 0; i < HCZ_B; ++i) bh[(in[k * HCZ_B + i] >> 7) & 0xFF]++;
+                size_t covered = 0;
+                for (size_t r = 0; r < K; ++r) covered += bh[orders[g][r]];
+                sum += hcz_coded_bytes(b, HCZ_B - covered);
+            }
+            if (best_b == 0 || sum < best) { best = sum; best_b = b; }
+        }
+        bs[g] = best_b;
+    }
+    size_t hdr = hcz_header_bytes(nb), total = hdr;
+    for (size_t k = 0; k < nb; ++k) {
+        size_t m = (k + 1) * HCZ_B <= n ? HCZ_B : n - k * HCZ_B;
+        or_block_plan_t *pl = &plans[k];
+        pl->m = (uint32_t)m; pl->mode = 0; pl->b = 0; pl->n_esc = 0;
+        pl->rec_bytes = (uint32_t)hcz_raw_bytes(m);
+        if (m == HCZ_B) {
+            size_t g = k / G;
+            int b = bs[g];
+            size_t K = ((size_t)1 << b) - 1;
+            uint32_t bh[256] = {0};
+            for (size_t i = 0; i < HCZ_B; ++i) bh[(in[k * HCZ_B + i] >> 7) & 0xFF]++;
+            size_t covered = 0;
+            for (size_t r = 0; r < K; ++r) covered += bh[orders[g][r]];
+            size_t size = hcz_coded_bytes(b, HCZ_B - covered);
+            if (size < hcz_raw_bytes(m)) {
+                pl->mode = 1; pl->b = b; pl->n_esc = (uint32_t)(HCZ_B - covered); pl->rec_bytes = (uint32_t)size;
+            }
+        }
+        total += pl->rec_bytes;
+    }
+    if (total > cap) { free(orders); free(bs); free(plans); return 0; }
+    memset(out, 0, hdr);
+    put_u32(out + 0, HCZ_MAGIC);
+    put_u32(out + 4, HCZ_B);
+    put_u64(out + 8, (uint64_t)n);
+    put_u32(out + 16, (uint32_t)nb);
+    put_u32(out + 20, 0);
+    put_u64(out + 24, (uint64_t)total);
+    size_t off = hdr;
+    int identity[256];
+    for (int t = 0; t < 256; ++t) identity[t] = t;
+    for (size_t k = 0; k < nb; ++k) {
+        size_t m = (k + 1) * HCZ_B <= n ? HCZ_B : n - k * HCZ_B;
+        put_u64(out + 32 + 8 * k, (uint64_t)off);
+        write_record(in + k * HCZ_B, m, plans[k], m == HCZ_B ? orders[k / G] : identity, out + off);
+        off += plans[k].rec_bytes;
+    }
+    free(orders); free(bs); free(plans);
     return total;
 }
 

@@ -1,0 +1,61 @@
+"""Pins of the oracle's table-scope variant of the HCZ1 encoder: code tables
+shared by groups of blocks ("CCCL: In-GPU Compression-Coupled Collective
+Communication", section 4.3, a table from a sample larger than one block)
+and one global table (section 4.2's baseline).  CPU only."""
+import numpy as np
+import pytest
+
+import oracle
+from collective_communication_amd import inputs
+
+B = 16384
+
+
+def weights(n, seed, sigma=0.02):
+    g = np.random.default_rng(seed)
+    return inputs.f32_to_bf16_bits((g.standard_normal(n) * sigma).astype(np.float32))
+
+
+@pytest.mark.parametrize("n", [0, 5, B, 3 * B + 77, 9 * B])
+def test_group_one_is_the_per_block_encoder(n):
+    v = weights(n, 10 + n)
+    assert oracle.compress_scoped(v, 1) == oracle.compress(v)
+
+
+@pytest.mark.parametrize("group", [2, 8, 0])
+def test_scoped_streams_round_trip(group):
+    n = 11 * B + 1234
+    # blocks with different scales, so that a shared table costs escapes
+    v = np.concatenate([weights(B, 100 + k, sigma=10.0 ** -(k % 4)) for k in range(11)] + [weights(1234, 7)])
+    s = oracle.compress_scoped(v, group)
+    rc, back = oracle.decompress(s, n)
+    assert rc == 0 and np.array_equal(back, v)
+    assert len(s) <= oracle.compress_bound(n)
+
+
+def test_two_block_hand_example():
+    """Block A: 16384 x 1.0 (exponent 127); block B: 16384 x 2.0 (exponent 128).
+    Own tables: b=1, no escapes, 16+16+2048+16384 = 18,464 B each; stream
+    32 + 16 + 2 x 18,464 = 36,976 B.  One shared table (group 2, or global):
+    order 127, 128, ...; b=1 would escape all of block B (sum 18,464 + 34,848),
+    b=2 codes both (2 x (16+16+4096+16384) = 41,024), b=3 costs 2 x 22,560:
+    b=2, stream 48 + 41,024 = 41,072 B."""
+    v = np.concatenate([np.full(B, 0x3F80, np.uint16), np.full(B, 0x4000, np.uint16)])
+    assert len(oracle.compress(v)) == 36976
+    for group in (2, 0):
+        s = oracle.compress_scoped(v, group)
+        assert len(s) == 41072
+        rec0 = int.from_bytes(s[32:40], "little")
+        assert s[rec0] == 1 and s[rec0 + 1] == 2          # coded, b = 2
+        assert s[rec0 + 16] == 127 and s[rec0 + 17] == 128  # dictionary in rank order
+        rc, back = oracle.decompress(s, v.size)
+        assert rc == 0 and np.array_equal(back, v)
+
+
+def test_global_table_ratio_within_a_few_percent_on_weights():
+    """The pages' claim: a local (sampled) table stays within 7% of a global
+    one.  On Gaussian weights the per-block, 8-block and global streams differ
+    by well under that."""
+    v = weights(32 * B, 3)
+    local, g8, glob = (len(oracle.compress_scoped(v, k)) for k in (1, 8, 0))
+    assert abs(local - glob) / glob < 0.07 and abs(g8 - glob) / glob < 0.07
