@@ -12,7 +12,9 @@ compress/decompress of weights, activations, gradients), compressed (the
 fused compressed ring, R=8 x 2^25 bf16), contention (R=8 reduce-scatter of
 2^28 bf16 on a CU-budget stream next to a bf16 8192^3 GEMM, plus the matching
 all-gather on CU copy kernels and on the DMA engines), fused_sgd (the allreduce
-of R=8 x 2^26 bf16 gradients fused with an SGD update of the weights).  Each
+of R=8 x 2^26 bf16 gradients fused with an SGD update of the weights),
+table_scope (the codec's code tables per block, per group of blocks or global,
+on 2^28 bf16 weights, gradients and a multi-layer gradient bucket).  Each
 prints one JSON line of its own.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -214,6 +216,52 @@ def bench_codec(args):
             "higher_is_better": True, "dtype": "u8", "data": "synthetic",
             "config": {"workload": "standalone lossless bf16 codec, 2^28 elements per tensor"},
             "tensors": rows, "hbm_frac_of_peak_worst": round(worst / PEAK_HBM_GBPS, 4)}
+
+
+def bench_table_scope(args):
+    import torch
+
+    from collective_communication_amd import binding as hc
+    from collective_communication_amd import inputs
+
+    n = 1 << 28
+    cap = hc.hc_compress_bound_bf16(n)
+    out = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    nbytes = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ws = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_COMPRESS_SCOPED, n, 1), dtype=torch.uint8, device="cuda")
+    back = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    scopes = [("per_block", None), ("group_1", 1), ("group_8", 8), ("group_64", 64), ("global", 0)]
+    rows = {}
+    for name, maker in (("weights", lambda: inputs.normal_bf16_cuda("codec", 0, n, 0.02)),
+                        ("gradients", lambda: inputs.normal_bf16_cuda("codec", 2, n, 1e-4)),
+                        ("bucket", lambda: inputs.bucket_bf16_cuda("bucket", 0, n))):
+        x = maker()
+        row = {}
+        for label, group in scopes:
+            if group is None:
+                call = lambda: hc.hc_compress_bf16(x, n, out, nbytes, ws)
+            else:
+                call = lambda g=group: hc.hc_compress_bf16_scoped(x, n, out, nbytes, g, ws)
+            for _ in range(args.warmup):
+                call()
+            ms = timed_ms(call, args.steps)
+            size = int(nbytes.item())
+            hc.hc_decompress_bf16(out, cap, back, n, status)
+            torch.cuda.synchronize()
+            ok = int(status.item()) == 0 and torch.equal(back.view(torch.int16), x.view(torch.int16))
+            row[label] = {"ratio": round(size / (2 * n), 5), "compressed_bytes": size, "compress_ms": round(ms, 4),
+                          "compress_raw_gbps": round(2 * n / ms / 1e6, 1), "round_trip_exact": ok}
+        rows[name] = row
+        del x
+    b = rows["bucket"]
+    return {"metric": "HCZ1 compressed/raw size of a 2^28 bf16 gradient bucket with per-block code tables",
+            "value": b["per_block"]["ratio"], "unit": "ratio", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "higher_is_better": False, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "code-table scope sweep: per block, groups of 1/8/64 blocks, one global "
+                                   "table; 2^28 bf16 per tensor"},
+            "global_over_per_block_size": round(b["global"]["ratio"] / b["per_block"]["ratio"], 4),
+            "tensors": rows}
 
 
 def bench_compressed(args):
@@ -449,7 +497,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ring_bf16",
-                    choices=["ring_bf16", "ring_f32", "codec", "compressed", "contention", "fused_sgd"])
+                    choices=["ring_bf16", "ring_f32", "codec", "compressed", "contention", "fused_sgd",
+                             "table_scope"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 26,
                     help="elements per rank the oracle baseline runs on (default: the whole workload)")
@@ -473,6 +522,8 @@ def main():
         line = bench_compressed(args)
     elif args.workload == "fused_sgd":
         line = bench_fused_sgd(args)
+    elif args.workload == "table_scope":
+        line = bench_table_scope(args)
     else:
         line = bench_contention(args)
     print(json.dumps(line), flush=True)

@@ -31,6 +31,7 @@ HC_OP_COMPRESS = 1
 HC_OP_COMPRESSED_ALLREDUCE = 2
 HC_OP_ALLREDUCE = 3
 HC_OP_ALL_GATHER = 4
+HC_OP_COMPRESS_SCOPED = 5
 HC_BLOCK_ELEMS = 16384
 HC_MAX_RANKS = 64
 
@@ -39,6 +40,7 @@ EXPORTED = [
     "hc_compress_bf16", "hc_decompress_bf16", "hc_compressed_allreduce", "hc_workspace_bytes",
     "hc_stream_create_cu_budget", "hc_stream_destroy", "hc_chunk_elems", "hc_ring_tasks",
     "hc_status_string", "hc_last_error", "hc_version", "hc_step_count", "hc_allreduce_sgd",
+    "hc_compress_bf16_scoped",
 ]
 
 
@@ -82,6 +84,7 @@ def load(path: str = LIB_PATH):
     L.hc_compress_bound_bf16.argtypes = [S]
     L.hc_compress_bound_bf16.restype = S
     L.hc_compress_bf16.argtypes = [P, S, P, S, P, P, S, P]
+    L.hc_compress_bf16_scoped.argtypes = [P, S, P, S, P, S, P, S, P]
     L.hc_decompress_bf16.argtypes = [P, S, P, S, P, P]
     L.hc_compressed_allreduce.argtypes = [PP, PP, S, I, P, S, P, O, P]
     L.hc_workspace_bytes.argtypes = [I, S, I, I]
@@ -95,7 +98,7 @@ def load(path: str = LIB_PATH):
     L.hc_step_count.restype = I
     L.hc_ring_tasks.restype = S
     for name in ("hc_allreduce", "hc_reduce_scatter", "hc_all_gather", "hc_allreduce_sgd", "hc_compress_bf16",
-                 "hc_decompress_bf16", "hc_compressed_allreduce", "hc_stream_create_cu_budget",
+                 "hc_compress_bf16_scoped", "hc_decompress_bf16", "hc_compressed_allreduce", "hc_stream_create_cu_budget",
                  "hc_stream_destroy"):
         getattr(L, name).restype = I
     L.hc_status_string.argtypes = [I]
@@ -286,6 +289,24 @@ def hc_compress_bf16(d_in: torch.Tensor, n: int, d_out: torch.Tensor, d_out_byte
     wsp = _dptr(ws, 1, "ws")
     _check(L.hc_compress_bf16(inp, n, outp, out_cap, ob, wsp, ws.numel() * ws.element_size(),
                               _stream_handle(stream)))
+
+
+def hc_compress_bf16_scoped(d_in: torch.Tensor, n: int, d_out: torch.Tensor, d_out_bytes: torch.Tensor,
+                            table_blocks: int, ws: torch.Tensor, *, stream=None):
+    """hc_compress_bf16 with one code table per table_blocks full blocks
+    (0: one table for the whole stream)."""
+    L = load()
+    if d_in.element_size() != 2:
+        raise TypeError("input must hold 16-bit words")
+    if table_blocks < 0:
+        raise ValueError("table_blocks must be >= 0")
+    inp = _dptr(d_in, 2 * n, "d_in") if n else (d_in.data_ptr() if d_in.numel() else None)
+    out_cap = d_out.numel() * d_out.element_size()
+    outp = _dptr(d_out, 1, "d_out")
+    ob = _dptr(d_out_bytes, 8, "d_out_bytes")
+    wsp = _dptr(ws, 1, "ws")
+    _check(L.hc_compress_bf16_scoped(inp, n, outp, out_cap, ob, table_blocks, wsp,
+                                     ws.numel() * ws.element_size(), _stream_handle(stream)))
 
 
 def hc_decompress_bf16(d_in: torch.Tensor, in_bytes: int, d_out: torch.Tensor, n: int,

@@ -303,22 +303,22 @@ __device__ __forceinline__ void zero_hist(Smem& s) {
   for (int i = 0; i < (int)(kHistCopies * 256 / 4 / kCT); ++i) s.stage[threadIdx.x + kCT * i] = make_uint4(0, 0, 0, 0);
 }
 
-// ZEROED: the caller has already cleared the sub-histograms (zero_hist) and
-// passed a barrier since.
+// 256-bin histogram of a full block's exponents.  Returns the count of
+// exponent t to thread t < 256 (the "owner" of bin t) and 0 to the others;
+// the sub-histograms stay in the staging buffer.  ZEROED: the caller cleared
+// them (zero_hist) and passed a barrier since.  Ends with no barrier after
+// the owners' reads: the caller syncs before reusing the staging buffer.
+//
+// 32 sub-histograms, bin-major: the count of exponent e in copy c is word
+// 32e + c.  Lane l adds into copy l % 32, so the 32 lanes of a half-wave
+// always hit 32 different banks, and the byte address of bin e is e << 7 OR
+// c << 2: for the low element of a word that is the word ANDed with 0x7F80
+// (its exponent field already sits at bit 7).  Thread t sums the 32 copies
+// of bin t: eight 16-byte reads, started at a different quad in each group of
+// eight lanes to spread the banks.
 template <bool ZEROED = false>
-__device__ __forceinline__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, Smem& s) {
+__device__ __forceinline__ uint32_t block_histogram(const uint4 (&v)[kPer], Smem& s) {
   const uint32_t t = threadIdx.x, lane = __lane_id();
-  Plan p;
-  p.m = m;
-  if (m != kB) {  // partial blocks travel raw
-    p.mode = 0; p.b = 0; p.K = 0; p.n_esc = 0; p.rec_bytes = raw_bytes(m);
-    return p;
-  }
-  // 32 sub-histograms, bin-major: the count of exponent e in copy c is word
-  // 32e + c.  Lane l adds into copy l % 32, so the 32 lanes of a half-wave
-  // always hit 32 different banks, and the byte address of bin e is e << 7
-  // OR c << 2: for the low element of a word that is the word ANDed with
-  // 0x7F80 (its exponent field already sits at bit 7).
   uint8_t* sub8 = stage8(s);
   if constexpr (!ZEROED) {
     zero_hist(s);
@@ -337,19 +337,30 @@ __device__ __forceinline__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, S
     }
   }
   __syncthreads();
-  // Threads 0..255 (the first four waves) own one exponent bin each from here
-  // to the code table.  Thread t sums the 32 copies of bin t: eight 16-byte
-  // reads, started at a different quad in each group of eight lanes to
-  // spread the banks.  Other threads hold count 0 and write nothing.
-  const bool owner = t < 256u;
   uint32_t cnt = 0;
-  if (owner) {
+  if (t < 256u) {
 #pragma unroll
     for (uint32_t i = 0; i < 8; ++i) {
       const uint4 q = s.stage[t * 8 + ((i + t) & 7u)];
       cnt += q.x + q.y + q.z + q.w;
     }
   }
+  return cnt;
+}
+
+// ZEROED: the caller has already cleared the sub-histograms (zero_hist) and
+// passed a barrier since.
+template <bool ZEROED = false>
+__device__ __forceinline__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, Smem& s) {
+  const uint32_t t = threadIdx.x, lane = __lane_id();
+  Plan p;
+  p.m = m;
+  if (m != kB) {  // partial blocks travel raw
+    p.mode = 0; p.b = 0; p.K = 0; p.n_esc = 0; p.rec_bytes = raw_bytes(m);
+    return p;
+  }
+  const bool owner = t < 256u;
+  const uint32_t cnt = block_histogram<ZEROED>(v, s);
   // Rank = position in (count desc, exponent asc); key order is that order.
   const uint32_t key = (cnt << 8) | (255u - t);
   const uint64_t nzmask = __ballot(cnt > 0);
@@ -429,6 +440,28 @@ __device__ __forceinline__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, S
     const uint32_t rank = s.rank_of[t];
     s.code_of[t] = (uint8_t)(rank < p.K ? rank : p.K);
     if (rank < dict_bytes(p.b)) stage8(s)[16 + rank] = rank < p.K ? (uint8_t)t : (uint8_t)0;
+  }
+  __syncthreads();
+  return p;
+}
+
+// Shared code tables (the table-scope variant): the plan of a full block
+// from its group's symbol order (rank -> exponent, 256 bytes), the group's
+// code length b and the block's escape count for that b; a coded record is
+// not smaller than the raw one travels raw.  Leaves code_of[] and the
+// dictionary in LDS like plan_block.  Ends with a barrier.
+__device__ __forceinline__ Plan given_plan(const uint8_t* order, uint32_t b, uint32_t n_esc, uint32_t m, Smem& s) {
+  const uint32_t t = threadIdx.x;
+  Plan p;
+  p.m = m;
+  p.mode = 0; p.b = 0; p.K = 0; p.n_esc = 0; p.rec_bytes = raw_bytes(m);
+  if (m == kB && b >= 1 && b <= 7 && coded_bytes(b, n_esc) < kRawFull) {
+    p.mode = 1; p.b = b; p.K = (1u << b) - 1u; p.n_esc = n_esc; p.rec_bytes = coded_bytes(b, n_esc);
+  }
+  if (p.mode == 1 && t < 256u) {
+    const uint32_t sym = order[t];   // the exponent of rank t
+    s.code_of[sym] = (uint8_t)(t < p.K ? t : p.K);
+    if (t < dict_bytes(p.b)) stage8(s)[16 + t] = t < p.K ? (uint8_t)sym : (uint8_t)0;
   }
   __syncthreads();
   return p;

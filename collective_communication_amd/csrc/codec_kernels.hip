@@ -45,6 +45,32 @@ struct CompressWs {
 };
 constexpr size_t kCompressWsHeader = 64;
 
+// Shared-table pieces of the table-scope variant, laid out after the
+// look-back workspace (worst case: one group per block).
+struct ScopeWs {
+  uint32_t* ghist;                 // [groups][256] summed exponent counts
+  uint16_t* bhist;                 // [full blocks][256] each block's counts
+  uint8_t* order;                  // [groups][256] rank -> exponent
+  uint32_t* gb;                    // [groups] chosen b
+  uint32_t* esc;                   // [full blocks][8] escapes per b (index b, 1..7)
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Byte offsets of the ScopeWs arrays after a base of `base` bytes, for
+// `groups` groups and `full` full blocks; returns the end.
+size_t scope_layout(size_t base, size_t groups, size_t full, size_t (&off)[5]) {
+  size_t o = align256(base);
+  off[0] = o; o = align256(o + groups * 256 * 4);
+  off[1] = o; o = align256(o + full * 256 * 2);
+  off[2] = o; o = align256(o + groups * 256);
+  off[3] = o; o = align256(o + groups * 4);
+  off[4] = o; o = align256(o + full * 8 * 4);
+  return o;
+}
+
+constexpr uint32_t kSumChunk = 64;  // blocks one workgroup adds into a group histogram (at least)
+
 __device__ __forceinline__ void publish(uint64_t* d, uint64_t v) {
   __hip_atomic_store(d, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -89,21 +115,30 @@ __global__ void empty_stream_kernel(uint8_t* out, uint64_t* out_bytes) {
   *out_bytes = 32;
 }
 
-__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void compress_kernel(const uint16_t* __restrict__ in, uint64_t n,
-                                                            uint8_t* __restrict__ out,
-                                                            uint64_t* __restrict__ out_bytes,
-                                                            CompressWs* __restrict__ ws, uint32_t nb) {
+// SCOPED: the block's code table comes from its group's shared table (sc),
+// built by the scope kernels below, instead of its own histogram.
+template <bool SCOPED>
+__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void compress_kernel(
+    const uint16_t* __restrict__ in, uint64_t n, uint8_t* __restrict__ out, uint64_t* __restrict__ out_bytes,
+    CompressWs* __restrict__ ws, uint32_t nb, ScopeWs sc, uint32_t group) {
   __shared__ Smem s;
   const int t = threadIdx.x;
   if (t == 0) s.plan[6] = atomicAdd(&ws->ticket, 1u);
-  zero_hist(s);  // while the ticket is on its way
+  if constexpr (!SCOPED) zero_hist(s);  // while the ticket is on its way
   __syncthreads();
   const uint32_t bid = s.plan[6];
   const uint64_t first = (uint64_t)bid * kB;
   const uint32_t m = (uint32_t)((n - first) < kB ? (n - first) : kB);
   uint4 v[kPer];
   load_block(in + first, m, v);
-  const Plan p = plan_block<true>(v, m, s);
+  Plan p;
+  if constexpr (SCOPED) {
+    const uint32_t g = bid / group;  // only read for full blocks
+    p = m == kB ? given_plan(sc.order + 256ull * g, sc.gb[g], sc.esc[8ull * bid + sc.gb[g]], m, s)
+                : given_plan(nullptr, 0, 0, m, s);
+  } else {
+    p = plan_block<true>(v, m, s);
+  }
   if (t == 0) publish(&ws->desc[bid], (bid == 0 ? kFlagIncl : kFlagAgg) | p.rec_bytes);
   write_block(v, p, s);
   if (t < 64) {
@@ -157,6 +192,140 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
       write_stream_header(out, n, nb, total);
       *out_bytes = __hip_atomic_load(&ws->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? 0 : total;
     }
+  }
+}
+
+// Table scope, step 1: each full block's exponent histogram.  A workgroup
+// walks blocks blockIdx.x, + gridDim.x, ... and loads the next block while it
+// counts the current one.
+__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void scope_hist_kernel(
+    const uint16_t* __restrict__ in, ScopeWs sc, uint32_t full) {
+  __shared__ Smem s;
+  const uint32_t t = threadIdx.x, stride = gridDim.x;
+  uint32_t k = blockIdx.x;
+  uint4 v[kPer], nv[kPer];
+  if (k < full) load_block(in + (uint64_t)k * kB, kB, v);
+  for (; k < full; k += stride) {
+    const uint32_t kn = k + stride;
+    if (kn < full) load_block(in + (uint64_t)kn * kB, kB, nv);
+    const uint32_t cnt = block_histogram<false>(v, s);   // cnt <= 16384
+    if (t < 256u) sc.bhist[256ull * k + t] = (uint16_t)cnt;
+    __syncthreads();   // the counts are read before the next block clears them
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) v[i] = nv[i];
+  }
+}
+
+// Step 2: each group's histogram, `chunk` blocks per workgroup (grid:
+// groups x chunks per group), added into the zeroed ghist.
+__global__ __launch_bounds__(256) void scope_sum_kernel(ScopeWs sc, uint32_t group, uint32_t full, uint32_t chunk) {
+  const uint32_t g = blockIdx.x, t = threadIdx.x;
+  const uint64_t g0 = (uint64_t)g * group;
+  const uint64_t k0 = g0 + (uint64_t)blockIdx.y * chunk;
+  const uint64_t gend = g0 + group < full ? g0 + group : full;
+  const uint64_t k1 = k0 + chunk < gend ? k0 + chunk : gend;
+  uint32_t sum = 0;
+  for (uint64_t k = k0; k < k1; ++k) sum += sc.bhist[256ull * k + t];
+  if (sum) atomicAdd(&sc.ghist[256ull * g + t], sum);
+}
+
+// Step 3: each group's symbol order, (count desc, exponent asc).  Exponents
+// that never occur rank last in exponent order; the occurring ones (a few
+// dozen in practice) are compacted and ranked against each other only.
+__global__ __launch_bounds__(256) void scope_rank_kernel(ScopeWs sc) {
+  __shared__ unsigned long long key[256];
+  __shared__ uint32_t wcount[4];
+  const uint32_t g = blockIdx.x, t = threadIdx.x, lane = t & 63u, wave = t >> 6;
+  const uint32_t cnt = sc.ghist[256ull * g + t];
+  const unsigned long long mine = ((unsigned long long)cnt << 8) | (255u - t);
+  const uint64_t nz = __ballot(cnt > 0);
+  if (lane == 0) wcount[wave] = (uint32_t)__popcll(nz);
+  __syncthreads();
+  uint32_t before = 0, total = 0;
+#pragma unroll
+  for (uint32_t w = 0; w < 4; ++w) {
+    before += w < wave ? wcount[w] : 0u;
+    total += wcount[w];
+  }
+  const uint32_t nz_below = before + (uint32_t)__popcll(nz & ((1ull << lane) - 1ull));
+  if (cnt) key[nz_below] = mine;
+  __syncthreads();
+  uint32_t rank;
+  if (cnt) {
+    rank = 0;
+    for (uint32_t j = 0; j < total; ++j) rank += key[j] > mine;
+  } else {
+    rank = total + (t - nz_below);
+  }
+  sc.order[256ull * g + rank] = (uint8_t)t;
+}
+
+// Step 4: every full block's escapes for each b under its group's order:
+// an inclusive scan of the block's counts in rank order, read at 2^b - 1.
+__global__ __launch_bounds__(128) void scope_esc_kernel(ScopeWs sc, uint32_t group) {
+  __shared__ uint32_t scan[2][128];
+  const uint32_t k = blockIdx.x, t = threadIdx.x, g = k / group;
+  uint32_t x = t < 127u ? sc.bhist[256ull * k + sc.order[256ull * g + t]] : 0u;
+  int cur = 0;
+  scan[cur][t] = x;
+  __syncthreads();
+#pragma unroll
+  for (uint32_t d = 1; d < 128; d <<= 1) {
+    x = scan[cur][t] + (t >= d ? scan[cur][t - d] : 0u);
+    cur ^= 1;
+    scan[cur][t] = x;
+    __syncthreads();
+  }
+  if (t >= 1u && t <= 7u) sc.esc[8ull * k + t] = kB - scan[cur][(1u << t) - 2u];
+}
+
+__device__ __forceinline__ uint32_t pick_b(const unsigned long long (&sum)[8]) {
+  uint32_t best_b = 1;
+#pragma unroll
+  for (uint32_t b = 2; b <= 7; ++b)
+    if (sum[b] < sum[best_b]) best_b = b;
+  return best_b;
+}
+
+// Step 5: each group's b, the smallest summed coded size over its blocks,
+// ties to the smaller b.  Small groups: one thread per group.
+__global__ __launch_bounds__(256) void scope_pick_small_kernel(ScopeWs sc, uint32_t group, uint32_t full,
+                                                               uint32_t groups) {
+  const uint32_t g = blockIdx.x * 256u + threadIdx.x;
+  if (g >= groups) return;
+  const uint64_t g0 = (uint64_t)g * group;
+  const uint64_t gend = g0 + group < full ? g0 + group : full;
+  unsigned long long sum[8] = {};
+  for (uint64_t k = g0; k < gend; ++k) {
+#pragma unroll
+    for (uint32_t b = 1; b <= 7; ++b) sum[b] += coded_bytes(b, sc.esc[8ull * k + b]);
+  }
+  sc.gb[g] = pick_b(sum);
+}
+
+// Large groups: a workgroup per group.
+__global__ __launch_bounds__(256) void scope_pick_kernel(ScopeWs sc, uint32_t group, uint32_t full) {
+  __shared__ unsigned long long part[4][8];
+  const uint32_t g = blockIdx.x, t = threadIdx.x, lane = t & 63u, wave = t >> 6;
+  const uint64_t g0 = (uint64_t)g * group;
+  const uint64_t gend = g0 + group < full ? g0 + group : full;
+  unsigned long long sum[8] = {};
+  for (uint64_t k = g0 + t; k < gend; k += 256) {
+#pragma unroll
+    for (uint32_t b = 1; b <= 7; ++b) sum[b] += coded_bytes(b, sc.esc[8ull * k + b]);
+  }
+#pragma unroll
+  for (uint32_t b = 1; b <= 7; ++b) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) sum[b] += __shfl_xor(sum[b], o);
+    if (lane == 0) part[wave][b] = sum[b];
+  }
+  __syncthreads();
+  if (t == 0) {
+    unsigned long long tot[8] = {};
+#pragma unroll
+    for (uint32_t b = 1; b <= 7; ++b) tot[b] = part[0][b] + part[1][b] + part[2][b] + part[3][b];
+    sc.gb[g] = pick_b(tot);
   }
 }
 
@@ -410,8 +579,59 @@ hipError_t launch_compress(const uint16_t* in, size_t n, void* out, uint64_t* ou
   if (nb >= (1ull << 31)) return hipErrorInvalidValue;
   hipError_t e = launch_fill_u32(ws, 0u, compress_ws_bytes(n) / 4, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(compress_kernel, dim3((uint32_t)nb), dim3(kCT), 0, stream, in, (uint64_t)n,
-                     static_cast<uint8_t*>(out), out_bytes, static_cast<CompressWs*>(ws), (uint32_t)nb);
+  hipLaunchKernelGGL(compress_kernel<false>, dim3((uint32_t)nb), dim3(kCT), 0, stream, in, (uint64_t)n,
+                     static_cast<uint8_t*>(out), out_bytes, static_cast<CompressWs*>(ws), (uint32_t)nb, ScopeWs{},
+                     1u);
+  return hipGetLastError();
+}
+
+size_t compress_scoped_ws_bytes(size_t n) {
+  const size_t full = n / kB;
+  size_t off[5];
+  return scope_layout(compress_ws_bytes(n), full, full, off);
+}
+
+hipError_t launch_compress_scoped(const uint16_t* in, size_t n, void* out, uint64_t* out_bytes, void* ws,
+                                  size_t group, hipStream_t stream) {
+  const size_t nb = ceil_div(n, kB), full = n / kB;
+  if (nb == 0) return launch_compress(in, n, out, out_bytes, ws, stream);
+  if (nb >= (1ull << 31)) return hipErrorInvalidValue;
+  // groups larger than the stream are one group; this keeps G within 32 bits
+  const size_t G = (group == 0 || group > full) ? (full ? full : 1) : group;
+  const size_t groups = full ? ceil_div(full, G) : 0;
+  size_t off[5];
+  const size_t base = compress_ws_bytes(n);
+  scope_layout(base, groups, full, off);
+  char* w = static_cast<char*>(ws);
+  ScopeWs sc{reinterpret_cast<uint32_t*>(w + off[0]), reinterpret_cast<uint16_t*>(w + off[1]),
+             reinterpret_cast<uint8_t*>(w + off[2]), reinterpret_cast<uint32_t*>(w + off[3]),
+             reinterpret_cast<uint32_t*>(w + off[4])};
+  // zero the look-back head and descriptors, and the group histograms
+  hipError_t e = launch_fill_u32(ws, 0u, base / 4, stream);
+  if (e == hipSuccess && groups) e = launch_fill_u32(w + off[0], 0u, groups * 256, stream);
+  if (e != hipSuccess) return e;
+  if (full) {
+    const uint32_t F = (uint32_t)full, Gu = (uint32_t)G;
+    // one resident round of workgroups (4 per CU of 256), each walking blocks
+    const uint32_t hist_grid = F < 1024u ? F : 1024u;
+    size_t chunk = kSumChunk;
+    while (ceil_div(G, chunk) > 32768) chunk *= 2;   // keeps grid.y small
+    const uint32_t chunks = (uint32_t)ceil_div(G, chunk);
+    hipLaunchKernelGGL(scope_hist_kernel, dim3(hist_grid), dim3(kCT), 0, stream, in, sc, F);
+    hipLaunchKernelGGL(scope_sum_kernel, dim3((uint32_t)groups, chunks), dim3(256), 0, stream, sc, Gu, F,
+                       (uint32_t)chunk);
+    hipLaunchKernelGGL(scope_rank_kernel, dim3((uint32_t)groups), dim3(256), 0, stream, sc);
+    hipLaunchKernelGGL(scope_esc_kernel, dim3(F), dim3(128), 0, stream, sc, Gu);
+    if (G <= 64)
+      hipLaunchKernelGGL(scope_pick_small_kernel, dim3((uint32_t)ceil_div(groups, 256)), dim3(256), 0, stream, sc,
+                         Gu, F, (uint32_t)groups);
+    else
+      hipLaunchKernelGGL(scope_pick_kernel, dim3((uint32_t)groups), dim3(256), 0, stream, sc, Gu, F);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(compress_kernel<true>, dim3((uint32_t)nb), dim3(kCT), 0, stream, in, (uint64_t)n,
+                     static_cast<uint8_t*>(out), out_bytes, static_cast<CompressWs*>(ws), (uint32_t)nb, sc,
+                     (uint32_t)G);
   return hipGetLastError();
 }
 

@@ -258,7 +258,8 @@ int hc_step_count(hc_op_t op, int nranks) {
     case HC_OP_REDUCE_SCATTER: return nranks - 1;
     case HC_OP_ALL_GATHER: return nranks - 1;
     case HC_OP_COMPRESSED_ALLREDUCE: return 2 * nranks - 1;
-    case HC_OP_COMPRESS: return -1;
+    case HC_OP_COMPRESS:
+    case HC_OP_COMPRESS_SCOPED: return -1;
   }
   return -1;
 }
@@ -343,6 +344,8 @@ size_t hc_workspace_bytes(hc_op_t op, size_t count, int nranks, hc_dtype_t dtype
       return 2 * count * esize(dtype);          // two slices per rank, R ranks
     case HC_OP_COMPRESS:
       return hc::compress_ws_bytes(count);
+    case HC_OP_COMPRESS_SCOPED:
+      return hc::compress_scoped_ws_bytes(count);
     case HC_OP_COMPRESSED_ALLREDUCE:
       if (dtype != HC_BF16) return 0;
       return hc::compressed_ar_ws_bytes(count, nranks);
@@ -464,8 +467,11 @@ size_t hc_compress_bound_bf16(size_t n) {
   return total;
 }
 
-hc_status_t hc_compress_bf16(const uint16_t* d_in, size_t n, void* d_out, size_t out_cap,
-                             uint64_t* d_out_bytes, void* d_ws, size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+// Both compress entry points; scoped = false is the per-block table rule.
+hc_status_t compress_common(const uint16_t* d_in, size_t n, void* d_out, size_t out_cap, uint64_t* d_out_bytes,
+                            void* d_ws, size_t ws_bytes, bool scoped, size_t table_blocks, hipStream_t stream) {
   g_last_error.clear();
   if (!d_out || !d_out_bytes || !d_ws || (n && !d_in))
     return fail(HC_ERR_INVALID_ARGUMENT, "NULL pointer argument");
@@ -475,16 +481,30 @@ hc_status_t hc_compress_bf16(const uint16_t* d_in, size_t n, void* d_out, size_t
   const size_t bound = hc_compress_bound_bf16(n);
   if (out_cap < bound)
     return fail(HC_ERR_INSUFFICIENT_CAPACITY, "out_cap %zu < bound %zu", out_cap, bound);
-  const size_t need = hc::compress_ws_bytes(n);
+  const size_t need = scoped ? hc::compress_scoped_ws_bytes(n) : hc::compress_ws_bytes(n);
   if (ws_bytes < need)
     return fail(HC_ERR_INSUFFICIENT_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, need);
   Range ir{(uintptr_t)d_in, (uintptr_t)d_in + 2 * n}, orr{(uintptr_t)d_out, (uintptr_t)d_out + bound},
       wr{(uintptr_t)d_ws, (uintptr_t)d_ws + need};
   if (overlap(ir, orr) || overlap(ir, wr) || overlap(orr, wr))
     return fail(HC_ERR_INVALID_ARGUMENT, "input, output and workspace must not overlap");
-  hipError_t e = hc::launch_compress(d_in, n, d_out, d_out_bytes, d_ws, stream);
+  hipError_t e = scoped ? hc::launch_compress_scoped(d_in, n, d_out, d_out_bytes, d_ws, table_blocks, stream)
+                        : hc::launch_compress(d_in, n, d_out, d_out_bytes, d_ws, stream);
   if (e == hipErrorNotSupported) return fail(HC_ERR_UNSUPPORTED, "compress not built");
   return e == hipSuccess ? HC_SUCCESS : device_fail(e, "compress launch");
+}
+
+}  // namespace
+
+hc_status_t hc_compress_bf16(const uint16_t* d_in, size_t n, void* d_out, size_t out_cap,
+                             uint64_t* d_out_bytes, void* d_ws, size_t ws_bytes, hipStream_t stream) {
+  return compress_common(d_in, n, d_out, out_cap, d_out_bytes, d_ws, ws_bytes, false, 1, stream);
+}
+
+hc_status_t hc_compress_bf16_scoped(const uint16_t* d_in, size_t n, void* d_out, size_t out_cap,
+                                    uint64_t* d_out_bytes, size_t table_blocks, void* d_ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  return compress_common(d_in, n, d_out, out_cap, d_out_bytes, d_ws, ws_bytes, true, table_blocks, stream);
 }
 
 hc_status_t hc_decompress_bf16(const void* d_in, size_t in_bytes, uint16_t* d_out, size_t n,

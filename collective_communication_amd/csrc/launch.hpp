@@ -39,6 +39,11 @@ hipError_t launch_compress(const uint16_t* in, size_t n, void* out, uint64_t* ou
 hipError_t launch_decompress(const void* in, size_t in_bytes, uint16_t* out, size_t n,
                              int32_t* status, hipStream_t stream);
 size_t compress_ws_bytes(size_t n);
+// Table-scope variant: code tables shared by groups of `group` full blocks
+// (0: one table for the whole stream).
+size_t compress_scoped_ws_bytes(size_t n);
+hipError_t launch_compress_scoped(const uint16_t* in, size_t n, void* out, uint64_t* out_bytes, void* ws,
+                                  size_t group, hipStream_t stream);
 
 // Compressed ring allreduce (bf16).
 size_t compressed_ar_ws_bytes(size_t count, int R);

@@ -14,6 +14,9 @@ describe them; the pages' nccl-tests sweeps span 2 MB to 1 GB per message):
   per-element mixture of N(0, 1) and Laplace(0, 4); gradients N(0, 1e-4)
 * ``compressed`` -- R=8 ranks x 2^25 bf16, N(0, 1e-3)
 * ``contention`` -- R=8 ranks x 2^28 bf16, N(0, 1e-3)
+* ``bucket``     -- a flattened gradient bucket of many layers: layer sizes
+  log-uniform in [2^12, 2^22) elements (so layer edges fall inside codec
+  blocks), layer l drawn N(0, s_l) with s_l log-uniform in [1e-5, 1e-1]
 
 N(mu, s) names the standard deviation s.  Seeds are
 ``SeedSequence([20261202, workload_id, index])``.  Two generators draw from
@@ -30,7 +33,7 @@ import numpy as np
 ROOT_SEED = 20261202
 
 WORKLOAD_IDS = {"ring_f32": 1, "ring_bf16": 2, "codec": 3, "compressed": 4, "contention": 5,
-                "fused_sgd": 6, "test": 99}
+                "fused_sgd": 6, "bucket": 7, "test": 99}
 
 
 def rng_for(workload: str | int, index: int) -> np.random.Generator:
@@ -63,6 +66,37 @@ def normal_bf16_cuda(workload, index: int, n: int, sigma: float, zero_frac: floa
         u = torch.rand(n, generator=g, device="cuda", dtype=torch.float32)
         x.masked_fill_(u < zero_frac, 0.0)
         del u
+    return x.to(torch.bfloat16)
+
+
+def bucket_layers(workload, index: int, n: int):
+    """Layer plan of a gradient bucket of n elements: (sizes, sigmas), drawn
+    on the host from the seed; the last layer is cut to fill n exactly."""
+    return _bucket_plan(rng_for(workload, index), n)
+
+
+def _bucket_plan(g: np.random.Generator, n: int):
+    sizes, sigmas, total = [], [], 0
+    while total < n:
+        size = int(2.0 ** g.uniform(12.0, 22.0))
+        size = min(size, n - total)
+        sizes.append(size)
+        sigmas.append(float(10.0 ** g.uniform(-5.0, -1.0)))
+        total += size
+    return sizes, sigmas
+
+
+def bucket_bf16_cuda(workload, index: int, n: int):
+    """Device bf16 tensor: a gradient bucket (see bucket_layers)."""
+    import torch
+
+    sizes, sigmas = bucket_layers(workload, index, n)
+    g = _cuda_gen(workload, index)
+    x = torch.randn(n, generator=g, device="cuda", dtype=torch.float32)
+    scale = torch.repeat_interleave(torch.tensor(sigmas, dtype=torch.float32),
+                                    torch.tensor(sizes, dtype=torch.int64)).to("cuda")
+    x.mul_(scale)
+    del scale
     return x.to(torch.bfloat16)
 
 
@@ -150,6 +184,15 @@ def activation_bf16(workload, index: int, n: int) -> np.ndarray:
     x = g.standard_normal(n, dtype=np.float32)
     lap = g.laplace(0.0, 4.0, n).astype(np.float32)
     x[pick] = lap[pick]
+    return f32_to_bf16_bits(x)
+
+
+def bucket_bf16(workload, index: int, n: int) -> np.ndarray:
+    """Host bf16 bits of a gradient bucket (see bucket_layers)."""
+    g = rng_for(workload, index)
+    sizes, sigmas = _bucket_plan(g, n)
+    x = g.standard_normal(n, dtype=np.float32)
+    x *= np.repeat(np.array(sigmas, dtype=np.float32), sizes)
     return f32_to_bf16_bits(x)
 
 

@@ -209,6 +209,29 @@ hc_status_t hc_compress_bf16(const uint16_t *d_in, size_t n, void *d_out, size_t
                              hipStream_t stream);
 
 /*
+ * hc_compress_bf16_scoped -- hc_compress_bf16 with code tables shared by
+ * groups of blocks.  "CCCL ...", section 4.3 weighs one global table (more
+ * work before any block can be coded) against a table per block (the
+ * overhead of many small tables) and picks the per-block one; this call
+ * makes the choice a parameter so both ends can be measured.
+ *   table_blocks: G >= 1 groups the full blocks in order, G at a time (the
+ *   last group may be shorter); 0 puts every full block in one group.  A
+ *   group's dictionary is its summed exponent histogram ranked count
+ *   descending, exponent ascending; its b (1..7) is the one with the fewest
+ *   summed coded bytes over its blocks, ties to the smaller b.  Each full
+ *   block is coded with its group's dictionary and b unless that record
+ *   would not be below 16 + 32768 bytes, then it is raw; the partial tail
+ *   block is raw.  Each record still carries its dictionary, so the result
+ *   is an ordinary HCZ1 stream for hc_decompress_bf16, and G = 1 writes the
+ *   same bytes as hc_compress_bf16.
+ *   d_ws: >= hc_workspace_bytes(HC_OP_COMPRESS_SCOPED, n, 1, HC_BF16) bytes
+ *   (independent of G).  Other arguments and errors as hc_compress_bf16.
+ */
+hc_status_t hc_compress_bf16_scoped(const uint16_t *d_in, size_t n, void *d_out, size_t out_cap,
+                                    uint64_t *d_out_bytes, size_t table_blocks, void *d_ws,
+                                    size_t ws_bytes, hipStream_t stream);
+
+/*
  * hc_decompress_bf16 -- exact inverse of hc_compress_bf16.
  *   d_in: in_bytes readable bytes holding a stream of n elements (the stream
  *   may be shorter than in_bytes).  d_out: n bf16 words.  d_status: one
@@ -247,7 +270,8 @@ typedef enum {
     HC_OP_COMPRESS = 1,
     HC_OP_COMPRESSED_ALLREDUCE = 2,
     HC_OP_ALLREDUCE = 3,
-    HC_OP_ALL_GATHER = 4
+    HC_OP_ALL_GATHER = 4,
+    HC_OP_COMPRESS_SCOPED = 5
 } hc_op_t;
 
 /* Workspace bytes for an operation; count = elements per rank buffer

@@ -63,6 +63,9 @@ def test_workspace_sizes(hc):
     assert hc.hc_workspace_bytes(hc.HC_OP_REDUCE_SCATTER, 8 * 1000, 8, hc.HC_BF16) == 2 * 8000 * 2
     assert hc.hc_workspace_bytes(hc.HC_OP_REDUCE_SCATTER, 7, 2, hc.HC_F32) == 0  # 7 % 2 != 0
     assert hc.hc_workspace_bytes(hc.HC_OP_COMPRESS, 1 << 20, 1) > 0
+    # the table-scope encoder also holds per-block histograms and escape counts
+    assert hc.hc_workspace_bytes(hc.HC_OP_COMPRESS_SCOPED, 1 << 20, 1) > \
+        hc.hc_workspace_bytes(hc.HC_OP_COMPRESS, 1 << 20, 1) + 64 * 256 * 2
     assert hc.hc_workspace_bytes(hc.HC_OP_COMPRESSED_ALLREDUCE, 1 << 20, 8, hc.HC_BF16) > 0
     assert hc.hc_workspace_bytes(hc.HC_OP_COMPRESSED_ALLREDUCE, 1 << 20, 8, hc.HC_F32) == 0
     assert hc.hc_workspace_bytes(hc.HC_OP_REDUCE_SCATTER, 64, 0, hc.HC_F32) == 0
@@ -137,6 +140,15 @@ def test_argument_errors_before_any_launch(hc):
     assert L.hc_compress_bf16(0x100000, 1000, 0x200000, 100, 0x300000, 0x400000, 1 << 20, None) == \
         hc.HC_ERR_INSUFFICIENT_CAPACITY
     assert L.hc_compress_bf16(0x100000, 1000, 0x200000, 1 << 20, None, 0x400000, 1 << 20, None) == E
+    # scoped compress: the plain encoder's workspace is too small, capacity below the bound
+    n = 1 << 20
+    small = hc.hc_workspace_bytes(hc.HC_OP_COMPRESS, n, 1)
+    assert L.hc_compress_bf16_scoped(0x10000000, n, 0x20000000, 1 << 24, 0x30000000, 0, 0x40000000, small,
+                                     None) == hc.HC_ERR_INSUFFICIENT_CAPACITY
+    assert L.hc_compress_bf16_scoped(0x10000000, n, 0x20000000, 100, 0x30000000, 4, 0x40000000, 1 << 26,
+                                     None) == hc.HC_ERR_INSUFFICIENT_CAPACITY
+    assert L.hc_compress_bf16_scoped(None, n, 0x20000000, 1 << 24, 0x30000000, 4, 0x40000000, 1 << 26,
+                                     None) == E
     # decompress: status word is required
     assert L.hc_decompress_bf16(0x100000, 1000, 0x200000, 100, None, None) == E
     # compressed allreduce: workspace too small
@@ -153,6 +165,7 @@ def test_step_counts(hc):
         assert hc.hc_step_count(hc.HC_OP_REDUCE_SCATTER, R) == R - 1
         assert hc.hc_step_count(hc.HC_OP_ALL_GATHER, R) == R - 1
         assert hc.hc_step_count(hc.HC_OP_COMPRESSED_ALLREDUCE, R) == 2 * R - 1
+    assert hc.hc_step_count(hc.HC_OP_COMPRESS_SCOPED, 2) == -1
     assert hc.hc_step_count(hc.HC_OP_ALLREDUCE, 1) == 1
     assert hc.hc_step_count(hc.HC_OP_ALLREDUCE, 0) == -1
 

@@ -59,3 +59,38 @@ def test_global_table_ratio_within_a_few_percent_on_weights():
     v = weights(32 * B, 3)
     local, g8, glob = (len(oracle.compress_scoped(v, k)) for k in (1, 8, 0))
     assert abs(local - glob) / glob < 0.07 and abs(g8 - glob) / glob < 0.07
+
+
+def test_shared_table_sends_a_block_raw():
+    """Block A: 16384 x 1.0 (exponent 127).  Block B: exponents 64..191, 128
+    of each, random sign and fraction.  Alone, B codes with b=7 (K=127 covers
+    all but one exponent: 128 escapes, 16+128+7x2048+16384+128 = 30,992 B).
+    Shared (group 2): exponent 127 leads, the rest tie at 128 and follow in
+    exponent order.  Summed sizes: b=1 codes A (18,464) and leaves B with
+    16,256 escapes (16+16+2048+16384+16256 = 34,720), 53,184 in all; b=7
+    gives 30,864 + 30,992 = 61,856; b=1 wins, and B's 34,720 is not below
+    the raw 32,784, so B goes raw: 48 + 18,464 + 32,784 = 51,296 B, against
+    48 + 18,464 + 30,992 = 49,504 B with per-block tables."""
+    g = np.random.default_rng(9)
+    a = np.full(B, 0x3F80, np.uint16)
+    e = np.repeat(np.arange(64, 192, dtype=np.uint16), 128)
+    g.shuffle(e)
+    b = (e << 7) | g.integers(0, 128, B).astype(np.uint16) | (g.integers(0, 2, B).astype(np.uint16) << 15)
+    v = np.concatenate([a, b.astype(np.uint16)])
+    assert len(oracle.compress(v)) == 49504
+    s = oracle.compress_scoped(v, 2)
+    assert len(s) == 51296
+    r0, r1 = (int.from_bytes(s[32 + 8 * k:40 + 8 * k], "little") for k in range(2))
+    assert (s[r0], s[r0 + 1]) == (1, 1) and (s[r1], s[r1 + 1]) == (0, 0)
+    rc, back = oracle.decompress(s, v.size)
+    assert rc == 0 and np.array_equal(back, v)
+
+
+def test_layered_bucket_favours_per_block_tables():
+    """A bucket of layers with different scales: sharing a table across layer
+    edges costs escapes, so the stream grows with the group, per-block
+    smallest and global largest (section 4.3's reason for per-block tables)."""
+    n = 256 * B
+    v = inputs.bucket_bf16("test", 3, n)
+    sizes = [len(oracle.compress_scoped(v, k)) for k in (1, 4, 32, 0)]
+    assert sizes == sorted(sizes) and sizes[0] < sizes[-1]
