@@ -16,6 +16,8 @@ function's C docstring cites the passage it follows:
   Resource-Efficient Scheduling for Collective Communication" (section 1);
 * the codec follows "CCCL: In-GPU Compression-Coupled Collective
   Communication", sections 4.1, 4.3, 4.4 and 5 ("Handling data alignment");
+* the entropy-coded variant (``hce_oracle.c``) codes the exponent with a
+  per-block canonical Huffman code instead (CCCL sections 4.1 and 6.5);
 * the contention rate follows "HOCCL: Offloading Collective Communication from
   GPU Cores to Accelerate Distributed Training", section 2 (its formula is
   lost from the page; the reading is stated in ``hc_oracle.c``).
@@ -33,7 +35,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "hc_oracle.c")
+_SRCS = [os.path.join(_HERE, "hc_oracle.c"), os.path.join(_HERE, "hce_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "liboracle_hc.so")
 
 F32 = 0
@@ -49,11 +51,13 @@ OP_COPY = 2
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (IEEE adds: no fast-math, no contraction)."""
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+    stale = not os.path.exists(_LIB_PATH) or any(
+        os.path.getmtime(_LIB_PATH) < os.path.getmtime(src) for src in _SRCS)
+    if force or stale:
         tmp = _LIB_PATH + ".tmp"
         subprocess.check_call(
             ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-             "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+             "-Wall", "-Wextra", "-o", tmp, *_SRCS, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -127,6 +131,18 @@ def lib():
         L.or_hop_bf16_array.restype = None
         L.or_hop_f32_array.argtypes = [P, P, P, S]
         L.or_hop_f32_array.restype = None
+        L.or_huff_lengths.argtypes = [P, ctypes.c_int, P]
+        L.or_huff_lengths.restype = ctypes.c_int
+        L.or_huff_codes.argtypes = [P, ctypes.c_int, P]
+        L.or_huff_codes.restype = None
+        L.or_hce_bound.argtypes = [S]
+        L.or_hce_bound.restype = S
+        L.or_hce_compress.argtypes = [P, S, P, S]
+        L.or_hce_compress.restype = S
+        L.or_hce_decompress.argtypes = [P, S, P, S]
+        L.or_hce_decompress.restype = ctypes.c_int
+        L.or_hce_plan_block.argtypes = [P, S, P]
+        L.or_hce_plan_block.restype = ctypes.c_int
         D = ctypes.POINTER(ctypes.c_double)
         L.or_contention_rate.argtypes = [D, D, S, D, D, D, S, ctypes.c_double]
         L.or_contention_rate.restype = ctypes.c_double
@@ -364,6 +380,58 @@ def decompress(stream: bytes, n: int):
     buf = np.frombuffer(stream, dtype=np.uint8).copy() if len(stream) else np.zeros(1, np.uint8)
     out = np.zeros(max(n, 1), dtype=np.uint16)
     rc = int(lib().or_decompress(buf.ctypes.data, len(stream), out.ctypes.data, n))
+    return rc, out[:n]
+
+
+# ----------------------------------------------------------------------------
+# entropy-coded variant (HCE1)
+# ----------------------------------------------------------------------------
+
+def huff_lengths(counts, lmax: int = 12) -> np.ndarray:
+    """Length-limited Huffman code lengths (uint8[256]) for 256 counts."""
+    c = np.ascontiguousarray(counts, dtype=np.uint32)
+    if c.size != 256:
+        raise ValueError("256 counts")
+    out = np.zeros(256, dtype=np.uint8)
+    lib().or_huff_lengths(c.ctypes.data, lmax, out.ctypes.data)
+    return out
+
+
+def huff_codes(lengths, lmax: int = 12) -> np.ndarray:
+    """Canonical codes (uint32[256], right-aligned) for 256 code lengths."""
+    ln = np.ascontiguousarray(lengths, dtype=np.uint8)
+    out = np.zeros(256, dtype=np.uint32)
+    lib().or_huff_codes(ln.ctypes.data, lmax, out.ctypes.data)
+    return out
+
+
+def hce_bound(n: int) -> int:
+    return int(lib().or_hce_bound(n))
+
+
+def hce_plan_block(v: np.ndarray):
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    out = np.zeros(4, dtype=np.uint32)
+    if lib().or_hce_plan_block(v.ctypes.data, v.size, out.ctypes.data) != 0:
+        raise ValueError("block size")
+    return {"mode": int(out[0]), "n_sym": int(out[1]), "n_words": int(out[2]), "rec_bytes": int(out[3])}
+
+
+def hce_compress(v: np.ndarray) -> bytes:
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    cap = hce_bound(v.size)
+    out = np.zeros(cap, dtype=np.uint8)
+    sz = int(lib().or_hce_compress(v.ctypes.data, v.size, out.ctypes.data, cap))
+    if sz == 0:
+        raise RuntimeError("oracle hce_compress: capacity")
+    return out[:sz].tobytes()
+
+
+def hce_decompress(stream: bytes, n: int):
+    """Returns (status, array).  On a corrupt stream the array is all zero."""
+    buf = np.frombuffer(stream, dtype=np.uint8).copy() if len(stream) else np.zeros(1, np.uint8)
+    out = np.zeros(max(n, 1), dtype=np.uint16)
+    rc = int(lib().or_hce_decompress(buf.ctypes.data, len(stream), out.ctypes.data, n))
     return rc, out[:n]
 
 
