@@ -14,8 +14,10 @@ fused compressed ring, R=8 x 2^25 bf16), contention (R=8 reduce-scatter of
 all-gather on CU copy kernels and on the DMA engines), fused_sgd (the allreduce
 of R=8 x 2^26 bf16 gradients fused with an SGD update of the weights),
 table_scope (the codec's code tables per block, per group of blocks or global,
-on 2^28 bf16 weights, gradients and a multi-layer gradient bucket).  Each
-prints one JSON line of its own.
+on 2^28 bf16 weights, gradients and a multi-layer gradient bucket), entropy
+(the HCE1 variant with per-block Huffman codes for the exponent, next to the
+fixed-length codec on the same 2^28 tensors).  Each prints one JSON line of
+its own.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 The headline time is K back-to-back calls with nothing else on the stream.
@@ -216,6 +218,54 @@ def bench_codec(args):
             "higher_is_better": True, "dtype": "u8", "data": "synthetic",
             "config": {"workload": "standalone lossless bf16 codec, 2^28 elements per tensor"},
             "tensors": rows, "hbm_frac_of_peak_worst": round(worst / PEAK_HBM_GBPS, 4)}
+
+
+def bench_entropy(args):
+    import torch
+
+    from collective_communication_amd import binding as hc
+    from collective_communication_amd import inputs
+
+    n = 1 << 28
+    cap = hc.hc_compress_bound_bf16(n)
+    out = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    nbytes = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ws = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_COMPRESS_ENTROPY, n, 1), dtype=torch.uint8, device="cuda")
+    back = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    coders = {"fixed": (hc.hc_compress_bf16, hc.hc_decompress_bf16),
+              "entropy": (hc.hc_compress_bf16_entropy, hc.hc_decompress_bf16_entropy)}
+    rows = {}
+    for name, maker in (("weights", lambda: inputs.normal_bf16_cuda("codec", 0, n, 0.02)),
+                        ("activations", lambda: inputs.activation_bf16_cuda("codec", 1, n)),
+                        ("gradients", lambda: inputs.normal_bf16_cuda("codec", 2, n, 1e-4)),
+                        ("bucket", lambda: inputs.bucket_bf16_cuda("bucket", 0, n))):
+        x = maker()
+        row = {}
+        for label, (comp, decomp) in coders.items():
+            for _ in range(args.warmup):
+                comp(x, n, out, nbytes, ws)
+            mc = timed_ms(lambda: comp(x, n, out, nbytes, ws), args.steps)
+            size = int(nbytes.item())
+            md = timed_ms(lambda: decomp(out, cap, back, n, status), args.steps)
+            ok = int(status.item()) == 0 and torch.equal(back.view(torch.int16), x.view(torch.int16))
+            raw = 2 * n
+            row[label] = {"ratio": round(size / raw, 5), "compressed_bytes": size, "compress_ms": round(mc, 4),
+                          "decompress_ms": round(md, 4), "compress_raw_gbps": round(raw / mc / 1e6, 1),
+                          "decompress_raw_gbps": round(raw / md / 1e6, 1),
+                          "compress_hbm_gbps": round((raw + size) / mc / 1e6, 1),
+                          "decompress_hbm_gbps": round((raw + size) / md / 1e6, 1), "round_trip_exact": ok}
+        row["entropy_size_saving"] = round(1 - row["entropy"]["ratio"] / row["fixed"]["ratio"], 4)
+        rows[name] = row
+        del x
+    w = rows["weights"]["entropy"]
+    return {"metric": "HCE1 (Huffman exponent) bf16 codec: compressed/raw size and throughput, 2^28 elements",
+            "value": min(r["entropy"]["compress_hbm_gbps"] for r in rows.values()), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "u8",
+            "data": "synthetic",
+            "config": {"workload": "entropy-coded exponent variant next to the fixed-length codec, 2^28 bf16 per "
+                                   "tensor (weights, activations, gradients, gradient bucket)"},
+            "weights_ratio": w["ratio"], "tensors": rows}
 
 
 def bench_table_scope(args):
@@ -498,7 +548,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ring_bf16",
                     choices=["ring_bf16", "ring_f32", "codec", "compressed", "contention", "fused_sgd",
-                             "table_scope"])
+                             "table_scope", "entropy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 26,
                     help="elements per rank the oracle baseline runs on (default: the whole workload)")
@@ -524,6 +574,8 @@ def main():
         line = bench_fused_sgd(args)
     elif args.workload == "table_scope":
         line = bench_table_scope(args)
+    elif args.workload == "entropy":
+        line = bench_entropy(args)
     else:
         line = bench_contention(args)
     print(json.dumps(line), flush=True)

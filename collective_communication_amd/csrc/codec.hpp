@@ -78,8 +78,11 @@ struct Smem {
   uint64_t misc[2];
 };
 
-__device__ __forceinline__ uint8_t* stage8(Smem& s) { return reinterpret_cast<uint8_t*>(s.stage); }
-__device__ __forceinline__ uint32_t* stage32(Smem& s) { return reinterpret_cast<uint32_t*>(s.stage); }
+// The staging buffer of any workgroup's LDS struct with a `stage` member.
+template <class S>
+__device__ __forceinline__ uint8_t* stage8(S& s) { return reinterpret_cast<uint8_t*>(s.stage); }
+template <class S>
+__device__ __forceinline__ uint32_t* stage32(S& s) { return reinterpret_cast<uint32_t*>(s.stage); }
 
 __host__ __device__ constexpr uint32_t dict_bytes(uint32_t b) { return (1u << b) < 16u ? 16u : (1u << b); }
 __host__ __device__ constexpr uint32_t coded_bytes(uint32_t b, uint32_t n_esc) {
@@ -298,7 +301,8 @@ __device__ __forceinline__ void store_block(uint16_t* dst, uint32_t m, const uin
 // (uniform).  Ends with a barrier.
 // Clears the sub-histograms (the first 32 KB of the staging buffer).  The
 // caller puts a barrier between this and plan_block<true>.
-__device__ __forceinline__ void zero_hist(Smem& s) {
+template <class S>
+__device__ __forceinline__ void zero_hist(S& s) {
 #pragma unroll
   for (int i = 0; i < (int)(kHistCopies * 256 / 4 / kCT); ++i) s.stage[threadIdx.x + kCT * i] = make_uint4(0, 0, 0, 0);
 }
@@ -316,8 +320,8 @@ __device__ __forceinline__ void zero_hist(Smem& s) {
 // (its exponent field already sits at bit 7).  Thread t sums the 32 copies
 // of bin t: eight 16-byte reads, started at a different quad in each group of
 // eight lanes to spread the banks.
-template <bool ZEROED = false>
-__device__ __forceinline__ uint32_t block_histogram(const uint4 (&v)[kPer], Smem& s) {
+template <bool ZEROED = false, class S>
+__device__ __forceinline__ uint32_t block_histogram(const uint4 (&v)[kPer], S& s) {
   const uint32_t t = threadIdx.x, lane = __lane_id();
   uint8_t* sub8 = stage8(s);
   if constexpr (!ZEROED) {
@@ -551,13 +555,15 @@ __device__ __forceinline__ void write_block(const uint4 (&v)[kPer], const Plan& 
 }
 
 // Copies a staged record (rec_bytes, a multiple of 16) to global memory.
-__device__ __forceinline__ void copy_out(const Smem& s, uint8_t* dst, uint32_t rec_bytes) {
+template <class S>
+__device__ __forceinline__ void copy_out(const S& s, uint8_t* dst, uint32_t rec_bytes) {
   const uint32_t n16 = rec_bytes / 16u;
   for (uint32_t i = threadIdx.x; i < n16; i += kCT) st16(dst + 16 * i, s.stage[i]);
 }
 
 // Copies a record from global memory into the staging buffer.
-__device__ __forceinline__ void copy_in(Smem& s, const uint8_t* src, uint32_t rec_bytes) {
+template <class S>
+__device__ __forceinline__ void copy_in(S& s, const uint8_t* src, uint32_t rec_bytes) {
   const uint32_t n16 = rec_bytes / 16u;
   for (uint32_t i = threadIdx.x; i < n16; i += kCT) s.stage[i] = ld16(src + 16 * i);
 }

@@ -22,6 +22,7 @@
 // slots, one per block (the preallocated regions of section 4.4).
 #include "codec.hpp"
 #include "launch.hpp"
+#include "lookback.hpp"
 #include "schedule.hpp"
 
 namespace hc {
@@ -29,21 +30,6 @@ namespace hc {
 using namespace codec;
 
 namespace {
-
-constexpr uint64_t kFlagAgg = 1ull << 62;
-constexpr uint64_t kFlagIncl = 2ull << 62;
-constexpr uint64_t kValueMask = (1ull << 62) - 1;
-constexpr uint32_t kSpinLimit = 1u << 22;
-
-// Workspace of hc_compress_bf16: a ticket counter, an error word, then one
-// 64-bit look-back descriptor per block.
-struct CompressWs {
-  uint32_t ticket;
-  uint32_t error;
-  uint32_t pad[14];
-  uint64_t desc[1];
-};
-constexpr size_t kCompressWsHeader = 64;
 
 // Shared-table pieces of the table-scope variant, laid out after the
 // look-back workspace (worst case: one group per block).
@@ -71,12 +57,6 @@ size_t scope_layout(size_t base, size_t groups, size_t full, size_t (&off)[5]) {
 
 constexpr uint32_t kSumChunk = 64;  // blocks one workgroup adds into a group histogram (at least)
 
-__device__ __forceinline__ void publish(uint64_t* d, uint64_t v) {
-  __hip_atomic_store(d, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t peek(uint64_t* d) {
-  return __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 __global__ void fill_u32_kernel(uint32_t* dst, uint32_t value, size_t words) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
@@ -86,32 +66,19 @@ __global__ void fill_u32_kernel(uint32_t* dst, uint32_t value, size_t words) {
 
 __global__ void set_u64_kernel(uint64_t* dst, uint64_t value) { *dst = value; }
 
-__device__ __forceinline__ uint32_t header_bytes(uint32_t nb) { return 32u + ((8u * nb + 15u) & ~15u); }
-
-__device__ void write_stream_header(uint8_t* out, uint64_t n, uint32_t nb, uint64_t total) {
-  uint32_t* h = reinterpret_cast<uint32_t*>(out);
-  h[0] = kMagic;
-  h[1] = kB;
-  *reinterpret_cast<uint64_t*>(out + 8) = n;
-  h[4] = nb;
-  h[5] = 0;
-  *reinterpret_cast<uint64_t*>(out + 24) = total;
-  if (nb & 1u) *reinterpret_cast<uint64_t*>(out + 32 + 8ull * nb) = 0;  // table padding
-}
-
 // Validates a stream that holds no elements: just the 32-byte header.
-__global__ void check_empty_stream_kernel(const uint8_t* in, uint64_t in_bytes, int32_t* status) {
+__global__ void check_empty_stream_kernel(const uint8_t* in, uint64_t in_bytes, uint32_t magic, int32_t* status) {
   bool ok = in_bytes >= 32;
   if (ok) {
     const uint32_t* h = reinterpret_cast<const uint32_t*>(in);
-    ok = h[0] == kMagic && h[1] == kB && *reinterpret_cast<const uint64_t*>(in + 8) == 0 && h[4] == 0 &&
+    ok = h[0] == magic && h[1] == kB && *reinterpret_cast<const uint64_t*>(in + 8) == 0 && h[4] == 0 &&
          h[5] == 0 && *reinterpret_cast<const uint64_t*>(in + 24) == 32;
   }
   if (!ok) *status = HC_ERR_CORRUPT_STREAM;
 }
 
-__global__ void empty_stream_kernel(uint8_t* out, uint64_t* out_bytes) {
-  write_stream_header(out, 0, 0, 32);
+__global__ void empty_stream_kernel(uint8_t* out, uint32_t magic, uint64_t* out_bytes) {
+  write_stream_header(out, magic, kB, 0, 0, 32);
   *out_bytes = 32;
 }
 
@@ -142,45 +109,8 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
   if (t == 0) publish(&ws->desc[bid], (bid == 0 ? kFlagIncl : kFlagAgg) | p.rec_bytes);
   write_block(v, p, s);
   if (t < 64) {
-    // Decoupled look-back, one wave wide: lane l reads the descriptor of block
-    // bid-1-l.  The nearest predecessor with an inclusive prefix ends the walk;
-    // the aggregates of the blocks between add to it.  A window with an
-    // unpublished descriptor before that point is read again (bounded).
-    const uint32_t lane = t;
-    uint64_t excl = 0;
-    int64_t base = (int64_t)bid - 1;
-    uint32_t spins = 0;
-    while (base >= 0) {
-      const int64_t j = base - (int64_t)lane;
-      const uint64_t d = j >= 0 ? peek(&ws->desc[j]) : kFlagIncl;
-      const uint64_t incl_mask = __ballot((d >> 62) == 2);
-      const uint64_t zero_mask = __ballot((d >> 62) == 0);
-      const int first = incl_mask ? __ffsll((unsigned long long)incl_mask) - 1 : 64;
-      const uint64_t need = first == 64 ? ~0ull : ((2ull << first) - 1ull);
-      if (zero_mask & need) {
-        if (++spins >= kSpinLimit) {  // a predecessor never published: give up, flag it
-          if (lane == 0) atomicExch(&ws->error, 1u);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        continue;
-      }
-      uint32_t agg = (int)lane < first ? (uint32_t)(d & kValueMask) : 0u;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) agg += __shfl_xor(agg, o, 64);
-      excl += agg;
-      if (first < 64) {
-        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)d, first);
-        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(d >> 32), first);
-        excl += (((uint64_t)hi << 32) | lo) & kValueMask;
-        break;
-      }
-      base -= 64;
-    }
-    if (lane == 0) {
-      if (bid != 0) publish(&ws->desc[bid], kFlagIncl | (excl + p.rec_bytes));
-      s.misc[0] = excl;
-    }
+    const uint64_t excl = lookback_wave(ws, bid, p.rec_bytes);
+    if (t == 0) s.misc[0] = excl;
   }
   __syncthreads();
   const uint64_t off = header_bytes(nb) + s.misc[0];
@@ -189,7 +119,7 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
     reinterpret_cast<uint64_t*>(out + 32)[bid] = off;
     if (bid == nb - 1) {
       const uint64_t total = off + p.rec_bytes;
-      write_stream_header(out, n, nb, total);
+      write_stream_header(out, kMagic, kB, n, nb, total);
       *out_bytes = __hip_atomic_load(&ws->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? 0 : total;
     }
   }
@@ -329,29 +259,6 @@ __global__ __launch_bounds__(256) void scope_pick_kernel(ScopeWs sc, uint32_t gr
   }
 }
 
-// Validates the stream header and the offsets of block bid; on success
-// returns the record's offset and length (next offset minus this one).
-// Thread 0 only; all loads are independent, one round trip.
-__device__ bool check_stream(const uint8_t* in, uint64_t in_bytes, uint64_t n, uint32_t nb, uint32_t bid,
-                             uint64_t* off_out, uint32_t* len_out) {
-  const uint64_t hdr = header_bytes(nb);
-  if (in_bytes < hdr) return false;
-  const uint64_t* offs = reinterpret_cast<const uint64_t*>(in + 32);
-  const uint4 h0 = ld16(in), h1 = ld16(in + 16);
-  const uint64_t off = offs[bid];
-  const uint64_t next_off = bid + 1 < nb ? offs[bid + 1] : 0;
-  const uint64_t pad = (bid == 0 && (nb & 1u)) ? offs[nb] : 0;
-  const uint64_t hn = ((uint64_t)h0.w << 32) | h0.z;
-  const uint64_t total = ((uint64_t)h1.w << 32) | h1.z;
-  const uint64_t next = bid + 1 < nb ? next_off : total;
-  const bool ok = h0.x == kMagic && h0.y == kB && hn == n && h1.x == nb && h1.y == 0 && total <= in_bytes &&
-                  total >= hdr && pad == 0 && (bid != 0 || off == hdr) && (off & 15u) == 0 && off >= hdr &&
-                  next <= total && next >= off + 16 && next - off <= kRawFull && ((next - off) & 15u) == 0;
-  *off_out = off;
-  *len_out = ok ? (uint32_t)(next - off) : 0u;
-  return ok;
-}
-
 // Validates a staged record header against the format for a block of m
 // elements and the record length len.  Thread 0 only.
 __device__ bool check_record_header(const Smem& s, uint32_t m, uint32_t len, uint32_t* mode, uint32_t* b,
@@ -376,7 +283,7 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
   if (t == 0) {
     uint64_t off = 0;
     uint32_t len = 0;
-    s.plan[0] = check_stream(in, in_bytes, n, nb, bid, &off, &len);
+    s.plan[0] = check_stream(in, in_bytes, kMagic, n, nb, bid, &off, &len);
     s.plan[4] = len;
     s.misc[0] = off;
   }
@@ -573,7 +480,8 @@ hipError_t launch_compress(const uint16_t* in, size_t n, void* out, uint64_t* ou
                            hipStream_t stream) {
   const size_t nb = ceil_div(n, kB);
   if (nb == 0) {
-    hipLaunchKernelGGL(empty_stream_kernel, dim3(1), dim3(1), 0, stream, static_cast<uint8_t*>(out), out_bytes);
+    hipLaunchKernelGGL(empty_stream_kernel, dim3(1), dim3(1), 0, stream, static_cast<uint8_t*>(out), kMagic,
+                       out_bytes);
     return hipGetLastError();
   }
   if (nb >= (1ull << 31)) return hipErrorInvalidValue;
@@ -635,21 +543,33 @@ hipError_t launch_compress_scoped(const uint16_t* in, size_t n, void* out, uint6
   return hipGetLastError();
 }
 
+hipError_t launch_empty_stream(void* out, uint32_t magic, uint64_t* out_bytes, hipStream_t stream) {
+  hipLaunchKernelGGL(empty_stream_kernel, dim3(1), dim3(1), 0, stream, static_cast<uint8_t*>(out), magic, out_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_empty_stream(const void* in, size_t in_bytes, uint32_t magic, int32_t* status,
+                                     hipStream_t stream) {
+  hipLaunchKernelGGL(check_empty_stream_kernel, dim3(1), dim3(1), 0, stream, static_cast<const uint8_t*>(in),
+                     (uint64_t)in_bytes, magic, status);
+  return hipGetLastError();
+}
+
 hipError_t launch_decompress(const void* in, size_t in_bytes, uint16_t* out, size_t n, int32_t* status,
                              hipStream_t stream) {
   hipError_t e = launch_fill_u32(status, 0u, 1, stream);
   if (e != hipSuccess) return e;
   const size_t nb = ceil_div(n, kB);
   if (nb >= (1ull << 31)) return hipErrorInvalidValue;
-  if (nb == 0) {
-    hipLaunchKernelGGL(check_empty_stream_kernel, dim3(1), dim3(1), 0, stream, static_cast<const uint8_t*>(in),
-                       (uint64_t)in_bytes, status);
-    return hipGetLastError();
-  }
+  if (nb == 0) return launch_check_empty_stream(in, in_bytes, kMagic, status, stream);
   hipLaunchKernelGGL(decompress_kernel, dim3((uint32_t)nb), dim3(kCT), 0, stream,
                      static_cast<const uint8_t*>(in), (uint64_t)in_bytes, out, (uint64_t)n, status, (uint32_t)nb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_zero_if_corrupt(status, out, n, stream);
+}
+
+hipError_t launch_zero_if_corrupt(const int32_t* status, uint16_t* out, size_t n, hipStream_t stream) {
   const size_t words = n / 2;
   size_t grid = (words + 255) / 256;
   if (grid > 1024) grid = 1024;

@@ -1,0 +1,604 @@
+// entropy_kernels.hip -- HCE1, the bf16 codec with an entropy-coded exponent,
+// for gfx950.
+//
+// "CCCL: In-GPU Compression-Coupled Collective Communication", section 4.1
+// codes the bf16 exponent from a frequency table and keeps sign and fraction
+// raw; the CCCL core uses fixed-length codes, and section 6.5 compares it with
+// an entropy coder whose output is smaller by under 7%.  HCE1 is that
+// comparison built in the same container: each full block of 16,384 elements
+// codes its exponents with its own canonical Huffman code, lengths at most 12
+// bits, and keeps the sign/fraction byte plane raw.  The full format is
+// stated in include/hc.h (hc_compress_bf16_entropy).
+//
+// Parallel layout.  A block is read by 64 lanes of 256 elements (lane j:
+// elements 64 i + j, step i).  Each lane's codes form one bit stream cut into
+// 32-bit words, and the words of all lanes are stored in the order in which a
+// decoder running the 64 lanes in lockstep takes them: a lane takes its next
+// word when the bits it holds do not contain its next code, lanes in order
+// within a step.  So no per-lane offsets are stored, and each lane pads only
+// its last word.
+//
+// compress: one workgroup of 512 threads per block, blocks in ticket order,
+// the record published and placed by the decoupled look-back of the
+// fixed-length encoder (one read of the input, one write of the output).
+// After the histogram, one thread builds the Huffman lengths (two queues over
+// the exponents sorted by count); the canonical codes come out in parallel.
+// The eight waves then each code 32 steps of all 64 lanes: a first pass adds
+// up the bits of every (step segment, lane), which fixes each segment's start
+// bit in every lane and the number of words taken before it, so the record
+// size is known and published before any word is written; the second pass
+// writes the words at their final positions, and the one word that two
+// segments of a lane share is merged afterwards.
+//
+// decompress: one wave per block (the 64 lanes are the 64 streams).  The
+// code lengths give a 4,096-entry table (12-bit window -> symbol, length) in
+// LDS; the next 128 words of the record sit in two registers across the
+// wave and a lane takes its word by a lane shuffle, so the only memory on
+// the per-step chain is the table read.
+#include "codec.hpp"
+#include "launch.hpp"
+#include "lookback.hpp"
+#include "schedule.hpp"
+
+namespace hc {
+
+using namespace codec;
+
+namespace {
+
+constexpr uint32_t kHceMagic = 0x31454348u;   // "HCE1"
+constexpr uint32_t kLmax = 12;                  // longest code
+constexpr uint32_t kLanes = 64;                 // bit streams per block
+constexpr uint32_t kSteps = kB / kLanes;        // codes per stream (256)
+constexpr uint32_t kSegs = kCW;                 // encoder: one wave per segment of steps
+constexpr uint32_t kSegSteps = kSteps / kSegs;  // 32
+constexpr uint32_t kSmOff = 144;                // sign/fraction plane
+constexpr uint32_t kWordsOff = kSmOff + kB;     // 16,528: the interleaved words
+constexpr uint32_t kMaxWords = 4060;            // most words of a record smaller than the raw one
+
+__host__ __device__ constexpr uint32_t hce_coded_bytes(uint32_t n_words) {
+  return kWordsOff + ((4u * n_words + 15u) & ~15u);
+}
+static_assert(hce_coded_bytes(kMaxWords) < kRawFull && hce_coded_bytes(kMaxWords + 1) >= kRawFull,
+              "kMaxWords is the largest coded record below the raw size");
+static_assert(kSegSteps == 32, "one bit per step of a segment in a 32-bit mask");
+
+// Huffman scratch inside the record's words region (free until the words are
+// written): weights of leaves and merged nodes, parents, leaves in increasing
+// (count, decreasing exponent) order, sort keys, leaf lengths.
+constexpr uint32_t kHwOff = kWordsOff;              // u32 [511]
+constexpr uint32_t kHparOff = kWordsOff + 2048;     // u16 [511]
+constexpr uint32_t kSymOff = kWordsOff + 3072;      // u8 [256]
+constexpr uint32_t kKeyOff = kWordsOff + 3328;      // u32 [256]
+constexpr uint32_t kLeafLenOff = kWordsOff + 4352;  // u8 [256]
+static_assert(kLeafLenOff + 256 <= kRawFull, "scratch fits the staging buffer");
+
+struct HceEncSmem {
+  uint4 stage[kStage16 + 1];        // sub-histograms, then the record
+  uint32_t enc[256];                // exponent -> code bits in stream order | length << 16
+  uint32_t seg[kSegs][kLanes];      // bits of each (segment, lane); then carried words
+  uint16_t lastpos[kSegs][kLanes];  // position of each (segment, lane)'s unfinished last word
+  uint8_t len[256];                 // exponent -> code length (0: absent)
+  uint32_t cbl[4][kLmax + 1];       // per owner wave: codes of each length
+  uint32_t wcount[4];
+  uint32_t plan[8];
+  uint64_t misc[2];
+};
+
+__device__ __forceinline__ uint32_t lanemask_lt_count(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Word k (0..15) of the packed elements.
+__device__ __forceinline__ uint32_t word_of(const uint4 (&v)[kPer], int k) {
+  const uint4& q = v[k >> 2];
+  switch (k & 3) {
+    case 0: return q.x;
+    case 1: return q.y;
+    case 2: return q.z;
+    default: return q.w;
+  }
+}
+
+// The thread's 32 elements: 2048 seg + 64 i + lane, i = 0..31 (its lane's
+// steps 32 seg + i), two per word, element i in half i & 1 of word i / 2.
+// Elements at or past m read as 0.
+__device__ __forceinline__ void load_lane_steps(const uint16_t* src, uint32_t m, uint32_t seg, uint32_t lane,
+                                                uint4 (&v)[kPer]) {
+  uint32_t w[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const uint32_t i0 = 2048u * seg + 64u * (2u * k) + lane, i1 = i0 + 64u;
+    const uint32_t lo = i0 < m ? src[i0] : 0u, hi = i1 < m ? src[i1] : 0u;
+    w[k] = lo | (hi << 16);
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) v[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
+}
+
+__device__ __forceinline__ uint32_t elem_of(const uint4 (&v)[kPer], int i) {
+  const uint32_t w = word_of(v, i >> 1);
+  return (i & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// Code lengths (Huffman, limited to kLmax) and canonical codes for the
+// exponent counts (thread t < 256 holds the count of exponent t).  Leaves
+// s.enc, s.len and the record's length table (bytes 16..143); returns the
+// number of exponents present.  Starts and ends with a barrier.
+__device__ uint32_t build_code(uint32_t cnt, HceEncSmem& s) {
+  const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
+  uint32_t* hw = reinterpret_cast<uint32_t*>(stage8(s) + kHwOff);
+  uint16_t* hpar = reinterpret_cast<uint16_t*>(stage8(s) + kHparOff);
+  uint8_t* sym_asc = stage8(s) + kSymOff;
+  uint32_t* keys = reinterpret_cast<uint32_t*>(stage8(s) + kKeyOff);
+  uint8_t* leaf_len = stage8(s) + kLeafLenOff;
+  const bool owner = t < 256u;
+  const bool present = owner && cnt > 0;
+  const uint64_t pm = __ballot(present);
+  if (owner && lane == 0) s.wcount[wave] = (uint32_t)__popcll(pm);
+  if (t == 0) s.plan[5] = 0;
+  __syncthreads();
+  uint32_t before = 0, n = 0;
+#pragma unroll
+  for (uint32_t w = 0; w < 4; ++w) {
+    const uint32_t c = s.wcount[w];
+    before += w < wave ? c : 0u;
+    n += c;
+  }
+  // Occurring exponents, ranked by (count, then exponent descending):
+  // leaf a of the Huffman construction is the a-th lightest.
+  const uint32_t key = (cnt << 8) | (255u - t);
+  if (present) keys[before + lanemask_lt_count(pm)] = key;
+  if (owner) s.len[t] = 0;
+  __syncthreads();
+  if (present) {
+    uint32_t above = 0;
+    for (uint32_t j = 0; j < n; ++j) above += keys[j] > key;
+    const uint32_t a = n - 1u - above;
+    sym_asc[a] = (uint8_t)t;
+    hw[a] = cnt;
+  }
+  __syncthreads();
+  // Two queues: the next leaf and the next merged node; the lighter goes
+  // first, a leaf on a tie.  Merged nodes are made in increasing weight.
+  if (t == 0 && n >= 2) {
+    uint32_t leaf = 0, node = n, made = n;
+    for (uint32_t k = 0; k + 1 < n; ++k) {
+      uint32_t pick[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bool take_leaf = leaf < n && (node >= made || hw[leaf] <= hw[node]);
+        pick[c] = take_leaf ? leaf++ : node++;
+      }
+      hw[made] = hw[pick[0]] + hw[pick[1]];
+      hpar[pick[0]] = (uint16_t)made;
+      hpar[pick[1]] = (uint16_t)made;
+      ++made;
+    }
+  }
+  __syncthreads();
+  // Each leaf's depth: the walk to the root (node 2n - 2) rises every step.
+  if (t < n) {
+    uint32_t depth = 1;
+    if (n >= 2) {
+      depth = 0;
+      for (uint32_t j = t; j != 2u * n - 2u; j = hpar[j]) ++depth;
+    }
+    if (depth > kLmax) s.plan[5] = 1;
+    leaf_len[t] = (uint8_t)(depth > kLmax ? kLmax : depth);
+  }
+  __syncthreads();
+  if (s.plan[5]) {
+    // Over-long codes were cut to kLmax; while the Kraft sum exceeds 1, the
+    // longest code shorter than kLmax grows by one bit (ties: the lightest
+    // leaf, i.e. the smallest count, then the largest exponent).
+    if (t == 0) {
+      uint32_t kraft = 0;
+      for (uint32_t j = 0; j < n; ++j) kraft += 1u << (kLmax - leaf_len[j]);
+      while (kraft > (1u << kLmax)) {
+        uint32_t best = n, bl = 0;
+        for (uint32_t j = 0; j < n; ++j) {
+          const uint32_t l = leaf_len[j];
+          if (l < kLmax && (best == n || l > bl)) { best = j; bl = l; }
+        }
+        kraft -= 1u << (kLmax - bl - 1u);
+        leaf_len[best] = (uint8_t)(bl + 1u);
+      }
+    }
+    __syncthreads();
+  }
+  if (t < n) s.len[sym_asc[t]] = leaf_len[t];
+  __syncthreads();
+  // Canonical codes: codes of one length are consecutive in exponent order,
+  // and the first code of length L is (first of L-1 + count of L-1) << 1.
+  const uint32_t l = owner ? s.len[t] : 0u;
+  uint32_t rank = 0;
+#pragma unroll
+  for (uint32_t L = 1; L <= kLmax; ++L) {
+    const uint64_t bm = __ballot(owner && l == L);
+    if (l == L) rank = lanemask_lt_count(bm);
+    if (owner && lane == 0) s.cbl[wave][L] = (uint32_t)__popcll(bm);
+  }
+  __syncthreads();
+  if (owner) {
+    uint32_t e = 0;
+    if (l) {
+      uint32_t code = 0, prev = 0;
+      for (uint32_t L = 1; L <= l; ++L) {
+        code = (code + prev) << 1;
+        prev = s.cbl[0][L] + s.cbl[1][L] + s.cbl[2][L] + s.cbl[3][L];
+      }
+      for (uint32_t w = 0; w < wave; ++w) code += s.cbl[w][l];
+      code += rank;
+      e = (__builtin_bitreverse32(code) >> (32u - l)) | (l << 16);
+    }
+    s.enc[t] = e;
+  }
+  if (t < 128u) stage8(s)[16 + t] = (uint8_t)(s.len[2 * t] | (s.len[2 * t + 1] << 4));
+  __syncthreads();
+  return n;
+}
+
+__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void hce_compress_kernel(
+    const uint16_t* __restrict__ in, uint64_t n, uint8_t* __restrict__ out, uint64_t* __restrict__ out_bytes,
+    CompressWs* __restrict__ ws, uint32_t nb) {
+  __shared__ HceEncSmem s;
+  const uint32_t t = threadIdx.x, lane = t & 63u, seg = t >> 6;
+  if (t == 0) s.plan[6] = atomicAdd(&ws->ticket, 1u);
+  zero_hist(s);  // while the ticket is on its way
+  __syncthreads();
+  const uint32_t bid = s.plan[6];
+  const uint64_t first = (uint64_t)bid * kB;
+  const uint32_t m = (uint32_t)((n - first) < kB ? (n - first) : kB);
+  uint4 v[kPer];
+  load_lane_steps(in + first, m, seg, lane, v);
+  uint32_t mode = 0, n_sym = 0, n_words = 0, rec_bytes = raw_bytes(m);
+  uint32_t codes[16];   // step i's code bits (low 12) and length (high 4), two per word
+  uint32_t cum_start = 0, base = 0;
+  if (m == kB) {
+    const uint32_t cnt = block_histogram<true>(v, s);
+    __syncthreads();   // the sub-histograms are read: the staging buffer is free
+    n_sym = build_code(cnt, s);
+    // First pass: this lane's bits in this segment.
+    uint32_t bits = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t w = word_of(v, k);
+      const uint32_t e0 = s.enc[(w >> 7) & 0xFFu], e1 = s.enc[(w >> 23) & 0xFFu];
+      const uint32_t c0 = (e0 & 0xFFFu) | ((e0 >> 16) << 12), c1 = (e1 & 0xFFFu) | ((e1 >> 16) << 12);
+      codes[k] = c0 | (c1 << 16);
+      bits += (e0 >> 16) + (e1 >> 16);
+    }
+    s.seg[seg][lane] = bits;
+    __syncthreads();
+    uint32_t total = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < kSegs; ++q) {
+      const uint32_t b = s.seg[q][lane];
+      cum_start += q < seg ? b : 0u;
+      total += b;
+    }
+    n_words = wave_sum((total + 31u) >> 5);        // every wave holds all 64 lanes
+    base = wave_sum((cum_start + 31u) >> 5);       // words taken before this segment
+    if (n_words <= kMaxWords) {
+      mode = 2;
+      rec_bytes = hce_coded_bytes(n_words);
+    }
+    __syncthreads();   // s.seg is read; it holds carried words from here on
+  }
+  if (t == 0) publish(&ws->desc[bid], (bid == 0 ? kFlagIncl : kFlagAgg) | rec_bytes);
+  uint8_t* st8 = stage8(s);
+  if (mode == 2) {
+    uint32_t* words = stage32(s) + kWordsOff / 4;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t x = elem_of(v, i);
+      st8[kSmOff + 2048u * seg + 64u * i + lane] = (uint8_t)(((x >> 8) & 0x80u) | (x & 0x7Fu));
+    }
+    if (t < 3u && ((n_words + t) * 4u) < ((4u * n_words + 15u) & ~15u)) words[n_words + t] = 0;  // padding
+    // Second pass: write this segment's codes of this lane.
+    uint32_t cum = cum_start;
+    const uint32_t w0 = cum >> 5;             // the word holding bit cum
+    const bool carry_in = (cum & 31u) != 0;   // word w0 was taken and begun by the previous segment
+    uint32_t r = (cum + 31u) >> 5;            // words of this lane taken so far
+    uint32_t written = w0;                    // words of this lane finished (w0 counts when carried)
+    uint64_t acc = 0;                         // bits from bit 32 * written on
+    uint32_t pa = 0, pb = 0, pend = 0;        // words taken here and not yet written, oldest first
+    uint32_t carry = 0, b = base;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t c = (codes[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      const uint32_t l = c >> 12;
+      const bool need = cum + l > 32u * r;
+      const uint64_t mask = __ballot(need);
+      if (need) {
+        const uint32_t p = b + lanemask_lt_count(mask);
+        if (pend == 0) pa = p; else pb = p;
+        ++pend;
+        ++r;
+      }
+      b += (uint32_t)__popcll(mask);
+      acc |= (uint64_t)(c & 0xFFFu) << (cum - 32u * written);
+      cum += l;
+      if (cum >= 32u * (written + 1u)) {
+        const uint32_t wv = (uint32_t)acc;
+        if (carry_in && written == w0) {
+          carry = wv;
+        } else {
+          words[pa] = wv;
+          pa = pb;
+          --pend;
+        }
+        acc >>= 32;
+        ++written;
+      }
+    }
+    uint32_t last = 0xFFFFu;
+    if (cum > 32u * written) {   // an unfinished last word: the next segment adds its bits
+      words[pa] = (uint32_t)acc;
+      last = pa;
+    }
+    s.seg[seg][lane] = carry;
+    s.lastpos[seg][lane] = (uint16_t)last;
+    __syncthreads();
+    if (carry_in) words[s.lastpos[seg - 1][lane]] |= s.seg[seg][lane];
+    if (t == 0) {
+      uint32_t* h = stage32(s);
+      h[0] = 2u | (kLmax << 8) | (n_sym << 16);
+      h[1] = m;
+      h[2] = n_words;
+      h[3] = rec_bytes;
+    }
+  } else {
+    // raw record: the m words, then zero padding (elements past m loaded as 0)
+    uint16_t* st16 = reinterpret_cast<uint16_t*>(st8 + 16);
+    const uint32_t lim = (m + 7u) & ~7u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t idx = 2048u * seg + 64u * i + lane;
+      if (idx < lim) st16[idx] = (uint16_t)elem_of(v, i);
+    }
+    if (t == 0) {
+      uint32_t* h = stage32(s);
+      h[0] = 0;
+      h[1] = m;
+      h[2] = 0;
+      h[3] = rec_bytes;
+    }
+  }
+  __syncthreads();
+  if (t < 64) {
+    const uint64_t excl = lookback_wave(ws, bid, rec_bytes);
+    if (t == 0) s.misc[0] = excl;
+  }
+  __syncthreads();
+  const uint64_t off = header_bytes(nb) + s.misc[0];
+  copy_out(s, out + off, rec_bytes);
+  if (t == 0) {
+    reinterpret_cast<uint64_t*>(out + 32)[bid] = off;
+    if (bid == nb - 1) {
+      const uint64_t tot = off + rec_bytes;
+      write_stream_header(out, kHceMagic, kB, n, nb, tot);
+      *out_bytes = __hip_atomic_load(&ws->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? 0 : tot;
+    }
+  }
+}
+
+struct HceDecSmem {
+  uint16_t lut[1u << kLmax];   // 12-bit window, first stream bit on top -> symbol | length << 8 (0: no code)
+  uint16_t start[257];         // window value where each code (in length, exponent order) begins
+  uint8_t sorted[256];         // exponents in (length, exponent) order
+  uint8_t slen[256];           // their lengths
+};
+
+__global__ __launch_bounds__(64) void hce_decompress_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes,
+                                                            uint16_t* __restrict__ out, uint64_t n,
+                                                            int32_t* __restrict__ status, uint32_t nb) {
+  __shared__ HceDecSmem s;
+  const uint32_t lane = threadIdx.x, bid = blockIdx.x;
+  const uint64_t first = (uint64_t)bid * kB;
+  const uint32_t m = (uint32_t)((n - first) < kB ? (n - first) : kB);
+  uint64_t off = 0;
+  uint32_t len = 0;
+  if (!check_stream(in, in_bytes, kHceMagic, n, nb, bid, &off, &len)) {
+    if (lane == 0) atomicExch(status, (int32_t)HC_ERR_CORRUPT_STREAM);
+    return;
+  }
+  const uint8_t* rec = in + off;
+  const uint4 h = ld16(rec);
+  const uint32_t mode = h.x & 0xFFu, lmax = (h.x >> 8) & 0xFFu, n_sym = h.x >> 16, n_words = h.z, rb = h.w;
+  const bool hok = h.y == m && rb == len &&
+                   ((mode == 0 && lmax == 0 && n_sym == 0 && n_words == 0 && rb == raw_bytes(m)) ||
+                    (mode == 2 && m == kB && lmax == kLmax && n_sym >= 1 && n_sym <= 256 && n_words <= kMaxWords &&
+                     rb == hce_coded_bytes(n_words)));
+  if (!hok) {
+    if (lane == 0) atomicExch(status, (int32_t)HC_ERR_CORRUPT_STREAM);
+    return;
+  }
+  uint16_t* dst = out + first;
+  bool bad = false;
+  if (mode == 0) {
+    const uint32_t chunks = (rb - 16u) / 16u;   // 8 elements each, padding zero
+    for (uint32_t c = lane; c < chunks; c += 64) {
+      const uint4 q = ld16(rec + 16 + 16 * c);
+      if (8u * c + 8u <= m) {
+        st16(dst + 8u * c, q);
+      } else {
+        const uint32_t wds[4] = {q.x, q.y, q.z, q.w};
+        for (uint32_t k = 0; k < 8; ++k) {
+          const uint32_t x = (wds[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+          if (8u * c + k < m) dst[8u * c + k] = (uint16_t)x;
+          else bad |= x != 0;
+        }
+      }
+    }
+  } else {
+    // Code lengths: lane holds exponents lane + 64 k.
+    uint32_t ln[4];
+    uint32_t kraft = 0, present = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t e = lane + 64u * k;
+      const uint32_t byte = rec[16 + (e >> 1)];
+      ln[k] = (e & 1u) ? (byte >> 4) : (byte & 0xFu);
+      bad |= ln[k] > kLmax;
+      kraft += (ln[k] && ln[k] <= kLmax) ? (1u << (kLmax - ln[k])) : 0u;
+      present += ln[k] != 0;
+    }
+    kraft = wave_sum(kraft);
+    present = wave_sum(present);
+    bad |= kraft > (1u << kLmax) || present != n_sym;
+    if (!__ballot(bad)) {
+      // canonical tables (uniform): codes of each length, their first code and first sorted index
+      uint32_t cnt[kLmax + 1], fcode[kLmax + 1], fidx[kLmax + 1], run[kLmax + 1];
+      cnt[0] = 0;
+#pragma unroll
+      for (uint32_t L = 1; L <= kLmax; ++L) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c += (uint32_t)__popcll(__ballot(ln[k] == L));
+        cnt[L] = c;
+      }
+      uint32_t code = 0, idx = 0;
+#pragma unroll
+      for (uint32_t L = 1; L <= kLmax; ++L) {
+        code = (code + cnt[L - 1]) << 1;
+        fcode[L] = code;
+        fidx[L] = idx;
+        idx += cnt[L];
+        run[L] = 0;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (uint32_t L = 1; L <= kLmax; ++L) {
+          const uint64_t bm = __ballot(ln[k] == L);
+          if (ln[k] == L) {
+            const uint32_t r = run[L] + lanemask_lt_count(bm);
+            s.sorted[fidx[L] + r] = (uint8_t)(lane + 64u * k);
+            s.slen[fidx[L] + r] = (uint8_t)L;
+            s.start[fidx[L] + r] = (uint16_t)((fcode[L] + r) << (kLmax - L));
+          }
+          run[L] += (uint32_t)__popcll(bm);
+        }
+      }
+      if (lane == 0) s.start[n_sym] = (uint16_t)kraft;   // end of the last code's range
+      __syncthreads();
+      // Table: lane fills windows [64 lane, 64 lane + 64); the codes' ranges
+      // are consecutive in sorted order.
+      {
+        const uint32_t x0 = 64u * lane;
+        uint32_t lo = 0, hi = n_sym;   // the last code starting at or before x0
+        while (hi - lo > 1u) {
+          const uint32_t mid = (lo + hi) >> 1;
+          if (s.start[mid] <= x0) lo = mid; else hi = mid;
+        }
+        uint32_t k = lo, next = s.start[k + 1];
+        for (uint32_t j = 0; j < 64; ++j) {
+          const uint32_t x = x0 + j;
+          while (x >= next && k + 1 < n_sym) next = s.start[++k + 1];
+          s.lut[x] = x < kraft ? (uint16_t)(s.sorted[k] | (s.slen[k] << 8)) : (uint16_t)0;
+        }
+      }
+      __syncthreads();
+      // Decode: 256 steps, every lane one code per step.
+      const uint32_t* wg = reinterpret_cast<const uint32_t*>(rec + kWordsOff);
+      uint32_t win = lane < n_words ? wg[lane] : 0u;
+      uint32_t win2 = 64u + lane < n_words ? wg[64u + lane] : 0u;
+      uint32_t wbase = 0, base = 0, avail = 0;
+      uint64_t buf = 0;
+      const uint8_t* smp = rec + kSmOff + lane;
+      uint32_t smn[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) smn[q] = smp[64u * q];
+      for (uint32_t i0 = 0; i0 < kSteps; i0 += 8) {
+        uint32_t smv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) smv[q] = smn[q];
+        if (i0 + 8 < kSteps) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) smn[q] = smp[64u * (i0 + 8 + q)];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          uint32_t e = s.lut[__builtin_bitreverse32((uint32_t)buf) >> (32u - kLmax)];
+          uint32_t L = e >> 8;
+          const bool need = L == 0 ? avail < kLmax : L > avail;
+          const uint64_t mask = __ballot(need);
+          if (mask) {
+            const uint32_t p = base + lanemask_lt_count(mask);
+            const uint32_t rel = p - wbase;   // < 128: base - wbase < 64 at every step
+            uint32_t word = __shfl(win, (int)(rel & 63u), 64);
+            if (__ballot(need && rel >= 64u)) {
+              const uint32_t w2 = __shfl(win2, (int)(rel & 63u), 64);
+              word = rel >= 64u ? w2 : word;
+            }
+            if (need) {
+              bad |= p >= n_words;
+              buf |= (uint64_t)word << avail;
+              avail += 32;
+              e = s.lut[__builtin_bitreverse32((uint32_t)buf) >> (32u - kLmax)];
+              L = e >> 8;
+            }
+            base += (uint32_t)__popcll(mask);
+            if (base - wbase >= 64u) {
+              wbase += 64;
+              win = win2;
+              const uint32_t nx = wbase + 64u + lane;
+              win2 = nx < n_words ? wg[nx] : 0u;
+            }
+          }
+          if (L == 0 || L > avail) {   // only in a corrupt stream
+            bad = true;
+            L = avail < 1u ? 0u : 1u;
+          }
+          buf >>= L;
+          avail -= L;
+          const uint32_t smb = smv[q];
+          dst[64u * (i0 + q) + lane] = (uint16_t)(((smb & 0x80u) << 8) | ((e & 0xFFu) << 7) | (smb & 0x7Fu));
+        }
+      }
+      bad |= base != n_words || buf != 0;
+      // zero padding after the last word
+      const uint32_t pw = n_words + lane;
+      if (lane < 3u && 4u * pw < ((4u * n_words + 15u) & ~15u)) bad |= wg[pw] != 0;
+    }
+  }
+  if (__ballot(bad) && lane == 0) atomicExch(status, (int32_t)HC_ERR_CORRUPT_STREAM);
+}
+
+}  // namespace
+
+hipError_t launch_hce_compress(const uint16_t* in, size_t n, void* out, uint64_t* out_bytes, void* ws,
+                               hipStream_t stream) {
+  const size_t nb = ceil_div(n, kB);
+  if (nb == 0) return launch_empty_stream(out, kHceMagic, out_bytes, stream);
+  if (nb >= (1ull << 31)) return hipErrorInvalidValue;
+  hipError_t e = launch_fill_u32(ws, 0u, compress_ws_bytes(n) / 4, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(hce_compress_kernel, dim3((uint32_t)nb), dim3(kCT), 0, stream, in, (uint64_t)n,
+                     static_cast<uint8_t*>(out), out_bytes, static_cast<CompressWs*>(ws), (uint32_t)nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_hce_decompress(const void* in, size_t in_bytes, uint16_t* out, size_t n, int32_t* status,
+                                 hipStream_t stream) {
+  hipError_t e = launch_fill_u32(status, 0u, 1, stream);
+  if (e != hipSuccess) return e;
+  const size_t nb = ceil_div(n, kB);
+  if (nb >= (1ull << 31)) return hipErrorInvalidValue;
+  if (nb == 0) return launch_check_empty_stream(in, in_bytes, kHceMagic, status, stream);
+  hipLaunchKernelGGL(hce_decompress_kernel, dim3((uint32_t)nb), dim3(64), 0, stream,
+                     static_cast<const uint8_t*>(in), (uint64_t)in_bytes, out, (uint64_t)n, status, (uint32_t)nb);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_zero_if_corrupt(status, out, n, stream);
+}
+
+}  // namespace hc

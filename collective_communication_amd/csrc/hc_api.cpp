@@ -259,7 +259,8 @@ int hc_step_count(hc_op_t op, int nranks) {
     case HC_OP_ALL_GATHER: return nranks - 1;
     case HC_OP_COMPRESSED_ALLREDUCE: return 2 * nranks - 1;
     case HC_OP_COMPRESS:
-    case HC_OP_COMPRESS_SCOPED: return -1;
+    case HC_OP_COMPRESS_SCOPED:
+    case HC_OP_COMPRESS_ENTROPY: return -1;
   }
   return -1;
 }
@@ -346,6 +347,8 @@ size_t hc_workspace_bytes(hc_op_t op, size_t count, int nranks, hc_dtype_t dtype
       return hc::compress_ws_bytes(count);
     case HC_OP_COMPRESS_SCOPED:
       return hc::compress_scoped_ws_bytes(count);
+    case HC_OP_COMPRESS_ENTROPY:
+      return hc::compress_ws_bytes(count);
     case HC_OP_COMPRESSED_ALLREDUCE:
       if (dtype != HC_BF16) return 0;
       return hc::compressed_ar_ws_bytes(count, nranks);
@@ -469,9 +472,13 @@ size_t hc_compress_bound_bf16(size_t n) {
 
 namespace {
 
-// Both compress entry points; scoped = false is the per-block table rule.
+enum class Coder { kPerBlock, kScoped, kEntropy };
+
+// The compress entry points: per-block fixed-length tables, tables shared by
+// groups of blocks, or per-block Huffman codes (HCE1).
 hc_status_t compress_common(const uint16_t* d_in, size_t n, void* d_out, size_t out_cap, uint64_t* d_out_bytes,
-                            void* d_ws, size_t ws_bytes, bool scoped, size_t table_blocks, hipStream_t stream) {
+                            void* d_ws, size_t ws_bytes, Coder coder, size_t table_blocks, hipStream_t stream) {
+  const bool scoped = coder == Coder::kScoped;
   g_last_error.clear();
   if (!d_out || !d_out_bytes || !d_ws || (n && !d_in))
     return fail(HC_ERR_INVALID_ARGUMENT, "NULL pointer argument");
@@ -488,8 +495,10 @@ hc_status_t compress_common(const uint16_t* d_in, size_t n, void* d_out, size_t 
       wr{(uintptr_t)d_ws, (uintptr_t)d_ws + need};
   if (overlap(ir, orr) || overlap(ir, wr) || overlap(orr, wr))
     return fail(HC_ERR_INVALID_ARGUMENT, "input, output and workspace must not overlap");
-  hipError_t e = scoped ? hc::launch_compress_scoped(d_in, n, d_out, d_out_bytes, d_ws, table_blocks, stream)
-                        : hc::launch_compress(d_in, n, d_out, d_out_bytes, d_ws, stream);
+  hipError_t e = coder == Coder::kScoped
+                     ? hc::launch_compress_scoped(d_in, n, d_out, d_out_bytes, d_ws, table_blocks, stream)
+                 : coder == Coder::kEntropy ? hc::launch_hce_compress(d_in, n, d_out, d_out_bytes, d_ws, stream)
+                                            : hc::launch_compress(d_in, n, d_out, d_out_bytes, d_ws, stream);
   if (e == hipErrorNotSupported) return fail(HC_ERR_UNSUPPORTED, "compress not built");
   return e == hipSuccess ? HC_SUCCESS : device_fail(e, "compress launch");
 }
@@ -498,17 +507,25 @@ hc_status_t compress_common(const uint16_t* d_in, size_t n, void* d_out, size_t 
 
 hc_status_t hc_compress_bf16(const uint16_t* d_in, size_t n, void* d_out, size_t out_cap,
                              uint64_t* d_out_bytes, void* d_ws, size_t ws_bytes, hipStream_t stream) {
-  return compress_common(d_in, n, d_out, out_cap, d_out_bytes, d_ws, ws_bytes, false, 1, stream);
+  return compress_common(d_in, n, d_out, out_cap, d_out_bytes, d_ws, ws_bytes, Coder::kPerBlock, 1, stream);
 }
 
 hc_status_t hc_compress_bf16_scoped(const uint16_t* d_in, size_t n, void* d_out, size_t out_cap,
                                     uint64_t* d_out_bytes, size_t table_blocks, void* d_ws, size_t ws_bytes,
                                     hipStream_t stream) {
-  return compress_common(d_in, n, d_out, out_cap, d_out_bytes, d_ws, ws_bytes, true, table_blocks, stream);
+  return compress_common(d_in, n, d_out, out_cap, d_out_bytes, d_ws, ws_bytes, Coder::kScoped, table_blocks,
+                         stream);
 }
 
-hc_status_t hc_decompress_bf16(const void* d_in, size_t in_bytes, uint16_t* d_out, size_t n,
-                               int32_t* d_status, hipStream_t stream) {
+hc_status_t hc_compress_bf16_entropy(const uint16_t* d_in, size_t n, void* d_out, size_t out_cap,
+                                     uint64_t* d_out_bytes, void* d_ws, size_t ws_bytes, hipStream_t stream) {
+  return compress_common(d_in, n, d_out, out_cap, d_out_bytes, d_ws, ws_bytes, Coder::kEntropy, 1, stream);
+}
+
+namespace {
+
+hc_status_t decompress_common(const void* d_in, size_t in_bytes, uint16_t* d_out, size_t n, int32_t* d_status,
+                              bool entropy, hipStream_t stream) {
   g_last_error.clear();
   if (!d_in || !d_status || (n && !d_out)) return fail(HC_ERR_INVALID_ARGUMENT, "NULL pointer argument");
   if (!aligned16(d_in) || (d_out && !aligned16(d_out)) || ((uintptr_t)d_status & 3u))
@@ -516,9 +533,22 @@ hc_status_t hc_decompress_bf16(const void* d_in, size_t in_bytes, uint16_t* d_ou
   if (n > ((size_t)1 << 40)) return fail(HC_ERR_INVALID_ARGUMENT, "n %zu too large", n);
   Range ir{(uintptr_t)d_in, (uintptr_t)d_in + in_bytes}, orr{(uintptr_t)d_out, (uintptr_t)d_out + 2 * n};
   if (n && overlap(ir, orr)) return fail(HC_ERR_INVALID_ARGUMENT, "input and output overlap");
-  hipError_t e = hc::launch_decompress(d_in, in_bytes, d_out, n, d_status, stream);
+  hipError_t e = entropy ? hc::launch_hce_decompress(d_in, in_bytes, d_out, n, d_status, stream)
+                         : hc::launch_decompress(d_in, in_bytes, d_out, n, d_status, stream);
   if (e == hipErrorNotSupported) return fail(HC_ERR_UNSUPPORTED, "decompress not built");
   return e == hipSuccess ? HC_SUCCESS : device_fail(e, "decompress launch");
+}
+
+}  // namespace
+
+hc_status_t hc_decompress_bf16(const void* d_in, size_t in_bytes, uint16_t* d_out, size_t n,
+                               int32_t* d_status, hipStream_t stream) {
+  return decompress_common(d_in, in_bytes, d_out, n, d_status, false, stream);
+}
+
+hc_status_t hc_decompress_bf16_entropy(const void* d_in, size_t in_bytes, uint16_t* d_out, size_t n,
+                                       int32_t* d_status, hipStream_t stream) {
+  return decompress_common(d_in, in_bytes, d_out, n, d_status, true, stream);
 }
 
 hc_status_t hc_compressed_allreduce(void* const* sendbufs, void* const* recvbufs, size_t count,

@@ -39,6 +39,18 @@ hipError_t launch_compress(const uint16_t* in, size_t n, void* out, uint64_t* ou
 hipError_t launch_decompress(const void* in, size_t in_bytes, uint16_t* out, size_t n,
                              int32_t* status, hipStream_t stream);
 size_t compress_ws_bytes(size_t n);
+// Stream helpers shared by the codec formats (magic: the format's).
+hipError_t launch_empty_stream(void* out, uint32_t magic, uint64_t* out_bytes, hipStream_t stream);
+hipError_t launch_check_empty_stream(const void* in, size_t in_bytes, uint32_t magic, int32_t* status,
+                                     hipStream_t stream);
+// Zeroes the n-element output when *status reports a corrupt stream.
+hipError_t launch_zero_if_corrupt(const int32_t* status, uint16_t* out, size_t n, hipStream_t stream);
+// Entropy-coded variant (HCE1): per-block canonical Huffman codes for the
+// exponent; same workspace as the fixed-length encoder.
+hipError_t launch_hce_compress(const uint16_t* in, size_t n, void* out, uint64_t* out_bytes, void* ws,
+                               hipStream_t stream);
+hipError_t launch_hce_decompress(const void* in, size_t in_bytes, uint16_t* out, size_t n, int32_t* status,
+                                 hipStream_t stream);
 // Table-scope variant: code tables shared by groups of `group` full blocks
 // (0: one table for the whole stream).
 size_t compress_scoped_ws_bytes(size_t n);

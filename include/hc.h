@@ -232,6 +232,54 @@ hc_status_t hc_compress_bf16_scoped(const uint16_t *d_in, size_t n, void *d_out,
                                     size_t ws_bytes, hipStream_t stream);
 
 /*
+ * hc_compress_bf16_entropy -- lossless bf16 compression with an entropy-coded
+ * exponent: one "HCE1" stream.  "CCCL ...", section 4.1 codes the exponent
+ * from a frequency table with sign and fraction raw, and section 6.5
+ * compares the fixed-length core with an entropy coder whose output is
+ * smaller by under 7%; here each full block codes its exponents with its own
+ * canonical Huffman code (lengths limited to 12 bits; codes assigned as in
+ * RFC 1951, section 3.2.2), the same container and single-pass writer as
+ * hc_compress_bf16.
+ * Format (little-endian, all padding zero): the HCZ1 container with magic
+ * 0x31454348.  Record: 16-byte header {u8 mode (0 raw, 2 coded), u8 lmax (12
+ * coded, 0 raw), u16 n_sym (exponents present; 0 raw), u32 m, u32 n_words
+ * (0 raw), u32 rec_bytes}; raw: m words padded to 16; coded (m == 16384
+ * only): code length of exponent e (0 absent, 1..12) in the low nibble of
+ * byte 16 + e/2 for even e, the high nibble for odd e; bytes 144..16527 the
+ * sign/fraction plane sm[i] = sign<<7 | fraction; from byte 16528 the
+ * n_words 32-bit words, padded to 16: rec_bytes = 16528 +
+ * round_up(4*n_words, 16).  A full block is coded when that is below
+ * 16 + 32768 bytes, else raw; the partial tail block is raw.
+ * Code construction: leaves in increasing count, equal counts by decreasing
+ * exponent; the lighter of (next leaf, next merged node) is taken first, a
+ * leaf on a tie; a single exponent gets length 1.  Lengths over 12 become 12,
+ * then while the Kraft sum exceeds 1 the longest code shorter than 12
+ * (ties: smallest count, then largest exponent) grows by one bit.
+ * Word layout: 64 lanes, lane j takes elements 64*i + j (step i = 0..255);
+ * its codes, most significant bit first, form a bit stream whose bit b is bit
+ * b%32 of its word b/32.  Word w of a lane is stored at the first step whose
+ * code ends past bit 32*w of that stream, and the words are stored in (that
+ * step, lane) order -- the order in which a decoder running the 64 lanes in
+ * lockstep needs them.
+ *   d_ws: >= hc_workspace_bytes(HC_OP_COMPRESS_ENTROPY, n, 1, HC_BF16)
+ *   bytes.  Other arguments and errors as hc_compress_bf16 (the bound is
+ *   hc_compress_bound_bf16(n)).
+ */
+hc_status_t hc_compress_bf16_entropy(const uint16_t *d_in, size_t n, void *d_out, size_t out_cap,
+                                     uint64_t *d_out_bytes, void *d_ws, size_t ws_bytes,
+                                     hipStream_t stream);
+
+/*
+ * hc_decompress_bf16_entropy -- exact inverse of hc_compress_bf16_entropy.
+ * Arguments and errors as hc_decompress_bf16; besides the container, a coded
+ * record is rejected when its lengths exceed 12 or break the Kraft
+ * inequality, n_sym disagrees with them, a code is missing, the words do not
+ * run out exactly at the last code, or a padding bit is set.
+ */
+hc_status_t hc_decompress_bf16_entropy(const void *d_in, size_t in_bytes, uint16_t *d_out, size_t n,
+                                       int32_t *d_status, hipStream_t stream);
+
+/*
  * hc_decompress_bf16 -- exact inverse of hc_compress_bf16.
  *   d_in: in_bytes readable bytes holding a stream of n elements (the stream
  *   may be shorter than in_bytes).  d_out: n bf16 words.  d_status: one
@@ -271,7 +319,8 @@ typedef enum {
     HC_OP_COMPRESSED_ALLREDUCE = 2,
     HC_OP_ALLREDUCE = 3,
     HC_OP_ALL_GATHER = 4,
-    HC_OP_COMPRESS_SCOPED = 5
+    HC_OP_COMPRESS_SCOPED = 5,
+    HC_OP_COMPRESS_ENTROPY = 6
 } hc_op_t;
 
 /* Workspace bytes for an operation; count = elements per rank buffer
