@@ -127,6 +127,48 @@ __device__ __forceinline__ uint32_t elem_of(const uint4 (&v)[kPer], int i) {
   return (i & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
+// Huffman depths of up to 64 leaves (weights lw: leaf `lane`, increasing)
+// in the registers of one wave: the same two-queue construction as the LDS
+// loop below, with the fronts read by readlane and the merged nodes' weights
+// and parents written by writelane.  Returns leaf `lane`'s depth.
+// v with lane `at` (uniform) replaced by x.
+__device__ __forceinline__ uint32_t set_lane(uint32_t v, uint32_t at, uint32_t x) {
+  return __lane_id() == at ? x : v;
+}
+
+__device__ __forceinline__ uint32_t huffman_depths_wave(uint32_t lw, uint32_t n) {
+  uint32_t nw = 0, lpar = 0, npar = 0;   // merged node k's weight; parents (merged-node numbers)
+  uint32_t leaf = 0, node = 0, made = 0;
+  uint32_t wl = __builtin_amdgcn_readlane(lw, 0), wn = 0;
+  for (uint32_t k = 0; k + 1 < n; ++k) {
+    uint32_t sum = 0;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      if (leaf < n && (node >= made || wl <= wn)) {
+        sum += wl;
+        lpar = set_lane(lpar, leaf, made);
+        ++leaf;
+        wl = __builtin_amdgcn_readlane(lw, leaf < 64u ? leaf : 63u);
+      } else {
+        sum += wn;
+        npar = set_lane(npar, node, made);
+        ++node;
+        wn = __builtin_amdgcn_readlane(nw, node < 64u ? node : 63u);
+      }
+    }
+    nw = set_lane(nw, made, sum);
+    if (node == made) wn = sum;   // the new node is the front of its queue
+    ++made;
+  }
+  // depths of the merged nodes, root (made - 1) first: a parent is made after its children
+  uint32_t nd = 0;
+  for (int32_t j = (int32_t)made - 2; j >= 0; --j) {
+    const uint32_t pd = __builtin_amdgcn_readlane(nd, __builtin_amdgcn_readlane(npar, j));
+    nd = set_lane(nd, (uint32_t)j, pd + 1u);
+  }
+  return __shfl(nd, (int)lpar, 64) + 1u;
+}
+
 // Code lengths (Huffman, limited to kLmax) and canonical codes for the
 // exponent counts (thread t < 256 holds the count of exponent t).  Leaves
 // s.enc, s.len and the record's length table (bytes 16..143); returns the
@@ -167,7 +209,15 @@ __device__ uint32_t build_code(uint32_t cnt, HceEncSmem& s) {
   __syncthreads();
   // Two queues: the next leaf and the next merged node; the lighter goes
   // first, a leaf on a tie.  Merged nodes are made in increasing weight.
-  if (t == 0 && n >= 2) {
+  if (n >= 2 && n <= 64) {
+    if (wave == 0) {
+      const uint32_t depth = huffman_depths_wave(lane < n ? hw[lane] : 0u, n);
+      if (lane < n) {
+        if (depth > kLmax) s.plan[5] = 1;
+        leaf_len[lane] = (uint8_t)(depth > kLmax ? kLmax : depth);
+      }
+    }
+  } else if (t == 0 && n >= 2) {
     uint32_t leaf = 0, node = n, made = n;
     for (uint32_t k = 0; k + 1 < n; ++k) {
       uint32_t pick[2];
@@ -184,7 +234,7 @@ __device__ uint32_t build_code(uint32_t cnt, HceEncSmem& s) {
   }
   __syncthreads();
   // Each leaf's depth: the walk to the root (node 2n - 2) rises every step.
-  if (t < n) {
+  if ((n == 1 || n > 64) && t < n) {
     uint32_t depth = 1;
     if (n >= 2) {
       depth = 0;
@@ -390,12 +440,77 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
   }
 }
 
+// Decoding table entry: exponent << 7 | code length; every window that
+// starts no code holds kNoCode (length field 15, above any real length).
+constexpr uint16_t kNoCode = 0xFFFFu;
+
 struct HceDecSmem {
-  uint16_t lut[1u << kLmax];   // 12-bit window, first stream bit on top -> symbol | length << 8 (0: no code)
+  uint16_t lut[1u << kLmax];   // 12-bit window, first stream bit on top -> entry
   uint16_t start[257];         // window value where each code (in length, exponent order) begins
-  uint8_t sorted[256];         // exponents in (length, exponent) order
-  uint8_t slen[256];           // their lengths
+  uint16_t ent[256];           // table entry of each code in that order
 };
+
+// One code per lane per step for the 256 steps, writing each element (the
+// sign and fraction from the record's plane, the exponent decoded).  The
+// words are read from the record through a window of 128 words held across
+// the wave (lane k: word wbase + k, and wbase + 64 + k).  Returns this
+// lane's "corrupt" flag.
+__device__ __forceinline__ bool decode_steps(const HceDecSmem& s, const uint8_t* __restrict__ rec, uint32_t n_words,
+                                             uint16_t* __restrict__ dst) {
+  const uint32_t lane = threadIdx.x;
+  const uint32_t* wg = reinterpret_cast<const uint32_t*>(rec + kWordsOff);
+  uint32_t win = lane < n_words ? wg[lane] : 0u;
+  uint32_t win2 = 64u + lane < n_words ? wg[64u + lane] : 0u;
+  uint32_t wbase = 0, base = 0, avail = 0;
+  uint64_t buf = 0;   // the lane's next `avail` stream bits, from the top bit down
+  bool bad = false;
+  const uint8_t* smp = rec + kSmOff + lane;
+  uint32_t smn[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) smn[q] = smp[64u * q];
+  for (uint32_t i0 = 0; i0 < kSteps; i0 += 8) {
+    uint32_t smv[8];   // sign at bit 15, fraction in bits 0..6
+#pragma unroll
+    for (int q = 0; q < 8; ++q) smv[q] = (smn[q] * 0x101u) & 0x807Fu;
+    if (i0 + 8 < kSteps) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) smn[q] = smp[64u * (i0 + 8 + q)];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      uint32_t e = s.lut[(uint32_t)(buf >> 32) >> (32u - kLmax)];
+      uint32_t L = e & 15u;
+      const bool need = L > avail;
+      const uint64_t mask = __ballot(need);
+      if (mask) {
+        const uint32_t rel = base - wbase + lanemask_lt_count(mask);   // < 128: base - wbase < 64 at every step
+        uint32_t word = __shfl(win, (int)(rel & 63u), 64);
+        if (__ballot(need && rel >= 64u)) {
+          const uint32_t w2 = __shfl(win2, (int)(rel & 63u), 64);
+          word = rel >= 64u ? w2 : word;
+        }
+        if (need) {
+          buf |= (uint64_t)__builtin_bitreverse32(word) << (32u - avail);
+          avail += 32;
+          e = s.lut[(uint32_t)(buf >> 32) >> (32u - kLmax)];
+          L = e & 15u;
+        }
+        base += (uint32_t)__popcll(mask);
+        if (base - wbase >= 64u) {
+          wbase += 64;
+          win = win2;
+          const uint32_t nx = wbase + 64u + lane;
+          win2 = nx < n_words ? wg[nx] : 0u;
+        }
+      }
+      bad |= L == 15u;   // no code in the window: a corrupt stream
+      buf <<= L;
+      avail -= L;
+      dst[64u * (i0 + q) + lane] = (uint16_t)(smv[q] | (e & 0x7F80u));
+    }
+  }
+  return bad || base != n_words || buf != 0;
+}
 
 __global__ __launch_bounds__(64) void hce_decompress_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes,
                                                             uint16_t* __restrict__ out, uint64_t n,
@@ -439,6 +554,7 @@ __global__ __launch_bounds__(64) void hce_decompress_kernel(const uint8_t* __res
       }
     }
   } else {
+    const uint32_t* wg = reinterpret_cast<const uint32_t*>(rec + kWordsOff);
     // Code lengths: lane holds exponents lane + 64 k.
     uint32_t ln[4];
     uint32_t kraft = 0, present = 0;
@@ -481,8 +597,7 @@ __global__ __launch_bounds__(64) void hce_decompress_kernel(const uint8_t* __res
           const uint64_t bm = __ballot(ln[k] == L);
           if (ln[k] == L) {
             const uint32_t r = run[L] + lanemask_lt_count(bm);
-            s.sorted[fidx[L] + r] = (uint8_t)(lane + 64u * k);
-            s.slen[fidx[L] + r] = (uint8_t)L;
+            s.ent[fidx[L] + r] = (uint16_t)(((lane + 64u * k) << 7) | L);
             s.start[fidx[L] + r] = (uint16_t)((fcode[L] + r) << (kLmax - L));
           }
           run[L] += (uint32_t)__popcll(bm);
@@ -490,81 +605,38 @@ __global__ __launch_bounds__(64) void hce_decompress_kernel(const uint8_t* __res
       }
       if (lane == 0) s.start[n_sym] = (uint16_t)kraft;   // end of the last code's range
       __syncthreads();
-      // Table: lane fills windows [64 lane, 64 lane + 64); the codes' ranges
-      // are consecutive in sorted order.
+      // Table: lane fills windows [64 lane, 64 lane + 64), the codes' ranges
+      // being consecutive in sorted order; it starts at a lane-dependent
+      // point of its run and wraps, so the lanes' writes fall in different
+      // banks.
       {
-        const uint32_t x0 = 64u * lane;
-        uint32_t lo = 0, hi = n_sym;   // the last code starting at or before x0
-        while (hi - lo > 1u) {
-          const uint32_t mid = (lo + hi) >> 1;
-          if (s.start[mid] <= x0) lo = mid; else hi = mid;
+        const uint32_t x0 = 64u * lane, r = lane;
+        uint32_t k0, kr;
+        {
+          uint32_t lo = 0, hi = n_sym;   // the last code starting at or before x0
+          while (hi - lo > 1u) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (s.start[mid] <= x0) lo = mid; else hi = mid;
+          }
+          k0 = lo;
+          lo = k0; hi = n_sym;           // ... at or before x0 + r
+          while (hi - lo > 1u) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (s.start[mid] <= x0 + r) lo = mid; else hi = mid;
+          }
+          kr = lo;
         }
-        uint32_t k = lo, next = s.start[k + 1];
+        uint32_t k = kr, next = s.start[k + 1], cur = s.ent[k];
         for (uint32_t j = 0; j < 64; ++j) {
-          const uint32_t x = x0 + j;
-          while (x >= next && k + 1 < n_sym) next = s.start[++k + 1];
-          s.lut[x] = x < kraft ? (uint16_t)(s.sorted[k] | (s.slen[k] << 8)) : (uint16_t)0;
+          const uint32_t o = (r + j) & 63u;
+          if (o == 0 && j != 0) { k = k0; next = s.start[k + 1]; cur = s.ent[k]; }
+          const uint32_t x = x0 + o;
+          while (x >= next && k + 1 < n_sym) { ++k; next = s.start[k + 1]; cur = s.ent[k]; }
+          s.lut[x] = x < kraft ? (uint16_t)cur : kNoCode;
         }
       }
       __syncthreads();
-      // Decode: 256 steps, every lane one code per step.
-      const uint32_t* wg = reinterpret_cast<const uint32_t*>(rec + kWordsOff);
-      uint32_t win = lane < n_words ? wg[lane] : 0u;
-      uint32_t win2 = 64u + lane < n_words ? wg[64u + lane] : 0u;
-      uint32_t wbase = 0, base = 0, avail = 0;
-      uint64_t buf = 0;
-      const uint8_t* smp = rec + kSmOff + lane;
-      uint32_t smn[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) smn[q] = smp[64u * q];
-      for (uint32_t i0 = 0; i0 < kSteps; i0 += 8) {
-        uint32_t smv[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) smv[q] = smn[q];
-        if (i0 + 8 < kSteps) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) smn[q] = smp[64u * (i0 + 8 + q)];
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          uint32_t e = s.lut[__builtin_bitreverse32((uint32_t)buf) >> (32u - kLmax)];
-          uint32_t L = e >> 8;
-          const bool need = L == 0 ? avail < kLmax : L > avail;
-          const uint64_t mask = __ballot(need);
-          if (mask) {
-            const uint32_t p = base + lanemask_lt_count(mask);
-            const uint32_t rel = p - wbase;   // < 128: base - wbase < 64 at every step
-            uint32_t word = __shfl(win, (int)(rel & 63u), 64);
-            if (__ballot(need && rel >= 64u)) {
-              const uint32_t w2 = __shfl(win2, (int)(rel & 63u), 64);
-              word = rel >= 64u ? w2 : word;
-            }
-            if (need) {
-              bad |= p >= n_words;
-              buf |= (uint64_t)word << avail;
-              avail += 32;
-              e = s.lut[__builtin_bitreverse32((uint32_t)buf) >> (32u - kLmax)];
-              L = e >> 8;
-            }
-            base += (uint32_t)__popcll(mask);
-            if (base - wbase >= 64u) {
-              wbase += 64;
-              win = win2;
-              const uint32_t nx = wbase + 64u + lane;
-              win2 = nx < n_words ? wg[nx] : 0u;
-            }
-          }
-          if (L == 0 || L > avail) {   // only in a corrupt stream
-            bad = true;
-            L = avail < 1u ? 0u : 1u;
-          }
-          buf >>= L;
-          avail -= L;
-          const uint32_t smb = smv[q];
-          dst[64u * (i0 + q) + lane] = (uint16_t)(((smb & 0x80u) << 8) | ((e & 0xFFu) << 7) | (smb & 0x7Fu));
-        }
-      }
-      bad |= base != n_words || buf != 0;
+      bad = decode_steps(s, rec, n_words, dst);
       // zero padding after the last word
       const uint32_t pw = n_words + lane;
       if (lane < 3u && 4u * pw < ((4u * n_words + 15u) & ~15u)) bad |= wg[pw] != 0;

@@ -179,3 +179,21 @@ def test_full_size(name):
     hc.hc_decompress_bf16_entropy(out, size, back, n, status)
     torch.cuda.synchronize()
     assert int(status.item()) == 0 and torch.equal(back.view(torch.int16), x.view(torch.int16))
+
+
+@pytest.mark.parametrize("k", [2, 3, 63, 64, 65, 80, 200])
+def test_exponent_count_boundaries(k):
+    """k distinct exponents per block with skewed counts: up to 64 the code
+    is built in one wave's registers, above that by the LDS loop."""
+    g = np.random.default_rng(100 + k)
+    p = 1.0 / np.arange(1, k + 1) ** 1.1
+    p /= p.sum()
+    blocks = []
+    for b in range(3):
+        e = g.choice(np.arange(60, 60 + k), size=B, p=p).astype(np.uint16)
+        e[:k] = np.arange(60, 60 + k)            # every exponent present
+        g.shuffle(e)
+        blocks.append((e << 7) | g.integers(0, 128, B).astype(np.uint16))
+    v = np.concatenate(blocks)
+    assert all(len(np.unique((blk >> 7) & 0xFF)) == k for blk in blocks)
+    check(v, f"k={k}")
