@@ -44,6 +44,11 @@ PEAK_BF16_TFLOPS = 2500.0       # dense bf16 MFMA, published
 N_CU = 256
 
 METRIC = "AllReduce algbw GB/s and achieved HBM GB/s (% of peak), R=8, 1 MI355X"
+# sources whose change voids the recorded traffic counters of a kernel
+CODEC_FILES = ["collective_communication_amd/csrc/codec_kernels.hip", "collective_communication_amd/csrc/codec.hpp",
+               "collective_communication_amd/csrc/lookback.hpp"]
+ENTROPY_FILES = ["collective_communication_amd/csrc/entropy_kernels.hip", "collective_communication_amd/csrc/codec.hpp",
+                 "collective_communication_amd/csrc/lookback.hpp"]
 
 
 def kernel_hash(files) -> str:
@@ -88,6 +93,28 @@ def median(xs):
     s = sorted(xs)
     n = len(s)
     return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def roofline_obj(kernel: str, alg_bytes: int, ms: float, traffic=None, duration: str | None = None):
+    """The dominant kernel against MI355X's HBM peak: algorithmic bytes per
+    launch over the launch's duration (HIP events on its stream)."""
+    gbps = alg_bytes / (ms / 1e3) / 1e9
+    d = {"bound": "hbm", "kernel": kernel, "achieved": round(gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+         "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": traffic, "alg_bytes_per_launch": int(alg_bytes),
+         "launch_ms": round(ms, 6)}
+    if duration:
+        d["duration"] = duration
+    return d
+
+
+def oracle_timed(fn, nbytes: int, sample: str, unit: str = "GB/s"):
+    """The oracle as it stands, one host thread, on a bounded sample; nbytes
+    is what the sample moves in the metric's sense."""
+    t0 = time.perf_counter()
+    fn()
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 6), "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": f"{sample}; {dt:.2f} s"}
 
 
 def cpu_baseline_ring(R: int, n_sample: int):
@@ -165,6 +192,12 @@ def bench_ring(args, workload: str):
     }
     if not args.no_cpu_baseline and workload == "ring_bf16":
         line["cpu_baseline"] = cpu_baseline_ring(R, args.cpu_sample)
+    elif not args.no_cpu_baseline:
+        import oracle
+
+        xs = [inputs.host_bits(t) for t in send]
+        line["cpu_baseline"] = oracle_timed(lambda: oracle.allreduce_ring(xs), n * es,
+                                            f"the whole workload (R={R} x {n} {dtype}), ring step simulator")
     return line
 
 
@@ -213,11 +246,30 @@ def bench_codec(args):
                       "round_trip_exact": ok}
         del x
     worst = min(min(r["compress_hbm_gbps"], r["decompress_hbm_gbps"]) for r in rows.values())
-    return {"metric": "HCZ1 bf16 codec throughput (HBM GB/s, raw GB/s) and ratio, 2^28 elements",
+    w = rows["weights"]
+    codec_files = CODEC_FILES
+    line = {"metric": "HCZ1 bf16 codec throughput (HBM GB/s, raw GB/s) and ratio, 2^28 elements",
             "value": worst, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "dtype": "u8", "data": "synthetic",
             "config": {"workload": "standalone lossless bf16 codec, 2^28 elements per tensor"},
-            "tensors": rows, "hbm_frac_of_peak_worst": round(worst / PEAK_HBM_GBPS, 4)}
+            "tensors": rows, "hbm_frac_of_peak_worst": round(worst / PEAK_HBM_GBPS, 4),
+            "roofline": roofline_obj("compress_kernel (weights)", 2 * n + w["compressed_bytes"], w["compress_ms"],
+                                     load_traffic("compress", "codec", codec_files),
+                                     "per hc_compress_bf16 call: the kernel and the clear of its look-back workspace"),
+            "roofline_decompress": roofline_obj("decompress_kernel (weights)", 2 * n + w["compressed_bytes"],
+                                                w["decompress_ms"], load_traffic("decompress", "codec", codec_files),
+                                                "per hc_decompress_bf16 call: the kernel, the status clear and the "
+                                                "corrupt-stream check")}
+    if not args.no_cpu_baseline:
+        import oracle
+
+        m = 1 << 26
+        host = inputs.host_bits(inputs.normal_bf16_cuda("codec", 0, n, 0.02)[:m])
+        stream = oracle.compress(host)
+        line["cpu_baseline"] = oracle_timed(lambda: oracle.compress(host), 2 * m + len(stream),
+                                            f"oracle compress of the first {m} elements of the weights tensor "
+                                            "(HBM-equivalent bytes: input + stream)")
+    return line
 
 
 def bench_entropy(args):
@@ -259,13 +311,32 @@ def bench_entropy(args):
         rows[name] = row
         del x
     w = rows["weights"]["entropy"]
-    return {"metric": "HCE1 (Huffman exponent) bf16 codec: compressed/raw size and throughput, 2^28 elements",
+    line = {"metric": "HCE1 (Huffman exponent) bf16 codec: compressed/raw size and throughput, 2^28 elements",
             "value": min(r["entropy"]["compress_hbm_gbps"] for r in rows.values()), "unit": "GB/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "u8",
             "data": "synthetic",
             "config": {"workload": "entropy-coded exponent variant next to the fixed-length codec, 2^28 bf16 per "
                                    "tensor (weights, activations, gradients, gradient bucket)"},
-            "weights_ratio": w["ratio"], "tensors": rows}
+            "weights_ratio": w["ratio"], "tensors": rows,
+            "roofline": roofline_obj("hce_compress_kernel (weights)", 2 * n + w["compressed_bytes"], w["compress_ms"],
+                                     load_traffic("hce_compress", "entropy", ENTROPY_FILES),
+                                     "per hc_compress_bf16_entropy call: the kernel and the clear of its "
+                                     "look-back workspace"),
+            "roofline_decompress": roofline_obj("hce_decompress_kernel (weights)", 2 * n + w["compressed_bytes"],
+                                                w["decompress_ms"], load_traffic("hce_decompress", "entropy",
+                                                                                 ENTROPY_FILES),
+                                                "per hc_decompress_bf16_entropy call: the kernel, the status clear "
+                                                "and the corrupt-stream check")}
+    if not args.no_cpu_baseline:
+        import oracle
+
+        m = 1 << 26
+        host = inputs.host_bits(inputs.normal_bf16_cuda("codec", 0, n, 0.02)[:m])
+        stream = oracle.hce_compress(host)
+        line["cpu_baseline"] = oracle_timed(lambda: oracle.hce_compress(host), 2 * m + len(stream),
+                                            f"oracle HCE1 compress of the first {m} elements of the weights tensor "
+                                            "(HBM-equivalent bytes: input + stream)")
+    return line
 
 
 def bench_table_scope(args):
@@ -305,13 +376,28 @@ def bench_table_scope(args):
         rows[name] = row
         del x
     b = rows["bucket"]
-    return {"metric": "HCZ1 compressed/raw size of a 2^28 bf16 gradient bucket with per-block code tables",
+    g = b["global"]
+    line = {"metric": "HCZ1 compressed/raw size of a 2^28 bf16 gradient bucket with per-block code tables",
             "value": b["per_block"]["ratio"], "unit": "ratio", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "higher_is_better": False, "dtype": "u8", "data": "synthetic",
             "config": {"workload": "code-table scope sweep: per block, groups of 1/8/64 blocks, one global "
                                    "table; 2^28 bf16 per tensor"},
             "global_over_per_block_size": round(b["global"]["ratio"] / b["per_block"]["ratio"], 4),
-            "tensors": rows}
+            "tensors": rows,
+            "roofline": roofline_obj("hc_compress_bf16_scoped, one global table (bucket)",
+                                     2 * n + g["compressed_bytes"], g["compress_ms"], None,
+                                     "per call: the histogram pass, the four small scope kernels, the workspace "
+                                     "clears and compress_kernel<true>; bytes are the input and the stream only")}
+    if not args.no_cpu_baseline:
+        import oracle
+
+        m = 1 << 26
+        host = inputs.host_bits(inputs.bucket_bf16_cuda("bucket", 0, n)[:m])
+        stream = oracle.compress_scoped(host, 0)
+        line["cpu_baseline"] = oracle_timed(lambda: oracle.compress_scoped(host, 0), 2 * m + len(stream),
+                                            f"oracle compress_scoped (one global table) of the first {m} elements of "
+                                            "the bucket (HBM-equivalent bytes: input + stream)")
+    return line
 
 
 def bench_compressed(args):
@@ -356,7 +442,21 @@ def bench_compressed(args):
         parts["rs"] += d[1:R]
         parts["ag"] += d[R:]
     raw_wire = 2 * (R - 1) * n * 2
-    return {"metric": "Compressed ring AllReduce algbw and achieved HBM GB/s, R=8, 2^25 bf16",
+    rs_ms = sum(parts["rs"]) / len(parts["rs"])
+    rec_hop = rec_bytes / (2 * (R - 1))           # records moved by one hop, all ranks
+    extra = {"roofline": roofline_obj("car_rs_kernel (one reduce-scatter hop: decode, hop, encode)",
+                                      int(2 * n + 2 * rec_hop), rs_ms, None,
+                                      "mean reduce-scatter step by HIP events at the step boundaries "
+                                      "(the last step also writes the output)")}
+    if not args.no_cpu_baseline:
+        import oracle
+
+        m = 1 << 23
+        xs = [inputs.host_bits(t[:m]) for t in send]
+        extra["cpu_baseline"] = oracle_timed(lambda: oracle.compressed_allreduce(xs), 2 * m,
+                                             f"oracle compressed allreduce of the first {m} elements of every rank "
+                                             "(algbw: elements x 2 bytes per second)")
+    return {**extra, "metric": "Compressed ring AllReduce algbw and achieved HBM GB/s, R=8, 2^25 bf16",
             "value": round(n * 2 / (ms / 1e3) / 1e9, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "dtype": "bf16",
             "data": "synthetic",
@@ -408,7 +508,19 @@ def bench_fused_sgd(args):
     # write 1), R-1 copy steps (read 1, write 1), every one over n elements
     alg = 2 * n * (3 * (R - 2) + 4 + 2 * (R - 1))
     alg_unfused = 2 * n * (3 * (R - 1) + 2 * (R - 1)) + 2 * n * R * 3
-    return {"metric": "Allreduce fused with an SGD update: algbw and achieved HBM GB/s, R=8, 2^26 bf16",
+    last_ms = sum(last) / len(last)
+    extra = {"roofline": roofline_obj("step_kernel<2,sgd> (the last reduce-scatter step with the update)", 8 * n,
+                                      last_ms, None, "HIP events at the step boundaries")}
+    if not args.no_cpu_baseline:
+        import oracle
+
+        m = 1 << 24
+        gs = [inputs.host_bits(t[:m]) for t in grads]
+        wh = [inputs.host_bits(w0[:m])] * R
+        extra["cpu_baseline"] = oracle_timed(lambda: oracle.allreduce_sgd(gs, wh, lr), 2 * m,
+                                             f"oracle allreduce + SGD of the first {m} elements of every rank "
+                                             "(algbw: elements x 2 bytes per second)")
+    return {**extra, "metric": "Allreduce fused with an SGD update: algbw and achieved HBM GB/s, R=8, 2^26 bf16",
             "value": round(n * 2 / (ms / 1e3) / 1e9, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "dtype": "bf16",
             "data": "synthetic",
@@ -518,6 +630,18 @@ def bench_contention(args):
         if k:
             del side
             hc.hc_stream_destroy(handle)
+    full = rows[-1]
+    extra = {"roofline": roofline_obj("step_kernel<reduce> (reduce-scatter alone on all CUs, mean of its launches)",
+                                      3 * 2 * n, full["rs_alone_ms"] / (R - 1), None,
+                                      "one reduce-scatter of R-1 launches by HIP events, divided by R-1")}
+    if not args.no_cpu_baseline:
+        import oracle
+
+        m = 1 << 24
+        xs = [inputs.host_bits(t[:m]) for t in send]
+        extra["cpu_baseline"] = oracle_timed(lambda: oracle.reduce_scatter_ring(xs), 3 * 2 * m * (R - 1),
+                                             f"oracle reduce-scatter of the first {m} elements of every rank "
+                                             "(algorithmic bytes per second, as the GPU rows)")
     # The all-gather that follows this reduce-scatter (R slices of L -> R
     # outputs of n), on copy kernels and on the DMA copy engines (the offload
     # of "HOCCL ...", section 2), measured by dma_contention in a process of
@@ -538,7 +662,7 @@ def bench_contention(args):
                                    "main stream torch.matmul 8192^3 bf16; then the matching all-gather "
                                    f"({R} x {L} -> {R} x {n}) on CU copy kernels and on the DMA copy engines"},
             "gemm_tflops_alone": round(2 * 8192 ** 3 / (t_gemm / 1e3) / 1e12, 1), "rows": rows,
-            "all_gather": ag}
+            "all_gather": ag, **extra}
 
 
 def main():
