@@ -14,7 +14,8 @@ fused compressed ring, R=8 x 2^25 bf16), contention (R=8 reduce-scatter of
 all-gather on CU copy kernels and on the DMA engines), fused_sgd (the allreduce
 of R=8 x 2^26 bf16 gradients fused with an SGD update of the weights),
 table_scope (the codec's code tables per block, per group of blocks or global,
-on 2^28 bf16 weights, gradients and a multi-layer gradient bucket), entropy
+and the per-block encoder in three global rounds, on 2^28 bf16 weights,
+gradients and a multi-layer gradient bucket), entropy
 (the HCE1 variant with per-block Huffman codes for the exponent, next to the
 fixed-length codec on the same 2^28 tensors).  Each prints one JSON line of
 its own.
@@ -352,7 +353,9 @@ def bench_table_scope(args):
     ws = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_COMPRESS_SCOPED, n, 1), dtype=torch.uint8, device="cuda")
     back = torch.empty(n, dtype=torch.bfloat16, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    scopes = [("per_block", None), ("group_1", 1), ("group_8", 8), ("group_64", 64), ("global", 0)]
+    scopes = [("per_block", None), ("per_block_3_rounds", "staged"), ("group_1", 1), ("group_8", 8),
+              ("group_64", 64), ("global", 0)]
+    ws3 = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_COMPRESS_STAGED, n, 1), dtype=torch.uint8, device="cuda")
     rows = {}
     for name, maker in (("weights", lambda: inputs.normal_bf16_cuda("codec", 0, n, 0.02)),
                         ("gradients", lambda: inputs.normal_bf16_cuda("codec", 2, n, 1e-4)),
@@ -362,6 +365,8 @@ def bench_table_scope(args):
         for label, group in scopes:
             if group is None:
                 call = lambda: hc.hc_compress_bf16(x, n, out, nbytes, ws)
+            elif group == "staged":
+                call = lambda: hc.hc_compress_bf16_staged(x, n, out, nbytes, ws3)
             else:
                 call = lambda g=group: hc.hc_compress_bf16_scoped(x, n, out, nbytes, g, ws)
             for _ in range(args.warmup):
@@ -383,6 +388,8 @@ def bench_table_scope(args):
             "config": {"workload": "code-table scope sweep: per block, groups of 1/8/64 blocks, one global "
                                    "table; 2^28 bf16 per tensor"},
             "global_over_per_block_size": round(b["global"]["ratio"] / b["per_block"]["ratio"], 4),
+            "three_rounds_over_one_round_time": round(b["per_block_3_rounds"]["compress_ms"]
+                                                      / b["per_block"]["compress_ms"], 3),
             "tensors": rows,
             "roofline": roofline_obj("hc_compress_bf16_scoped, one global table (bucket)",
                                      2 * n + g["compressed_bytes"], g["compress_ms"], None,

@@ -33,6 +33,7 @@ HC_OP_ALLREDUCE = 3
 HC_OP_ALL_GATHER = 4
 HC_OP_COMPRESS_SCOPED = 5
 HC_OP_COMPRESS_ENTROPY = 6
+HC_OP_COMPRESS_STAGED = 7
 HC_BLOCK_ELEMS = 16384
 HC_MAX_RANKS = 64
 
@@ -42,6 +43,7 @@ EXPORTED = [
     "hc_stream_create_cu_budget", "hc_stream_destroy", "hc_chunk_elems", "hc_ring_tasks",
     "hc_status_string", "hc_last_error", "hc_version", "hc_step_count", "hc_allreduce_sgd",
     "hc_compress_bf16_scoped", "hc_compress_bf16_entropy", "hc_decompress_bf16_entropy",
+    "hc_compress_bf16_staged",
 ]
 
 
@@ -87,6 +89,7 @@ def load(path: str = LIB_PATH):
     L.hc_compress_bf16.argtypes = [P, S, P, S, P, P, S, P]
     L.hc_compress_bf16_scoped.argtypes = [P, S, P, S, P, S, P, S, P]
     L.hc_compress_bf16_entropy.argtypes = [P, S, P, S, P, P, S, P]
+    L.hc_compress_bf16_staged.argtypes = [P, S, P, S, P, P, S, P]
     L.hc_decompress_bf16_entropy.argtypes = [P, S, P, S, P, P]
     L.hc_decompress_bf16.argtypes = [P, S, P, S, P, P]
     L.hc_compressed_allreduce.argtypes = [PP, PP, S, I, P, S, P, O, P]
@@ -101,7 +104,8 @@ def load(path: str = LIB_PATH):
     L.hc_step_count.restype = I
     L.hc_ring_tasks.restype = S
     for name in ("hc_allreduce", "hc_reduce_scatter", "hc_all_gather", "hc_allreduce_sgd", "hc_compress_bf16",
-                 "hc_compress_bf16_scoped", "hc_compress_bf16_entropy", "hc_decompress_bf16",
+                 "hc_compress_bf16_scoped", "hc_compress_bf16_entropy", "hc_compress_bf16_staged",
+                 "hc_decompress_bf16",
                  "hc_decompress_bf16_entropy", "hc_compressed_allreduce", "hc_stream_create_cu_budget",
                  "hc_stream_destroy"):
         getattr(L, name).restype = I
@@ -320,6 +324,21 @@ def hc_decompress_bf16(d_in: torch.Tensor, in_bytes: int, d_out: torch.Tensor, n
     outp = _dptr(d_out, 2 * n, "d_out") if n else None
     st = _dptr(d_status, 4, "d_status")
     _check(L.hc_decompress_bf16(inp, in_bytes, outp, n, st, _stream_handle(stream)))
+
+
+def hc_compress_bf16_staged(d_in: torch.Tensor, n: int, d_out: torch.Tensor, d_out_bytes: torch.Tensor,
+                            ws: torch.Tensor, *, stream=None):
+    """hc_compress_bf16 in three global rounds (slots, prefix, coalescing copy)."""
+    L = load()
+    if d_in.element_size() != 2:
+        raise TypeError("input must hold 16-bit words")
+    inp = _dptr(d_in, 2 * n, "d_in") if n else (d_in.data_ptr() if d_in.numel() else None)
+    out_cap = d_out.numel() * d_out.element_size()
+    outp = _dptr(d_out, 1, "d_out")
+    ob = _dptr(d_out_bytes, 8, "d_out_bytes")
+    wsp = _dptr(ws, 1, "ws")
+    _check(L.hc_compress_bf16_staged(inp, n, outp, out_cap, ob, wsp, ws.numel() * ws.element_size(),
+                                     _stream_handle(stream)))
 
 
 def hc_compress_bf16_entropy(d_in: torch.Tensor, n: int, d_out: torch.Tensor, d_out_bytes: torch.Tensor,

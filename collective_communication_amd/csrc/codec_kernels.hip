@@ -125,6 +125,74 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
   }
 }
 
+// The three-round baseline of "CCCL ...", section 4.4 (compress into
+// temporaries, prefix of the sizes, coalescing copy), with the same encoder.
+// Round 1: every block encodes into its own fixed-size slot.
+__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void staged_encode_kernel(
+    const uint16_t* __restrict__ in, uint64_t n, uint8_t* __restrict__ slots, uint32_t* __restrict__ sizes) {
+  __shared__ Smem s;
+  const uint32_t bid = blockIdx.x;
+  zero_hist(s);
+  __syncthreads();
+  const uint64_t first = (uint64_t)bid * kB;
+  const uint32_t m = (uint32_t)((n - first) < kB ? (n - first) : kB);
+  uint4 v[kPer];
+  load_block(in + first, m, v);
+  const Plan p = plan_block<true>(v, m, s);
+  write_block(v, p, s);
+  __syncthreads();
+  copy_out(s, slots + (uint64_t)bid * kRawFull, p.rec_bytes);
+  if (threadIdx.x == 0) sizes[bid] = p.rec_bytes;
+}
+
+// Round 2: byte offset of every record (exclusive prefix of the sizes after
+// the stream header and offset table); offs[nb] is the stream size.  One
+// workgroup: each thread sums a run of sizes, the 1024 run sums are scanned
+// in LDS, and each thread writes its run's offsets.
+__global__ __launch_bounds__(1024) void staged_scan_kernel(const uint32_t* __restrict__ sizes, uint32_t nb,
+                                                           uint64_t* __restrict__ offs) {
+  __shared__ uint64_t part[2][1024];
+  const uint32_t t = threadIdx.x;
+  const uint32_t per = (nb + 1023u) / 1024u;
+  const uint32_t lo = t * per < nb ? t * per : nb, hi = lo + per < nb ? lo + per : nb;
+  uint64_t sum = 0;
+  for (uint32_t j = lo; j < hi; ++j) sum += sizes[j];
+  int cur = 0;
+  part[cur][t] = sum;
+  __syncthreads();
+  for (uint32_t d = 1; d < 1024; d <<= 1) {   // inclusive scan
+    const uint64_t x = part[cur][t] + (t >= d ? part[cur][t - d] : 0ull);
+    cur ^= 1;
+    part[cur][t] = x;
+    __syncthreads();
+  }
+  uint64_t base = header_bytes(nb) + part[cur][t] - sum;
+  for (uint32_t j = lo; j < hi; ++j) {
+    offs[j] = base;
+    base += sizes[j];
+  }
+  if (t == 1023) offs[nb] = header_bytes(nb) + part[cur][t];
+}
+
+// Round 3: every record copied from its slot to its place in the stream.
+__global__ __launch_bounds__(256) void staged_copy_kernel(const uint8_t* __restrict__ slots,
+                                                          const uint32_t* __restrict__ sizes,
+                                                          const uint64_t* __restrict__ offs, uint8_t* __restrict__ out,
+                                                          uint64_t n, uint32_t nb, uint64_t* __restrict__ out_bytes) {
+  const uint32_t bid = blockIdx.x, t = threadIdx.x;
+  const uint32_t n16 = sizes[bid] / 16u;
+  const uint64_t off = offs[bid];
+  const uint8_t* src = slots + (uint64_t)bid * kRawFull;
+  for (uint32_t i = t; i < n16; i += 256) st16(out + off + 16ull * i, ld16(src + 16ull * i));
+  if (t == 0) {
+    reinterpret_cast<uint64_t*>(out + 32)[bid] = off;
+    if (bid == nb - 1) {
+      write_stream_header(out, kMagic, kB, n, nb, offs[nb]);
+      *out_bytes = offs[nb];
+    }
+  }
+}
+
 // Table scope, step 1: each full block's exponent histogram.  A workgroup
 // walks blocks blockIdx.x, + gridDim.x, ... and loads the next block while it
 // counts the current one.
@@ -490,6 +558,27 @@ hipError_t launch_compress(const uint16_t* in, size_t n, void* out, uint64_t* ou
   hipLaunchKernelGGL(compress_kernel<false>, dim3((uint32_t)nb), dim3(kCT), 0, stream, in, (uint64_t)n,
                      static_cast<uint8_t*>(out), out_bytes, static_cast<CompressWs*>(ws), (uint32_t)nb, ScopeWs{},
                      1u);
+  return hipGetLastError();
+}
+
+// Workspace of the three-round baseline: one slot per block, the sizes, the offsets.
+size_t staged_ws_bytes(size_t n) {
+  const size_t nb = ceil_div(n, kB);
+  return align256(nb * kRawFull) + align256(4 * nb) + align256(8 * (nb + 1));
+}
+
+hipError_t launch_compress_staged(const uint16_t* in, size_t n, void* out, uint64_t* out_bytes, void* ws,
+                                  hipStream_t stream) {
+  const size_t nb = ceil_div(n, kB);
+  if (nb == 0) return launch_empty_stream(out, kMagic, out_bytes, stream);
+  if (nb >= (1ull << 31)) return hipErrorInvalidValue;
+  uint8_t* slots = static_cast<uint8_t*>(ws);
+  uint32_t* sizes = reinterpret_cast<uint32_t*>(slots + align256(nb * kRawFull));
+  uint64_t* offs = reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(sizes) + align256(4 * nb));
+  hipLaunchKernelGGL(staged_encode_kernel, dim3((uint32_t)nb), dim3(kCT), 0, stream, in, (uint64_t)n, slots, sizes);
+  hipLaunchKernelGGL(staged_scan_kernel, dim3(1), dim3(1024), 0, stream, sizes, (uint32_t)nb, offs);
+  hipLaunchKernelGGL(staged_copy_kernel, dim3((uint32_t)nb), dim3(256), 0, stream, slots, sizes, offs,
+                     static_cast<uint8_t*>(out), (uint64_t)n, (uint32_t)nb, out_bytes);
   return hipGetLastError();
 }
 

@@ -260,7 +260,8 @@ int hc_step_count(hc_op_t op, int nranks) {
     case HC_OP_COMPRESSED_ALLREDUCE: return 2 * nranks - 1;
     case HC_OP_COMPRESS:
     case HC_OP_COMPRESS_SCOPED:
-    case HC_OP_COMPRESS_ENTROPY: return -1;
+    case HC_OP_COMPRESS_ENTROPY:
+    case HC_OP_COMPRESS_STAGED: return -1;
   }
   return -1;
 }
@@ -349,6 +350,8 @@ size_t hc_workspace_bytes(hc_op_t op, size_t count, int nranks, hc_dtype_t dtype
       return hc::compress_scoped_ws_bytes(count);
     case HC_OP_COMPRESS_ENTROPY:
       return hc::compress_ws_bytes(count);
+    case HC_OP_COMPRESS_STAGED:
+      return hc::staged_ws_bytes(count);
     case HC_OP_COMPRESSED_ALLREDUCE:
       if (dtype != HC_BF16) return 0;
       return hc::compressed_ar_ws_bytes(count, nranks);
@@ -472,7 +475,7 @@ size_t hc_compress_bound_bf16(size_t n) {
 
 namespace {
 
-enum class Coder { kPerBlock, kScoped, kEntropy };
+enum class Coder { kPerBlock, kScoped, kEntropy, kStaged };
 
 // The compress entry points: per-block fixed-length tables, tables shared by
 // groups of blocks, or per-block Huffman codes (HCE1).
@@ -488,7 +491,9 @@ hc_status_t compress_common(const uint16_t* d_in, size_t n, void* d_out, size_t 
   const size_t bound = hc_compress_bound_bf16(n);
   if (out_cap < bound)
     return fail(HC_ERR_INSUFFICIENT_CAPACITY, "out_cap %zu < bound %zu", out_cap, bound);
-  const size_t need = scoped ? hc::compress_scoped_ws_bytes(n) : hc::compress_ws_bytes(n);
+  const size_t need = scoped                     ? hc::compress_scoped_ws_bytes(n)
+                      : coder == Coder::kStaged ? hc::staged_ws_bytes(n)
+                                                : hc::compress_ws_bytes(n);
   if (ws_bytes < need)
     return fail(HC_ERR_INSUFFICIENT_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, need);
   Range ir{(uintptr_t)d_in, (uintptr_t)d_in + 2 * n}, orr{(uintptr_t)d_out, (uintptr_t)d_out + bound},
@@ -498,6 +503,7 @@ hc_status_t compress_common(const uint16_t* d_in, size_t n, void* d_out, size_t 
   hipError_t e = coder == Coder::kScoped
                      ? hc::launch_compress_scoped(d_in, n, d_out, d_out_bytes, d_ws, table_blocks, stream)
                  : coder == Coder::kEntropy ? hc::launch_hce_compress(d_in, n, d_out, d_out_bytes, d_ws, stream)
+                 : coder == Coder::kStaged  ? hc::launch_compress_staged(d_in, n, d_out, d_out_bytes, d_ws, stream)
                                             : hc::launch_compress(d_in, n, d_out, d_out_bytes, d_ws, stream);
   if (e == hipErrorNotSupported) return fail(HC_ERR_UNSUPPORTED, "compress not built");
   return e == hipSuccess ? HC_SUCCESS : device_fail(e, "compress launch");
@@ -515,6 +521,11 @@ hc_status_t hc_compress_bf16_scoped(const uint16_t* d_in, size_t n, void* d_out,
                                     hipStream_t stream) {
   return compress_common(d_in, n, d_out, out_cap, d_out_bytes, d_ws, ws_bytes, Coder::kScoped, table_blocks,
                          stream);
+}
+
+hc_status_t hc_compress_bf16_staged(const uint16_t* d_in, size_t n, void* d_out, size_t out_cap,
+                                    uint64_t* d_out_bytes, void* d_ws, size_t ws_bytes, hipStream_t stream) {
+  return compress_common(d_in, n, d_out, out_cap, d_out_bytes, d_ws, ws_bytes, Coder::kStaged, 1, stream);
 }
 
 hc_status_t hc_compress_bf16_entropy(const uint16_t* d_in, size_t n, void* d_out, size_t out_cap,

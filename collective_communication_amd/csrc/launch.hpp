@@ -51,6 +51,11 @@ hipError_t launch_hce_compress(const uint16_t* in, size_t n, void* out, uint64_t
                                hipStream_t stream);
 hipError_t launch_hce_decompress(const void* in, size_t in_bytes, uint16_t* out, size_t n, int32_t* status,
                                  hipStream_t stream);
+// Three-round baseline (blocks into slots, prefix of the sizes, coalescing
+// copy); the same stream as launch_compress.
+size_t staged_ws_bytes(size_t n);
+hipError_t launch_compress_staged(const uint16_t* in, size_t n, void* out, uint64_t* out_bytes, void* ws,
+                                  hipStream_t stream);
 // Table-scope variant: code tables shared by groups of `group` full blocks
 // (0: one table for the whole stream).
 size_t compress_scoped_ws_bytes(size_t n);

@@ -232,6 +232,21 @@ hc_status_t hc_compress_bf16_scoped(const uint16_t *d_in, size_t n, void *d_out,
                                     size_t ws_bytes, hipStream_t stream);
 
 /*
+ * hc_compress_bf16_staged -- hc_compress_bf16 in three global rounds, the
+ * design "CCCL ...", section 4.4 replaces: every block encodes into a
+ * fixed-size temporary slot (16 + 32768 bytes), a prefix over the record
+ * sizes places the records, and a coalescing copy writes them into the
+ * stream.  The same encoder and format: the stream equals hc_compress_bf16's
+ * byte for byte.  For measuring the single-round design against it.
+ *   d_ws: >= hc_workspace_bytes(HC_OP_COMPRESS_STAGED, n, 1, HC_BF16) bytes
+ *   (the slots, about 2.0 bytes per element).  Other arguments and errors as
+ *   hc_compress_bf16.
+ */
+hc_status_t hc_compress_bf16_staged(const uint16_t *d_in, size_t n, void *d_out, size_t out_cap,
+                                    uint64_t *d_out_bytes, void *d_ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
+/*
  * hc_compress_bf16_entropy -- lossless bf16 compression with an entropy-coded
  * exponent: one "HCE1" stream.  "CCCL ...", section 4.1 codes the exponent
  * from a frequency table with sign and fraction raw, and section 6.5
@@ -320,7 +335,8 @@ typedef enum {
     HC_OP_ALLREDUCE = 3,
     HC_OP_ALL_GATHER = 4,
     HC_OP_COMPRESS_SCOPED = 5,
-    HC_OP_COMPRESS_ENTROPY = 6
+    HC_OP_COMPRESS_ENTROPY = 6,
+    HC_OP_COMPRESS_STAGED = 7
 } hc_op_t;
 
 /* Workspace bytes for an operation; count = elements per rank buffer

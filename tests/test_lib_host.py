@@ -63,6 +63,8 @@ def test_workspace_sizes(hc):
     assert hc.hc_workspace_bytes(hc.HC_OP_REDUCE_SCATTER, 8 * 1000, 8, hc.HC_BF16) == 2 * 8000 * 2
     assert hc.hc_workspace_bytes(hc.HC_OP_REDUCE_SCATTER, 7, 2, hc.HC_F32) == 0  # 7 % 2 != 0
     assert hc.hc_workspace_bytes(hc.HC_OP_COMPRESS, 1 << 20, 1) > 0
+    # the three-round baseline holds one 32,784-byte slot per block
+    assert hc.hc_workspace_bytes(hc.HC_OP_COMPRESS_STAGED, 1 << 20, 1) >= 64 * 32784
     # the table-scope encoder also holds per-block histograms and escape counts
     assert hc.hc_workspace_bytes(hc.HC_OP_COMPRESS_SCOPED, 1 << 20, 1) > \
         hc.hc_workspace_bytes(hc.HC_OP_COMPRESS, 1 << 20, 1) + 64 * 256 * 2
