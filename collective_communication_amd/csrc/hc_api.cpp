@@ -146,12 +146,22 @@ hc_status_t run_allreduce(void* const* send, void* const* recv, size_t count, hc
     hc::Seg segs[hc::kMaxSegs];
     int nseg = 0, last_dst = -1;
     uint64_t last_end = 0;
+    hipError_t e = tap.mark(stream);
+    if (e != hipSuccess) return device_fail(e, "hipEventRecord");
+    auto launch = [&]() {
+      return op == 1 ? hc::launch_reduce_step(segs, nseg, dtype, budget, stream)
+                     : copy_step(segs, nseg, es, budget, dma, stream);
+    };
     while (k < tasks.size() && tasks[k].op == op && tasks[k].step == step) {
       const hc_task_t& t = tasks[k];
       const size_t off = t.off * es;
       if (t.dst == last_dst && t.off == last_end) {
         segs[nseg - 1].len += t.len;  // next chunk of the same receiver's slice
       } else {
+        if (nseg == hc::kMaxSegs) {   // a full launch (the task order gives one segment per receiver)
+          if ((e = launch()) != hipSuccess) return device_fail(e, op == 1 ? "reduce step launch" : "copy step launch");
+          nseg = 0;
+        }
         segs[nseg].a = (op == 1 && step == 0) ? cp(send[t.src], off) : cp(recv[t.src], off);
         segs[nseg].b = cp(send[t.dst], off);
         segs[nseg].dst = mp(recv[t.dst], off);
@@ -162,10 +172,7 @@ hc_status_t run_allreduce(void* const* send, void* const* recv, size_t count, hc
       last_end = t.off + t.len;
       ++k;
     }
-    hipError_t e = tap.mark(stream);
-    if (e != hipSuccess) return device_fail(e, "hipEventRecord");
-    e = op == 1 ? hc::launch_reduce_step(segs, nseg, dtype, budget, stream)
-                : copy_step(segs, nseg, es, budget, dma, stream);
+    e = launch();
     if (e != hipSuccess) return device_fail(e, op == 1 ? "reduce step launch" : "copy step launch");
   }
   hipError_t e = tap.mark(stream);
@@ -186,12 +193,23 @@ hc_status_t run_allreduce_sgd(void* const* grads, void* const* weights, size_t c
     hc::Seg segs[hc::kMaxSegs];
     int nseg = 0, last_dst = -1;
     uint64_t last_end = 0;
+    hipError_t e = tap.mark(stream);
+    if (e != hipSuccess) return device_fail(e, "hipEventRecord");
+    auto launch = [&]() {
+      if (op != 1) return copy_step(segs, nseg, es, budget, dma, stream);
+      return last_rs ? hc::launch_sgd_step(segs, nseg, dtype, lr, budget, stream)
+                     : hc::launch_reduce_step(segs, nseg, dtype, budget, stream);
+    };
     while (k < tasks.size() && tasks[k].op == op && tasks[k].step == step) {
       const hc_task_t& t = tasks[k];
       const size_t off = t.off * es;
       if (t.dst == last_dst && t.off == last_end) {
         segs[nseg - 1].len += t.len;
       } else {
+        if (nseg == hc::kMaxSegs) {   // a full launch (the task order gives one segment per receiver)
+          if ((e = launch()) != hipSuccess) return device_fail(e, op == 1 ? "reduce step launch" : "copy step launch");
+          nseg = 0;
+        }
         if (op == 1) {  // partials stay in the gradients; the last step writes weights
           segs[nseg].a = cp(grads[t.src], off);
           segs[nseg].b = cp(grads[t.dst], off);
@@ -208,11 +226,7 @@ hc_status_t run_allreduce_sgd(void* const* grads, void* const* weights, size_t c
       last_end = t.off + t.len;
       ++k;
     }
-    hipError_t e = tap.mark(stream);
-    if (e != hipSuccess) return device_fail(e, "hipEventRecord");
-    if (op == 1) e = last_rs ? hc::launch_sgd_step(segs, nseg, dtype, lr, budget, stream)
-                             : hc::launch_reduce_step(segs, nseg, dtype, budget, stream);
-    else e = copy_step(segs, nseg, es, budget, dma, stream);
+    e = launch();
     if (e != hipSuccess) return device_fail(e, op == 1 ? "reduce step launch" : "copy step launch");
   }
   hipError_t e = tap.mark(stream);

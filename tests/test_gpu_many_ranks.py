@@ -1,0 +1,99 @@
+"""GPU parity at many ranks: 16, 33 and 64 (the library's limit, where one
+ring step's launch carries its most segments: one per receiver), for the
+allreduce, reduce-scatter, all-gather, compressed allreduce and the fused
+allreduce + SGD update, against the oracle, bit for bit.  Sizes include
+fewer elements than ranks (empty slices) and slices that end mid-tile."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from collective_communication_amd import binding as hc
+from collective_communication_amd import inputs
+from hc_util import bits, first_mismatch, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+B = 16384
+
+
+def rand(R, n, dtype, seed, scale):
+    g = np.random.default_rng(seed)
+    xs = [(g.standard_normal(n) * scale).astype(np.float32) for _ in range(R)]
+    if dtype == "bf16":
+        xs = [inputs.f32_to_bf16_bits(x) for x in xs]
+    return xs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("R", [16, 33, 64])
+def test_allreduce_many_ranks(dtype, R):
+    for n in (R - 1, 5000 + R, 3 * B + 7):
+        print(f"allreduce R={R} n={n} {dtype}", flush=True)
+        xs = rand(R, n, dtype, 10 * R + n, 1e-3 if dtype == "bf16" else 1.0)
+        ref = oracle.allreduce_fold(xs)
+        send = [to_dev(x) for x in xs]
+        recv = [torch.empty_like(s) for s in send]
+        hc.hc_allreduce(send, recv)
+        torch.cuda.synchronize()
+        for r in range(R):
+            got = to_host(recv[r])
+            assert np.array_equal(got, bits(ref[r])), f"n={n} rank={r}: {first_mismatch(got, bits(ref[r]))}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_reduce_scatter_and_all_gather_64_ranks(dtype):
+    R = 64
+    for L in (1, 777):
+        n = L * R
+        xs = rand(R, n, dtype, 5 + L, 1.0)
+        ref = oracle.reduce_scatter_ring(xs)
+        send = [to_dev(x) for x in xs]
+        recv = [torch.empty(L, dtype=send[0].dtype, device="cuda") for _ in range(R)]
+        ws = torch.empty(max(hc.hc_workspace_bytes(hc.HC_OP_REDUCE_SCATTER, n, R, hc._dtype(send[0])), 16),
+                         dtype=torch.uint8, device="cuda")
+        hc.hc_reduce_scatter(send, recv, L, ws)
+        torch.cuda.synchronize()
+        for r in range(R):
+            assert np.array_equal(to_host(recv[r]), bits(ref[r])), f"reduce-scatter L={L} rank={r}"
+        ys = rand(R, L, dtype, 9 + L, 1.0)
+        refg = oracle.all_gather_ring(ys)
+        gs = [to_dev(y) for y in ys]
+        outs = [torch.empty(n, dtype=gs[0].dtype, device="cuda") for _ in range(R)]
+        hc.hc_all_gather(gs, outs, L)
+        torch.cuda.synchronize()
+        for r in range(R):
+            assert np.array_equal(to_host(outs[r]), bits(refg[r])), f"all-gather L={L} rank={r}"
+
+
+@pytest.mark.parametrize("R", [16, 33])
+def test_compressed_allreduce_many_ranks(R):
+    for n in (7, 5 * B + 3):
+        print(f"compressed R={R} n={n}", flush=True)
+        xs = [inputs.normal_bf16("test", 900 + r, n, 1e-3) for r in range(R)]
+        ref = oracle.allreduce_fold(xs)
+        _, ref_wire = oracle.compressed_allreduce(xs, chunk=oracle.chunk_elems(n, B))
+        send = [to_dev(x) for x in xs]
+        recv = [torch.empty_like(s) for s in send]
+        ws = torch.empty(max(hc.hc_workspace_bytes(hc.HC_OP_COMPRESSED_ALLREDUCE, n, R), 16), dtype=torch.uint8,
+                         device="cuda")
+        wire = torch.full((1,), -1, dtype=torch.int64, device="cuda")
+        hc.hc_compressed_allreduce(send, recv, n, ws, wire)
+        torch.cuda.synchronize()
+        for r in range(R):
+            assert np.array_equal(to_host(recv[r]), ref[r]), f"n={n} rank={r}"
+        assert int(wire.item()) == ref_wire
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_allreduce_sgd_64_ranks(dtype):
+    R, n = 64, 64 * 300 + 11
+    grads = rand(R, n, dtype, 71, 1e-3)
+    weights = rand(R, n, dtype, 72, 1.0)
+    ref = oracle.allreduce_sgd(grads, weights, 0.01)
+    gd = [to_dev(x) for x in grads]
+    wd = [to_dev(x) for x in weights]
+    hc.hc_allreduce_sgd(gd, wd, 0.01)
+    torch.cuda.synchronize()
+    for r in range(R):
+        got = to_host(wd[r])
+        assert np.array_equal(got, bits(ref[r])), f"rank {r}: {first_mismatch(got, bits(ref[r]))}"
