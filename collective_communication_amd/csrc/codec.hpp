@@ -26,9 +26,11 @@
 //               straight out of the bf16 word with one AND-OR), held in the
 //               staging buffer before the record needs it
 //   ranking   : occurring exponents are compacted (ballot + popcount) into
-//               a short list of keys (count desc, exponent asc); eight lanes
-//               rank one key by counting the larger ones, one LDS round trip
-//               per 64 keys; absent exponents rank after them in order
+//               a short list of keys (count desc, exponent asc) padded with
+//               zero keys; eight lanes rank one key by counting the larger
+//               ones, two 16-byte LDS reads per lane per 64 keys, and DPP
+//               row shifts add their counts; absent exponents rank after
+//               them in order
 //   b choice  : a DPP prefix sum over the ranked counts gives the escape
 //               count of every b; each wave reads the seven candidates with
 //               readlane and keeps the smallest record (ties: smaller b)
@@ -381,7 +383,9 @@ __device__ __forceinline__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, S
   }
   const uint32_t nz_below = before + below;
   // An exponent that never occurs ranks after all that do, in exponent order;
-  // the occurring ones are compacted into a short list of keys.
+  // the occurring ones are compacted into a short list of keys, padded with
+  // zero keys to a multiple of 64 (a zero key is below every real one).
+  const uint32_t npad = (nz_total + 63u) & ~63u;
   if (owner) {
     if (cnt > 0) {
       s.key[nz_below] = key;
@@ -390,27 +394,30 @@ __device__ __forceinline__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, S
       s.cbr[r] = 0;
       s.rank_of[t] = (uint8_t)r;
     }
+    if (t >= nz_total && t < npad) s.key[t] = 0;
   }
   __syncthreads();
   // rank(key i) = #{keys j > key i} (keys are distinct).  Eight lanes rank
-  // one key: lane g of the group compares it with keys g, g+8, g+16, ...,
-  // eight independent LDS reads per 64 keys, and three shuffles add the
-  // eight partial counts.  64 keys per pass over the workgroup's 512 lanes.
+  // one key: lane g of the group compares it with keys 8g .. 8g+7 of every
+  // run of 64 (two 16-byte LDS reads, the same for all groups of a wave),
+  // and three DPP row shifts add the eight partial counts into lane 7 of the
+  // group.  64 keys per pass over the workgroup's 512 lanes; a wave whose
+  // keys all lie past the list stops.
   for (uint32_t i0 = 0; i0 < nz_total; i0 += kCT / 8) {
+    if (i0 + 8u * wave >= nz_total) break;  // wave-uniform
     const uint32_t i = i0 + (t >> 3), g = t & 7u;
     const uint32_t ki = i < nz_total ? s.key[i] : 0xFFFFFFFFu;
     uint32_t c = 0;
-    for (uint32_t j0 = 0; j0 < nz_total; j0 += 64) {
-#pragma unroll
-      for (uint32_t u = 0; u < 8; ++u) {
-        const uint32_t j = j0 + g + 8u * u;
-        c += (j < nz_total ? s.key[j] : 0u) > ki;
-      }
+    for (uint32_t j0 = 0; j0 < npad; j0 += 64) {
+      const uint4 a = *reinterpret_cast<const uint4*>(&s.key[j0 + 8u * g]);
+      const uint4 b = *reinterpret_cast<const uint4*>(&s.key[j0 + 8u * g + 4u]);
+      c += (uint32_t)(a.x > ki) + (uint32_t)(a.y > ki) + (uint32_t)(a.z > ki) + (uint32_t)(a.w > ki) +
+           (uint32_t)(b.x > ki) + (uint32_t)(b.y > ki) + (uint32_t)(b.z > ki) + (uint32_t)(b.w > ki);
     }
-    c += __shfl_xor(c, 1, 8);
-    c += __shfl_xor(c, 2, 8);
-    c += __shfl_xor(c, 4, 8);
-    if (g == 0 && i < nz_total) {
+    c += dpp0<0x111>(c);  // row_shr:1
+    c += dpp0<0x112>(c);  // row_shr:2
+    c += dpp0<0x114>(c);  // row_shr:4: lane 8m+7 holds the group's sum
+    if (g == 7u && i < nz_total) {
       s.cbr[c] = ki >> 8;
       s.rank_of[255u - (ki & 0xFFu)] = (uint8_t)c;
     }
@@ -471,6 +478,16 @@ __device__ __forceinline__ Plan given_plan(const uint8_t* order, uint32_t b, uin
   return p;
 }
 
+// Codes of four elements (two words), one byte each in element order.  The
+// table bytes are loaded into 16-bit halves, two per register, and one byte
+// permute packs the four.
+__device__ __forceinline__ uint32_t codes4(const uint8_t* code_of, uint32_t w0, uint32_t w1) {
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+  const us2 a = {code_of[exp_lo(w0)], code_of[exp_hi(w0)]};
+  const us2 b = {code_of[exp_lo(w1)], code_of[exp_hi(w1)]};
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a), 0x06040200u);
+}
+
 // Writes the coded record of a block with B-bit codes into the staging
 // buffer (everything after the 16-byte header and the dictionary).
 template <int B>
@@ -484,10 +501,7 @@ __device__ __forceinline__ void write_coded(const uint4 (&v)[kPer], const Plan& 
   for (int k = 0; k < kPer; ++k) {
     const uint32_t c = t + kCT * k;
     const uint32_t w0 = v[k].x, w1 = v[k].y, w2 = v[k].z, w3 = v[k].w;
-    uint32_t lo = (uint32_t)s.code_of[exp_lo(w0)] | ((uint32_t)s.code_of[exp_hi(w0)] << 8) |
-                  ((uint32_t)s.code_of[exp_lo(w1)] << 16) | ((uint32_t)s.code_of[exp_hi(w1)] << 24);
-    uint32_t hi = (uint32_t)s.code_of[exp_lo(w2)] | ((uint32_t)s.code_of[exp_hi(w2)] << 8) |
-                  ((uint32_t)s.code_of[exp_lo(w3)] << 16) | ((uint32_t)s.code_of[exp_hi(w3)] << 24);
+    uint32_t lo = codes4(s.code_of, w0, w1), hi = codes4(s.code_of, w2, w3);
     transpose8(lo, hi);  // now byte j of (lo, hi) = plane j of this chunk
     uint32_t em = lo;
 #pragma unroll
