@@ -107,6 +107,8 @@ def lib():
         for name in ("or_allreduce_fold",):
             getattr(L, name).argtypes = [PP, PP, S, ctypes.c_int, ctypes.c_int]
             getattr(L, name).restype = ctypes.c_int
+        L.or_allreduce_fold_f32carry.argtypes = [PP, PP, S, ctypes.c_int]
+        L.or_allreduce_fold_f32carry.restype = ctypes.c_int
         L.or_allreduce_fold_at.argtypes = [PP, S, ctypes.c_int, ctypes.c_int, P, S, P]
         L.or_allreduce_fold_at.restype = ctypes.c_int
         for name in ("or_allreduce_ring", "or_reduce_scatter_ring", "or_all_gather_ring"):
@@ -275,6 +277,22 @@ def allreduce_sgd(grads, weights, lr: float):
     rc = lib().or_allreduce_sgd(gp, wp, op, n, _dtype_code(grads[0]), R, lr)
     if rc != OK:
         raise ValueError(f"or_allreduce_sgd status {rc}")
+    return outs
+
+
+def allreduce_fold_f32carry(xs):
+    """bf16 ring allreduce with fp32 partials and one final rounding (the
+    fp32-carry reading); returns the R output arrays (all equal)."""
+    xs = _check_same(xs)
+    if xs[0].dtype != np.uint16:
+        raise TypeError("the fp32-carry fold takes bf16 bit patterns (uint16)")
+    R, n = len(xs), xs[0].size
+    outs = [np.empty_like(xs[0]) for _ in range(R)]
+    xp, _k1 = _ptrs(xs)
+    op, _k2 = _ptrs(outs)
+    rc = lib().or_allreduce_fold_f32carry(xp, op, n, R)
+    if rc != OK:
+        raise ValueError(f"or_allreduce_fold_f32carry status {rc}")
     return outs
 
 

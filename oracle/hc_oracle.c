@@ -295,6 +295,37 @@ int or_allreduce_fold_at(const void *const *x, size_t n, int dtype, int R,
 }
 
 /*
+ * The fp32-carry reading of "fp32 accumulation, bf16 round-to-nearest-even
+ * output" (bf16 data only): the reduce-scatter partials stay in fp32 and the
+ * sum is rounded to bf16 once.  Element i of slice j: acc starts as the exact
+ * fp32 value of x[j+1][i]; each later rank's value (x[j+2], ..., x[j]) is
+ * widened exactly and added with one fp32 add (a NaN sum becomes the
+ * canonical fp32 NaN); then out = bf16(acc), nearest even.  With one rank
+ * nothing is added and the output is the input, bit for bit.
+ */
+int or_allreduce_fold_f32carry(const void *const *x, void *const *out, size_t n, int R)
+{
+    if (R < 1) return OR_INVALID;
+    size_t L = or_slice_len(n, R);
+    for (size_t i = 0; i < n; ++i) {
+        int j = (int)(i / L);
+        uint16_t res;
+        if (R == 1) {
+            res = ((const uint16_t *)x[0])[i];
+        } else {
+            uint32_t acc = bits_of_f32(or_bf16_to_f32(((const uint16_t *)x[mod(j + 1, R)])[i]));
+            for (int k = 2; k <= R; ++k) {
+                uint16_t v = ((const uint16_t *)x[mod(j + k, R)])[i];
+                acc = or_hop_f32(acc, bits_of_f32(or_bf16_to_f32(v)));
+            }
+            res = or_f32_to_bf16(acc);
+        }
+        for (int r = 0; r < R; ++r) ((uint16_t *)out[r])[i] = res;
+    }
+    return OR_OK;
+}
+
+/*
  * Step simulator of the ring allreduce: R explicit output buffers, the task
  * list above executed in order.  At reduce-scatter step 0 the sender's
  * contribution is its input; later it is the partial the sender wrote in its
