@@ -34,6 +34,7 @@ HC_OP_ALL_GATHER = 4
 HC_OP_COMPRESS_SCOPED = 5
 HC_OP_COMPRESS_ENTROPY = 6
 HC_OP_COMPRESS_STAGED = 7
+HC_OP_ALLREDUCE_F32_CARRY = 8
 HC_BLOCK_ELEMS = 16384
 HC_MAX_RANKS = 64
 
@@ -43,7 +44,7 @@ EXPORTED = [
     "hc_stream_create_cu_budget", "hc_stream_destroy", "hc_chunk_elems", "hc_ring_tasks",
     "hc_status_string", "hc_last_error", "hc_version", "hc_step_count", "hc_allreduce_sgd",
     "hc_compress_bf16_scoped", "hc_compress_bf16_entropy", "hc_decompress_bf16_entropy",
-    "hc_compress_bf16_staged",
+    "hc_compress_bf16_staged", "hc_allreduce_bf16_f32carry",
 ]
 
 
@@ -84,6 +85,7 @@ def load(path: str = LIB_PATH):
     L.hc_reduce_scatter.argtypes = [PP, PP, S, I, I, P, S, O, P]
     L.hc_all_gather.argtypes = [PP, PP, S, I, I, O, P]
     L.hc_allreduce_sgd.argtypes = [PP, PP, S, I, I, ctypes.c_float, O, P]
+    L.hc_allreduce_bf16_f32carry.argtypes = [PP, PP, S, I, P, S, O, P]
     L.hc_compress_bound_bf16.argtypes = [S]
     L.hc_compress_bound_bf16.restype = S
     L.hc_compress_bf16.argtypes = [P, S, P, S, P, P, S, P]
@@ -103,7 +105,8 @@ def load(path: str = LIB_PATH):
     L.hc_step_count.argtypes = [I, I]
     L.hc_step_count.restype = I
     L.hc_ring_tasks.restype = S
-    for name in ("hc_allreduce", "hc_reduce_scatter", "hc_all_gather", "hc_allreduce_sgd", "hc_compress_bf16",
+    for name in ("hc_allreduce", "hc_reduce_scatter", "hc_all_gather", "hc_allreduce_sgd",
+                 "hc_allreduce_bf16_f32carry", "hc_compress_bf16",
                  "hc_compress_bf16_scoped", "hc_compress_bf16_entropy", "hc_compress_bf16_staged",
                  "hc_decompress_bf16",
                  "hc_decompress_bf16_entropy", "hc_compressed_allreduce", "hc_stream_create_cu_budget",
@@ -206,6 +209,30 @@ def hc_allreduce(sendbufs, recvbufs, count: int | None = None, *, chunk_fraction
     rp, _k2 = _ptr_array(recvbufs, count, "recvbufs")
     _check(L.hc_allreduce(sp, rp, count, dt, R, _opts(chunk_fraction, cu_budget, step_events, copy_engine),
                           _stream_handle(stream)))
+
+
+def hc_allreduce_bf16_f32carry(sendbufs, recvbufs, count: int | None = None, ws=None, *,
+                               chunk_fraction: float = 0.0, cu_budget: int = 0,
+                               step_events: StepEvents | None = None, copy_engine: int = 0, stream=None):
+    """bf16 ring allreduce with fp32 partials and one final rounding (see
+    include/hc.h); ws: hc_workspace_bytes(HC_OP_ALLREDUCE_F32_CARRY, ...)
+    bytes, may be None for one or two ranks."""
+    L = load()
+    R = len(sendbufs)
+    if count is None:
+        count = sendbufs[0].numel()
+    if len(recvbufs) != R:
+        raise ValueError("sendbufs and recvbufs need one tensor per rank")
+    if any(t.dtype != torch.bfloat16 for t in list(sendbufs) + list(recvbufs)):
+        raise TypeError("the fp32-carry allreduce takes bfloat16 buffers")
+    sp, _k1 = _ptr_array(sendbufs, count, "sendbufs")
+    rp, _k2 = _ptr_array(recvbufs, count, "recvbufs")
+    need = hc_workspace_bytes(HC_OP_ALLREDUCE_F32_CARRY, count, R, HC_BF16)
+    wsp = _dptr(ws, need, "ws") if ws is not None else None
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(L.hc_allreduce_bf16_f32carry(sp, rp, count, R, wsp, ws_bytes,
+                                        _opts(chunk_fraction, cu_budget, step_events, copy_engine),
+                                        _stream_handle(stream)))
 
 
 def hc_allreduce_sgd(grads, weights, lr: float, count: int | None = None, *, chunk_fraction: float = 0.0,

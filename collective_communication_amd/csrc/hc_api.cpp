@@ -233,6 +233,71 @@ hc_status_t run_allreduce_sgd(void* const* grads, void* const* weights, size_t c
   return e == hipSuccess ? HC_SUCCESS : device_fail(e, "hipEventRecord");
 }
 
+// Workspace of the fp32-carry allreduce: two fp32 partial slots per rank of
+// Lp = ceil(count/R) rounded up to 64 elements, so that every slot starts
+// 256-byte aligned.  No partial is stored with one or two ranks.
+size_t carry_slot_elems(size_t count, int R) { return (hc::ceil_div(count, (size_t)R) + 63) & ~(size_t)63; }
+size_t carry_ws_bytes(size_t count, int R) {
+  return R <= 2 ? 0 : (size_t)R * 2 * carry_slot_elems(count, R) * 4;
+}
+
+// The bf16 allreduce with fp32 partials.  Reduce-scatter partials of rank q
+// ping-pong between its fp32 workspace slots (q, s%2), each element at its
+// offset inside its slice; step 0 reads both operands from the inputs, the
+// last step rounds into recvbufs (for two ranks step 0 is the last and this
+// is the per-hop bf16 ring).  The all-gather is the usual bf16 copy ring.
+hc_status_t run_allreduce_carry(void* const* send, void* const* recv, size_t count, int R, size_t chunk, void* ws,
+                                int budget, bool dma, Tap& tap, hipStream_t stream) {
+  const size_t es = 2, L = hc::ceil_div(count, (size_t)R), Lp = carry_slot_elems(count, R);
+  std::vector<hc_task_t> tasks = hc::ring_tasks(R, count, chunk);
+  size_t k = 0;
+  while (k < tasks.size()) {
+    const int op = tasks[k].op, step = tasks[k].step;
+    const bool first = op == 1 && step == 0, last = op == 1 && step == R - 2;
+    hc::Seg segs[hc::kMaxSegs];
+    int nseg = 0, last_dst = -1;
+    uint64_t last_end = 0;
+    hipError_t e = tap.mark(stream);
+    if (e != hipSuccess) return device_fail(e, "hipEventRecord");
+    auto launch = [&]() {
+      return op == 1 ? hc::launch_carry_step(segs, nseg, !first, !last, budget, stream)
+                     : copy_step(segs, nseg, es, budget, dma, stream);
+    };
+    while (k < tasks.size() && tasks[k].op == op && tasks[k].step == step) {
+      const hc_task_t& t = tasks[k];
+      const size_t off = t.off * es;
+      if (t.dst == last_dst && t.off == last_end) {
+        segs[nseg - 1].len += t.len;  // next chunk of the same receiver's slice
+      } else {
+        if (nseg == hc::kMaxSegs) {   // a full launch (the task order gives one segment per receiver)
+          if ((e = launch()) != hipSuccess) return device_fail(e, op == 1 ? "reduce step launch" : "copy step launch");
+          nseg = 0;
+        }
+        if (op == 1) {
+          const size_t in_slice = t.off - (size_t)t.slice * L;
+          segs[nseg].a = first ? cp(send[t.src], off)
+                               : cp(ws, ((size_t)(2 * t.src + ((step - 1) & 1)) * Lp + in_slice) * 4);
+          segs[nseg].b = cp(send[t.dst], off);
+          segs[nseg].dst = last ? mp(recv[t.dst], off) : mp(ws, ((size_t)(2 * t.dst + (step & 1)) * Lp + in_slice) * 4);
+        } else {
+          segs[nseg].a = cp(recv[t.src], off);
+          segs[nseg].b = nullptr;
+          segs[nseg].dst = mp(recv[t.dst], off);
+        }
+        segs[nseg].len = t.len;
+        ++nseg;
+      }
+      last_dst = t.dst;
+      last_end = t.off + t.len;
+      ++k;
+    }
+    e = launch();
+    if (e != hipSuccess) return device_fail(e, op == 1 ? "reduce step launch" : "copy step launch");
+  }
+  hipError_t e = tap.mark(stream);
+  return e == hipSuccess ? HC_SUCCESS : device_fail(e, "hipEventRecord");
+}
+
 // One-rank operations: a single step that copies (or nothing in place).
 hc_status_t run_single(const void* src, void* dst, size_t count, size_t es, int budget, bool dma, Tap& tap,
                        hipStream_t stream) {
@@ -268,7 +333,8 @@ int hc_step_count(hc_op_t op, int nranks) {
   if (nranks < 1 || nranks > HC_MAX_RANKS) return -1;
   if (nranks == 1) return 1;
   switch (op) {
-    case HC_OP_ALLREDUCE: return 2 * (nranks - 1);
+    case HC_OP_ALLREDUCE:
+    case HC_OP_ALLREDUCE_F32_CARRY: return 2 * (nranks - 1);
     case HC_OP_REDUCE_SCATTER: return nranks - 1;
     case HC_OP_ALL_GATHER: return nranks - 1;
     case HC_OP_COMPRESSED_ALLREDUCE: return 2 * nranks - 1;
@@ -316,6 +382,42 @@ hc_status_t hc_allreduce(void* const* sendbufs, void* const* recvbufs, size_t co
     return run_single(sendbufs[0], recvbufs[0], count, es, cu_budget(opts), copy_engine(opts), tap, stream);
   return run_allreduce(sendbufs, recvbufs, count, dtype, nranks, chunk, cu_budget(opts), copy_engine(opts), tap,
                        stream);
+}
+
+hc_status_t hc_allreduce_bf16_f32carry(void* const* sendbufs, void* const* recvbufs, size_t count, int nranks,
+                                       void* d_ws, size_t ws_bytes, const hc_opts_t* opts, hipStream_t stream) {
+  g_last_error.clear();
+  hc_status_t st = check_common(nranks, HC_BF16, opts);
+  if (st) return st;
+  if (count == 0) return HC_SUCCESS;
+  if ((st = check_ptrs(sendbufs, nranks, "sendbufs", 2))) return st;
+  if ((st = check_ptrs(recvbufs, nranks, "recvbufs", 2))) return st;
+  if (count > ((size_t)1 << 40)) return fail(HC_ERR_INVALID_ARGUMENT, "count %zu too large", count);
+  std::vector<Range> in, out;
+  std::vector<bool> ok;
+  for (int r = 0; r < nranks; ++r) {
+    in.push_back({(uintptr_t)sendbufs[r], (uintptr_t)sendbufs[r] + count * 2});
+    out.push_back({(uintptr_t)recvbufs[r], (uintptr_t)recvbufs[r] + count * 2});
+    ok.push_back(sendbufs[r] == recvbufs[r]);
+  }
+  if ((st = check_disjoint(in, out, ok))) return st;
+  const size_t need = carry_ws_bytes(count, nranks);
+  if (need) {
+    if (!d_ws) return fail(HC_ERR_INVALID_ARGUMENT, "d_ws is NULL");
+    if (!aligned16(d_ws)) return fail(HC_ERR_INVALID_ARGUMENT, "d_ws is not 16-byte aligned");
+    if (ws_bytes < need) return fail(HC_ERR_INSUFFICIENT_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, need);
+    Range wr{(uintptr_t)d_ws, (uintptr_t)d_ws + need};
+    for (int r = 0; r < nranks; ++r)
+      if (overlap(wr, in[r]) || overlap(wr, out[r]))
+        return fail(HC_ERR_INVALID_ARGUMENT, "d_ws overlaps rank %d buffers", r);
+  }
+  Tap tap;
+  if ((st = make_tap(opts, HC_OP_ALLREDUCE_F32_CARRY, nranks, &tap))) return st;
+  if (nranks == 1)
+    return run_single(sendbufs[0], recvbufs[0], count, 2, cu_budget(opts), copy_engine(opts), tap, stream);
+  const size_t chunk = hc::chunk_elems(count, chunk_fraction(opts), 1024);
+  return run_allreduce_carry(sendbufs, recvbufs, count, nranks, chunk, d_ws, cu_budget(opts), copy_engine(opts),
+                             tap, stream);
 }
 
 hc_status_t hc_allreduce_sgd(void* const* grads, void* const* weights, size_t count, hc_dtype_t dtype,
@@ -369,6 +471,9 @@ size_t hc_workspace_bytes(hc_op_t op, size_t count, int nranks, hc_dtype_t dtype
     case HC_OP_COMPRESSED_ALLREDUCE:
       if (dtype != HC_BF16) return 0;
       return hc::compressed_ar_ws_bytes(count, nranks);
+    case HC_OP_ALLREDUCE_F32_CARRY:
+      if (dtype != HC_BF16) return 0;
+      return carry_ws_bytes(count, nranks);
     case HC_OP_ALLREDUCE:
     case HC_OP_ALL_GATHER:
       return 0;

@@ -31,6 +31,11 @@ hipError_t launch_copy_step(const Seg* segs, int nseg, size_t elem_bytes, int cu
 // (dst holds the owner's weights).
 hipError_t launch_sgd_step(const Seg* segs, int nseg, hc_dtype_t dtype, float lr, int cu_budget,
                            hipStream_t stream);
+// A reduce-scatter step of the bf16 ring with fp32 partials: dst = a + b in
+// fp32, b bf16; a is an fp32 partial when a_f32 (else bf16 data); the sum is
+// stored as an fp32 partial when dst_f32, else rounded once to bf16.
+hipError_t launch_carry_step(const Seg* segs, int nseg, bool a_f32, bool dst_f32, int cu_budget,
+                             hipStream_t stream);
 
 // Codec.
 hipError_t launch_fill_u32(void* dst, uint32_t value, size_t words, hipStream_t stream);

@@ -184,7 +184,120 @@ __global__ __launch_bounds__(kThreads) void step_kernel(SegArgs args) {
   }
 }
 
+// Reduce-scatter hops of the bf16 ring with fp32 partials (one rounding at
+// the end).  AF: the arriving operand a is an fp32 partial (else bf16 data);
+// DF: the sum stays an fp32 partial (else it is rounded to bf16, nearest
+// even).  b, the receiver's own data, is bf16.  Each sum is one fp32 add of
+// exactly widened operands; a NaN sum is the canonical fp32 NaN.  A lane
+// moves 8 elements per vector: 16 or 32 bytes of a, 16 of b, 32 or 16 of dst.
+template <bool AF>
+__device__ __forceinline__ void carry_load_a(const char* p, uint64_t e, uint32_t (&w)[8]) {
+  if constexpr (AF) {
+    const uint4 lo = ld_stream<HC_RING_NT_A>(p + 4 * e), hi = ld_stream<HC_RING_NT_A>(p + 4 * e + 16);
+    w[0] = lo.x; w[1] = lo.y; w[2] = lo.z; w[3] = lo.w; w[4] = hi.x; w[5] = hi.y; w[6] = hi.z; w[7] = hi.w;
+  } else {
+    const uint4 v = ld_stream<HC_RING_NT_A>(p + 2 * e);
+    const uint32_t h[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { w[2 * i] = h[i] << 16; w[2 * i + 1] = h[i] & 0xFFFF0000u; }
+  }
+}
+
+template <bool AF, bool DF, bool VEC>
+__global__ __launch_bounds__(kThreads) void carry_kernel(SegArgs args) {
+  constexpr uint64_t kTile = (uint64_t)kThreads * 8 * kUnroll;
+  const uint32_t total = args.tile0[args.nseg];
+  const int tid = threadIdx.x;
+  for (uint32_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    int lo = 0, hi = args.nseg - 1;
+    while (lo < hi) {  // last segment whose first tile is <= tile
+      const int mid = (lo + hi + 1) >> 1;
+      if (args.tile0[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    const int s = lo;
+    const uint64_t base = (uint64_t)(tile - args.tile0[s]) * kTile;
+    const uint64_t len = args.len[s];
+    const char* pa = static_cast<const char*>(args.a[s]);
+    const char* pb = static_cast<const char*>(args.b[s]);
+    char* pd = static_cast<char*>(args.dst[s]);
+    if (VEC && base + kTile <= len) {
+      uint32_t wa[kUnroll][8];
+      uint4 vb[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint64_t e = base + (uint64_t)(u * kThreads + tid) * 8;
+        carry_load_a<AF>(pa, e, wa[u]);
+        vb[u] = ld_stream<HC_RING_NT_B>(pb + 2 * e);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint64_t e = base + (uint64_t)(u * kThreads + tid) * 8;
+        const uint32_t h[4] = {vb[u].x, vb[u].y, vb[u].z, vb[u].w};
+        uint32_t sm[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sm[2 * i] = hop_f32(wa[u][2 * i], h[i] << 16);
+          sm[2 * i + 1] = hop_f32(wa[u][2 * i + 1], h[i] & 0xFFFF0000u);
+        }
+        if constexpr (DF) {
+          st_stream(pd + 4 * e, make_uint4(sm[0], sm[1], sm[2], sm[3]));
+          st_stream(pd + 4 * e + 16, make_uint4(sm[4], sm[5], sm[6], sm[7]));
+        } else {
+          st_stream(pd + 2 * e, make_uint4(bf16_rne(sm[0]) | (bf16_rne(sm[1]) << 16),
+                                           bf16_rne(sm[2]) | (bf16_rne(sm[3]) << 16),
+                                           bf16_rne(sm[4]) | (bf16_rne(sm[5]) << 16),
+                                           bf16_rne(sm[6]) | (bf16_rne(sm[7]) << 16)));
+        }
+      }
+    } else {
+      const uint64_t end = base + kTile < len ? base + kTile : len;
+      for (uint64_t i = base + tid; i < end; i += kThreads) {
+        const uint32_t a = AF ? ld_elem<4>(pa, i) : ld_elem<2>(pa, i) << 16;
+        const uint32_t sum = hop_f32(a, ld_elem<2>(pb, i) << 16);
+        if constexpr (DF) st_elem<4>(pd, i, sum);
+        else st_elem<2>(pd, i, bf16_rne(sum));
+      }
+    }
+  }
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Launch of one fp32-carry reduce-scatter step (see carry_kernel).
+template <bool AF, bool DF>
+hipError_t launch_carry(const Seg* segs, int nseg, int cu_budget, hipStream_t stream) {
+  constexpr uint64_t kTile = (uint64_t)kThreads * 8 * kUnroll;
+  if (nseg <= 0) return hipSuccess;
+  if (nseg > kMaxSegs) return hipErrorInvalidValue;
+  SegArgs args;
+  uint64_t tiles = 0;
+  bool vec = true;
+  int k = 0;
+  for (int i = 0; i < nseg; ++i) {
+    if (segs[i].len == 0) continue;
+    args.a[k] = segs[i].a;
+    args.b[k] = segs[i].b;
+    args.dst[k] = segs[i].dst;
+    args.len[k] = segs[i].len;
+    args.tile0[k] = (uint32_t)tiles;
+    tiles += (segs[i].len + kTile - 1) / kTile;
+    vec = vec && aligned16(segs[i].a) && aligned16(segs[i].b) && aligned16(segs[i].dst);
+    ++k;
+  }
+  if (k == 0) return hipSuccess;
+  if (tiles >= 0xFFFFFFFFull) return hipErrorInvalidValue;
+  args.nseg = k;
+  args.tile0[k] = (uint32_t)tiles;
+  args.lr = 0.0f;
+  uint32_t grid = (uint32_t)tiles;
+  if (cu_budget > 0) {
+    const uint64_t cap = (uint64_t)cu_budget * kWgPerCuBudget;
+    if (grid > cap) grid = (uint32_t)cap;
+  }
+  if (vec) hipLaunchKernelGGL((carry_kernel<AF, DF, true>), dim3(grid), dim3(kThreads), 0, stream, args);
+  else hipLaunchKernelGGL((carry_kernel<AF, DF, false>), dim3(grid), dim3(kThreads), 0, stream, args);
+  return hipGetLastError();
+}
 
 template <int ES, int OP>
 hipError_t launch_step(const Seg* segs, int nseg, int cu_budget, hipStream_t stream, float lr = 0.0f) {
@@ -238,6 +351,14 @@ hipError_t launch_sgd_step(const Seg* segs, int nseg, hc_dtype_t dtype, float lr
                : launch_step<4, kSgd>(segs, nseg, cu_budget, stream, lr);
   return one ? launch_step<2, kSgdOne>(segs, nseg, cu_budget, stream, lr)
              : launch_step<2, kSgd>(segs, nseg, cu_budget, stream, lr);
+}
+
+hipError_t launch_carry_step(const Seg* segs, int nseg, bool a_f32, bool dst_f32, int cu_budget,
+                             hipStream_t stream) {
+  if (a_f32) return dst_f32 ? launch_carry<true, true>(segs, nseg, cu_budget, stream)
+                            : launch_carry<true, false>(segs, nseg, cu_budget, stream);
+  return dst_f32 ? launch_carry<false, true>(segs, nseg, cu_budget, stream)
+                 : launch_carry<false, false>(segs, nseg, cu_budget, stream);
 }
 
 hipError_t launch_copy_step(const Seg* segs, int nseg, size_t elem_bytes, int cu_budget,

@@ -124,6 +124,31 @@ hc_status_t hc_allreduce(void *const *sendbufs, void *const *recvbufs, size_t co
                          hipStream_t stream);
 
 /*
+ * hc_allreduce_bf16_f32carry -- the bf16 ring AllReduce of hc_allreduce with
+ * the other reading of "fp32 accumulation, bf16 round-to-nearest-even
+ * output": the reduce-scatter carries fp32 partials and the sum is rounded to
+ * bf16 once, by the slice's owner at the last reduce-scatter step.  Same ring,
+ * slices, chunks and fold order as hc_allreduce: element i of slice j is
+ * bf16(((f(x[j+1][i]) + f(x[j+2][i])) + ...) + f(x[j][i])) with f the exact
+ * widening and every + one fp32 add (a NaN sum becomes the canonical NaN);
+ * the all-gather copies the bf16 result.  With 2 ranks this equals
+ * hc_allreduce; with 1 it is a copy.  Partials cost 4 bytes instead of 2, so
+ * a middle reduce-scatter hop moves 10 bytes per element instead of 6.
+ *   sendbufs[r], recvbufs[r]: count bf16 elements each; in place is allowed
+ *   (sendbufs[r] == recvbufs[r] for every r).
+ *   d_ws: >= hc_workspace_bytes(HC_OP_ALLREDUCE_F32_CARRY, count, nranks,
+ *   HC_BF16) bytes, 16-byte aligned, overlapping no rank buffer: two fp32
+ *   partial slots per rank (ping-pong between steps).  May be NULL when
+ *   nranks <= 2 (no partial is stored).  The caller owns it; its contents
+ *   after the call are unspecified.
+ *   Errors as hc_allreduce, plus HC_ERR_INSUFFICIENT_CAPACITY for a short
+ *   workspace; nothing is enqueued on an argument error.
+ */
+hc_status_t hc_allreduce_bf16_f32carry(void *const *sendbufs, void *const *recvbufs, size_t count,
+                                       int nranks, void *d_ws, size_t ws_bytes, const hc_opts_t *opts,
+                                       hipStream_t stream);
+
+/*
  * hc_reduce_scatter -- ring ReduceScatter (sum): rank r receives slice r of
  * the elementwise sum ("Breaking the computation and communication
  * abstraction barrier ...", "The idea": each rank keeps its 1/N slice;
@@ -336,7 +361,8 @@ typedef enum {
     HC_OP_ALL_GATHER = 4,
     HC_OP_COMPRESS_SCOPED = 5,
     HC_OP_COMPRESS_ENTROPY = 6,
-    HC_OP_COMPRESS_STAGED = 7
+    HC_OP_COMPRESS_STAGED = 7,
+    HC_OP_ALLREDUCE_F32_CARRY = 8
 } hc_op_t;
 
 /* Workspace bytes for an operation; count = elements per rank buffer

@@ -71,6 +71,11 @@ def test_workspace_sizes(hc):
     assert hc.hc_workspace_bytes(hc.HC_OP_COMPRESSED_ALLREDUCE, 1 << 20, 8, hc.HC_BF16) > 0
     assert hc.hc_workspace_bytes(hc.HC_OP_COMPRESSED_ALLREDUCE, 1 << 20, 8, hc.HC_F32) == 0
     assert hc.hc_workspace_bytes(hc.HC_OP_REDUCE_SCATTER, 64, 0, hc.HC_F32) == 0
+    # fp32-carry allreduce: two fp32 slots of ceil(count/R) rounded up to 64 per rank; none for R <= 2
+    assert hc.hc_workspace_bytes(hc.HC_OP_ALLREDUCE_F32_CARRY, 1000, 8, hc.HC_BF16) == 8 * 2 * 128 * 4
+    assert hc.hc_workspace_bytes(hc.HC_OP_ALLREDUCE_F32_CARRY, 1 << 26, 8, hc.HC_BF16) == 2 * (1 << 26) * 4
+    assert hc.hc_workspace_bytes(hc.HC_OP_ALLREDUCE_F32_CARRY, 1000, 2, hc.HC_BF16) == 0
+    assert hc.hc_workspace_bytes(hc.HC_OP_ALLREDUCE_F32_CARRY, 1000, 8, hc.HC_F32) == 0
 
 
 def _raw(hc):
@@ -156,6 +161,20 @@ def test_argument_errors_before_any_launch(hc):
     # compressed allreduce: workspace too small
     assert L.hc_compressed_allreduce(good, good2, 1 << 16, 2, 0x900000, 16, None, None, None) == \
         hc.HC_ERR_INSUFFICIENT_CAPACITY
+    # fp32-carry allreduce: workspace needed from 3 ranks on, aligned, large enough, apart from the buffers
+    three, _k7 = arr([0x100000, 0x200000, 0x300000])
+    three_out, _k8 = arr([0x400000, 0x500000, 0x600000])
+    need = hc.hc_workspace_bytes(hc.HC_OP_ALLREDUCE_F32_CARRY, 16, 3, hc.HC_BF16)
+    assert L.hc_allreduce_bf16_f32carry(three, three_out, 16, 3, None, 0, None, None) == E
+    assert L.hc_allreduce_bf16_f32carry(three, three_out, 16, 3, 0x900000, need - 1, None, None) == \
+        hc.HC_ERR_INSUFFICIENT_CAPACITY
+    assert L.hc_allreduce_bf16_f32carry(three, three_out, 16, 3, 0x900008, need, None, None) == E
+    assert L.hc_allreduce_bf16_f32carry(three, three_out, 16, 3, 0x400000, need, None, None) == E
+    assert b"overlaps" in L.hc_last_error()
+    odd, _k9 = arr([0x100001, 0x200000])   # bf16 pointers need 2-byte alignment
+    assert L.hc_allreduce_bf16_f32carry(odd, good2, 16, 2, None, 0, None, None) == E
+    assert L.hc_allreduce_bf16_f32carry(good, good2, 16, 65, None, 0, None, None) == E
+    assert L.hc_allreduce_bf16_f32carry(good, good2, 0, 2, None, 0, None, None) == hc.HC_SUCCESS
     # CU-budget stream: k out of range (no device is touched for k < 1)
     s = ctypes.c_void_p(0)
     assert L.hc_stream_create_cu_budget(0, ctypes.byref(s)) != hc.HC_SUCCESS
@@ -167,6 +186,7 @@ def test_step_counts(hc):
         assert hc.hc_step_count(hc.HC_OP_REDUCE_SCATTER, R) == R - 1
         assert hc.hc_step_count(hc.HC_OP_ALL_GATHER, R) == R - 1
         assert hc.hc_step_count(hc.HC_OP_COMPRESSED_ALLREDUCE, R) == 2 * R - 1
+        assert hc.hc_step_count(hc.HC_OP_ALLREDUCE_F32_CARRY, R) == 2 * (R - 1)
     assert hc.hc_step_count(hc.HC_OP_COMPRESS_SCOPED, 2) == -1
     assert hc.hc_step_count(hc.HC_OP_ALLREDUCE, 1) == 1
     assert hc.hc_step_count(hc.HC_OP_ALLREDUCE, 0) == -1
