@@ -7,7 +7,8 @@ exact zeros, fp32 accumulation per hop with bf16 nearest-even output, chunk
 ~1% of the buffer, reduce-scatter then all-gather.  One "step" is one whole
 allreduce (14 ring steps) over inputs already resident in HBM.
 
-Other workloads (--workload): ring_f32 (R=4 x 2^20 fp32), codec (2^28 bf16
+Other workloads (--workload): ring_f32 (R=4 x 2^20 fp32), ring_bf16_carry
+(the default ring with fp32 partials and one final rounding), codec (2^28 bf16
 compress/decompress of weights, activations, gradients), compressed (the
 fused compressed ring, R=8 x 2^25 bf16), contention (R=8 reduce-scatter of
 2^28 bf16 on a CU-budget stream next to a bf16 8192^3 GEMM, plus the matching
@@ -199,6 +200,103 @@ def bench_ring(args, workload: str):
         xs = [inputs.host_bits(t) for t in send]
         line["cpu_baseline"] = oracle_timed(lambda: oracle.allreduce_ring(xs), n * es,
                                             f"the whole workload (R={R} x {n} {dtype}), ring step simulator")
+    return line
+
+
+def bench_ring_carry(args):
+    """The bf16 ring with fp32 partials and one final rounding
+    (hc_allreduce_bf16_f32carry) on the default workload, with the per-hop
+    ring timed beside it, and the error of both against the exact sum on a
+    sample of elements."""
+    import numpy as np
+    import torch
+
+    from collective_communication_amd import binding as hc
+    from collective_communication_amd import inputs
+
+    R, n = 8, 1 << 26
+    send = inputs.ring_inputs_cuda("ring_bf16", R, n)
+    recv = [torch.empty_like(s) for s in send]
+    hop = [torch.empty_like(s) for s in send]
+    ws = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_ALLREDUCE_F32_CARRY, n, R, hc.HC_BF16), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(args.warmup):
+        hc.hc_allreduce_bf16_f32carry(send, recv, n, ws)
+        hc.hc_allreduce(send, hop)
+    ms = timed_ms(lambda: hc.hc_allreduce_bf16_f32carry(send, recv, n, ws), args.steps)
+    ms_hop = timed_ms(lambda: hc.hc_allreduce(send, hop), args.steps)
+    steps = hc.hc_step_count(hc.HC_OP_ALLREDUCE_F32_CARRY, R)
+    evsets = [hc.StepEvents([torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)])
+              for _ in range(args.steps)]
+    for k in range(args.steps):
+        hc.hc_allreduce_bf16_f32carry(send, recv, n, ws, step_events=evsets[k])
+    torch.cuda.synchronize()
+    first, mid, last, cpy = [], [], [], []
+    for ev in evsets:
+        d = ev.elapsed_ms()
+        first.append(d[0])
+        mid += d[1:R - 2]
+        last.append(d[R - 2])
+        cpy += d[R - 1:]
+    avg = lambda v: sum(v) / len(v)
+    # bytes per element of one step (N elements per step over the R receivers):
+    # first hop 2 + 2 read, 4 written; a middle hop 4 + 2 read, 4 written; the
+    # last hop 4 + 2 read, 2 written; an all-gather copy 2 read, 2 written.
+    alg_bytes = n * (8 + 10 * (R - 3) + 8 + 4 * (R - 1))
+    mid_bytes = 10 * n
+    algbw = n * 2 / (ms / 1e3) / 1e9
+    # Error against the exact sum on 65,536 elements (fp64 holds every 8-term
+    # bf16 sum exactly here): the share of results that are the exact sum
+    # correctly rounded (within half a bf16 ulp of it), and the error in bf16
+    # ulps of the sum of magnitudes (the scale the summation error bound uses).
+    g = np.random.default_rng(3)
+    idx = torch.from_numpy(g.integers(0, n, 1 << 16).astype(np.int64)).to("cuda")
+    vals = (np.stack([inputs.host_bits(s[idx]) for s in send]).astype(np.uint32) << 16).view(np.float32)
+    exact = vals.astype(np.float64).sum(axis=0)
+    mag = np.abs(vals.astype(np.float64)).sum(axis=0)
+
+    def bf16_ulp(x):
+        nz = x != 0
+        return np.where(nz, np.exp2(np.floor(np.log2(np.where(nz, np.abs(x), 1.0))) - 7), 0.0)
+
+    def ulp_err(t):
+        got = (inputs.host_bits(t[idx]).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        d = np.abs(got - exact)
+        ok = np.where(exact != 0, d <= 0.5 * bf16_ulp(exact), got == 0)
+        scale = np.where(mag != 0, bf16_ulp(mag), 1.0)
+        e = d / scale
+        return {"correctly_rounded": round(float(ok.mean()), 5),
+                "max_ulps_of_sum_of_magnitudes": round(float(e.max()), 4),
+                "mean_ulps_of_sum_of_magnitudes": round(float(e.mean()), 5)}
+
+    line = {
+        "metric": METRIC, "value": round(algbw, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"emulated ring allreduce (sum) with fp32 partials and one final bf16 rounding, "
+                               f"R={R} ranks x {n} bf16 per rank, N(0,1e-3) with 1% zeros, chunk ~1%, "
+                               f"reduce-scatter then all-gather",
+                   "ranks": R, "elems_per_rank": n, "chunk": hc.hc_chunk_elems(n)},
+        "hbm_gbps": round(alg_bytes / (ms / 1e3) / 1e9, 2),
+        "hbm_frac_of_peak": round(alg_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "alg_bytes_per_step": alg_bytes,
+        "per_hop_ms_per_step": round(ms_hop, 6),
+        "per_hop_algbw_gbps": round(n * 2 / (ms_hop / 1e3) / 1e9, 3),
+        "first_rs_ms": round(avg(first), 6), "middle_rs_ms": round(avg(mid), 6), "last_rs_ms": round(avg(last), 6),
+        "copy_ms": round(avg(cpy), 6),
+        "error_vs_exact": {"f32_carry": ulp_err(recv[0]), "per_hop": ulp_err(hop[0])},
+        "roofline": roofline_obj("carry_kernel<fp32 in, fp32 out> (a middle reduce-scatter step)", mid_bytes,
+                                 avg(mid), None, "mean middle reduce-scatter step by HIP events at the step "
+                                                 "boundaries"),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        m = min(n, args.cpu_sample)
+        xs = [inputs.host_bits(s[:m]) for s in send]
+        line["cpu_baseline"] = oracle_timed(lambda: oracle.allreduce_fold_f32carry(xs), m * 2,
+                                            f"R={R} x {m} bf16 (the first {m} elements of every rank), "
+                                            f"the oracle's fp32-carry fold")
     return line
 
 
@@ -678,8 +776,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ring_bf16",
-                    choices=["ring_bf16", "ring_f32", "codec", "compressed", "contention", "fused_sgd",
-                             "table_scope", "entropy"])
+                    choices=["ring_bf16", "ring_f32", "ring_bf16_carry", "codec", "compressed", "contention",
+                             "fused_sgd", "table_scope", "entropy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 26,
                     help="elements per rank the oracle baseline runs on (default: the whole workload)")
@@ -697,6 +795,8 @@ def main():
         sys.exit(1)
     if args.workload in ("ring_bf16", "ring_f32"):
         line = bench_ring(args, args.workload)
+    elif args.workload == "ring_bf16_carry":
+        line = bench_ring_carry(args)
     elif args.workload == "codec":
         line = bench_codec(args)
     elif args.workload == "compressed":

@@ -62,6 +62,16 @@ __device__ __forceinline__ uint4 ld_stream(const char* p) {
     return ld16(p);
   }
 }
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+template <bool NT>
+__device__ __forceinline__ uint2 ld_stream8(const char* p) {
+  if constexpr (NT) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    return make_uint2(v.x, v.y);
+  } else {
+    return *reinterpret_cast<const uint2*>(p);
+  }
+}
 __device__ __forceinline__ void st_stream(char* p, uint4 v) {
   if constexpr (HC_RING_NT_STORE) {
     const u32x4 w = {v.x, v.y, v.z, v.w};
@@ -189,23 +199,23 @@ __global__ __launch_bounds__(kThreads) void step_kernel(SegArgs args) {
 // DF: the sum stays an fp32 partial (else it is rounded to bf16, nearest
 // even).  b, the receiver's own data, is bf16.  Each sum is one fp32 add of
 // exactly widened operands; a NaN sum is the canonical fp32 NaN.  A lane
-// moves 8 elements per vector: 16 or 32 bytes of a, 16 of b, 32 or 16 of dst.
-template <bool AF>
-__device__ __forceinline__ void carry_load_a(const char* p, uint64_t e, uint32_t (&w)[8]) {
-  if constexpr (AF) {
-    const uint4 lo = ld_stream<HC_RING_NT_A>(p + 4 * e), hi = ld_stream<HC_RING_NT_A>(p + 4 * e + 16);
-    w[0] = lo.x; w[1] = lo.y; w[2] = lo.z; w[3] = lo.w; w[4] = hi.x; w[5] = hi.y; w[6] = hi.z; w[7] = hi.w;
+// moves 4 consecutive elements per access, so every wave instruction covers
+// one contiguous range: 1 KB of fp32 or 512 bytes of bf16.
+template <bool F32>
+__device__ __forceinline__ void carry_load4(const char* p, uint64_t e, uint32_t (&w)[4]) {
+  if constexpr (F32) {
+    const uint4 v = ld_stream<HC_RING_NT_A>(p + 4 * e);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   } else {
-    const uint4 v = ld_stream<HC_RING_NT_A>(p + 2 * e);
-    const uint32_t h[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { w[2 * i] = h[i] << 16; w[2 * i + 1] = h[i] & 0xFFFF0000u; }
+    const uint2 v = ld_stream8<HC_RING_NT_A>(p + 2 * e);
+    w[0] = v.x << 16; w[1] = v.x & 0xFFFF0000u; w[2] = v.y << 16; w[3] = v.y & 0xFFFF0000u;
   }
 }
 
 template <bool AF, bool DF, bool VEC>
 __global__ __launch_bounds__(kThreads) void carry_kernel(SegArgs args) {
-  constexpr uint64_t kTile = (uint64_t)kThreads * 8 * kUnroll;
+  constexpr int kSub = 2 * kUnroll;                           // 4-element accesses per lane per tile
+  constexpr uint64_t kTile = (uint64_t)kThreads * 4 * kSub;
   const uint32_t total = args.tile0[args.nseg];
   const int tid = threadIdx.x;
   for (uint32_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
@@ -221,33 +231,22 @@ __global__ __launch_bounds__(kThreads) void carry_kernel(SegArgs args) {
     const char* pb = static_cast<const char*>(args.b[s]);
     char* pd = static_cast<char*>(args.dst[s]);
     if (VEC && base + kTile <= len) {
-      uint32_t wa[kUnroll][8];
-      uint4 vb[kUnroll];
+      uint32_t wa[kSub][4];
+      uint2 vb[kSub];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint64_t e = base + (uint64_t)(u * kThreads + tid) * 8;
-        carry_load_a<AF>(pa, e, wa[u]);
-        vb[u] = ld_stream<HC_RING_NT_B>(pb + 2 * e);
+      for (int q = 0; q < kSub; ++q) {
+        const uint64_t e = base + (uint64_t)(q * kThreads + tid) * 4;
+        carry_load4<AF>(pa, e, wa[q]);
+        vb[q] = ld_stream8<HC_RING_NT_B>(pb + 2 * e);
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint64_t e = base + (uint64_t)(u * kThreads + tid) * 8;
-        const uint32_t h[4] = {vb[u].x, vb[u].y, vb[u].z, vb[u].w};
-        uint32_t sm[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sm[2 * i] = hop_f32(wa[u][2 * i], h[i] << 16);
-          sm[2 * i + 1] = hop_f32(wa[u][2 * i + 1], h[i] & 0xFFFF0000u);
-        }
-        if constexpr (DF) {
-          st_stream(pd + 4 * e, make_uint4(sm[0], sm[1], sm[2], sm[3]));
-          st_stream(pd + 4 * e + 16, make_uint4(sm[4], sm[5], sm[6], sm[7]));
-        } else {
-          st_stream(pd + 2 * e, make_uint4(bf16_rne(sm[0]) | (bf16_rne(sm[1]) << 16),
-                                           bf16_rne(sm[2]) | (bf16_rne(sm[3]) << 16),
-                                           bf16_rne(sm[4]) | (bf16_rne(sm[5]) << 16),
-                                           bf16_rne(sm[6]) | (bf16_rne(sm[7]) << 16)));
-        }
+      for (int q = 0; q < kSub; ++q) {
+        const uint64_t e = base + (uint64_t)(q * kThreads + tid) * 4;
+        const uint32_t s0 = hop_f32(wa[q][0], vb[q].x << 16), s1 = hop_f32(wa[q][1], vb[q].x & 0xFFFF0000u);
+        const uint32_t s2 = hop_f32(wa[q][2], vb[q].y << 16), s3 = hop_f32(wa[q][3], vb[q].y & 0xFFFF0000u);
+        if constexpr (DF) st_stream(pd + 4 * e, make_uint4(s0, s1, s2, s3));
+        else *reinterpret_cast<uint2*>(pd + 2 * e) =
+            make_uint2(bf16_rne(s0) | (bf16_rne(s1) << 16), bf16_rne(s2) | (bf16_rne(s3) << 16));
       }
     } else {
       const uint64_t end = base + kTile < len ? base + kTile : len;
@@ -266,7 +265,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Launch of one fp32-carry reduce-scatter step (see carry_kernel).
 template <bool AF, bool DF>
 hipError_t launch_carry(const Seg* segs, int nseg, int cu_budget, hipStream_t stream) {
-  constexpr uint64_t kTile = (uint64_t)kThreads * 8 * kUnroll;
+  constexpr uint64_t kTile = (uint64_t)kThreads * 8 * kUnroll;   // as carry_kernel's
   if (nseg <= 0) return hipSuccess;
   if (nseg > kMaxSegs) return hipErrorInvalidValue;
   SegArgs args;
