@@ -30,7 +30,7 @@ def load_into(dev_tensors, host_arrays):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("op", ["allreduce", "allreduce_sgd", "reduce_scatter"])
+@pytest.mark.parametrize("op", ["allreduce", "allreduce_sgd", "reduce_scatter", "allreduce_f32carry"])
 def test_captured_collective_replays_match_eager(dtype, op):
     R, n = 8, 8 * 12345 + 3 if op != "reduce_scatter" else 8 * 12345
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
@@ -42,9 +42,18 @@ def test_captured_collective_replays_match_eager(dtype, op):
     ws = torch.empty(max(hc.hc_workspace_bytes(hc.HC_OP_REDUCE_SCATTER, n, R, hc._dtype(send[0])), 16),
                      dtype=torch.uint8, device="cuda")
 
+    if op == "allreduce_f32carry" and dtype != "bf16":
+        pytest.skip("the fp32-carry allreduce is bf16 only")
+    cws = None
+    if op == "allreduce_f32carry":
+        cws = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_ALLREDUCE_F32_CARRY, n, R, hc.HC_BF16), dtype=torch.uint8,
+                          device="cuda")
+
     def call():
         if op == "allreduce":
             hc.hc_allreduce(send, recv)
+        elif op == "allreduce_f32carry":
+            hc.hc_allreduce_bf16_f32carry(send, recv, n, cws)
         elif op == "allreduce_sgd":
             hc.hc_allreduce_sgd(send, weights, 0.01)
         else:
@@ -71,6 +80,9 @@ def test_captured_collective_replays_match_eager(dtype, op):
         torch.cuda.synchronize()
         if op == "allreduce":
             ref = oracle.allreduce_fold(xs)
+            outs = recv
+        elif op == "allreduce_f32carry":
+            ref = oracle.allreduce_fold_f32carry(xs)
             outs = recv
         elif op == "allreduce_sgd":
             ref = oracle.allreduce_sgd(xs, ws_host, 0.01)

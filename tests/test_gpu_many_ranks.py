@@ -1,7 +1,8 @@
 """GPU parity at many ranks: 16, 33 and 64 (the library's limit, where one
 ring step's launch carries its most segments: one per receiver), for the
-allreduce, reduce-scatter, all-gather, compressed allreduce and the fused
-allreduce + SGD update, against the oracle, bit for bit.  Sizes include
+allreduce, reduce-scatter, all-gather, compressed allreduce, the fused
+allreduce + SGD update and the allreduce with fp32 partials, against the
+oracle, bit for bit.  Sizes include
 fewer elements than ranks (empty slices) and slices that end mid-tile."""
 import numpy as np
 import pytest
@@ -97,3 +98,20 @@ def test_allreduce_sgd_64_ranks(dtype):
     for r in range(R):
         got = to_host(wd[r])
         assert np.array_equal(got, bits(ref[r])), f"rank {r}: {first_mismatch(got, bits(ref[r]))}"
+
+
+@pytest.mark.parametrize("R", [16, 33, 64])
+def test_allreduce_f32carry_many_ranks(R):
+    for n in (R - 1, 5000 + R, 3 * B + 7):
+        print(f"f32carry R={R} n={n}", flush=True)
+        xs = rand(R, n, "bf16", 20 * R + n, 1e-3)
+        ref = oracle.allreduce_fold_f32carry(xs)
+        send = [to_dev(x) for x in xs]
+        recv = [torch.empty_like(s) for s in send]
+        ws = torch.empty(max(hc.hc_workspace_bytes(hc.HC_OP_ALLREDUCE_F32_CARRY, n, R, hc.HC_BF16), 16),
+                         dtype=torch.uint8, device="cuda")
+        hc.hc_allreduce_bf16_f32carry(send, recv, n, ws)
+        torch.cuda.synchronize()
+        for r in range(R):
+            got = to_host(recv[r])
+            assert np.array_equal(got, ref[r]), f"n={n} rank={r}: {first_mismatch(got, ref[r])}"
