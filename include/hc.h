@@ -1,6 +1,7 @@
 /*
  * hc.h -- C ABI of the MI355X (gfx950) emulated ring AllReduce data path and
- * the HCZ1 lossless bf16 exponent codec (library: libhc.so).
+ * the lossless bf16 exponent codecs, HCZ1 (fixed-length codes) and HCE1
+ * (Huffman codes) (library: libhc.so).
  *
  * The ring is emulated on ONE GPU: R "ranks" are R device buffers in the same
  * HBM; a hop's link transfer is the receiver reading the sender's buffer.  All
@@ -27,11 +28,15 @@
  *   - HC_ERR_INVALID_ARGUMENT: NULL pointer, nranks outside 1..HC_MAX_RANKS,
  *     misaligned pointer, count constraints, unknown dtype or option value.
  *   - HC_ERR_INSUFFICIENT_CAPACITY: workspace or output capacity too small.
+ *   - HC_ERR_UNSUPPORTED: an option the call cannot honour (the copy engine
+ *     for hc_compressed_allreduce).
  *   - HC_ERR_DEVICE: a HIP call failed; hc_last_error() has the text.
  *   - HC_ERR_CORRUPT_STREAM: only ever written by the device into the
- *     caller's status word of hc_decompress_bf16.
- *   Nothing is enqueued when a call returns an error.  No call aborts or
- *   throws across the ABI.
+ *     caller's status word of hc_decompress_bf16 / hc_decompress_bf16_entropy.
+ *   The first three are found on the host before anything is enqueued.  An
+ *   HC_ERR_DEVICE return can follow launches of the same call that were
+ *   already enqueued; the stream then holds a partial operation.  No call
+ *   aborts or throws across the ABI.
  */
 #ifndef HC_H
 #define HC_H
@@ -225,7 +230,9 @@ size_t hc_compress_bound_bf16(size_t n);
  * order, padded to 16.  b is the smallest 1..7 with the fewest bytes; a block
  * is raw when that is not below 16 + 32768 bytes.
  *   d_in: n bf16 words.  d_out: out_cap >= hc_compress_bound_bf16(n) bytes.
- *   d_out_bytes: one device u64, receives the stream size.
+ *   d_out_bytes: one device u64, receives the stream size; it receives 0
+ *   (and the stream is not valid) only if a block's wait for its
+ *   predecessors' sizes ran past its bound (about four million polls).
  *   d_ws: >= hc_workspace_bytes(HC_OP_COMPRESS, n, 1, HC_BF16) bytes (block
  *   offsets in flight).  Calls sharing a workspace must not overlap.
  */
