@@ -442,13 +442,73 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
 
 // Decoding table entry: exponent << 7 | code length; every window that
 // starts no code holds kNoCode (length field 15, above any real length).
+// Two levels: the primary table is indexed by the top kPrimBits bits of the
+// 12-bit window and resolves every code of at most kPrimBits bits.  Canonical
+// codes put all longer codes after the shorter ones, so their windows form
+// one range [T, kraft) that starts 4-aligned; a primary entry inside it holds
+// kLongMark and (window - T) << 4, and the secondary table resolves the
+// window.  Codes of 11 and 12 bits cover at most 2 windows each, so the
+// secondary table needs at most 2 * 256 entries plus the rounding of kraft up
+// to 4.  A block thus takes 4.1 KB of LDS instead of the 9.2 KB of one
+// 4096-entry table, and more blocks stay resident per compute unit.
 constexpr uint16_t kNoCode = 0xFFFFu;
+constexpr uint32_t kPrimBits = 10;
+constexpr uint32_t kLongMark = 14u;
+constexpr uint32_t kSecMax = 2 * 256 + 4;
 
 struct HceDecSmem {
-  uint16_t lut[1u << kLmax];   // 12-bit window, first stream bit on top -> entry
-  uint16_t start[257];         // window value where each code (in length, exponent order) begins
-  uint16_t ent[256];           // table entry of each code in that order
+  uint16_t lut[1u << kPrimBits];  // top 10 window bits -> entry, or a pointer into lut2
+  uint16_t lut2[kSecMax];         // windows T .. round_up(kraft, 4) - 1 -> entry
+  uint16_t start[257];            // window value where each code (in length, exponent order) begins
+  uint16_t ent[256];              // table entry of each code in that order
 };
+
+// Entry of the code at the top of buf (the next stream bits, first bit on top).
+__device__ __forceinline__ uint32_t lookup(const HceDecSmem& s, uint64_t buf) {
+  const uint32_t w = (uint32_t)(buf >> (64u - kLmax));
+  uint32_t e = s.lut[w >> (kLmax - kPrimBits)];
+  if ((e & 15u) == kLongMark) e = s.lut2[(e >> 4) | (w & ((1u << (kLmax - kPrimBits)) - 1u))];
+  return e;
+}
+
+// Fills tbl[i] for i in [0, cnt) with the entry of the code holding window
+// base + stride*i: kNoCode at or past kraft, a pointer into lut2 at or past
+// long_from, else the code's own entry.  Lane l takes entries
+// [per*l, per*l + per); it starts at a lane-dependent point of its run and
+// wraps, so that the lanes' writes fall in different banks, and walks the
+// codes forward (they are consecutive in window order).
+__device__ __forceinline__ void fill_table(const HceDecSmem& s, uint16_t* tbl, uint32_t cnt, uint32_t per,
+                                           uint32_t base, uint32_t stride, uint32_t long_from, uint32_t n_sym,
+                                           uint32_t kraft) {
+  const uint32_t lane = threadIdx.x, i0 = per * lane;
+  if (i0 >= cnt) return;
+  const uint32_t len = (cnt - i0) < per ? (cnt - i0) : per, r = lane % len;
+  uint32_t k0, k;
+  {
+    uint32_t lo = 0, hi = n_sym;   // the last code starting at or before the run's first window
+    while (hi - lo > 1u) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (s.start[mid] <= base + stride * i0) lo = mid; else hi = mid;
+    }
+    k0 = lo;
+    hi = n_sym;                    // ... at or before the window where this lane starts
+    while (hi - lo > 1u) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (s.start[mid] <= base + stride * (i0 + r)) lo = mid; else hi = mid;
+    }
+    k = lo;
+  }
+  uint32_t next = s.start[k + 1], cur = s.ent[k];
+  for (uint32_t j = 0; j < len; ++j) {
+    uint32_t o = r + j;
+    if (o >= len) o -= len;
+    if (o == 0 && j != 0) { k = k0; next = s.start[k + 1]; cur = s.ent[k]; }
+    const uint32_t x = base + stride * (i0 + o);
+    while (x >= next && k + 1 < n_sym) { ++k; next = s.start[k + 1]; cur = s.ent[k]; }
+    tbl[i0 + o] = x >= kraft ? kNoCode
+                             : x >= long_from ? (uint16_t)(((x - long_from) << 4) | kLongMark) : (uint16_t)cur;
+  }
+}
 
 // One code per lane per step for the 256 steps, writing each element (the
 // sign and fraction from the record's plane, the exponent decoded).  The
@@ -478,7 +538,7 @@ __device__ __forceinline__ bool decode_steps(const HceDecSmem& s, const uint8_t*
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      uint32_t e = s.lut[(uint32_t)(buf >> 32) >> (32u - kLmax)];
+      uint32_t e = lookup(s, buf);
       uint32_t L = e & 15u;
       const bool need = L > avail;
       const uint64_t mask = __ballot(need);
@@ -492,7 +552,7 @@ __device__ __forceinline__ bool decode_steps(const HceDecSmem& s, const uint8_t*
         if (need) {
           buf |= (uint64_t)__builtin_bitreverse32(word) << (32u - avail);
           avail += 32;
-          e = s.lut[(uint32_t)(buf >> 32) >> (32u - kLmax)];
+          e = lookup(s, buf);
           L = e & 15u;
         }
         base += (uint32_t)__popcll(mask);
@@ -605,35 +665,18 @@ __global__ __launch_bounds__(64) void hce_decompress_kernel(const uint8_t* __res
       }
       if (lane == 0) s.start[n_sym] = (uint16_t)kraft;   // end of the last code's range
       __syncthreads();
-      // Table: lane fills windows [64 lane, 64 lane + 64), the codes' ranges
-      // being consecutive in sorted order; it starts at a lane-dependent
-      // point of its run and wraps, so the lanes' writes fall in different
-      // banks.
+      // The two tables.  T: the windows of the codes of at most kPrimBits
+      // bits, which come first; the secondary table covers T .. kraft
+      // rounded up to 4.
       {
-        const uint32_t x0 = 64u * lane, r = lane;
-        uint32_t k0, kr;
-        {
-          uint32_t lo = 0, hi = n_sym;   // the last code starting at or before x0
-          while (hi - lo > 1u) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if (s.start[mid] <= x0) lo = mid; else hi = mid;
-          }
-          k0 = lo;
-          lo = k0; hi = n_sym;           // ... at or before x0 + r
-          while (hi - lo > 1u) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if (s.start[mid] <= x0 + r) lo = mid; else hi = mid;
-          }
-          kr = lo;
-        }
-        uint32_t k = kr, next = s.start[k + 1], cur = s.ent[k];
-        for (uint32_t j = 0; j < 64; ++j) {
-          const uint32_t o = (r + j) & 63u;
-          if (o == 0 && j != 0) { k = k0; next = s.start[k + 1]; cur = s.ent[k]; }
-          const uint32_t x = x0 + o;
-          while (x >= next && k + 1 < n_sym) { ++k; next = s.start[k + 1]; cur = s.ent[k]; }
-          s.lut[x] = x < kraft ? (uint16_t)cur : kNoCode;
-        }
+        uint32_t T = 0;
+#pragma unroll
+        for (uint32_t L = 1; L <= kPrimBits; ++L) T += cnt[L] << (kLmax - L);
+        const uint32_t sec = ((kraft + 3u) & ~3u) - T;   // <= 2 * 256 + 3 (codes of 11, 12 bits)
+        fill_table(s, s.lut, 1u << kPrimBits, (1u << kPrimBits) / 64u, 0u, 1u << (kLmax - kPrimBits), T, n_sym,
+                   kraft);
+        fill_table(s, s.lut2, sec < kSecMax ? sec : kSecMax, (kSecMax + 63u) / 64u, T, 1u, 0xFFFFFFFFu, n_sym,
+                   kraft);
       }
       __syncthreads();
       bad = decode_steps(s, rec, n_words, dst);
