@@ -572,7 +572,7 @@ __device__ __forceinline__ bool decode_steps(const HceDecSmem& s, const uint8_t*
   return bad || base != n_words || buf != 0;
 }
 
-__global__ __launch_bounds__(64) void hce_decompress_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(8))) void hce_decompress_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes,
                                                             uint16_t* __restrict__ out, uint64_t n,
                                                             int32_t* __restrict__ status, uint32_t nb) {
   __shared__ HceDecSmem s;
