@@ -67,6 +67,14 @@ def test_in_place_copy_engine_and_garbage_workspace():
     check(xs, run(xs, fill=0xFF), "workspace of 0xFF bytes")   # NaN patterns in every slot
 
 
+@pytest.mark.parametrize("budget", [8, 32])
+def test_cu_budget_grid(budget):
+    # A persistent grid of 8 workgroups per budgeted CU (64 or 256) walks the
+    # ~320 tiles of every step in a grid-stride loop.
+    xs = rand_bf16(8, 8 * 4096 * 40 + 11, 300 + budget)
+    check(xs, run(xs, cu_budget=budget), f"cu_budget {budget}")
+
+
 def test_one_rounding_against_per_hop():
     # n = R = 4: element j lies in slice j; rank j+1 holds 1.0, the others
     # 2^-8.  One rounding gives 1 + 2^-6 (0x3F82), per-hop rounding 1.0.
