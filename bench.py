@@ -158,15 +158,21 @@ def bench_ring(args, workload: str):
     for k in range(args.steps):
         hc.hc_allreduce(send, recv, step_events=evsets[k])
     torch.cuda.synchronize()
-    red, cpy = [], []
+    # Step intervals: R-2 plain reduce-scatter steps, the last one (a
+    # reduce-and-send that also writes each slice into the next rank's
+    # output), the first all-gather step (empty: done by the step before) and
+    # R-2 copy steps.
+    red, fused, cpy = [], [], []
     for ev in evsets:
         d = ev.elapsed_ms()
-        red += d[: R - 1]
-        cpy += d[R - 1:]
+        red += d[: R - 2]
+        fused.append(d[R - 2])
+        cpy += d[R:]
     avg_red, avg_cpy = sum(red) / len(red), sum(cpy) / len(cpy)
+    avg_fused = sum(fused) / len(fused)
     L = n // R
-    rs_bytes = 3 * es * n * (R - 1)                    # per allreduce
-    ag_bytes = 2 * es * n * (R - 1)
+    rs_bytes = 3 * es * n * (R - 2) + 4 * es * n       # per allreduce; the last step writes twice
+    ag_bytes = 2 * es * n * (R - 2)
     alg_bytes = rs_bytes + ag_bytes
     red_launch_bytes = 3 * es * n                        # one reduce step: R receivers x L elements
     algbw = n * es / (ms / 1e3) / 1e9
@@ -185,7 +191,8 @@ def bench_ring(args, workload: str):
         "busbw_gbps": round(algbw * 2 * (R - 1) / R, 3),
         "hbm_gbps": round(hbm, 2), "hbm_frac_of_peak": round(hbm / PEAK_HBM_GBPS, 4),
         "alg_bytes_per_step": alg_bytes,
-        "reduce_launch_ms": round(avg_red, 6), "copy_launch_ms": round(avg_cpy, 6),
+        "reduce_launch_ms": round(avg_red, 6), "reduce_send_launch_ms": round(avg_fused, 6),
+        "copy_launch_ms": round(avg_cpy, 6),
         "copy_launch_gbps": round(2 * es * n / (avg_cpy / 1e3) / 1e9, 2),
         "roofline": {"bound": "hbm", "kernel": "step_kernel<reduce> (one reduce-scatter step)",
                      "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",

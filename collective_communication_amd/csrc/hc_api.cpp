@@ -136,21 +136,33 @@ char* mp(void* p, size_t bytes) { return static_cast<char*>(p) + bytes; }
 
 // Runs the allreduce task list one ring step per launch: all receivers of a
 // step in one kernel, their chunks merged into one segment per receiver.
+// The last reduce-scatter step is a reduce-and-send: the receiver that forms
+// a slice's final sum writes it into its own output and sends it on into the
+// next rank's output, which is that rank's first all-gather copy; that copy
+// step then has nothing left to do (its step event is still recorded).  With
+// the copy engine the first all-gather copy stays a copy of its own.
 hc_status_t run_allreduce(void* const* send, void* const* recv, size_t count, hc_dtype_t dtype,
                           int R, size_t chunk, int budget, bool dma, Tap& tap, hipStream_t stream) {
   const size_t es = esize(dtype);
+  const bool fuse = !dma;
   std::vector<hc_task_t> tasks = hc::ring_tasks(R, count, chunk);
   size_t k = 0;
   while (k < tasks.size()) {
     const int op = tasks[k].op, step = tasks[k].step;
+    const bool send_on = fuse && op == 1 && step == R - 2;
     hc::Seg segs[hc::kMaxSegs];
     int nseg = 0, last_dst = -1;
     uint64_t last_end = 0;
     hipError_t e = tap.mark(stream);
     if (e != hipSuccess) return device_fail(e, "hipEventRecord");
+    if (fuse && op != 1 && step == 0) {   // done by the reduce-and-send step
+      while (k < tasks.size() && tasks[k].op == op && tasks[k].step == step) ++k;
+      continue;
+    }
     auto launch = [&]() {
-      return op == 1 ? hc::launch_reduce_step(segs, nseg, dtype, budget, stream)
-                     : copy_step(segs, nseg, es, budget, dma, stream);
+      if (op != 1) return copy_step(segs, nseg, es, budget, dma, stream);
+      return send_on ? hc::launch_reduce_send_step(segs, nseg, dtype, budget, stream)
+                     : hc::launch_reduce_step(segs, nseg, dtype, budget, stream);
     };
     while (k < tasks.size() && tasks[k].op == op && tasks[k].step == step) {
       const hc_task_t& t = tasks[k];
@@ -165,6 +177,7 @@ hc_status_t run_allreduce(void* const* send, void* const* recv, size_t count, hc
         segs[nseg].a = (op == 1 && step == 0) ? cp(send[t.src], off) : cp(recv[t.src], off);
         segs[nseg].b = cp(send[t.dst], off);
         segs[nseg].dst = mp(recv[t.dst], off);
+        segs[nseg].dst2 = send_on ? mp(recv[(t.dst + 1) % R], off) : nullptr;
         segs[nseg].len = t.len;
         ++nseg;
       }

@@ -17,6 +17,7 @@ struct Seg {
   const void* b;
   void* dst;
   uint64_t len;
+  void* dst2 = nullptr;   // a second destination of the same values (reduce-and-send step), or NULL
 };
 
 constexpr int kMaxSegs = 64;
@@ -26,6 +27,11 @@ hipError_t launch_reduce_step(const Seg* segs, int nseg, hc_dtype_t dtype, int c
                               hipStream_t stream);
 hipError_t launch_copy_step(const Seg* segs, int nseg, size_t elem_bytes, int cu_budget,
                             hipStream_t stream);
+// A reduce step that stores each sum twice, at dst and dst2: the last
+// reduce-scatter step writing the slice's final sum into its owner's output
+// and sending it on into the next rank's output (that rank's first
+// all-gather copy).
+hipError_t launch_reduce_send_step(const Seg* segs, int nseg, hc_dtype_t dtype, int cu_budget, hipStream_t stream);
 // The last reduce-scatter step fused with an SGD update: g = hop(a, b) (or
 // g = a when b is NULL, a one-rank "sum"), then dst = dst - lr*g in place
 // (dst holds the owner's weights).

@@ -86,11 +86,13 @@ constexpr int kCopy = 0;     // dst = a
 constexpr int kReduce = 1;   // dst = hop(a, b)
 constexpr int kSgd = 2;      // dst = dst - lr * hop(a, b)
 constexpr int kSgdOne = 3;   // dst = dst - lr * a (one rank: the sum is a)
+constexpr int kReduceSend = 4;   // dst = dst2 = hop(a, b)
 
 struct SegArgs {
   const void* a[kMaxSegs];
   const void* b[kMaxSegs];
   void* dst[kMaxSegs];
+  void* dst2[kMaxSegs];          // second destination (kReduceSend only)
   uint64_t len[kMaxSegs];
   uint32_t tile0[kMaxSegs + 1];  // first tile of each segment; tile0[nseg] = total
   int32_t nseg;
@@ -145,7 +147,7 @@ __device__ __forceinline__ uint4 vec_hop(uint4 a, uint4 b) {
 // moves elements.
 template <int ES, int OP, bool VEC>
 __global__ __launch_bounds__(kThreads) void step_kernel(SegArgs args) {
-  constexpr bool kUsesB = OP == kReduce || OP == kSgd;
+  constexpr bool kUsesB = OP == kReduce || OP == kSgd || OP == kReduceSend;
   constexpr bool kUpdates = OP == kSgd || OP == kSgdOne;
   constexpr int V = 16 / ES;
   constexpr uint64_t kTile = (uint64_t)kThreads * V * kUnroll;
@@ -163,6 +165,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(SegArgs args) {
     const char* pa = static_cast<const char*>(args.a[s]);
     const char* pb = static_cast<const char*>(args.b[s]);
     char* pd = static_cast<char*>(args.dst[s]);
+    char* pd2 = OP == kReduceSend ? static_cast<char*>(args.dst2[s]) : nullptr;
     if (VEC && base + kTile <= len) {
       uint4 va[kUnroll], vb[kUnroll], vw[kUnroll];
 #pragma unroll
@@ -177,6 +180,11 @@ __global__ __launch_bounds__(kThreads) void step_kernel(SegArgs args) {
         const uint64_t off = (base + (uint64_t)(u * kThreads + tid) * V) * ES;
         if constexpr (OP == kCopy) st_stream(pd + off, va[u]);
         else if constexpr (OP == kReduce) st_stream(pd + off, vec_hop<ES>(va[u], vb[u]));
+        else if constexpr (OP == kReduceSend) {
+          const uint4 r = vec_hop<ES>(va[u], vb[u]);
+          st_stream(pd + off, r);
+          st_stream(pd2 + off, r);
+        }
         else if constexpr (OP == kSgd) st_stream(pd + off, vec_sgd<ES>(vw[u], vec_hop<ES>(va[u], vb[u]), args.lr));
         else st_stream(pd + off, vec_sgd<ES>(vw[u], va[u], args.lr));
       }
@@ -186,6 +194,11 @@ __global__ __launch_bounds__(kThreads) void step_kernel(SegArgs args) {
         const uint32_t x = ld_elem<ES>(pa, i);
         if constexpr (OP == kCopy) st_elem<ES>(pd, i, x);
         else if constexpr (OP == kReduce) st_elem<ES>(pd, i, scalar_hop<ES>(x, ld_elem<ES>(pb, i)));
+        else if constexpr (OP == kReduceSend) {
+          const uint32_t r = scalar_hop<ES>(x, ld_elem<ES>(pb, i));
+          st_elem<ES>(pd, i, r);
+          st_elem<ES>(pd2, i, r);
+        }
         else if constexpr (OP == kSgd)
           st_elem<ES>(pd, i, scalar_sgd<ES>(ld_elem<ES>(pd, i), scalar_hop<ES>(x, ld_elem<ES>(pb, i)), args.lr));
         else st_elem<ES>(pd, i, scalar_sgd<ES>(ld_elem<ES>(pd, i), x, args.lr));
@@ -300,7 +313,7 @@ hipError_t launch_carry(const Seg* segs, int nseg, int cu_budget, hipStream_t st
 
 template <int ES, int OP>
 hipError_t launch_step(const Seg* segs, int nseg, int cu_budget, hipStream_t stream, float lr = 0.0f) {
-  constexpr bool kUsesB = OP == kReduce || OP == kSgd;
+  constexpr bool kUsesB = OP == kReduce || OP == kSgd || OP == kReduceSend;
   constexpr uint64_t kTile = (uint64_t)kThreads * (16 / ES) * kUnroll;
   if (nseg <= 0) return hipSuccess;
   if (nseg > kMaxSegs) return hipErrorInvalidValue;
@@ -313,10 +326,13 @@ hipError_t launch_step(const Seg* segs, int nseg, int cu_budget, hipStream_t str
     args.a[k] = segs[i].a;
     args.b[k] = kUsesB ? segs[i].b : segs[i].a;
     args.dst[k] = segs[i].dst;
+    args.dst2[k] = segs[i].dst2;
+    if (OP == kReduceSend && !segs[i].dst2) return hipErrorInvalidValue;
     args.len[k] = segs[i].len;
     args.tile0[k] = (uint32_t)tiles;
     tiles += (segs[i].len + kTile - 1) / kTile;
-    vec = vec && aligned16(segs[i].a) && aligned16(segs[i].dst) && (!kUsesB || aligned16(segs[i].b));
+    vec = vec && aligned16(segs[i].a) && aligned16(segs[i].dst) && (!kUsesB || aligned16(segs[i].b)) &&
+          (OP != kReduceSend || aligned16(segs[i].dst2));
     ++k;
   }
   if (k == 0) return hipSuccess;
@@ -340,6 +356,11 @@ hipError_t launch_reduce_step(const Seg* segs, int nseg, hc_dtype_t dtype, int c
                               hipStream_t stream) {
   if (dtype == HC_F32) return launch_step<4, kReduce>(segs, nseg, cu_budget, stream);
   return launch_step<2, kReduce>(segs, nseg, cu_budget, stream);
+}
+
+hipError_t launch_reduce_send_step(const Seg* segs, int nseg, hc_dtype_t dtype, int cu_budget, hipStream_t stream) {
+  if (dtype == HC_F32) return launch_step<4, kReduceSend>(segs, nseg, cu_budget, stream);
+  return launch_step<2, kReduceSend>(segs, nseg, cu_budget, stream);
 }
 
 hipError_t launch_sgd_step(const Seg* segs, int nseg, hc_dtype_t dtype, float lr, int cu_budget,
