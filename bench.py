@@ -244,12 +244,13 @@ def bench_ring_carry(args):
         first.append(d[0])
         mid += d[1:R - 2]
         last.append(d[R - 2])
-        cpy += d[R - 1:]
+        cpy += d[R:]   # d[R - 1], the first all-gather step, is empty: the last hop sent it
     avg = lambda v: sum(v) / len(v)
     # bytes per element of one step (N elements per step over the R receivers):
     # first hop 2 + 2 read, 4 written; a middle hop 4 + 2 read, 4 written; the
-    # last hop 4 + 2 read, 2 written; an all-gather copy 2 read, 2 written.
-    alg_bytes = n * (8 + 10 * (R - 3) + 8 + 4 * (R - 1))
+    # last hop 4 + 2 read, 2 + 2 written (the rounded sum into its owner and
+    # into the next rank); R-2 all-gather copies 2 read, 2 written.
+    alg_bytes = n * (8 + 10 * (R - 3) + 10 + 4 * (R - 2))
     mid_bytes = 10 * n
     algbw = n * 2 / (ms / 1e3) / 1e9
     # Error against the exact sum on 65,536 elements (fp64 holds every 8-term
@@ -617,11 +618,12 @@ def bench_fused_sgd(args):
     torch.cuda.synchronize()
     last = [ev.elapsed_ms()[R - 2] for ev in evsets]
     # bytes: R-2 plain reduce steps (read 2, write 1), the fused step (read 3,
-    # write 1), R-1 copy steps (read 1, write 1), every one over n elements
-    alg = 2 * n * (3 * (R - 2) + 4 + 2 * (R - 1))
+    # write 2: the new weights in place and into the next rank), R-2 copy
+    # steps (read 1, write 1), every one over n bf16 elements
+    alg = 2 * n * (3 * (R - 2) + 5 + 2 * (R - 2))
     alg_unfused = 2 * n * (3 * (R - 1) + 2 * (R - 1)) + 2 * n * R * 3
     last_ms = sum(last) / len(last)
-    extra = {"roofline": roofline_obj("step_kernel<2,sgd> (the last reduce-scatter step with the update)", 8 * n,
+    extra = {"roofline": roofline_obj("step_kernel<2,sgd-send> (the last reduce-scatter step with the update)", 10 * n,
                                       last_ms, None, "HIP events at the step boundaries")}
     if not args.no_cpu_baseline:
         import oracle
@@ -641,7 +643,7 @@ def bench_fused_sgd(args):
             "hbm_gbps": round(alg / (ms / 1e3) / 1e9, 1),
             "hbm_frac_of_peak": round(alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4), "alg_bytes": alg,
             "fused_step_ms": round(sum(last) / len(last), 5),
-            "fused_step_gbps": round(8 * n / (sum(last) / len(last) / 1e3) / 1e9, 1),
+            "fused_step_gbps": round(10 * n / (sum(last) / len(last) / 1e3) / 1e9, 1),
             "unfused_ms": round(ms_unfused, 5), "unfused_alg_bytes": alg_unfused,
             "speedup_vs_unfused": round(ms_unfused / ms, 3)}
 

@@ -198,6 +198,7 @@ hc_status_t run_allreduce(void* const* send, void* const* recv, size_t count, hc
 hc_status_t run_allreduce_sgd(void* const* grads, void* const* weights, size_t count, hc_dtype_t dtype, int R,
                               size_t chunk, float lr, int budget, bool dma, Tap& tap, hipStream_t stream) {
   const size_t es = esize(dtype);
+  const bool fuse = !dma;   // the update step also sends each new slice on (as in run_allreduce)
   std::vector<hc_task_t> tasks = hc::ring_tasks(R, count, chunk);
   size_t k = 0;
   while (k < tasks.size()) {
@@ -208,6 +209,10 @@ hc_status_t run_allreduce_sgd(void* const* grads, void* const* weights, size_t c
     uint64_t last_end = 0;
     hipError_t e = tap.mark(stream);
     if (e != hipSuccess) return device_fail(e, "hipEventRecord");
+    if (fuse && op != 1 && step == 0) {   // done by the update-and-send step
+      while (k < tasks.size() && tasks[k].op == op && tasks[k].step == step) ++k;
+      continue;
+    }
     auto launch = [&]() {
       if (op != 1) return copy_step(segs, nseg, es, budget, dma, stream);
       return last_rs ? hc::launch_sgd_step(segs, nseg, dtype, lr, budget, stream)
@@ -227,6 +232,7 @@ hc_status_t run_allreduce_sgd(void* const* grads, void* const* weights, size_t c
           segs[nseg].a = cp(grads[t.src], off);
           segs[nseg].b = cp(grads[t.dst], off);
           segs[nseg].dst = last_rs ? mp(weights[t.dst], off) : mp(grads[t.dst], off);
+          segs[nseg].dst2 = (last_rs && fuse) ? mp(weights[(t.dst + 1) % R], off) : nullptr;
         } else {
           segs[nseg].a = cp(weights[t.src], off);
           segs[nseg].b = nullptr;
@@ -262,6 +268,7 @@ size_t carry_ws_bytes(size_t count, int R) {
 hc_status_t run_allreduce_carry(void* const* send, void* const* recv, size_t count, int R, size_t chunk, void* ws,
                                 int budget, bool dma, Tap& tap, hipStream_t stream) {
   const size_t es = 2, L = hc::ceil_div(count, (size_t)R), Lp = carry_slot_elems(count, R);
+  const bool fuse = !dma;   // the rounding step also sends each slice on (as in run_allreduce)
   std::vector<hc_task_t> tasks = hc::ring_tasks(R, count, chunk);
   size_t k = 0;
   while (k < tasks.size()) {
@@ -272,6 +279,10 @@ hc_status_t run_allreduce_carry(void* const* send, void* const* recv, size_t cou
     uint64_t last_end = 0;
     hipError_t e = tap.mark(stream);
     if (e != hipSuccess) return device_fail(e, "hipEventRecord");
+    if (fuse && op != 1 && step == 0) {   // done by the rounding-and-send step
+      while (k < tasks.size() && tasks[k].op == op && tasks[k].step == step) ++k;
+      continue;
+    }
     auto launch = [&]() {
       return op == 1 ? hc::launch_carry_step(segs, nseg, !first, !last, budget, stream)
                      : copy_step(segs, nseg, es, budget, dma, stream);
@@ -292,6 +303,7 @@ hc_status_t run_allreduce_carry(void* const* send, void* const* recv, size_t cou
                                : cp(ws, ((size_t)(2 * t.src + ((step - 1) & 1)) * Lp + in_slice) * 4);
           segs[nseg].b = cp(send[t.dst], off);
           segs[nseg].dst = last ? mp(recv[t.dst], off) : mp(ws, ((size_t)(2 * t.dst + (step & 1)) * Lp + in_slice) * 4);
+          segs[nseg].dst2 = (last && fuse) ? mp(recv[(t.dst + 1) % R], off) : nullptr;
         } else {
           segs[nseg].a = cp(recv[t.src], off);
           segs[nseg].b = nullptr;

@@ -34,12 +34,14 @@ hipError_t launch_copy_step(const Seg* segs, int nseg, size_t elem_bytes, int cu
 hipError_t launch_reduce_send_step(const Seg* segs, int nseg, hc_dtype_t dtype, int cu_budget, hipStream_t stream);
 // The last reduce-scatter step fused with an SGD update: g = hop(a, b) (or
 // g = a when b is NULL, a one-rank "sum"), then dst = dst - lr*g in place
-// (dst holds the owner's weights).
+// (dst holds the owner's weights); when the segments carry dst2 (and b), the
+// new weights are also sent on into dst2.
 hipError_t launch_sgd_step(const Seg* segs, int nseg, hc_dtype_t dtype, float lr, int cu_budget,
                            hipStream_t stream);
 // A reduce-scatter step of the bf16 ring with fp32 partials: dst = a + b in
 // fp32, b bf16; a is an fp32 partial when a_f32 (else bf16 data); the sum is
-// stored as an fp32 partial when dst_f32, else rounded once to bf16.
+// stored as an fp32 partial when dst_f32, else rounded once to bf16 (and,
+// when a segment carries dst2, also sent on into dst2).
 hipError_t launch_carry_step(const Seg* segs, int nseg, bool a_f32, bool dst_f32, int cu_budget,
                              hipStream_t stream);
 

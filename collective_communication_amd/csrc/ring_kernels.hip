@@ -87,6 +87,7 @@ constexpr int kReduce = 1;   // dst = hop(a, b)
 constexpr int kSgd = 2;      // dst = dst - lr * hop(a, b)
 constexpr int kSgdOne = 3;   // dst = dst - lr * a (one rank: the sum is a)
 constexpr int kReduceSend = 4;   // dst = dst2 = hop(a, b)
+constexpr int kSgdSend = 5;      // dst = dst2 = dst - lr * hop(a, b)
 
 struct SegArgs {
   const void* a[kMaxSegs];
@@ -142,13 +143,15 @@ __device__ __forceinline__ uint4 vec_hop(uint4 a, uint4 b) {
 }
 
 // ES: element bytes (4 fp32, 2 bf16).  OP: kCopy, kReduce (recvReduceCopy),
-// kSgd, kSgdOne.  VEC: every segment pointer is 16-byte aligned, so whole
+// kSgd, kSgdOne, and the two that also send their result on (kReduceSend,
+// kSgdSend).  VEC: every segment pointer is 16-byte aligned, so whole
 // tiles move as 16-byte vectors; otherwise (odd slice offsets) each lane
 // moves elements.
 template <int ES, int OP, bool VEC>
 __global__ __launch_bounds__(kThreads) void step_kernel(SegArgs args) {
-  constexpr bool kUsesB = OP == kReduce || OP == kSgd || OP == kReduceSend;
-  constexpr bool kUpdates = OP == kSgd || OP == kSgdOne;
+  constexpr bool kUsesB = OP == kReduce || OP == kSgd || OP == kReduceSend || OP == kSgdSend;
+  constexpr bool kUpdates = OP == kSgd || OP == kSgdOne || OP == kSgdSend;
+  constexpr bool kSends = OP == kReduceSend || OP == kSgdSend;
   constexpr int V = 16 / ES;
   constexpr uint64_t kTile = (uint64_t)kThreads * V * kUnroll;
   const uint32_t total = args.tile0[args.nseg];
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(SegArgs args) {
     const char* pa = static_cast<const char*>(args.a[s]);
     const char* pb = static_cast<const char*>(args.b[s]);
     char* pd = static_cast<char*>(args.dst[s]);
-    char* pd2 = OP == kReduceSend ? static_cast<char*>(args.dst2[s]) : nullptr;
+    char* pd2 = kSends ? static_cast<char*>(args.dst2[s]) : nullptr;
     if (VEC && base + kTile <= len) {
       uint4 va[kUnroll], vb[kUnroll], vw[kUnroll];
 #pragma unroll
@@ -186,6 +189,11 @@ __global__ __launch_bounds__(kThreads) void step_kernel(SegArgs args) {
           st_stream(pd2 + off, r);
         }
         else if constexpr (OP == kSgd) st_stream(pd + off, vec_sgd<ES>(vw[u], vec_hop<ES>(va[u], vb[u]), args.lr));
+        else if constexpr (OP == kSgdSend) {
+          const uint4 r = vec_sgd<ES>(vw[u], vec_hop<ES>(va[u], vb[u]), args.lr);
+          st_stream(pd + off, r);
+          st_stream(pd2 + off, r);
+        }
         else st_stream(pd + off, vec_sgd<ES>(vw[u], va[u], args.lr));
       }
     } else {
@@ -201,6 +209,11 @@ __global__ __launch_bounds__(kThreads) void step_kernel(SegArgs args) {
         }
         else if constexpr (OP == kSgd)
           st_elem<ES>(pd, i, scalar_sgd<ES>(ld_elem<ES>(pd, i), scalar_hop<ES>(x, ld_elem<ES>(pb, i)), args.lr));
+        else if constexpr (OP == kSgdSend) {
+          const uint32_t r = scalar_sgd<ES>(ld_elem<ES>(pd, i), scalar_hop<ES>(x, ld_elem<ES>(pb, i)), args.lr);
+          st_elem<ES>(pd, i, r);
+          st_elem<ES>(pd2, i, r);
+        }
         else st_elem<ES>(pd, i, scalar_sgd<ES>(ld_elem<ES>(pd, i), x, args.lr));
       }
     }
@@ -243,6 +256,7 @@ __global__ __launch_bounds__(kThreads) void carry_kernel(SegArgs args) {
     const char* pa = static_cast<const char*>(args.a[s]);
     const char* pb = static_cast<const char*>(args.b[s]);
     char* pd = static_cast<char*>(args.dst[s]);
+    char* pd2 = DF ? nullptr : static_cast<char*>(args.dst2[s]);   // the rounded sum sent on, or NULL
     if (VEC && base + kTile <= len) {
       uint32_t wa[kSub][4];
       uint2 vb[kSub];
@@ -257,17 +271,25 @@ __global__ __launch_bounds__(kThreads) void carry_kernel(SegArgs args) {
         const uint64_t e = base + (uint64_t)(q * kThreads + tid) * 4;
         const uint32_t s0 = hop_f32(wa[q][0], vb[q].x << 16), s1 = hop_f32(wa[q][1], vb[q].x & 0xFFFF0000u);
         const uint32_t s2 = hop_f32(wa[q][2], vb[q].y << 16), s3 = hop_f32(wa[q][3], vb[q].y & 0xFFFF0000u);
-        if constexpr (DF) st_stream(pd + 4 * e, make_uint4(s0, s1, s2, s3));
-        else *reinterpret_cast<uint2*>(pd + 2 * e) =
-            make_uint2(bf16_rne(s0) | (bf16_rne(s1) << 16), bf16_rne(s2) | (bf16_rne(s3) << 16));
+        if constexpr (DF) {
+          st_stream(pd + 4 * e, make_uint4(s0, s1, s2, s3));
+        } else {
+          const uint2 r = make_uint2(bf16_rne(s0) | (bf16_rne(s1) << 16), bf16_rne(s2) | (bf16_rne(s3) << 16));
+          *reinterpret_cast<uint2*>(pd + 2 * e) = r;
+          if (pd2) *reinterpret_cast<uint2*>(pd2 + 2 * e) = r;
+        }
       }
     } else {
       const uint64_t end = base + kTile < len ? base + kTile : len;
       for (uint64_t i = base + tid; i < end; i += kThreads) {
         const uint32_t a = AF ? ld_elem<4>(pa, i) : ld_elem<2>(pa, i) << 16;
         const uint32_t sum = hop_f32(a, ld_elem<2>(pb, i) << 16);
-        if constexpr (DF) st_elem<4>(pd, i, sum);
-        else st_elem<2>(pd, i, bf16_rne(sum));
+        if constexpr (DF) {
+          st_elem<4>(pd, i, sum);
+        } else {
+          st_elem<2>(pd, i, bf16_rne(sum));
+          if (pd2) st_elem<2>(pd2, i, bf16_rne(sum));
+        }
       }
     }
   }
@@ -290,10 +312,12 @@ hipError_t launch_carry(const Seg* segs, int nseg, int cu_budget, hipStream_t st
     args.a[k] = segs[i].a;
     args.b[k] = segs[i].b;
     args.dst[k] = segs[i].dst;
+    args.dst2[k] = DF ? nullptr : segs[i].dst2;
     args.len[k] = segs[i].len;
     args.tile0[k] = (uint32_t)tiles;
     tiles += (segs[i].len + kTile - 1) / kTile;
-    vec = vec && aligned16(segs[i].a) && aligned16(segs[i].b) && aligned16(segs[i].dst);
+    vec = vec && aligned16(segs[i].a) && aligned16(segs[i].b) && aligned16(segs[i].dst) &&
+          (DF || !segs[i].dst2 || aligned16(segs[i].dst2));
     ++k;
   }
   if (k == 0) return hipSuccess;
@@ -313,7 +337,8 @@ hipError_t launch_carry(const Seg* segs, int nseg, int cu_budget, hipStream_t st
 
 template <int ES, int OP>
 hipError_t launch_step(const Seg* segs, int nseg, int cu_budget, hipStream_t stream, float lr = 0.0f) {
-  constexpr bool kUsesB = OP == kReduce || OP == kSgd || OP == kReduceSend;
+  constexpr bool kUsesB = OP == kReduce || OP == kSgd || OP == kReduceSend || OP == kSgdSend;
+  constexpr bool kSends = OP == kReduceSend || OP == kSgdSend;
   constexpr uint64_t kTile = (uint64_t)kThreads * (16 / ES) * kUnroll;
   if (nseg <= 0) return hipSuccess;
   if (nseg > kMaxSegs) return hipErrorInvalidValue;
@@ -327,12 +352,12 @@ hipError_t launch_step(const Seg* segs, int nseg, int cu_budget, hipStream_t str
     args.b[k] = kUsesB ? segs[i].b : segs[i].a;
     args.dst[k] = segs[i].dst;
     args.dst2[k] = segs[i].dst2;
-    if (OP == kReduceSend && !segs[i].dst2) return hipErrorInvalidValue;
+    if (kSends && !segs[i].dst2) return hipErrorInvalidValue;
     args.len[k] = segs[i].len;
     args.tile0[k] = (uint32_t)tiles;
     tiles += (segs[i].len + kTile - 1) / kTile;
     vec = vec && aligned16(segs[i].a) && aligned16(segs[i].dst) && (!kUsesB || aligned16(segs[i].b)) &&
-          (OP != kReduceSend || aligned16(segs[i].dst2));
+          (!kSends || aligned16(segs[i].dst2));
     ++k;
   }
   if (k == 0) return hipSuccess;
@@ -366,6 +391,10 @@ hipError_t launch_reduce_send_step(const Seg* segs, int nseg, hc_dtype_t dtype, 
 hipError_t launch_sgd_step(const Seg* segs, int nseg, hc_dtype_t dtype, float lr, int cu_budget,
                            hipStream_t stream) {
   const bool one = nseg > 0 && segs[0].b == nullptr;
+  const bool send = nseg > 0 && segs[0].dst2 != nullptr;
+  if (send && !one)
+    return dtype == HC_F32 ? launch_step<4, kSgdSend>(segs, nseg, cu_budget, stream, lr)
+                           : launch_step<2, kSgdSend>(segs, nseg, cu_budget, stream, lr);
   if (dtype == HC_F32)
     return one ? launch_step<4, kSgdOne>(segs, nseg, cu_budget, stream, lr)
                : launch_step<4, kSgd>(segs, nseg, cu_budget, stream, lr);
