@@ -23,10 +23,11 @@ its own.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 The headline time is K back-to-back calls with nothing else on the stream.
-The per-kernel figures come from a second pass of K calls in which the
-library records HIP events at ring-step boundaries on the launch stream
-(hc_opts_t.step_events); those event records add a few microseconds between
-dependent kernels, so that pass is kept out of the headline time.
+The per-kernel figures come from a second pass of K calls in which every
+ring step's kernels stamp two HIP events with their own start and end times
+(hc_opts_t.step_events in kernel-stamp mode, hipExtLaunchKernel): the same
+durations a kernel trace reports.  That pass launches through the event
+path, so it is kept out of the headline time.
 """
 from __future__ import annotations
 
@@ -99,7 +100,8 @@ def median(xs):
 
 def roofline_obj(kernel: str, alg_bytes: int, ms: float, traffic=None, duration: str | None = None):
     """The dominant kernel against MI355X's HBM peak: algorithmic bytes per
-    launch over the launch's duration (HIP events on its stream)."""
+    launch over the launch's duration (HIP events on its stream, stamped by
+    the kernel's own start and end where a step-event pass measures it)."""
     gbps = alg_bytes / (ms / 1e3) / 1e9
     d = {"bound": "hbm", "kernel": kernel, "achieved": round(gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
          "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": traffic, "alg_bytes_per_launch": int(alg_bytes),
@@ -150,11 +152,9 @@ def bench_ring(args, workload: str):
     for _ in range(args.warmup):
         hc.hc_allreduce(send, recv)
     ms = timed_ms(lambda: hc.hc_allreduce(send, recv), args.steps)
-    # Per-kernel durations: the same steps again with an event at every ring
-    # step boundary.  Each event record on the stream costs a few us between
-    # dependent kernels, so this pass is kept out of the headline time.
-    evsets = [hc.StepEvents([torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)])
-              for _ in range(args.steps)]
+    # Per-kernel durations: the same calls again, every step's kernels
+    # stamping their own start and end (kept out of the headline time).
+    evsets = [hc.StepEvents.for_steps(steps, mode=1) for _ in range(args.steps)]
     for k in range(args.steps):
         hc.hc_allreduce(send, recv, step_events=evsets[k])
     torch.cuda.synchronize()
@@ -197,7 +197,8 @@ def bench_ring(args, workload: str):
         "roofline": {"bound": "hbm", "kernel": "step_kernel<reduce> (one reduce-scatter step)",
                      "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic, "alg_bytes_per_launch": red_launch_bytes},
+                     "traffic": traffic, "alg_bytes_per_launch": red_launch_bytes, "launch_ms": round(avg_red, 6),
+                     "duration": "mean reduce-scatter step by its kernel's start and end stamps (HIP events)"},
     }
     if not args.no_cpu_baseline and workload == "ring_bf16":
         line["cpu_baseline"] = cpu_baseline_ring(R, args.cpu_sample)
@@ -233,8 +234,7 @@ def bench_ring_carry(args):
     ms = timed_ms(lambda: hc.hc_allreduce_bf16_f32carry(send, recv, n, ws), args.steps)
     ms_hop = timed_ms(lambda: hc.hc_allreduce(send, hop), args.steps)
     steps = hc.hc_step_count(hc.HC_OP_ALLREDUCE_F32_CARRY, R)
-    evsets = [hc.StepEvents([torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)])
-              for _ in range(args.steps)]
+    evsets = [hc.StepEvents.for_steps(steps, mode=1) for _ in range(args.steps)]
     for k in range(args.steps):
         hc.hc_allreduce_bf16_f32carry(send, recv, n, ws, step_events=evsets[k])
     torch.cuda.synchronize()
@@ -294,8 +294,8 @@ def bench_ring_carry(args):
         "copy_ms": round(avg(cpy), 6),
         "error_vs_exact": {"f32_carry": ulp_err(recv[0]), "per_hop": ulp_err(hop[0])},
         "roofline": roofline_obj("carry_kernel<fp32 in, fp32 out> (a middle reduce-scatter step)", mid_bytes,
-                                 avg(mid), None, "mean middle reduce-scatter step by HIP events at the step "
-                                                 "boundaries"),
+                                 avg(mid), None, "mean middle reduce-scatter step by its kernel's start and "
+                                                 "end stamps (HIP events)"),
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -529,12 +529,11 @@ def bench_compressed(args):
         hc.hc_compressed_allreduce(send, recv, n, ws)
     ms = timed_ms(lambda: hc.hc_compressed_allreduce(send, recv, n, ws), args.steps)
     # Untimed: the wire byte count (one device atomic per record) and the
-    # per-step breakdown (an event at every step boundary).
+    # per-step breakdown (each step's kernel stamps its start and end).
     hc.hc_compressed_allreduce(send, recv, n, ws, wire)
     torch.cuda.synchronize()
     wire_bytes = int(wire.item())
-    evsets = [hc.StepEvents([torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)])
-              for _ in range(args.steps)]
+    evsets = [hc.StepEvents.for_steps(steps, mode=1) for _ in range(args.steps)]
     for k in range(args.steps):
         hc.hc_compressed_allreduce(send, recv, n, ws, step_events=evsets[k])
     torch.cuda.synchronize()
@@ -559,8 +558,8 @@ def bench_compressed(args):
     rec_hop = rec_bytes / (2 * (R - 1))           # records moved by one hop, all ranks
     extra = {"roofline": roofline_obj("car_rs_kernel (one reduce-scatter hop: decode, hop, encode)",
                                       int(2 * n + 2 * rec_hop), rs_ms, None,
-                                      "mean reduce-scatter step by HIP events at the step boundaries "
-                                      "(the last step also writes the output)")}
+                                      "mean reduce-scatter step by its kernel's start and end stamps "
+                                      "(HIP events; the last step also writes the output)")}
     if not args.no_cpu_baseline:
         import oracle
 
@@ -611,8 +610,7 @@ def bench_fused_sgd(args):
     ms = timed_ms(fused, args.steps)
     ms_unfused = timed_ms(unfused, args.steps)
     steps = hc.hc_step_count(hc.HC_OP_ALLREDUCE, R)
-    evsets = [hc.StepEvents([torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)])
-              for _ in range(args.steps)]
+    evsets = [hc.StepEvents.for_steps(steps, mode=1) for _ in range(args.steps)]
     for k in range(args.steps):
         hc.hc_allreduce_sgd(grads, weights, lr, step_events=evsets[k])
     torch.cuda.synchronize()
@@ -624,7 +622,7 @@ def bench_fused_sgd(args):
     alg_unfused = 2 * n * (3 * (R - 1) + 2 * (R - 1)) + 2 * n * R * 3
     last_ms = sum(last) / len(last)
     extra = {"roofline": roofline_obj("step_kernel<2,sgd-send> (the last reduce-scatter step with the update)", 10 * n,
-                                      last_ms, None, "HIP events at the step boundaries")}
+                                      last_ms, None, "the step's kernel start and end stamps (HIP events)")}
     if not args.no_cpu_baseline:
         import oracle
 

@@ -57,7 +57,7 @@ class HcError(RuntimeError):
 class hc_opts_t(ctypes.Structure):
     _fields_ = [("chunk_fraction", ctypes.c_double), ("cu_budget", ctypes.c_int32),
                 ("n_step_events", ctypes.c_int32), ("step_events", ctypes.c_void_p),
-                ("copy_engine", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("copy_engine", ctypes.c_int32), ("step_event_mode", ctypes.c_int32)]
 
 
 class hc_task_t(ctypes.Structure):
@@ -145,17 +145,31 @@ def _stream_handle(stream) -> int:
 
 
 class StepEvents:
-    """Caller-owned HIP events for hc_opts_t.step_events (see include/hc.h).
-    ``handles`` are the raw hipEvent_t values of torch.cuda.Event objects."""
+    """Caller-owned HIP events for hc_opts_t.step_events (see include/hc.h):
+    timing-enabled torch.cuda.Event objects, whose raw hipEvent_t handles the
+    call records.  ``mode`` 0 records one event at every step boundary
+    (steps + 1 events); mode 1 has each step's kernels stamp two events with
+    their own start and end (2 * steps events)."""
 
-    def __init__(self, events):
+    def __init__(self, events, mode: int = 0):
         self.events = list(events)
+        self.mode = int(mode)
         for e in self.events:
             e.record()  # makes torch create the underlying hipEvent_t
         self._arr = (ctypes.c_void_p * len(self.events))(*[e.cuda_event for e in self.events])
 
+    @classmethod
+    def for_steps(cls, steps: int, mode: int = 0):
+        n = 2 * steps if mode == 1 else steps + 1
+        return cls([torch.cuda.Event(enable_timing=True) for _ in range(n)], mode)
+
     def elapsed_ms(self):
-        return [self.events[k].elapsed_time(self.events[k + 1]) for k in range(len(self.events) - 1)]
+        """Per-step durations in ms: between boundaries (mode 0), or each
+        step's own start-to-end stamps (mode 1)."""
+        ev = self.events
+        if self.mode == 1:
+            return [ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(len(ev) // 2)]
+        return [ev[k].elapsed_time(ev[k + 1]) for k in range(len(ev) - 1)]
 
 
 def _opts(chunk_fraction: float = 0.0, cu_budget: int = 0, step_events: StepEvents | None = None,
@@ -166,6 +180,7 @@ def _opts(chunk_fraction: float = 0.0, cu_budget: int = 0, step_events: StepEven
     if step_events is not None:
         o.n_step_events = len(step_events.events)
         o.step_events = ctypes.cast(step_events._arr, ctypes.c_void_p)
+        o.step_event_mode = step_events.mode
     return ctypes.pointer(o)
 
 

@@ -676,19 +676,13 @@ size_t compressed_ar_ws_bytes(size_t count, int R) {
 }
 
 hipError_t launch_compressed_allreduce(void* const* send, void* const* recv, size_t count, int R, size_t chunk,
-                                       void* ws, uint64_t* wire_bytes, hipEvent_t* events, int n_events,
-                                       hipStream_t stream) {
-  int k_event = 0;
-  auto mark = [&]() -> hipError_t {
-    if (!events || k_event >= n_events) return hipSuccess;
-    return hipEventRecord(events[k_event++], stream);
-  };
+                                       void* ws, uint64_t* wire_bytes, Tap& tap, hipStream_t stream) {
+  auto mark = [&]() -> hipError_t { return tap.mark(stream); };
   if (count == 0) {
     if (wire_bytes) hipLaunchKernelGGL(set_u64_kernel, dim3(1), dim3(1), 0, stream, wire_bytes, (uint64_t)0);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) e = mark();
-    if (e == hipSuccess) e = mark();
-    return e;
+    return e == hipSuccess ? tap.finish(stream) : e;   // every step empty
   }
   const size_t L = ceil_div(count, (size_t)R);
   const size_t nbs = ceil_div(L, kB);
@@ -736,19 +730,22 @@ hipError_t launch_compressed_allreduce(void* const* send, void* const* recv, siz
   const dim3 grid((uint32_t)(R * nbs)), block(kCT);
   hipError_t e = mark();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(car_first_kernel, grid, block, 0, stream, ptr, g);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  void* first_args[] = {&ptr, &g};
+  if ((e = launch_kernel((const void*)car_first_kernel, grid, block, first_args, stream)) != hipSuccess) return e;
+  uint32_t step = 0, buf = 0;
+  void* rs_args[] = {&ptr, &g, &step};
   for (int s = 0; s + 1 < R; ++s) {
     if ((e = mark()) != hipSuccess) return e;
-    hipLaunchKernelGGL(car_rs_kernel, grid, block, 0, stream, ptr, g, (uint32_t)s);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    step = (uint32_t)s;   // the launch copies the argument values
+    if ((e = launch_kernel((const void*)car_rs_kernel, grid, block, rs_args, stream)) != hipSuccess) return e;
   }
   // After reduce-scatter step R-2 the finished slice's record is in buffer (R-1)&1.
-  uint32_t buf = (uint32_t)((R - 1) & 1);
+  buf = (uint32_t)((R - 1) & 1);
+  void* ag_args[] = {&ptr, &g, &step, &buf};
   for (int s = 0; s + 1 < R; ++s) {
     if ((e = mark()) != hipSuccess) return e;
-    hipLaunchKernelGGL(car_ag_kernel, grid, block, 0, stream, ptr, g, (uint32_t)s, buf);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    step = (uint32_t)s;
+    if ((e = launch_kernel((const void*)car_ag_kernel, grid, block, ag_args, stream)) != hipSuccess) return e;
     buf ^= 1u;
   }
   return mark();

@@ -17,9 +17,95 @@
 #include "launch.hpp"
 #include "schedule.hpp"
 
+#include <hip/hip_ext.h>
+
 extern "C" int hc_step_count(hc_op_t op, int nranks);
 
+namespace hc {
+
 namespace {
+
+// The open mode-1 step of this thread: its two events, and whether a kernel
+// (or host work) has stamped its start and a kernel its end.
+struct Stamp {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool started = false, stopped = false, host = false;
+};
+thread_local Stamp t_stamp;
+
+hipError_t close_stamp(hipStream_t stream) {
+  const Stamp s = t_stamp;
+  t_stamp = Stamp{};
+  hipError_t e = hipSuccess;
+  if (!s.started) e = hipEventRecord(s.start, stream);
+  if (e == hipSuccess && (!s.stopped || s.host)) e = hipEventRecord(s.stop, stream);
+  return e;
+}
+
+}  // namespace
+
+hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, hipStream_t stream) {
+  Stamp& s = t_stamp;
+  if (!s.stop) return hipLaunchKernel(fn, grid, block, args, 0, stream);
+  hipEvent_t start = s.started ? nullptr : s.start;
+  s.started = s.stopped = true;
+  return hipExtLaunchKernel(fn, grid, block, args, 0, stream, start, s.stop, 0);
+}
+
+hipError_t stamp_host_work(hipStream_t stream) {
+  Stamp& s = t_stamp;
+  if (!s.stop) return hipSuccess;
+  s.host = true;
+  if (s.started) return hipSuccess;
+  s.started = true;
+  return hipEventRecord(s.start, stream);
+}
+
+hipError_t Tap::mark(hipStream_t s) {
+  if (!ev) return hipSuccess;
+  if (!stream) stream = s;
+  if (mode == 0) return k < n ? hipEventRecord(ev[k++], s) : hipSuccess;
+  hipError_t e = hipSuccess;
+  if (open) {
+    open = false;
+    e = close_stamp(s);
+  }
+  if (e == hipSuccess && k < steps) {
+    t_stamp = Stamp{ev[2 * k], ev[2 * k + 1]};
+    open = true;
+    ++k;
+  }
+  return e;
+}
+
+hipError_t Tap::finish(hipStream_t s) {
+  if (!ev) return hipSuccess;
+  hipError_t e = hipSuccess;
+  if (mode == 0) {
+    while (e == hipSuccess && k <= steps) e = hipEventRecord(ev[k++], s);
+    return e;
+  }
+  if (open) {
+    open = false;
+    e = close_stamp(s);
+  }
+  for (; e == hipSuccess && k < steps; ++k) {
+    e = hipEventRecord(ev[2 * k], s);
+    if (e == hipSuccess) e = hipEventRecord(ev[2 * k + 1], s);
+  }
+  return e;
+}
+
+Tap::~Tap() {
+  if (stream) (void)finish(stream);
+  if (open) t_stamp = Stamp{};
+}
+
+}  // namespace hc
+
+namespace {
+
+using hc::Tap;
 
 thread_local std::string g_last_error;
 
@@ -59,28 +145,22 @@ hc_status_t check_common(int nranks, hc_dtype_t dtype, const hc_opts_t* opts) {
     if (opts->n_step_events < 0) return fail(HC_ERR_INVALID_ARGUMENT, "n_step_events < 0");
     if (opts->copy_engine != 0 && opts->copy_engine != 1)
       return fail(HC_ERR_INVALID_ARGUMENT, "copy_engine %d is neither 0 nor 1", opts->copy_engine);
-    if (opts->reserved != 0) return fail(HC_ERR_INVALID_ARGUMENT, "reserved option field is not 0");
+    if (opts->step_event_mode != 0 && opts->step_event_mode != 1)
+      return fail(HC_ERR_INVALID_ARGUMENT, "step_event_mode %d is neither 0 nor 1", opts->step_event_mode);
   }
   return HC_SUCCESS;
 }
 
-// Records the caller's step events (hc_opts_t.step_events), if any.
-struct Tap {
-  hipEvent_t* ev = nullptr;
-  int n = 0, k = 0;
-  hipError_t mark(hipStream_t stream) {
-    if (!ev || k >= n) return hipSuccess;
-    return hipEventRecord(ev[k++], stream);
-  }
-};
-
 hc_status_t make_tap(const hc_opts_t* o, hc_op_t op, int nranks, Tap* tap) {
   if (!o || !o->step_events) return HC_SUCCESS;
   const int steps = hc_step_count(op, nranks);
-  if (o->n_step_events < steps + 1)
-    return fail(HC_ERR_INVALID_ARGUMENT, "n_step_events %d < %d", o->n_step_events, steps + 1);
+  const int need = o->step_event_mode == 1 ? 2 * steps : steps + 1;
+  if (o->n_step_events < need)
+    return fail(HC_ERR_INVALID_ARGUMENT, "n_step_events %d < %d", o->n_step_events, need);
   tap->ev = o->step_events;
   tap->n = o->n_step_events;
+  tap->mode = o->step_event_mode;
+  tap->steps = steps;
   return HC_SUCCESS;
 }
 
@@ -94,6 +174,7 @@ bool copy_engine(const hc_opts_t* o) { return o && o->copy_engine == 1; }
 // one DMA copy per segment on the copy engines (stream ordered).
 hipError_t copy_step(const hc::Seg* segs, int nseg, size_t es, int budget, bool dma, hipStream_t stream) {
   if (!dma) return hc::launch_copy_step(segs, nseg, es, budget, stream);
+  if (hipError_t e = hc::stamp_host_work(stream); e != hipSuccess) return e;
   for (int i = 0; i < nseg; ++i) {
     if (segs[i].len == 0) continue;
     hipError_t e = hipMemcpyAsync(segs[i].dst, segs[i].a, segs[i].len * es, hipMemcpyDeviceToDeviceNoCU, stream);
@@ -742,7 +823,8 @@ hc_status_t hc_compressed_allreduce(void* const* sendbufs, void* const* recvbufs
   if ((st = make_tap(opts, HC_OP_COMPRESSED_ALLREDUCE, nranks, &tap))) return st;
   const size_t chunk = hc::chunk_elems(count, chunk_fraction(opts), HC_BLOCK_ELEMS);
   hipError_t e = hc::launch_compressed_allreduce(sendbufs, recvbufs, count, nranks, chunk, d_ws,
-                                                 d_wire_bytes, tap.ev, tap.n, stream);
+                                                 d_wire_bytes, tap, stream);
+  if (e == hipSuccess) e = tap.finish(stream);
   if (e == hipErrorNotSupported) return fail(HC_ERR_UNSUPPORTED, "compressed allreduce not built");
   return e == hipSuccess ? HC_SUCCESS : device_fail(e, "compressed allreduce launch");
 }

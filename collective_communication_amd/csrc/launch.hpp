@@ -21,6 +21,38 @@ struct Seg {
 };
 
 constexpr int kMaxSegs = 64;
+
+// The caller's step events (hc_opts_t.step_events) of one call.  Mode 0
+// records one event on the stream at every step boundary.  Mode 1 gives each
+// step two events that its kernels stamp themselves: the step's first kernel
+// stamps ev[2k] with its start time and every kernel of the step stamps
+// ev[2k+1] with its end time, so that an interval is the kernels' own
+// execution, as a kernel trace measures it, without the gaps between
+// launches.  A step that launches no kernel records both events on the
+// stream around whatever it enqueues (copy-engine copies, or nothing).
+struct Tap {
+  hipEvent_t* ev = nullptr;
+  int n = 0, k = 0, mode = 0, steps = 0;
+  bool open = false;
+  hipStream_t stream = nullptr;   // of the first mark
+  // At the start of every step and once after the last: mode 0 records the
+  // next boundary event; mode 1 closes the open step and opens the next.
+  hipError_t mark(hipStream_t s);
+  // Records every event not recorded yet (steps that had no work, at the
+  // end); the destructor calls it too, so that every event of a call that
+  // marked a step ends up recorded.
+  hipError_t finish(hipStream_t s);
+  ~Tap();
+};
+
+// Launches a ring-step kernel (all of them go through here): a plain
+// hipLaunchKernel, or, while a mode-1 step is open on this thread,
+// hipExtLaunchKernel with the step's start and end events.
+hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, hipStream_t stream);
+// Tells an open mode-1 step that work other than a kernel (copy-engine
+// copies) follows: its start event is recorded on the stream now and its
+// end event when the step closes.
+hipError_t stamp_host_work(hipStream_t stream);
 constexpr int kWgPerCuBudget = 8;   // workgroups per CU of a CU-budget grid
 
 hipError_t launch_reduce_step(const Seg* segs, int nseg, hc_dtype_t dtype, int cu_budget,
@@ -77,9 +109,9 @@ hipError_t launch_compress_scoped(const uint16_t* in, size_t n, void* out, uint6
 
 // Compressed ring allreduce (bf16).
 size_t compressed_ar_ws_bytes(size_t count, int R);
-// events: optional step events (n of them, >= 2R when R > 1, else >= 2).
+// tap: the call's step events (marked once per step and after the last).
 hipError_t launch_compressed_allreduce(void* const* send, void* const* recv, size_t count, int R,
-                                       size_t chunk, void* ws, uint64_t* wire_bytes,
-                                       hipEvent_t* events, int n_events, hipStream_t stream);
+                                       size_t chunk, void* ws, uint64_t* wire_bytes, Tap& tap,
+                                       hipStream_t stream);
 
 }  // namespace hc

@@ -330,9 +330,9 @@ hipError_t launch_carry(const Seg* segs, int nseg, int cu_budget, hipStream_t st
     const uint64_t cap = (uint64_t)cu_budget * kWgPerCuBudget;
     if (grid > cap) grid = (uint32_t)cap;
   }
-  if (vec) hipLaunchKernelGGL((carry_kernel<AF, DF, true>), dim3(grid), dim3(kThreads), 0, stream, args);
-  else hipLaunchKernelGGL((carry_kernel<AF, DF, false>), dim3(grid), dim3(kThreads), 0, stream, args);
-  return hipGetLastError();
+  void* kargs[] = {&args};
+  return launch_kernel(vec ? (const void*)carry_kernel<AF, DF, true> : (const void*)carry_kernel<AF, DF, false>,
+                       dim3(grid), dim3(kThreads), kargs, stream);
 }
 
 template <int ES, int OP>
@@ -370,9 +370,9 @@ hipError_t launch_step(const Seg* segs, int nseg, int cu_budget, hipStream_t str
     const uint64_t cap = (uint64_t)cu_budget * kWgPerCuBudget;
     if (grid > cap) grid = (uint32_t)cap;
   }
-  if (vec) hipLaunchKernelGGL((step_kernel<ES, OP, true>), dim3(grid), dim3(kThreads), 0, stream, args);
-  else hipLaunchKernelGGL((step_kernel<ES, OP, false>), dim3(grid), dim3(kThreads), 0, stream, args);
-  return hipGetLastError();
+  void* kargs[] = {&args};
+  return launch_kernel(vec ? (const void*)step_kernel<ES, OP, true> : (const void*)step_kernel<ES, OP, false>,
+                       dim3(grid), dim3(kThreads), kargs, stream);
 }
 
 }  // namespace

@@ -75,11 +75,21 @@ typedef enum { HC_F32 = 0, HC_BF16 = 1 } hc_dtype_t;
  *     grid sized for k compute units (pair it with a stream from
  *     hc_stream_create_cu_budget(k)).
  *   step_events / n_step_events: optional timing hook.  When step_events is
- *     not NULL it holds n_step_events caller-created HIP events; the call
- *     records step_events[k] on its stream right before ring step k and
- *     step_events[steps] after the last step, where steps =
- *     hc_step_count(op, nranks).  n_step_events < steps + 1 is
- *     HC_ERR_INVALID_ARGUMENT.  NULL records nothing.
+ *     not NULL it holds n_step_events caller-created HIP events (created
+ *     with timing enabled), used as step_event_mode says, with steps =
+ *     hc_step_count(op, nranks).  Too few events is HC_ERR_INVALID_ARGUMENT.
+ *     NULL records nothing; so does a call with nothing to do (count 0).
+ *   step_event_mode: 0 = boundaries: step_events[k] is recorded on the stream
+ *     right before ring step k and step_events[steps] after the last step
+ *     (steps + 1 events), so an interval also holds the gap between two
+ *     launches.  1 = kernel stamps (2 * steps events): step k's first kernel
+ *     stamps step_events[2k] with its start time and its kernels stamp
+ *     step_events[2k+1] with their end time (hipExtLaunchKernel), so an
+ *     interval is the step's kernel execution as a kernel trace reports it.
+ *     A step that runs no kernel (copy-engine copies; the all-gather step
+ *     that the last reduce-scatter step already did) records both events on
+ *     the stream around what it enqueues.  Other values are
+ *     HC_ERR_INVALID_ARGUMENT.
  *   copy_engine: 0 = all-gather copy steps run as copy kernels on the
  *     compute units; 1 = they run on the GPU's DMA copy engines
  *     (hipMemcpyAsync of kind hipMemcpyDeviceToDeviceNoCU, stream ordered,
@@ -95,15 +105,14 @@ typedef enum { HC_F32 = 0, HC_BF16 = 1 } hc_dtype_t;
  *     in /opt/rocm uses the DMA engines (about 60 GB/s per copy, one copy at
  *     a time per stream), while the runtime bundled with the PyTorch 2.10
  *     wheel runs the same calls as blit kernels on the compute units.  The
- *     values are identical either way.
- *   reserved: must be 0. */
+ *     values are identical either way. */
 typedef struct {
     double chunk_fraction;
     int32_t cu_budget;
     int32_t n_step_events;
     hipEvent_t *step_events;
     int32_t copy_engine;
-    int32_t reserved;
+    int32_t step_event_mode;
 } hc_opts_t;
 
 /*

@@ -119,12 +119,18 @@ def test_argument_errors_before_any_launch(hc):
     evs = (ctypes.c_void_p * 2)(0x10, 0x20)
     o = hc.hc_opts_t(0.0, 0, 2, ctypes.cast(evs, ctypes.c_void_p))
     assert L.hc_allreduce(good, good2, 16, hc.HC_F32, 2, ctypes.byref(o), None) == E
-    # copy_engine must be 0 or 1, reserved must be 0
+    # kernel-stamped steps need two events per step: 3 serve boundaries, not stamps
+    evs3 = (ctypes.c_void_p * 3)(0x10, 0x20, 0x30)
+    o = hc.hc_opts_t(0.0, 0, 3, ctypes.cast(evs3, ctypes.c_void_p), 0, 1)
+    assert L.hc_allreduce(good, good2, 16, hc.HC_F32, 2, ctypes.byref(o), None) == E
+    assert b"n_step_events 3 < 4" in L.hc_last_error()
+    # copy_engine must be 0 or 1, step_event_mode 0 or 1
     o = hc.hc_opts_t(0.0, 0, 0, None, 2, 0)
     assert L.hc_allreduce(good, good2, 16, hc.HC_F32, 2, ctypes.byref(o), None) == E
     assert b"copy_engine" in L.hc_last_error()
-    o = hc.hc_opts_t(0.0, 0, 0, None, 0, 1)
+    o = hc.hc_opts_t(0.0, 0, 0, None, 0, 2)
     assert L.hc_allreduce(good, good2, 16, hc.HC_F32, 2, ctypes.byref(o), None) == E
+    assert b"step_event_mode" in L.hc_last_error()
     # the compressed allreduce decodes in its all-gather: no copy engine
     o = hc.hc_opts_t(0.0, 0, 0, None, 1, 0)
     assert L.hc_compressed_allreduce(good, good2, 1 << 16, 2, 0x900000, 1 << 30, None, ctypes.byref(o),
