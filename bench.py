@@ -98,6 +98,22 @@ def median(xs):
     return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
 
 
+def hbm_ceiling(operand_bytes: int) -> dict:
+    """Runs the hbm_ceiling tool built next to libhc (streaming add, copy and
+    read kernels at the given operand size) and returns its JSON object, or
+    {"error": ...}."""
+    from collective_communication_amd import binding as hc
+
+    tool = os.path.join(os.path.dirname(hc.LIB_PATH), "hbm_ceiling")
+    try:
+        r = subprocess.run([tool, str(operand_bytes >> 20)], capture_output=True, text=True, timeout=120)
+        if r.returncode != 0:
+            return {"error": r.stderr[-2000:]}
+        return json.loads(r.stdout.strip().splitlines()[-1])
+    except (OSError, ValueError, subprocess.TimeoutExpired) as exc:
+        return {"error": repr(exc)}
+
+
 def roofline_obj(kernel: str, alg_bytes: int, ms: float, traffic=None, duration: str | None = None):
     """The dominant kernel against MI355X's HBM peak: algorithmic bytes per
     launch over the launch's duration (HIP events on its stream, stamped by
@@ -200,6 +216,16 @@ def bench_ring(args, workload: str):
                      "traffic": traffic, "alg_bytes_per_launch": red_launch_bytes, "launch_ms": round(avg_red, 6),
                      "duration": "mean reduce-scatter step by its kernel's start and end stamps (HIP events)"},
     }
+    if workload == "ring_bf16":
+        # What a plain streaming kernel with the reduce hop's traffic (two
+        # reads, one write of 128 MiB operands, the same tiling) reaches on
+        # this GPU, measured in a process of its own: the practical ceiling
+        # the hop is held against next to the published peak.
+        ceil = hbm_ceiling(n * es)
+        line["hbm_ceiling"] = ceil
+        if "add" in ceil:
+            line["roofline"]["practical_ceiling_gbps"] = ceil["add"]["gbps"]
+            line["roofline"]["frac_of_practical_ceiling"] = round(achieved / ceil["add"]["gbps"], 4)
     if not args.no_cpu_baseline and workload == "ring_bf16":
         line["cpu_baseline"] = cpu_baseline_ring(R, args.cpu_sample)
     elif not args.no_cpu_baseline:

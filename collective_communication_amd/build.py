@@ -22,6 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhc.so")
 DMA_TOOL = os.path.join(PKG, "dma_contention")
+CEILING_TOOL = os.path.join(PKG, "hbm_ceiling")
 ARCH = os.environ.get("HC_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -60,8 +61,14 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"dma_contention build failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, DMA_TOOL)
+    tmp = CEILING_TOOL + ".tmp"
+    cmd = [HIPCC, *COMMON, *DEVICE, "-x", "hip", os.path.join(PKG, "hbm_ceiling.hip"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hbm_ceiling build failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, CEILING_TOOL)
     if verbose:
-        print(f"built {LIB} and {DMA_TOOL}")
+        print(f"built {LIB}, {DMA_TOOL} and {CEILING_TOOL}")
     return LIB
 
 

@@ -196,3 +196,17 @@ def test_all_gather_copy_engine_under_system_runtime():
     assert line["mismatched_words"] == 0, line
     assert line["no_compute_units"] is True, line
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+def test_hbm_ceiling_tool():
+    """The streaming-ceiling tool (the bar the reduce hop is held against next
+    to the published peak) runs and reports every mix with its bytes."""
+    tool = os.path.join(os.path.dirname(hc.LIB_PATH), "hbm_ceiling")
+    assert os.path.exists(tool), "hbm_ceiling is not built"
+    r = subprocess.run([tool, "64", "3"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["operand_bytes"] == 64 << 20
+    for mix, ops in (("add", 3), ("copy", 2), ("read", 2)):
+        assert line[mix]["bytes"] == ops * (64 << 20) and line[mix]["gbps"] > 0 and line[mix]["us"] > 0, line
+    assert subprocess.run([tool, "0"], capture_output=True, timeout=60).returncode == 2
