@@ -1,15 +1,15 @@
 // codec_kernels.hip -- HCZ1 compress / decompress and the fused compressed
 // ring allreduce, for gfx950.
 //
-// compress: one workgroup per 32 KB block, blocks taken in order from an
-// atomic ticket.  A block publishes its record size as soon as it has chosen
-// its code length, then encodes into LDS, then looks back over its
-// predecessors' published sizes for its byte offset (a decoupled look-back
-// scan) and writes the record straight into the final stream: one read of
-// the input, one write of the output, no temporary buffers and no coalescing
-// pass ("CCCL: In-GPU Compression-Coupled Collective Communication", section
-// 4.4).  The look-back waits only on blocks that took earlier tickets, which
-// are already resident, and every wait is bounded.
+// compress: one workgroup per 32 KB block, block = workgroup index.  A block
+// publishes its record size as soon as it has chosen its code length, then
+// encodes into LDS, then looks back over its predecessors' published sizes
+// for its byte offset (a decoupled look-back scan) and writes the record
+// straight into the final stream: one read of the input, one write of the
+// output, no temporary buffers and no coalescing pass ("CCCL: In-GPU
+// Compression-Coupled Collective Communication", section 4.4).  The
+// look-back waits only on lower-indexed blocks, and every wait is bounded
+// (lookback.hpp says why the waits end).
 //
 // decompress: one workgroup per block; every block validates the stream
 // header and its own record before it reads it; reads never leave in_bytes.
@@ -90,14 +90,13 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
     CompressWs* __restrict__ ws, uint32_t nb, ScopeWs sc, uint32_t group) {
   __shared__ Smem s;
   const int t = threadIdx.x;
-  if (t == 0) s.plan[6] = atomicAdd(&ws->ticket, 1u);
-  if constexpr (!SCOPED) zero_hist(s);  // while the ticket is on its way
-  __syncthreads();
-  const uint32_t bid = s.plan[6];
+  const uint32_t bid = blockIdx.x;
   const uint64_t first = (uint64_t)bid * kB;
   const uint32_t m = (uint32_t)((n - first) < kB ? (n - first) : kB);
   uint4 v[kPer];
   load_block(in + first, m, v);
+  if constexpr (!SCOPED) zero_hist(s);  // while the block is on its way
+  __syncthreads();
   Plan p;
   if constexpr (SCOPED) {
     const uint32_t g = bid / group;  // only read for full blocks

@@ -18,7 +18,7 @@
 // within a step.  So no per-lane offsets are stored, and each lane pads only
 // its last word.
 //
-// compress: one workgroup of 512 threads per block, blocks in ticket order,
+// compress: one workgroup of 512 threads per block, block = workgroup index,
 // the record published and placed by the decoupled look-back of the
 // fixed-length encoder (one read of the input, one write of the output).
 // After the histogram, one thread builds the Huffman lengths (two queues over
@@ -300,14 +300,13 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
     CompressWs* __restrict__ ws, uint32_t nb) {
   __shared__ HceEncSmem s;
   const uint32_t t = threadIdx.x, lane = t & 63u, seg = t >> 6;
-  if (t == 0) s.plan[6] = atomicAdd(&ws->ticket, 1u);
-  zero_hist(s);  // while the ticket is on its way
-  __syncthreads();
-  const uint32_t bid = s.plan[6];
+  const uint32_t bid = blockIdx.x;
   const uint64_t first = (uint64_t)bid * kB;
   const uint32_t m = (uint32_t)((n - first) < kB ? (n - first) : kB);
   uint4 v[kPer];
   load_lane_steps(in + first, m, seg, lane, v);
+  zero_hist(s);  // while the block is on its way
+  __syncthreads();
   uint32_t mode = 0, n_sym = 0, n_words = 0, rec_bytes = raw_bytes(m);
   uint32_t codes[16];   // step i's code bits (low 12) and length (high 4), two per word
   uint32_t cum_start = 0, base = 0;

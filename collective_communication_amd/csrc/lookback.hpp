@@ -1,12 +1,25 @@
 // lookback.hpp -- the single-pass stream writer shared by the codecs.
 //
-// Blocks take tickets in order; each publishes the size of its record as soon
-// as it knows it, then finds the record's byte offset by a decoupled look-back
-// over the descriptors of the blocks before it, and writes the record straight
-// into the final stream ("CCCL: In-GPU Compression-Coupled Collective
-// Communication", section 4.4: one write round, no coalescing pass).  The
-// look-back waits only on blocks that took earlier tickets, which are already
-// resident, and every wait is bounded.
+// Block j of the stream is workgroup j.  Each block publishes the size of its
+// record as soon as it knows it, then finds the record's byte offset by a
+// decoupled look-back over the descriptors of the blocks before it, and
+// writes the record straight into the final stream ("CCCL: In-GPU
+// Compression-Coupled Collective Communication", section 4.4: one write
+// round, no coalescing pass).
+//
+// Why the waits end.  A block waits only on lower-indexed blocks.  The
+// dispatcher of each XCD starts the workgroups it is given in increasing
+// index order.  So every workgroup that holds a slot on the XCD of the
+// lowest-indexed unfinished workgroup has a lower index, has therefore
+// finished, and has left a slot free: that workgroup starts, waits on
+// nothing unfinished, and finishes; by induction all do.  That order is how
+// the hardware dispatches, not a promise of the programming model, so every
+// wait is also bounded: a walk that polls an
+// unpublished descriptor kSpinLimit times sets the error word and gives up,
+// and the call then reports no stream (its byte count is 0) instead of
+// hanging.  An earlier design took an atomic ticket per block to make the
+// order explicit; its round trip before each block's first load cost 23 us of
+// a 269 us call on 2^28 elements, and no walk has timed out without it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,10 +36,10 @@ constexpr uint64_t kFlagIncl = 2ull << 62;    // descriptor holds the size of bl
 constexpr uint64_t kValueMask = (1ull << 62) - 1;
 constexpr uint32_t kSpinLimit = 1u << 22;
 
-// Workspace of a stream encoder: a ticket counter, an error word, then one
+// Workspace of a stream encoder: a spare word, an error word, then one
 // 64-bit look-back descriptor per block (all zero before the launch).
 struct CompressWs {
-  uint32_t ticket;
+  uint32_t spare;
   uint32_t error;
   uint32_t pad[14];
   uint64_t desc[1];
