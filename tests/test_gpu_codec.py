@@ -135,3 +135,34 @@ def test_codec_weights_full_size():
     n = 1 << 28
     v = inputs.host_bits(inputs.normal_bf16_cuda("codec", 0, n, 0.02))
     check_roundtrip(v, "weights 2^28")
+
+
+def test_back_to_back_calls_place_every_record():
+    """Block j is workgroup j and its look-back waits only on lower-indexed
+    blocks: 200 back-to-back calls on 2^24 elements (1,024 blocks, more than
+    fit on the GPU at once), on two encoders sharing the writer, each give the
+    full stream (a look-back that gave up would report 0 bytes) with the same
+    bytes as the oracle's."""
+    n = 1 << 24
+    g = np.random.default_rng(2024)
+    v = inputs.f32_to_bf16_bits((g.standard_normal(n) * 0.02).astype(np.float32))
+    ref = np.frombuffer(oracle.compress(v), np.uint8)
+    d_in = to_dev(v)
+    cap = hc.hc_compress_bound_bf16(n)
+    out = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_COMPRESS, n, 1), dtype=torch.uint8, device="cuda")
+    sizes = torch.zeros(200, dtype=torch.int64, device="cuda")
+    for k in range(200):
+        hc.hc_compress_bf16(d_in, n, out, sizes[k:k + 1], ws)
+    torch.cuda.synchronize()
+    assert torch.all(sizes == ref.size).item(), sizes.unique().tolist()
+    assert np.array_equal(to_host(out)[:ref.size], ref)
+    hsizes = torch.zeros(100, dtype=torch.int64, device="cuda")
+    hws = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_COMPRESS_ENTROPY, n, 1), dtype=torch.uint8, device="cuda")
+    hout = torch.empty(hc.hc_compress_bound_bf16(n), dtype=torch.uint8, device="cuda")
+    for k in range(100):
+        hc.hc_compress_bf16_entropy(d_in, n, hout, hsizes[k:k + 1], hws)
+    torch.cuda.synchronize()
+    href = np.frombuffer(oracle.hce_compress(v), np.uint8)
+    assert torch.all(hsizes == href.size).item(), hsizes.unique().tolist()
+    assert np.array_equal(to_host(hout)[:href.size], href)
