@@ -428,6 +428,7 @@ const char* hc_status_string(hc_status_t s) {
     case HC_ERR_INSUFFICIENT_CAPACITY: return "insufficient capacity";
     case HC_ERR_CORRUPT_STREAM: return "corrupt stream";
     case HC_ERR_DEVICE: return "device error";
+    default: break;
   }
   return "unknown status";
 }
@@ -448,6 +449,7 @@ int hc_step_count(hc_op_t op, int nranks) {
     case HC_OP_COMPRESS_SCOPED:
     case HC_OP_COMPRESS_ENTROPY:
     case HC_OP_COMPRESS_STAGED: return -1;
+    default: break;
   }
   return -1;
 }
@@ -562,6 +564,7 @@ hc_status_t hc_allreduce_sgd(void* const* grads, void* const* weights, size_t co
 
 size_t hc_workspace_bytes(hc_op_t op, size_t count, int nranks, hc_dtype_t dtype) {
   if (nranks < 1 || nranks > HC_MAX_RANKS) return 0;
+  if (dtype != HC_F32 && dtype != HC_BF16) return 0;
   switch (op) {
     case HC_OP_REDUCE_SCATTER:
       if (count % (size_t)nranks) return 0;
@@ -583,6 +586,7 @@ size_t hc_workspace_bytes(hc_op_t op, size_t count, int nranks, hc_dtype_t dtype
     case HC_OP_ALLREDUCE:
     case HC_OP_ALL_GATHER:
       return 0;
+    default: break;
   }
   return 0;
 }

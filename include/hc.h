@@ -54,16 +54,28 @@ extern "C" {
 #define HC_BLOCK_ELEMS 16384u        /* codec block: 16384 bf16 = 32 KB */
 #define HC_HCZ1_MAGIC 0x315A4348u    /* "HCZ1" little-endian */
 
+/* Every enum of this header also names the ends of the int32 range (the
+ * *_RANGE_MIN_ / *_RANGE_MAX_ entries, never valid arguments), so that any
+ * 32-bit value a C caller passes is a value of the type in C++ as well: the
+ * library's checks then reject unknown values instead of reading a value the
+ * type cannot hold. */
 typedef enum {
     HC_SUCCESS = 0,
     HC_ERR_INVALID_ARGUMENT = 1,
     HC_ERR_UNSUPPORTED = 2,
     HC_ERR_INSUFFICIENT_CAPACITY = 3,
     HC_ERR_CORRUPT_STREAM = 4,
-    HC_ERR_DEVICE = 5
+    HC_ERR_DEVICE = 5,
+    HC_STATUS_RANGE_MIN_ = INT32_MIN,
+    HC_STATUS_RANGE_MAX_ = INT32_MAX
 } hc_status_t;
 
-typedef enum { HC_F32 = 0, HC_BF16 = 1 } hc_dtype_t;
+typedef enum {
+    HC_F32 = 0,
+    HC_BF16 = 1,
+    HC_DTYPE_RANGE_MIN_ = INT32_MIN,
+    HC_DTYPE_RANGE_MAX_ = INT32_MAX
+} hc_dtype_t;
 
 /* Options.  Pass NULL for the defaults (all fields zero mean default).
  *   chunk_fraction: chunk size as a fraction of the per-rank buffer, default
@@ -378,7 +390,9 @@ typedef enum {
     HC_OP_COMPRESS_SCOPED = 5,
     HC_OP_COMPRESS_ENTROPY = 6,
     HC_OP_COMPRESS_STAGED = 7,
-    HC_OP_ALLREDUCE_F32_CARRY = 8
+    HC_OP_ALLREDUCE_F32_CARRY = 8,
+    HC_OP_RANGE_MIN_ = INT32_MIN,
+    HC_OP_RANGE_MAX_ = INT32_MAX
 } hc_op_t;
 
 /* Workspace bytes for an operation; count = elements per rank buffer
