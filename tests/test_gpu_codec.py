@@ -130,11 +130,18 @@ def test_corrupt_streams_rejected_like_oracle():
     assert st == hc.HC_ERR_CORRUPT_STREAM
 
 
-def test_codec_weights_full_size():
-    """2^28 bf16 weights N(0, 0.02): GPU stream == oracle stream; round trip."""
+@pytest.mark.parametrize("kind", ["weights", "activations", "gradients"])
+def test_codec_full_size(kind):
+    """The codec workload's three 2^28 bf16 tensors (weights N(0, 0.02),
+    activations, gradients N(0, 1e-4)): GPU stream == oracle stream; round trip."""
     n = 1 << 28
-    v = inputs.host_bits(inputs.normal_bf16_cuda("codec", 0, n, 0.02))
-    check_roundtrip(v, "weights 2^28")
+    t = {"weights": lambda: inputs.normal_bf16_cuda("codec", 0, n, 0.02),
+         "activations": lambda: inputs.activation_bf16_cuda("codec", 1, n),
+         "gradients": lambda: inputs.normal_bf16_cuda("codec", 2, n, 1e-4)}[kind]()
+    v = inputs.host_bits(t)
+    del t
+    check_roundtrip(v, f"{kind} 2^28")
+    torch.cuda.empty_cache()
 
 
 def test_back_to_back_calls_place_every_record():

@@ -210,3 +210,40 @@ def test_hbm_ceiling_tool():
     for mix, ops in (("add", 3), ("copy", 2), ("read", 2)):
         assert line[mix]["bytes"] == ops * (64 << 20) and line[mix]["gbps"] > 0 and line[mix]["us"] > 0, line
     assert subprocess.run([tool, "0"], capture_output=True, timeout=60).returncode == 2
+
+
+def test_reduce_scatter_contention_workload_full_size_sampled():
+    """The contention workload's reduce-scatter, R=8 x 2^28 bf16 N(0,1e-3) with
+    1% zeros, on all CUs and on a stream masked to 8 CUs (the persistent
+    grid): every rank's slice at 2^18 sampled elements plus its two ends
+    equals the oracle's fold, and both launches give the same bytes."""
+    R, n = 8, 1 << 28
+    L = n // R
+    send = inputs.ring_inputs_cuda("contention", R, n)
+    ws = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_REDUCE_SCATTER, n, R, hc.HC_BF16), dtype=torch.uint8,
+                     device="cuda")
+    recv = [torch.empty(L, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    hc.hc_reduce_scatter(send, recv, L, ws)
+    torch.cuda.synchronize()
+    handle = hc.hc_stream_create_cu_budget(8)
+    try:
+        side = torch.cuda.ExternalStream(handle)
+        masked = [torch.empty(L, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+        hc.hc_reduce_scatter(send, masked, L, ws, cu_budget=8, stream=side)
+        side.synchronize()
+        del side
+    finally:
+        hc.hc_stream_destroy(handle)
+    for r in range(R):
+        assert torch.equal(masked[r].view(torch.int16), recv[r].view(torch.int16)), f"rank {r}: cu_budget 8 differs"
+    xs = [inputs.host_bits(t) for t in send]
+    del send, masked
+    torch.cuda.empty_cache()
+    g = np.random.default_rng(5)
+    for r in range(R):
+        local = np.unique(np.concatenate([g.integers(0, L, 1 << 18), [0, L - 1]])).astype(np.int64)
+        want = oracle.allreduce_fold_at(xs, (local + r * L).astype(np.uint64))
+        got = to_host(recv[r])[local]
+        assert np.array_equal(got, want), f"rank {r}: {first_mismatch(got, want)}"
+    del recv, ws
+    torch.cuda.empty_cache()
