@@ -29,9 +29,9 @@ def load_into(dev_tensors, host_arrays):
         t.copy_(src.view(t.dtype) if x.dtype == np.uint16 else src)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("op", ["allreduce", "allreduce_sgd", "reduce_scatter", "allreduce_f32carry"])
-def test_captured_collective_replays_match_eager(dtype, op):
+@pytest.mark.parametrize("op,dtype", [(op, dt) for op in ("allreduce", "allreduce_sgd", "reduce_scatter")
+                                       for dt in ("f32", "bf16")] + [("allreduce_f32carry", "bf16")])
+def test_captured_collective_replays_match_eager(op, dtype):
     R, n = 8, 8 * 12345 + 3 if op != "reduce_scatter" else 8 * 12345
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     send = [torch.empty(n, dtype=tdt, device="cuda") for _ in range(R)]
@@ -42,8 +42,6 @@ def test_captured_collective_replays_match_eager(dtype, op):
     ws = torch.empty(max(hc.hc_workspace_bytes(hc.HC_OP_REDUCE_SCATTER, n, R, hc._dtype(send[0])), 16),
                      dtype=torch.uint8, device="cuda")
 
-    if op == "allreduce_f32carry" and dtype != "bf16":
-        pytest.skip("the fp32-carry allreduce is bf16 only")
     cws = None
     if op == "allreduce_f32carry":
         cws = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_ALLREDUCE_F32_CARRY, n, R, hc.HC_BF16), dtype=torch.uint8,
