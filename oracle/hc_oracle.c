@@ -17,6 +17,10 @@
  *             AllReduce is a ReduceScatter (each rank keeps its 1/N slice of
  *             the sum) followed by an AllGather (every rank ends with every
  *             slice); distribution layouts local -> sliced -> replicated.
+ *             The same section's fusion example: an AllReduce of gradients
+ *             followed by an elementwise optimizer update becomes a
+ *             ReduceScatter, the update on each rank's slice, and an
+ *             AllGather of the updated slices.
  *  [Overlap]  "Communication-computation overlap", TP case study: the
  *             identity AllReduce = AllGather o ReduceScatter; DDP case study:
  *             a ring moves about twice the buffer per rank.
@@ -26,10 +30,6 @@
  *             is one execution of the algorithm) and section 3 (Transfer(src,
  *             dst, step, chunkId, opType) tasks; data dependencies exist only
  *             within one chunk).
- *             The same section's fusion example: an AllReduce of gradients
- *             followed by an elementwise optimizer update becomes a
- *             ReduceScatter, the update on each rank's slice, and an
- *             AllGather of the updated slices.
  *  [CCCL]     "CCCL: In-GPU Compression-Coupled Collective Communication",
  *             section 4.1 (sign and fraction sent raw, the 8-bit bf16 exponent
  *             coded from a frequency table), 4.3 (a local table per thread

@@ -200,3 +200,57 @@ def test_chunk_is_about_one_percent():
         c = oracle.chunk_elems(n, align)
         assert c % align == 0
         assert c >= n / 100 and c < n / 100 + align
+
+
+# ------------------------------------------------ the fold at chosen indices
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("R", [1, 2, 3, 5, 7, 8, 16, 33, 64])
+def test_fold_at_equals_whole_fold_at_every_index(dtype, R):
+    """or_allreduce_fold_at is the checker of the full-size GPU tests, which
+    compare outputs too large for the whole fold at once.  At every index of
+    buffers where R divides n and where it does not (short and empty last
+    slices), it must return exactly the whole fold's word, in any index order
+    and with repeats."""
+    for n in (R * 37, R * 37 + 1, R * 37 + R - 1, 1, 5):
+        xs = rand_ranks(R, n, dtype, 7000 + 97 * R + n)
+        whole = oracle.allreduce_fold(xs)[0]
+        idx = np.arange(n, dtype=np.uint64)
+        np.testing.assert_array_equal(oracle.allreduce_fold_at(xs, idx), whole)
+        perm = np.random.default_rng(n).permutation(n).astype(np.uint64)
+        rep = np.concatenate([perm, perm[: max(1, n // 3)]])
+        np.testing.assert_array_equal(oracle.allreduce_fold_at(xs, rep), whole[rep.astype(np.int64)])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fold_at_slice_edges_order_revealing(dtype):
+    """Every slice's first and last index and the tail, with inputs whose sum
+    depends on the fold order (x[j+1] = 1, x[j+2] = 2^24, x[j+3] = -2^24 in
+    fp32; 1, 2^8, -2^8 in bf16): a fold started at the wrong rank or a slice
+    index off by one gives another word there."""
+    R, L = 4, 9
+    n = R * L - 2          # the last slice is short
+    big = 2.0 ** 24 if dtype == "f32" else 2.0 ** 8
+    vals = np.zeros((R, n), dtype=np.float64)
+    for i in range(n):
+        j = i // L
+        vals[(j + 1) % R, i] = 1.0
+        vals[(j + 2) % R, i] = big
+        vals[(j + 3) % R, i] = -big
+    xs = [v.astype(np.float32) for v in vals]
+    if dtype == "bf16":
+        xs = [to_bf16(x) for x in xs]
+    edges = sorted({0, n - 1, *[j * L for j in range(R) if j * L < n],
+                    *[min(n, (j + 1) * L) - 1 for j in range(R)]})
+    got = oracle.allreduce_fold_at(xs, np.array(edges, dtype=np.uint64))
+    got = got.astype(np.float64) if dtype == "f32" else bf16_to_f64(got)
+    # ((1 + big) - big) + 0: the 1 is lost to rounding in the first hop
+    np.testing.assert_array_equal(got, np.zeros(len(edges)))
+    np.testing.assert_array_equal(oracle.allreduce_fold_at(xs, np.array(edges, dtype=np.uint64)),
+                                  oracle.allreduce_fold(xs)[0][edges])
+
+
+def test_fold_at_rejects_out_of_range_index():
+    xs = rand_ranks(3, 10, "f32", 5)
+    with pytest.raises(ValueError):
+        oracle.allreduce_fold_at(xs, np.array([10], dtype=np.uint64))
