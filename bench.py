@@ -124,7 +124,48 @@ def roofline_obj(kernel: str, alg_bytes: int, ms: float, traffic=None, duration:
          "launch_ms": round(ms, 6)}
     if duration:
         d["duration"] = duration
+    if traffic is not None:
+        d["traffic_source"] = TRAFFIC_SOURCE
     return d
+
+
+def host_info() -> dict:
+    """The host the oracle runs on: logical CPUs this process may use and the
+    CPU model."""
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        nproc = os.cpu_count() or 0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": nproc, "cpu_model": model}
+
+
+def contention_rate(compute, comm, n_cu: float):
+    """The contention rate of "HOCCL: Offloading Collective Communication from
+    GPU Cores to Accelerate Distributed Training" (section 2: the share of
+    compute units that communication holds while compute kernels run), read
+    as I = integral of C(t) * CU(t) / n_cu over integral of C(t), with C(t) = 1
+    while any compute interval (t0, t1) runs and CU(t) the compute units of
+    the communication intervals (t0, t1, cus) running at t.  Returns None when
+    no compute ran."""
+    pts = sorted({t for a, b in compute for t in (a, b)} | {t for a, b, _ in comm for t in (a, b)})
+    num = den = 0.0
+    for a, b in zip(pts, pts[1:]):
+        mid = 0.5 * (a + b)
+        if not any(c0 <= mid < c1 for c0, c1 in compute):
+            continue
+        cu = sum(k for m0, m1, k in comm if m0 <= mid < m1)
+        den += b - a
+        num += (b - a) * cu / n_cu
+    return num / den if den > 0 else None
 
 
 def oracle_timed(fn, nbytes: int, sample: str, unit: str = "GB/s"):
@@ -134,7 +175,12 @@ def oracle_timed(fn, nbytes: int, sample: str, unit: str = "GB/s"):
     fn()
     dt = time.perf_counter() - t0
     return {"value": round(nbytes / dt / 1e9, 6), "unit": unit, "cores": 1, "kind": "oracle",
-            "sample": f"{sample}; {dt:.2f} s"}
+            "sample": f"{sample}; {dt:.2f} s", **host_info()}
+
+
+TRAFFIC_SOURCE = ("recorded, not measured in this run: rocprofv3 FETCH_SIZE and WRITE_SIZE per launch from "
+                  "profiles/pmc_traffic.json, taken on the same kernel source (matched by source hash), "
+                  "FETCH_SIZE scaled by the plain-copy calibration factor")
 
 
 def cpu_baseline_ring(R: int, n_sample: int):
@@ -149,7 +195,7 @@ def cpu_baseline_ring(R: int, n_sample: int):
     dt = time.perf_counter() - t0
     return {"value": round(n_sample * 2 / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"R={R} ranks x {n_sample} bf16 elements (same recipe), ring step simulator, "
-                      f"{dt:.2f} s"}
+                      f"{dt:.2f} s", **host_info()}
 
 
 def bench_ring(args, workload: str):
@@ -190,6 +236,7 @@ def bench_ring(args, workload: str):
     rs_bytes = 3 * es * n * (R - 2) + 4 * es * n       # per allreduce; the last step writes twice
     ag_bytes = 2 * es * n * (R - 2)
     alg_bytes = rs_bytes + ag_bytes
+    method_bytes = (3 + 2) * es * n * (R - 1)            # R-1 reduce hops and R-1 copy hops
     red_launch_bytes = 3 * es * n                        # one reduce step: R receivers x L elements
     algbw = n * es / (ms / 1e3) / 1e9
     hbm = alg_bytes / (ms / 1e3) / 1e9
@@ -207,6 +254,14 @@ def bench_ring(args, workload: str):
         "busbw_gbps": round(algbw * 2 * (R - 1) / R, 3),
         "hbm_gbps": round(hbm, 2), "hbm_frac_of_peak": round(hbm / PEAK_HBM_GBPS, 4),
         "alg_bytes_per_step": alg_bytes,
+        "alg_bytes_basis": "what this implementation moves: R-2 reduce hops (2 reads, 1 write), one "
+                           "reduce-and-send hop (2 reads, 2 writes) that also does the first all-gather copy, "
+                           "R-2 copy hops",
+        "method_alg_bytes_per_step": method_bytes,
+        "method_hbm_gbps": round(method_bytes / (ms / 1e3) / 1e9, 2),
+        "method_hbm_frac_of_peak": round(method_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "method_bytes_basis": "the ring method's own accesses: R-1 reduce hops (2 reads, 1 write) and R-1 copy "
+                              "hops (1 read, 1 write)",
         "reduce_launch_ms": round(avg_red, 6), "reduce_send_launch_ms": round(avg_fused, 6),
         "copy_launch_ms": round(avg_cpy, 6),
         "copy_launch_gbps": round(2 * es * n / (avg_cpy / 1e3) / 1e9, 2),
@@ -216,6 +271,8 @@ def bench_ring(args, workload: str):
                      "traffic": traffic, "alg_bytes_per_launch": red_launch_bytes, "launch_ms": round(avg_red, 6),
                      "duration": "mean reduce-scatter step by its kernel's start and end stamps (HIP events)"},
     }
+    if traffic is not None:
+        line["roofline"]["traffic_source"] = TRAFFIC_SOURCE
     if workload == "ring_bf16":
         # What a plain streaming kernel with the reduce hop's traffic (two
         # reads, one write of 128 MiB operands, the same tiling) reaches on
@@ -736,20 +793,13 @@ def bench_contention(args):
         t0, t1 = base.elapsed_time(r0), base.elapsed_time(r1)
         overl = [gt[i + 1] - gt[i] for i in range(iters) if gt[i] < t1 and gt[i + 1] > t0]
         t_gemm_conc = median(overl) if overl else float("nan")
-        # contention rate: share of CUs held by the collective while the GEMM runs
-        num = den = 0.0
-        for i in range(iters):
-            a_, b_ = gt[i], gt[i + 1]
-            lo, hi = max(a_, t0), min(b_, t1)
-            den += b_ - a_
-            if hi > lo:
-                num += (hi - lo) * cu_used / N_CU
+        rate = contention_rate([(gt[i], gt[i + 1]) for i in range(iters)], [(t0, t1, cu_used)], N_CU)
         return {f"{prefix}_alone_ms": round(t_alone, 4), f"{prefix}_concurrent_ms": round(t1 - t0, 4),
                 f"{prefix}_alone_gbps": round(nbytes / t_alone / 1e6, 1),
                 f"{prefix}_concurrent_gbps": round(nbytes / (t1 - t0) / 1e6, 1),
                 "gemm_alone_ms": round(t_gemm, 4), "gemm_concurrent_ms": round(t_gemm_conc, 4),
                 "gemm_slowdown": round(t_gemm_conc / t_gemm - 1, 4),
-                "contention_rate": round(num / den, 5) if den else None}
+                "contention_rate": round(rate, 5) if rate is not None else None}
 
     rows = []
     for k in (8, 16, 32, 0):

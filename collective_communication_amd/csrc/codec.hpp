@@ -433,7 +433,7 @@ __device__ __forceinline__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, S
     uint32_t best = 0xFFFFFFFFu;
 #pragma unroll
     for (uint32_t b = 1; b <= 7; ++b) {
-      const uint32_t cov = __builtin_amdgcn_readlane(cover, (1 << (b - 1)) - 1);
+      const uint32_t cov = lane_read(cover, (1u << (b - 1)) - 1u);
       const uint32_t size = coded_bytes(b, kB - cov);
       const uint32_t cand = (size << 3) | b;
       best = cand < best ? cand : best;
@@ -441,7 +441,7 @@ __device__ __forceinline__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, S
     const uint32_t b = best & 7u, size = best >> 3;
     if (size < kRawFull) {
       p.mode = 1; p.b = b; p.K = (1u << b) - 1u;
-      p.n_esc = kB - __builtin_amdgcn_readlane(cover, (1 << (b - 1)) - 1);
+      p.n_esc = kB - lane_read(cover, (1u << (b - 1)) - 1u);
       p.rec_bytes = size;
     } else {
       p.mode = 0; p.b = 0; p.K = 0; p.n_esc = 0; p.rec_bytes = kRawFull;

@@ -76,6 +76,20 @@ __device__ __forceinline__ uint4 sgd_f32x4(uint4 w, uint4 g, float lr) {
   return make_uint4(sgd_f32(w.x, g.x, lr), sgd_f32(w.y, g.y, lr), sgd_f32(w.z, g.z, lr), sgd_f32(w.w, g.w, lr));
 }
 
+// Cross-lane reads.  The builtins return a signed int: widened into a 64-bit
+// offset, a word with bit 31 set would sign-extend into a wild address.
+// These return the 32-bit pattern unsigned; kernels read lanes only through
+// them (a CPU lint over the sources keeps it so).
+__device__ __forceinline__ uint32_t lane_read(uint32_t x, uint32_t lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, (int)lane);
+}
+__device__ __forceinline__ uint32_t first_lane_read(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+__device__ __forceinline__ uint64_t lane_read64(uint64_t x, uint32_t lane) {
+  return ((uint64_t)lane_read((uint32_t)(x >> 32), lane) << 32) | lane_read((uint32_t)x, lane);
+}
+
 // Streaming 16-byte global accesses.
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }

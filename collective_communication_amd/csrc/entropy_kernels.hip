@@ -139,7 +139,7 @@ __device__ __forceinline__ uint32_t set_lane(uint32_t v, uint32_t at, uint32_t x
 __device__ __forceinline__ uint32_t huffman_depths_wave(uint32_t lw, uint32_t n) {
   uint32_t nw = 0, lpar = 0, npar = 0;   // merged node k's weight; parents (merged-node numbers)
   uint32_t leaf = 0, node = 0, made = 0;
-  uint32_t wl = __builtin_amdgcn_readlane(lw, 0), wn = 0;
+  uint32_t wl = lane_read(lw, 0), wn = 0;
   for (uint32_t k = 0; k + 1 < n; ++k) {
     uint32_t sum = 0;
 #pragma unroll
@@ -148,12 +148,12 @@ __device__ __forceinline__ uint32_t huffman_depths_wave(uint32_t lw, uint32_t n)
         sum += wl;
         lpar = set_lane(lpar, leaf, made);
         ++leaf;
-        wl = __builtin_amdgcn_readlane(lw, leaf < 64u ? leaf : 63u);
+        wl = lane_read(lw, leaf < 64u ? leaf : 63u);
       } else {
         sum += wn;
         npar = set_lane(npar, node, made);
         ++node;
-        wn = __builtin_amdgcn_readlane(nw, node < 64u ? node : 63u);
+        wn = lane_read(nw, node < 64u ? node : 63u);
       }
     }
     nw = set_lane(nw, made, sum);
@@ -163,7 +163,7 @@ __device__ __forceinline__ uint32_t huffman_depths_wave(uint32_t lw, uint32_t n)
   // depths of the merged nodes, root (made - 1) first: a parent is made after its children
   uint32_t nd = 0;
   for (int32_t j = (int32_t)made - 2; j >= 0; --j) {
-    const uint32_t pd = __builtin_amdgcn_readlane(nd, __builtin_amdgcn_readlane(npar, j));
+    const uint32_t pd = lane_read(nd, lane_read(npar, j));
     nd = set_lane(nd, (uint32_t)j, pd + 1u);
   }
   return __shfl(nd, (int)lpar, 64) + 1u;

@@ -86,9 +86,7 @@ __device__ __forceinline__ uint64_t lookback_wave(CompressWs* ws, uint32_t bid, 
     for (int o = 32; o >= 1; o >>= 1) agg += __shfl_xor(agg, o, 64);
     excl += agg;
     if (first < 64) {
-      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)d, first);
-      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(d >> 32), first);
-      excl += (((uint64_t)hi << 32) | lo) & kValueMask;
+      excl += lane_read64(d, (uint32_t)first) & kValueMask;
       break;
     }
     base -= 64;

@@ -37,3 +37,26 @@ def first_mismatch(a: np.ndarray, b: np.ndarray) -> str:
         return "equal"
     i = int(d[0])
     return f"{d.size} mismatches, first at {i}: got 0x{int(a[i]):x} want 0x{int(b[i]):x}"
+
+
+def fold_chunked(xs, lo: int = 0, hi: int = -1, chunk: int = 1 << 22, threads: int = 8) -> np.ndarray:
+    """The oracle's allreduce fold of the whole index range [lo, hi) (default:
+    every index), evaluated by the oracle's fold-at-indices in chunks so that
+    buffers too large for the whole fold's R outputs can be compared element
+    by element.  The chunks run on a few host threads (the oracle call holds
+    no Python lock); each call is the plain single-threaded oracle."""
+    import concurrent.futures as cf
+
+    import oracle
+
+    n = xs[0].size
+    hi = n if hi < 0 else hi
+    out = np.empty(hi - lo, dtype=xs[0].dtype)
+
+    def one(a):
+        b = min(hi, a + chunk)
+        out[a - lo:b - lo] = oracle.allreduce_fold_at(xs, np.arange(a, b, dtype=np.uint64))
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(one, range(lo, hi, chunk)))
+    return out

@@ -42,3 +42,43 @@ def test_roofline_object_fields():
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert abs(r["achieved"] - 8000.0) < 1e-6 and abs(r["frac"] - 1.0) < 1e-9
     assert r["traffic"] == 123 and r["alg_bytes_per_launch"] == 8_000_000_000
+    assert "traffic_source" in r and "recorded" in r["traffic_source"]
+    assert "traffic_source" not in bench.roofline_obj("k", 1, 1.0, None)
+
+
+def test_contention_rate_matches_the_oracle():
+    """The contention-rate arithmetic the bench line reports equals the
+    oracle's on hand-built interval sets (known integrals) and on random
+    ones: GEMM calls back to back, one or several communication intervals."""
+    import numpy as np
+    import oracle
+
+    cases = [
+        ([(0, 10)], [(2, 7, 32)], 256, 0.0625),            # 5/10 of the time at 32/256
+        ([(0, 4), (4, 8)], [(0, 8, 8)], 256, 8 / 256),     # communication spans every GEMM
+        ([(0, 10)], [(20, 30, 64)], 256, 0.0),             # no overlap
+        ([(0, 2), (5, 7)], [(1, 6, 128)], 256, 0.25),      # 2 of 4 compute units of time at 1/2
+    ]
+    for comp, comm, ncu, want in cases:
+        assert abs(bench.contention_rate(comp, comm, ncu) - want) < 1e-12
+        assert abs(oracle.contention_rate(comp, comm, ncu) - want) < 1e-12
+    g = np.random.default_rng(11)
+    for _ in range(200):
+        edges = np.cumsum(g.uniform(0.1, 2.0, g.integers(1, 12)))
+        comp = [(float(a), float(b)) for a, b in zip(np.r_[0.0, edges[:-1]], edges)]
+        comm = []
+        for _ in range(g.integers(1, 4)):
+            t0 = float(g.uniform(-2, edges[-1] + 1))
+            comm.append((t0, t0 + float(g.uniform(0.0, 6.0)), int(g.integers(1, 257))))
+        a = bench.contention_rate(comp, comm, 256)
+        b = oracle.contention_rate(comp, comm, 256)
+        assert abs(a - b) < 1e-12, (comp, comm, a, b)
+    assert bench.contention_rate([], [(0, 1, 8)], 256) is None
+
+
+def test_cpu_baseline_names_its_host():
+    info = bench.host_info()
+    assert info["nproc"] >= 1 and isinstance(info["cpu_model"], str)
+    rec = bench.oracle_timed(lambda: sum(range(1000)), 1000, "a sample")
+    assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["nproc"] == info["nproc"]
+    assert "cpu_model" in rec

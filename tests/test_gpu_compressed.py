@@ -57,9 +57,12 @@ def test_compressed_allreduce_in_place_and_chunking():
             assert wire == ref_wire, f"frac={frac}"
 
 
-def test_compressed_equals_uncompressed_on_gpu_full_size():
-    """R=8 x 2^25 bf16 N(0,1e-3): compressed ring == uncompressed ring on the
-    GPU, bit for bit, and sampled elements equal the oracle's fold."""
+@pytest.mark.timeout(600)
+def test_compressed_allreduce_full_size_matches_oracle():
+    """R=8 x 2^25 bf16 N(0,1e-3): every element of every rank's output and
+    the wire byte count equal the oracle's compressed ring (whose output is
+    the uncompressed fold, bit for bit), and the compressed ring equals the
+    uncompressed one on the GPU."""
     R, n = 8, 1 << 25
     send = inputs.ring_inputs_cuda("compressed", R, n)
     xs = [inputs.host_bits(s) for s in send]
@@ -72,11 +75,13 @@ def test_compressed_equals_uncompressed_on_gpu_full_size():
     torch.cuda.synchronize()
     for r in range(R):
         assert torch.equal(out_c[r].view(torch.int16), out_u[r].view(torch.int16)), f"rank {r}"
-    g = np.random.default_rng(4)
-    idx = np.unique(g.integers(0, n, 1 << 18).astype(np.uint64))
-    want = oracle.allreduce_fold_at(xs, idx)
-    got = to_host(out_c[5])[idx.astype(np.int64)]
-    assert np.array_equal(got, want), first_mismatch(got, want)
+    del send, out_u, ws
+    torch.cuda.empty_cache()
+    print("compressed ring equals the uncompressed ring; running the oracle", flush=True)
+    ref, ref_wire = oracle.compressed_allreduce(xs, chunk=oracle.chunk_elems(n, B))
+    for r in range(R):
+        got = to_host(out_c[r])
+        assert np.array_equal(got, ref[r]), f"rank {r}: {first_mismatch(got, ref[r])}"
+    assert int(wire.item()) == ref_wire, (int(wire.item()), ref_wire)
     raw = 2 * (R - 1) * n * 2   # uncompressed wire bytes of the ring (both phases)
-    ratio = int(wire.item()) / raw
-    assert 0.6 < ratio < 0.8, ratio
+    assert 0.6 < ref_wire / raw < 0.8, ref_wire / raw

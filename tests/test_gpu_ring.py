@@ -17,7 +17,7 @@ import torch
 import oracle
 from collective_communication_amd import binding as hc
 from collective_communication_amd import inputs
-from hc_util import bits, first_mismatch, to_dev, to_host
+from hc_util import bits, first_mismatch, fold_chunked, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -148,25 +148,21 @@ def test_ring_f32_workload_full_size():
         assert np.array_equal(got[r], bits(ref[r])), first_mismatch(got[r], bits(ref[r]))
 
 
-def test_ring_bf16_workload_full_size_sampled():
-    """R=8 x 2^26 bf16 N(0,1e-3) with 1% zeros: all ranks identical on the GPU,
-    and 2^20 sampled elements (plus every slice boundary) equal the oracle's fold."""
+def test_ring_bf16_workload_full_size():
+    """R=8 x 2^26 bf16 N(0,1e-3) with 1% zeros: every element of every rank's
+    output equals the oracle's fold."""
     R, n = 8, 1 << 26
     send = inputs.ring_inputs_cuda("ring_bf16", R, n)
     xs = [inputs.host_bits(s) for s in send]
     recv = [torch.empty_like(s) for s in send]
     hc.hc_allreduce(send, recv)
     torch.cuda.synchronize()
-    for r in range(1, R):
-        assert torch.equal(recv[r].view(torch.int16), recv[0].view(torch.int16)), f"rank {r} differs from rank 0"
-    g = np.random.default_rng(2)
-    L = n // R
-    idx = np.unique(np.concatenate([g.integers(0, n, 1 << 20),
-                                    np.arange(R) * L, np.arange(1, R + 1) * L - 1]).astype(np.uint64))
-    want = oracle.allreduce_fold_at(xs, idx)
-    got = to_host(recv[3])[idx.astype(np.int64)]
-    assert np.array_equal(got, want), first_mismatch(got, want)
-    del send, recv
+    del send
+    want = fold_chunked(xs)
+    for r in range(R):
+        got = to_host(recv[r])
+        assert np.array_equal(got, want), f"rank {r}: {first_mismatch(got, want)}"
+    del recv
     torch.cuda.empty_cache()
 
 
@@ -212,11 +208,12 @@ def test_hbm_ceiling_tool():
     assert subprocess.run([tool, "0"], capture_output=True, timeout=60).returncode == 2
 
 
-def test_reduce_scatter_contention_workload_full_size_sampled():
+@pytest.mark.timeout(900)
+def test_reduce_scatter_contention_workload_full_size():
     """The contention workload's reduce-scatter, R=8 x 2^28 bf16 N(0,1e-3) with
     1% zeros, on all CUs and on a stream masked to 8 CUs (the persistent
-    grid): every rank's slice at 2^18 sampled elements plus its two ends
-    equals the oracle's fold, and both launches give the same bytes."""
+    grid): both launches give the same bytes, and every element of every
+    rank's slice equals the oracle's fold."""
     R, n = 8, 1 << 28
     L = n // R
     send = inputs.ring_inputs_cuda("contention", R, n)
@@ -237,13 +234,12 @@ def test_reduce_scatter_contention_workload_full_size_sampled():
     for r in range(R):
         assert torch.equal(masked[r].view(torch.int16), recv[r].view(torch.int16)), f"rank {r}: cu_budget 8 differs"
     xs = [inputs.host_bits(t) for t in send]
-    del send, masked
+    del send, masked, ws
     torch.cuda.empty_cache()
-    g = np.random.default_rng(5)
     for r in range(R):
-        local = np.unique(np.concatenate([g.integers(0, L, 1 << 18), [0, L - 1]])).astype(np.int64)
-        want = oracle.allreduce_fold_at(xs, (local + r * L).astype(np.uint64))
-        got = to_host(recv[r])[local]
+        want = fold_chunked(xs, r * L, (r + 1) * L)
+        got = to_host(recv[r])
         assert np.array_equal(got, want), f"rank {r}: {first_mismatch(got, want)}"
-    del recv, ws
+        print(f"contention reduce-scatter: rank {r} slice equals the oracle", flush=True)
+    del recv
     torch.cuda.empty_cache()
