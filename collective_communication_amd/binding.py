@@ -44,7 +44,7 @@ EXPORTED = [
     "hc_stream_create_cu_budget", "hc_stream_destroy", "hc_chunk_elems", "hc_ring_tasks",
     "hc_status_string", "hc_last_error", "hc_version", "hc_step_count", "hc_allreduce_sgd",
     "hc_compress_bf16_scoped", "hc_compress_bf16_entropy", "hc_decompress_bf16_entropy",
-    "hc_compress_bf16_staged", "hc_allreduce_bf16_f32carry",
+    "hc_compress_bf16_staged", "hc_allreduce_bf16_f32carry", "hc_compress_bf16_noalloc",
 ]
 
 
@@ -92,6 +92,7 @@ def load(path: str = LIB_PATH):
     L.hc_compress_bf16_scoped.argtypes = [P, S, P, S, P, S, P, S, P]
     L.hc_compress_bf16_entropy.argtypes = [P, S, P, S, P, P, S, P]
     L.hc_compress_bf16_staged.argtypes = [P, S, P, S, P, P, S, P]
+    L.hc_compress_bf16_noalloc.argtypes = [P, S, P, S, P, P]
     L.hc_decompress_bf16_entropy.argtypes = [P, S, P, S, P, P]
     L.hc_decompress_bf16.argtypes = [P, S, P, S, P, P]
     L.hc_compressed_allreduce.argtypes = [PP, PP, S, I, P, S, P, O, P]
@@ -108,7 +109,7 @@ def load(path: str = LIB_PATH):
     for name in ("hc_allreduce", "hc_reduce_scatter", "hc_all_gather", "hc_allreduce_sgd",
                  "hc_allreduce_bf16_f32carry", "hc_compress_bf16",
                  "hc_compress_bf16_scoped", "hc_compress_bf16_entropy", "hc_compress_bf16_staged",
-                 "hc_decompress_bf16",
+                 "hc_compress_bf16_noalloc", "hc_decompress_bf16",
                  "hc_decompress_bf16_entropy", "hc_compressed_allreduce", "hc_stream_create_cu_budget",
                  "hc_stream_destroy"):
         getattr(L, name).restype = I
@@ -339,6 +340,20 @@ def hc_compress_bf16(d_in: torch.Tensor, n: int, d_out: torch.Tensor, d_out_byte
     wsp = _dptr(ws, 1, "ws")
     _check(L.hc_compress_bf16(inp, n, outp, out_cap, ob, wsp, ws.numel() * ws.element_size(),
                               _stream_handle(stream)))
+
+
+def hc_compress_bf16_noalloc(d_in: torch.Tensor, n: int, d_out: torch.Tensor, d_out_bytes: torch.Tensor, *,
+                             stream=None):
+    """hc_compress_bf16 with the library's static scratch instead of a
+    workspace (allocates nothing; n <= 2^31)."""
+    L = load()
+    if d_in.element_size() != 2:
+        raise TypeError("input must hold 16-bit words")
+    inp = _dptr(d_in, 2 * n, "d_in") if n else (d_in.data_ptr() if d_in.numel() else None)
+    out_cap = d_out.numel() * d_out.element_size()
+    outp = _dptr(d_out, 1, "d_out")
+    ob = _dptr(d_out_bytes, 8, "d_out_bytes")
+    _check(L.hc_compress_bf16_noalloc(inp, n, outp, out_cap, ob, _stream_handle(stream)))
 
 
 def hc_compress_bf16_scoped(d_in: torch.Tensor, n: int, d_out: torch.Tensor, d_out_bytes: torch.Tensor,

@@ -20,10 +20,20 @@
 // the fused kernel does decompress -> hop -> compress per block in one pass
 // with the block's values in registers.  Wire records sit in fixed-size
 // slots, one per block (the preallocated regions of section 4.4).
+#include <mutex>
+
 #include "codec.hpp"
 #include "launch.hpp"
 #include "lookback.hpp"
 #include "schedule.hpp"
+
+// Static scratch of the allocation-free compress entry point: the look-back
+// head and one descriptor per block for up to kNoAllocMaxBlocks blocks.  Each
+// GPU the library runs on holds its own copy until the process ends.  Host
+// code never passes this name to a kernel (on the host it is a stand-in, not
+// a device address): it takes each device's address once, through
+// hipGetSymbolAddress, and passes that.
+static __device__ __align__(256) uint8_t scratch[hc::kNoAllocScratchBytes];
 
 namespace hc {
 
@@ -542,6 +552,28 @@ hipError_t launch_fill_u32(void* dst, uint32_t value, size_t words, hipStream_t 
 }
 
 size_t compress_ws_bytes(size_t n) { return kCompressWsHeader + 8 * ceil_div(n, kB); }
+
+static_assert(kNoAllocScratchBytes >= kCompressWsHeader + 8 * (size_t)kNoAllocMaxBlocks,
+              "the static scratch holds the look-back head and every block's descriptor");
+
+hipError_t noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // this device's copy (it is current)
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_compress(const uint16_t* in, size_t n, void* out, uint64_t* out_bytes, void* ws,
                            hipStream_t stream) {

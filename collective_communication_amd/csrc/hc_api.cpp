@@ -745,6 +745,26 @@ hc_status_t hc_compress_bf16(const uint16_t* d_in, size_t n, void* d_out, size_t
   return compress_common(d_in, n, d_out, out_cap, d_out_bytes, d_ws, ws_bytes, Coder::kPerBlock, 1, stream);
 }
 
+hc_status_t hc_compress_bf16_noalloc(const uint16_t* d_in, size_t n, void* d_out, size_t out_cap,
+                                     uint64_t* d_out_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  if (n > hc::kNoAllocMaxBlocks * (size_t)HC_BLOCK_ELEMS)
+    return fail(HC_ERR_INSUFFICIENT_CAPACITY, "n %zu exceeds the static scratch's %zu elements", n,
+                hc::kNoAllocMaxBlocks * (size_t)HC_BLOCK_ELEMS);
+  if (!d_out || !d_out_bytes || (n && !d_in)) return fail(HC_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if ((d_in && !aligned16(d_in)) || !aligned16(d_out) || ((uintptr_t)d_out_bytes & 7u))
+    return fail(HC_ERR_INVALID_ARGUMENT, "misaligned pointer argument");
+  const size_t bound = hc_compress_bound_bf16(n);
+  if (out_cap < bound) return fail(HC_ERR_INSUFFICIENT_CAPACITY, "out_cap %zu < bound %zu", out_cap, bound);
+  Range ir{(uintptr_t)d_in, (uintptr_t)d_in + 2 * n}, orr{(uintptr_t)d_out, (uintptr_t)d_out + bound};
+  if (n && overlap(ir, orr)) return fail(HC_ERR_INVALID_ARGUMENT, "input and output must not overlap");
+  void* ws = nullptr;
+  hipError_t e = hc::noalloc_scratch(&ws);
+  if (e != hipSuccess) return device_fail(e, "static scratch address");
+  e = hc::launch_compress(d_in, n, d_out, d_out_bytes, ws, stream);
+  return e == hipSuccess ? HC_SUCCESS : device_fail(e, "compress launch");
+}
+
 hc_status_t hc_compress_bf16_scoped(const uint16_t* d_in, size_t n, void* d_out, size_t out_cap,
                                     uint64_t* d_out_bytes, size_t table_blocks, void* d_ws, size_t ws_bytes,
                                     hipStream_t stream) {

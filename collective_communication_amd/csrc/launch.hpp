@@ -84,6 +84,14 @@ hipError_t launch_compress(const uint16_t* in, size_t n, void* out, uint64_t* ou
 hipError_t launch_decompress(const void* in, size_t in_bytes, uint16_t* out, size_t n,
                              int32_t* status, hipStream_t stream);
 size_t compress_ws_bytes(size_t n);
+// The allocation-free compress entry point's static scratch: room for the
+// look-back workspace of up to kNoAllocMaxBlocks blocks (2^31 elements).
+constexpr size_t kNoAllocMaxBlocks = (size_t)1 << 17;
+constexpr size_t kNoAllocScratchBytes = 64 + 8 * kNoAllocMaxBlocks;
+constexpr int kMaxDevices = 64;
+// This device's address of the static scratch (taken with
+// hipGetSymbolAddress on the device's first call, then kept).
+hipError_t noalloc_scratch(void** out);
 // Stream helpers shared by the codec formats (magic: the format's).
 hipError_t launch_empty_stream(void* out, uint32_t magic, uint64_t* out_bytes, hipStream_t stream);
 hipError_t launch_check_empty_stream(const void* in, size_t in_bytes, uint32_t magic, int32_t* status,

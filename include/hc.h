@@ -16,7 +16,8 @@
  *     sendbufs/recvbufs are HOST arrays of nranks DEVICE pointers.
  *   - The caller owns every buffer, workspace and stream.  The library never
  *     allocates or frees device memory and keeps no state between calls
- *     except a thread-local copy of the last error message.
+ *     except a thread-local copy of the last error message, and the static
+ *     device array (about 1 MiB per GPU) of hc_compress_bf16_noalloc.
  *   - Alignment (else HC_ERR_INVALID_ARGUMENT): rank buffers of the
  *     uncompressed ring calls to their element size (16-byte alignment of
  *     every slice takes the vector path, anything else a per-element path);
@@ -260,6 +261,26 @@ size_t hc_compress_bound_bf16(size_t n);
 hc_status_t hc_compress_bf16(const uint16_t *d_in, size_t n, void *d_out, size_t out_cap,
                              uint64_t *d_out_bytes, void *d_ws, size_t ws_bytes,
                              hipStream_t stream);
+
+/*
+ * hc_compress_bf16_noalloc -- hc_compress_bf16 without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  The same
+ * kernels, the same stream byte for byte.  The look-back workspace is a
+ * static device array inside the library (64 + 8 * 131072 bytes, about
+ * 1 MiB), one copy per GPU, held until the process ends; its address is
+ * taken once per device on that device's first call.  The call allocates
+ * nothing (no hipMalloc, no allocating library routine) and clears the part
+ * of the array it uses with a fill kernel on the stream.
+ *   n: at most 131072 * 16384 = 2^31 elements, else
+ *   HC_ERR_INSUFFICIENT_CAPACITY (nothing is enqueued).
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (on different streams, or from several threads) race and may write
+ *   wrong streams; order them on one stream.
+ *   Other arguments and errors as hc_compress_bf16.
+ */
+hc_status_t hc_compress_bf16_noalloc(const uint16_t *d_in, size_t n, void *d_out, size_t out_cap,
+                                     uint64_t *d_out_bytes, hipStream_t stream);
 
 /*
  * hc_compress_bf16_scoped -- hc_compress_bf16 with code tables shared by

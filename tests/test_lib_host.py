@@ -162,6 +162,18 @@ def test_argument_errors_before_any_launch(hc):
                                      None) == hc.HC_ERR_INSUFFICIENT_CAPACITY
     assert L.hc_compress_bf16_scoped(None, n, 0x20000000, 1 << 24, 0x30000000, 4, 0x40000000, 1 << 26,
                                      None) == E
+    # allocation-free compress: n beyond the static scratch, capacity, NULL and alignment, all before any
+    # device call
+    big = (1 << 31) + 1
+    assert L.hc_compress_bf16_noalloc(0x100000, big, 0x200000, 1 << 40, 0x300000, None) == \
+        hc.HC_ERR_INSUFFICIENT_CAPACITY
+    assert b"static scratch" in L.hc_last_error()
+    assert L.hc_compress_bf16_noalloc(0x100000, 1000, 0x200000, 100, 0x300000, None) == \
+        hc.HC_ERR_INSUFFICIENT_CAPACITY
+    assert L.hc_compress_bf16_noalloc(0x100000, 1000, 0x200000, 1 << 20, None, None) == E
+    assert L.hc_compress_bf16_noalloc(None, 1000, 0x200000, 1 << 20, 0x300000, None) == E
+    assert L.hc_compress_bf16_noalloc(0x100008, 1000, 0x200000, 1 << 20, 0x300000, None) == E
+    assert L.hc_compress_bf16_noalloc(0x100000, 1000, 0x100100, 1 << 20, 0x300000, None) == E   # overlap
     # decompress: status word is required
     assert L.hc_decompress_bf16(0x100000, 1000, 0x200000, 100, None, None) == E
     # compressed allreduce: workspace too small
