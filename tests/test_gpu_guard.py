@@ -214,7 +214,7 @@ def test_corrupt_stream_zeroes_only_the_output():
     stream = bytearray(oracle.compress(x))
     stream[40 + 8 * 2] ^= 0x10   # an offset of the table: the stream is corrupt
     src = Guarded(len(stream))
-    src.bytes().copy_(torch.frombuffer(bytes(stream), dtype=torch.uint8))
+    src.bytes().copy_(torch.frombuffer(stream, dtype=torch.uint8))
     back = Guarded(2 * n)
     status = Guarded(4)
     hc.hc_decompress_bf16(src.bytes(), len(stream), back.view(torch.int16), n, status.view(torch.int32))
