@@ -20,6 +20,8 @@
 // the fused kernel does decompress -> hop -> compress per block in one pass
 // with the block's values in registers.  Wire records sit in fixed-size
 // slots, one per block (the preallocated regions of section 4.4).
+#include <stdlib.h>
+
 #include <mutex>
 
 #include "codec.hpp"
@@ -97,7 +99,7 @@ __global__ void empty_stream_kernel(uint8_t* out, uint32_t magic, uint64_t* out_
 template <bool SCOPED>
 __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void compress_kernel(
     const uint16_t* __restrict__ in, uint64_t n, uint8_t* __restrict__ out, uint64_t* __restrict__ out_bytes,
-    CompressWs* __restrict__ ws, uint32_t nb, ScopeWs sc, uint32_t group) {
+    CompressWs* __restrict__ ws, uint32_t nb, ScopeWs sc, uint32_t group, uint32_t spin_limit) {
   __shared__ Smem s;
   const int t = threadIdx.x;
   const uint32_t bid = blockIdx.x;
@@ -118,18 +120,28 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
   if (t == 0) publish(&ws->desc[bid], (bid == 0 ? kFlagIncl : kFlagAgg) | p.rec_bytes);
   write_block(v, p, s);
   if (t < 64) {
-    const uint64_t excl = lookback_wave(ws, bid, p.rec_bytes);
-    if (t == 0) s.misc[0] = excl;
+    bool ok = true;
+    const uint64_t excl = lookback_wave(ws, bid, p.rec_bytes, spin_limit, &ok);
+    if (t == 0) {
+      s.misc[0] = excl;
+      s.misc[1] = ok;
+      if (bid != nb - 1) lookback_count_done(ws, bid, ok);
+    }
   }
   __syncthreads();
+  if (!s.misc[1]) {   // no offset: write nothing; the last block reports no stream
+    if (t == 0 && bid == nb - 1) *out_bytes = 0;
+    return;
+  }
   const uint64_t off = header_bytes(nb) + s.misc[0];
   copy_out(s, out + off, p.rec_bytes);
-  if (t == 0) {
-    reinterpret_cast<uint64_t*>(out + 32)[bid] = off;
-    if (bid == nb - 1) {
+  if (t == 0) reinterpret_cast<uint64_t*>(out + 32)[bid] = off;
+  if (bid == nb - 1 && t < 64) {   // the last block's first wave
+    const bool failed = lookback_failed(ws, nb, spin_limit);
+    if (t == 0) {
       const uint64_t total = off + p.rec_bytes;
       write_stream_header(out, kMagic, kB, n, nb, total);
-      *out_bytes = __hip_atomic_load(&ws->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? 0 : total;
+      *out_bytes = failed ? 0 : total;
     }
   }
 }
@@ -553,6 +565,14 @@ hipError_t launch_fill_u32(void* dst, uint32_t value, size_t words, hipStream_t 
 
 size_t compress_ws_bytes(size_t n) { return kCompressWsHeader + 8 * ceil_div(n, kB); }
 
+uint32_t lookback_spin_limit() {
+  const char* e = getenv("HC_LOOKBACK_SPIN_LIMIT");
+  if (!e || !*e) return kSpinLimit;
+  char* end = nullptr;
+  const unsigned long v = strtoul(e, &end, 10);
+  return (*end == 0 && v >= 1 && v <= 0xFFFFFFFFul) ? (uint32_t)v : kSpinLimit;
+}
+
 static_assert(kNoAllocScratchBytes >= kCompressWsHeader + 8 * (size_t)kNoAllocMaxBlocks,
               "the static scratch holds the look-back head and every block's descriptor");
 
@@ -588,7 +608,7 @@ hipError_t launch_compress(const uint16_t* in, size_t n, void* out, uint64_t* ou
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(compress_kernel<false>, dim3((uint32_t)nb), dim3(kCT), 0, stream, in, (uint64_t)n,
                      static_cast<uint8_t*>(out), out_bytes, static_cast<CompressWs*>(ws), (uint32_t)nb, ScopeWs{},
-                     1u);
+                     1u, lookback_spin_limit());
   return hipGetLastError();
 }
 
@@ -659,7 +679,7 @@ hipError_t launch_compress_scoped(const uint16_t* in, size_t n, void* out, uint6
   }
   hipLaunchKernelGGL(compress_kernel<true>, dim3((uint32_t)nb), dim3(kCT), 0, stream, in, (uint64_t)n,
                      static_cast<uint8_t*>(out), out_bytes, static_cast<CompressWs*>(ws), (uint32_t)nb, sc,
-                     (uint32_t)G);
+                     (uint32_t)G, lookback_spin_limit());
   return hipGetLastError();
 }
 

@@ -297,7 +297,7 @@ __device__ uint32_t build_code(uint32_t cnt, HceEncSmem& s) {
 
 __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void hce_compress_kernel(
     const uint16_t* __restrict__ in, uint64_t n, uint8_t* __restrict__ out, uint64_t* __restrict__ out_bytes,
-    CompressWs* __restrict__ ws, uint32_t nb) {
+    CompressWs* __restrict__ ws, uint32_t nb, uint32_t spin_limit) {
   __shared__ HceEncSmem s;
   const uint32_t t = threadIdx.x, lane = t & 63u, seg = t >> 6;
   const uint32_t bid = blockIdx.x;
@@ -423,18 +423,28 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
   }
   __syncthreads();
   if (t < 64) {
-    const uint64_t excl = lookback_wave(ws, bid, rec_bytes);
-    if (t == 0) s.misc[0] = excl;
+    bool ok = true;
+    const uint64_t excl = lookback_wave(ws, bid, rec_bytes, spin_limit, &ok);
+    if (t == 0) {
+      s.misc[0] = excl;
+      s.misc[1] = ok;
+      if (bid != nb - 1) lookback_count_done(ws, bid, ok);
+    }
   }
   __syncthreads();
+  if (!s.misc[1]) {   // no offset: write nothing; the last block reports no stream
+    if (t == 0 && bid == nb - 1) *out_bytes = 0;
+    return;
+  }
   const uint64_t off = header_bytes(nb) + s.misc[0];
   copy_out(s, out + off, rec_bytes);
-  if (t == 0) {
-    reinterpret_cast<uint64_t*>(out + 32)[bid] = off;
-    if (bid == nb - 1) {
+  if (t == 0) reinterpret_cast<uint64_t*>(out + 32)[bid] = off;
+  if (bid == nb - 1 && t < 64) {   // the last block's first wave
+    const bool failed = lookback_failed(ws, nb, spin_limit);
+    if (t == 0) {
       const uint64_t tot = off + rec_bytes;
       write_stream_header(out, kHceMagic, kB, n, nb, tot);
-      *out_bytes = __hip_atomic_load(&ws->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? 0 : tot;
+      *out_bytes = failed ? 0 : tot;
     }
   }
 }
@@ -697,7 +707,8 @@ hipError_t launch_hce_compress(const uint16_t* in, size_t n, void* out, uint64_t
   hipError_t e = launch_fill_u32(ws, 0u, compress_ws_bytes(n) / 4, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(hce_compress_kernel, dim3((uint32_t)nb), dim3(kCT), 0, stream, in, (uint64_t)n,
-                     static_cast<uint8_t*>(out), out_bytes, static_cast<CompressWs*>(ws), (uint32_t)nb);
+                     static_cast<uint8_t*>(out), out_bytes, static_cast<CompressWs*>(ws), (uint32_t)nb,
+                     lookback_spin_limit());
   return hipGetLastError();
 }
 

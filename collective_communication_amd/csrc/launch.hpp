@@ -78,6 +78,12 @@ hipError_t launch_carry_step(const Seg* segs, int nseg, bool a_f32, bool dst_f32
                              hipStream_t stream);
 
 // Codec.
+// Polls of an unpublished look-back descriptor before a stream encoder's
+// walk gives up: HC_LOOKBACK_SPIN_LIMIT from the environment (read at every
+// call; an unsigned decimal >= 1), else 2^22.  A small value makes walks give
+// up, which the encoders report as a zero-byte stream; tests use it to
+// exercise that path.
+uint32_t lookback_spin_limit();
 hipError_t launch_fill_u32(void* dst, uint32_t value, size_t words, hipStream_t stream);
 hipError_t launch_compress(const uint16_t* in, size_t n, void* out, uint64_t* out_bytes,
                            void* ws, hipStream_t stream);
@@ -87,7 +93,7 @@ size_t compress_ws_bytes(size_t n);
 // The allocation-free compress entry point's static scratch: room for the
 // look-back workspace of up to kNoAllocMaxBlocks blocks (2^31 elements).
 constexpr size_t kNoAllocMaxBlocks = (size_t)1 << 17;
-constexpr size_t kNoAllocScratchBytes = 64 + 8 * kNoAllocMaxBlocks;
+constexpr size_t kNoAllocScratchBytes = 8320 + 8 * kNoAllocMaxBlocks;
 constexpr int kMaxDevices = 64;
 // This device's address of the static scratch (taken with
 // hipGetSymbolAddress on the device's first call, then kept).

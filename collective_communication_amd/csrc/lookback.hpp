@@ -15,9 +15,9 @@
 // nothing unfinished, and finishes; by induction all do.  That order is how
 // the hardware dispatches, not a promise of the programming model, so every
 // wait is also bounded: a walk that polls an
-// unpublished descriptor kSpinLimit times sets the error word and gives up,
-// and the call then reports no stream (its byte count is 0) instead of
-// hanging.  An earlier design took an atomic ticket per block to make the
+// unpublished descriptor spin_limit times gives up, publishes poison (walks
+// that reach it give up too), sets the error word and writes no record; the
+// call then reports no stream (its byte count is 0) instead of hanging.  An earlier design took an atomic ticket per block to make the
 // order explicit; its round trip before each block's first load cost 23 us of
 // a 269 us call on 2^28 elements, and no walk has timed out without it.
 #pragma once
@@ -33,18 +33,23 @@ namespace hc {
 
 constexpr uint64_t kFlagAgg = 1ull << 62;     // descriptor holds the block's own size
 constexpr uint64_t kFlagIncl = 2ull << 62;    // descriptor holds the size of blocks 0..bid
+constexpr uint64_t kFlagPoison = 3ull << 62;  // the block gave up: no valid prefix through it
 constexpr uint64_t kValueMask = (1ull << 62) - 1;
-constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr uint32_t kSpinLimit = 1u << 22;   // polls of an unpublished descriptor before a walk gives up
 
-// Workspace of a stream encoder: a spare word, an error word, then one
-// 64-bit look-back descriptor per block (all zero before the launch).
+// Workspace of a stream encoder: counts of ended walks, then one 64-bit
+// look-back descriptor per block (all zero before the launch).
+// Ended walks are counted in kWalkCounters counters, one per 128-byte line
+// (block j adds to counter j % kWalkCounters): thousands of blocks adding to
+// one address would queue behind each other at the memory side.
+constexpr uint32_t kWalkCounters = 64;
 struct CompressWs {
-  uint32_t spare;
-  uint32_t error;
-  uint32_t pad[14];
+  uint32_t pad[32];
+  uint64_t walked[kWalkCounters][16];   // word 0 of each line: blocks j % 64 == line whose walk ended,
+                                        // in the low half; those that gave up, in the high half
   uint64_t desc[1];
 };
-constexpr size_t kCompressWsHeader = 64;
+constexpr size_t kCompressWsHeader = 128 + 128 * kWalkCounters;
 
 __device__ __forceinline__ void publish(uint64_t* d, uint64_t v) {
   __hip_atomic_store(d, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -53,32 +58,45 @@ __device__ __forceinline__ uint64_t peek(uint64_t* d) {
   return __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// One look-back window: lane l reads the descriptor of block base-l (blocks
+// before 0 read as an inclusive prefix of 0).
+__device__ __forceinline__ uint64_t lookback_peek(CompressWs* ws, int64_t base) {
+  const int64_t j = base - (int64_t)__lane_id();
+  return j >= 0 ? peek(&ws->desc[j]) : kFlagIncl;
+}
+
 // Byte offset of block bid's record among the records (the sum of the sizes
 // of blocks 0..bid-1).  Called by the 64 lanes of one wave after the block
-// published its own size; publishes the block's inclusive prefix and returns
-// the exclusive one to every lane.  Lane l reads the descriptor of block
-// bid-1-l; the nearest predecessor with an inclusive prefix ends the walk and
-// the sizes of the blocks between add to it.  A window with an unpublished
-// descriptor before that point is read again, a bounded number of times;
-// then the error word is set and the walk gives up.
-__device__ __forceinline__ uint64_t lookback_wave(CompressWs* ws, uint32_t bid, uint32_t rec_bytes) {
+// published its own size.  Lane l reads the descriptor of block bid-1-l; the
+// nearest predecessor with an inclusive prefix ends the walk and the sizes of
+// the blocks between add to it; a window with an unpublished descriptor
+// before that point is read again, a bounded number of times.
+// Publishes the block's inclusive prefix and returns the exclusive one to
+// every lane, with *ok true.  When a wait runs past its bound, or the walk
+// ends at a poisoned predecessor, the block publishes poison instead (later
+// walks that reach it give up too) and *ok is false: the caller then writes
+// no record.  Either way the block then counts its ended walk
+// (lookback_count_done).
+__device__ __forceinline__ uint64_t lookback_wave(CompressWs* ws, uint32_t bid, uint32_t rec_bytes, uint32_t spin_limit,
+                                                  bool* ok) {
   const uint32_t lane = __lane_id();
   uint64_t excl = 0;
   int64_t base = (int64_t)bid - 1;
+  uint64_t d = lookback_peek(ws, base);
   uint32_t spins = 0;
+  bool good = true;
   while (base >= 0) {
-    const int64_t j = base - (int64_t)lane;
-    const uint64_t d = j >= 0 ? peek(&ws->desc[j]) : kFlagIncl;
-    const uint64_t incl_mask = __ballot((d >> 62) == 2);
+    const uint64_t end_mask = __ballot((d >> 62) >= 2);   // an inclusive prefix or poison
     const uint64_t zero_mask = __ballot((d >> 62) == 0);
-    const int first = incl_mask ? __ffsll((unsigned long long)incl_mask) - 1 : 64;
+    const int first = end_mask ? __ffsll((unsigned long long)end_mask) - 1 : 64;
     const uint64_t need = first == 64 ? ~0ull : ((2ull << first) - 1ull);
     if (zero_mask & need) {
-      if (++spins >= kSpinLimit) {  // a predecessor never published: give up, flag it
-        if (lane == 0) atomicExch(&ws->error, 1u);
+      if (++spins >= spin_limit) {  // a predecessor never published: give up
+        good = false;
         break;
       }
       __builtin_amdgcn_s_sleep(1);
+      d = lookback_peek(ws, base);
       continue;
     }
     uint32_t agg = (int)lane < first ? (uint32_t)(d & kValueMask) : 0u;
@@ -86,13 +104,48 @@ __device__ __forceinline__ uint64_t lookback_wave(CompressWs* ws, uint32_t bid, 
     for (int o = 32; o >= 1; o >>= 1) agg += __shfl_xor(agg, o, 64);
     excl += agg;
     if (first < 64) {
-      excl += lane_read64(d, (uint32_t)first) & kValueMask;
+      const uint64_t e = lane_read64(d, (uint32_t)first);
+      good = (e >> 62) == 2;
+      excl += e & kValueMask;
       break;
     }
     base -= 64;
+    d = lookback_peek(ws, base);
   }
-  if (lane == 0 && bid != 0) publish(&ws->desc[bid], kFlagIncl | (excl + rec_bytes));
+  if (lane == 0 && bid != 0) publish(&ws->desc[bid], good ? (kFlagIncl | (excl + rec_bytes)) : kFlagPoison);
+  *ok = good;
   return excl;
+}
+
+// Every block but the last counts its ended walk, and whether it gave up,
+// in one 64-bit add: the count and the failure travel together, so no
+// ordering between two locations (and no fence) is needed.
+__device__ __forceinline__ void lookback_count_done(CompressWs* ws, uint32_t bid, bool ok) {
+  __hip_atomic_fetch_add(&ws->walked[bid % kWalkCounters][0], ok ? 1ull : (1ull | (1ull << 32)), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The last block, after its own walk, with the 64 lanes of one wave: waits
+// (bounded) until the other nb-1 blocks have counted their walks, then
+// reports whether any gave up.  A walk that gave up at any time is therefore
+// seen, even one the last block's own walk never reached (it summed that
+// block's size instead).  True (in every lane) when the stream is not valid.
+__device__ __forceinline__ bool lookback_failed(CompressWs* ws, uint32_t nb, uint32_t spin_limit) {
+  static_assert(kWalkCounters == 64, "one counter per lane");
+  const uint32_t lane = __lane_id();
+  uint32_t spins = 0;
+  for (;;) {
+    const uint64_t w = __hip_atomic_load(&ws->walked[lane][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t done = (uint32_t)w, failed = (uint32_t)(w >> 32);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      done += __shfl_xor(done, o, 64);
+      failed |= __shfl_xor(failed, o, 64);
+    }
+    if (done >= nb - 1) return failed != 0;
+    if (++spins >= spin_limit) return true;
+    __builtin_amdgcn_s_sleep(1);
+  }
 }
 
 // Stream container shared by the codec formats: a 32-byte header {u32 magic,

@@ -267,7 +267,7 @@ hc_status_t hc_compress_bf16(const uint16_t *d_in, size_t n, void *d_out, size_t
  * for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation).  The same
  * kernels, the same stream byte for byte.  The look-back workspace is a
- * static device array inside the library (64 + 8 * 131072 bytes, about
+ * static device array inside the library (8320 + 8 * 131072 bytes, about
  * 1 MiB), one copy per GPU, held until the process ends; its address is
  * taken once per device on that device's first call.  The call allocates
  * nothing (no hipMalloc, no allocating library routine) and clears the part
