@@ -44,7 +44,8 @@ EXPORTED = [
     "hc_stream_create_cu_budget", "hc_stream_destroy", "hc_chunk_elems", "hc_ring_tasks",
     "hc_status_string", "hc_last_error", "hc_version", "hc_step_count", "hc_allreduce_sgd",
     "hc_compress_bf16_scoped", "hc_compress_bf16_entropy", "hc_decompress_bf16_entropy",
-    "hc_compress_bf16_staged", "hc_allreduce_bf16_f32carry", "hc_compress_bf16_noalloc",
+    "hc_compress_bf16_staged", "hc_allreduce_bf16_f32carry", "hc_compress_bf16_noalloc", "hc_cu_census",
+    "hc_stream_create_cu_range",
 ]
 
 
@@ -99,7 +100,9 @@ def load(path: str = LIB_PATH):
     L.hc_workspace_bytes.argtypes = [I, S, I, I]
     L.hc_workspace_bytes.restype = S
     L.hc_stream_create_cu_budget.argtypes = [I, ctypes.POINTER(ctypes.c_void_p)]
+    L.hc_stream_create_cu_range.argtypes = [I, I, ctypes.POINTER(ctypes.c_void_p)]
     L.hc_stream_destroy.argtypes = [P]
+    L.hc_cu_census.argtypes = [P, I, I, P]
     L.hc_chunk_elems.argtypes = [S, ctypes.c_double, S]
     L.hc_chunk_elems.restype = S
     L.hc_ring_tasks.argtypes = [I, S, S, ctypes.POINTER(hc_task_t), S]
@@ -111,7 +114,7 @@ def load(path: str = LIB_PATH):
                  "hc_compress_bf16_scoped", "hc_compress_bf16_entropy", "hc_compress_bf16_staged",
                  "hc_compress_bf16_noalloc", "hc_decompress_bf16",
                  "hc_decompress_bf16_entropy", "hc_compressed_allreduce", "hc_stream_create_cu_budget",
-                 "hc_stream_destroy"):
+                 "hc_stream_destroy", "hc_cu_census", "hc_stream_create_cu_range"):
         getattr(L, name).restype = I
     L.hc_status_string.argtypes = [I]
     L.hc_status_string.restype = ctypes.c_char_p
@@ -449,8 +452,33 @@ def hc_stream_create_cu_budget(k: int) -> int:
     return int(s.value)
 
 
+def hc_stream_create_cu_range(first: int, k: int) -> int:
+    """A stream on CU mask bits [first, first + k); returns the raw handle."""
+    L = load()
+    s = ctypes.c_void_p(0)
+    _check(L.hc_stream_create_cu_range(first, k, ctypes.byref(s)))
+    return int(s.value)
+
+
 def hc_stream_destroy(handle: int):
     _check(load().hc_stream_destroy(handle))
+
+
+def hc_cu_census(n_workgroups: int, hold_us: int = 50, *, stream=None):
+    """Where n_workgroups one-wave workgroups run on `stream`: a (n, 2)
+    int64 tensor of (XCC_ID & 15, HW_ID bits 8..15) per workgroup, after the
+    launch completes (synchronises the stream)."""
+    L = load()
+    ids = torch.zeros(2 * n_workgroups, dtype=torch.int32, device="cuda")
+    _check(L.hc_cu_census(ids.data_ptr(), n_workgroups, hold_us, _stream_handle(stream)))
+    if stream is None:
+        torch.cuda.current_stream().synchronize()
+    elif isinstance(stream, int):
+        torch.cuda.synchronize()
+    else:
+        stream.synchronize()
+    h = ids.view(-1, 2).cpu().to(torch.int64)
+    return torch.stack([h[:, 1] & 15, (h[:, 0] >> 8) & 0xFF], dim=1)
 
 
 def hc_step_count(op: int, nranks: int) -> int:

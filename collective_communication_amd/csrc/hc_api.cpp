@@ -853,22 +853,40 @@ hc_status_t hc_compressed_allreduce(void* const* sendbufs, void* const* recvbufs
   return e == hipSuccess ? HC_SUCCESS : device_fail(e, "compressed allreduce launch");
 }
 
-hc_status_t hc_stream_create_cu_budget(int k, hipStream_t* out) {
+hc_status_t hc_stream_create_cu_range(int first, int k, hipStream_t* out) {
   g_last_error.clear();
   if (!out) return fail(HC_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (k < 1) return fail(HC_ERR_INVALID_ARGUMENT, "k %d < 1", k);
+  if (first < 0) return fail(HC_ERR_INVALID_ARGUMENT, "first %d < 0", first);
   int dev = 0, ncu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return device_fail(e, "hipGetDevice");
   e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return device_fail(e, "hipDeviceGetAttribute");
-  if (k < 1 || k > ncu) return fail(HC_ERR_INVALID_ARGUMENT, "k %d outside 1..%d", k, ncu);
-  // The first k mask bits: the driver spreads mask bits round-robin over the
-  // XCDs and shader engines, so a prefix is an even spread.
+  if (k > ncu || first > ncu - k)
+    return fail(HC_ERR_INVALID_ARGUMENT, "CUs [%d, %d) outside 0..%d", first, first + k, ncu);
+  // Mask bits [first, first + k): the runtime hands mask bits out round-robin
+  // over the XCDs and then the shader engines (bit i: XCD i % 8 on MI355X),
+  // so a run of bits is an even spread, and two disjoint runs are two
+  // disjoint sets of CUs (hc_cu_census measures both).
   std::vector<uint32_t> mask((size_t)(ncu + 31) / 32, 0u);
-  for (int i = 0; i < k; ++i) mask[(size_t)i / 32] |= 1u << (i % 32);
+  for (int i = first; i < first + k; ++i) mask[(size_t)i / 32] |= 1u << (i % 32);
   e = hipExtStreamCreateWithCUMask(out, (uint32_t)mask.size(), mask.data());
   if (e != hipSuccess) return device_fail(e, "hipExtStreamCreateWithCUMask");
   return HC_SUCCESS;
+}
+
+hc_status_t hc_stream_create_cu_budget(int k, hipStream_t* out) { return hc_stream_create_cu_range(0, k, out); }
+
+hc_status_t hc_cu_census(uint32_t* d_ids, int n_workgroups, int hold_us, hipStream_t stream) {
+  g_last_error.clear();
+  if (!d_ids) return fail(HC_ERR_INVALID_ARGUMENT, "d_ids is NULL");
+  if ((uintptr_t)d_ids & 3u) return fail(HC_ERR_INVALID_ARGUMENT, "d_ids is not 4-byte aligned");
+  if (n_workgroups < 1 || n_workgroups > 65536)
+    return fail(HC_ERR_INVALID_ARGUMENT, "n_workgroups %d outside 1..65536", n_workgroups);
+  if (hold_us < 0 || hold_us > 100000) return fail(HC_ERR_INVALID_ARGUMENT, "hold_us %d outside 0..100000", hold_us);
+  const hipError_t e = hc::launch_cu_census(d_ids, (uint32_t)n_workgroups, (uint32_t)hold_us, stream);
+  return e == hipSuccess ? HC_SUCCESS : device_fail(e, "census launch");
 }
 
 hc_status_t hc_stream_destroy(hipStream_t stream) {

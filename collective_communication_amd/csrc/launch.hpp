@@ -77,6 +77,9 @@ hipError_t launch_sgd_step(const Seg* segs, int nseg, hc_dtype_t dtype, float lr
 hipError_t launch_carry_step(const Seg* segs, int nseg, bool a_f32, bool dst_f32, int cu_budget,
                              hipStream_t stream);
 
+// Census of where a launch's workgroups run (see hc_cu_census).
+hipError_t launch_cu_census(uint32_t* ids, uint32_t n_workgroups, uint32_t hold_us, hipStream_t stream);
+
 // Codec.
 // Polls of an unpublished look-back descriptor before a stream encoder's
 // walk gives up: HC_LOOKBACK_SPIN_LIMIT from the environment (read at every

@@ -375,7 +375,29 @@ hipError_t launch_step(const Seg* segs, int nseg, int cu_budget, hipStream_t str
                        dim3(grid), dim3(kThreads), kargs, stream);
 }
 
+// Where each workgroup runs: word 2w = its HW_ID register (CU, shader array
+// and shader engine fields among others), word 2w + 1 = its XCC_ID (the XCD).
+// Each workgroup first holds its CU for hold_ticks of the 100 MHz real-time
+// clock (a bounded wait), so that the workgroups of one launch are resident
+// together and spread over every CU the stream may use.
+__global__ __launch_bounds__(64) void cu_census_kernel(uint32_t* ids, uint32_t hold_ticks) {
+  uint32_t hw, xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (__builtin_amdgcn_s_memrealtime() - t0 < hold_ticks) __builtin_amdgcn_s_sleep(8);
+  if (threadIdx.x == 0) {
+    ids[2 * blockIdx.x] = hw;
+    ids[2 * blockIdx.x + 1] = xcc;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_cu_census(uint32_t* ids, uint32_t n_workgroups, uint32_t hold_us, hipStream_t stream) {
+  hipLaunchKernelGGL(cu_census_kernel, dim3(n_workgroups), dim3(64), 0, stream, ids, hold_us * 100u);
+  return hipGetLastError();
+}
 
 hipError_t launch_reduce_step(const Seg* segs, int nseg, hc_dtype_t dtype, int cu_budget,
                               hipStream_t stream) {

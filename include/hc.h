@@ -433,11 +433,37 @@ int hc_step_count(hc_op_t op, int nranks);
  * running a collective beside compute on fewer CUs; "HOCCL: Offloading
  * Collective Communication from GPU Cores to Accelerate Distributed Training"
  * (section 2) measures the share of cores such traffic holds while compute
- * runs.  The k CUs are spread evenly over the GPU's XCDs.  *out receives the
- * stream; the caller destroys it with hc_stream_destroy.
+ * runs.  The k CUs are spread evenly over the GPU's XCDs and shader engines
+ * (measured with hc_cu_census: k = 8, 16, 32, 64 give exactly k CUs, k/8 on
+ * every XCD).  *out receives the stream; the caller destroys it with
+ * hc_stream_destroy.  Same as hc_stream_create_cu_range(0, k, out).
  */
 hc_status_t hc_stream_create_cu_budget(int k, hipStream_t *out);
+
+/* A stream limited to CU mask bits [first, first + k) (0 <= first, k >= 1,
+ * first + k <= the CU count; else HC_ERR_INVALID_ARGUMENT).  Bits are handed
+ * out round-robin over the XCDs, so a run is an even spread and
+ * hc_stream_create_cu_range(k, ncu - k) holds exactly the CUs that
+ * hc_stream_create_cu_budget(k) leaves free: compute on the one beside
+ * communication on the other shares no CU. */
+hc_status_t hc_stream_create_cu_range(int first, int k, hipStream_t *out);
 hc_status_t hc_stream_destroy(hipStream_t stream);
+
+/*
+ * hc_cu_census -- where the workgroups of a launch on `stream` run: the
+ * evidence that a CU-budget stream holds exactly the compute units it was
+ * given ("HOCCL ...", section 2: the share of cores that communication holds
+ * while compute runs is the quantity measured).  Launches n_workgroups
+ * one-wave workgroups; each holds its CU for hold_us microseconds (a bounded
+ * wait, so that the launch spreads over every CU the stream may use), then
+ * writes d_ids[2w] = its HW_ID register (bits 8..15 hold the CU, shader
+ * array and shader engine numbers) and d_ids[2w + 1] = its XCC_ID register
+ * (bits 0..3: the XCD).  A CU is identified by (XCC_ID & 15, HW_ID bits
+ * 8..15).
+ *   d_ids: 2 * n_workgroups device u32, 4-byte aligned.  n_workgroups:
+ *   1..65536; hold_us: 0..100000.  Asynchronous on stream.
+ */
+hc_status_t hc_cu_census(uint32_t *d_ids, int n_workgroups, int hold_us, hipStream_t stream);
 
 /* Chunk size in elements for a per-rank buffer of count elements
  * (align = 1024 uncompressed, 16384 compressed); 0 on invalid input. */

@@ -196,6 +196,15 @@ def test_argument_errors_before_any_launch(hc):
     # CU-budget stream: k out of range (no device is touched for k < 1)
     s = ctypes.c_void_p(0)
     assert L.hc_stream_create_cu_budget(0, ctypes.byref(s)) != hc.HC_SUCCESS
+    assert L.hc_stream_create_cu_range(0, 0, ctypes.byref(s)) == E
+    assert L.hc_stream_create_cu_range(-1, 8, ctypes.byref(s)) == E
+    assert L.hc_stream_create_cu_range(0, 8, None) == E
+    # CU census: arguments checked before any launch
+    assert L.hc_cu_census(None, 8, 10, None) == E
+    assert L.hc_cu_census(0x100002, 8, 10, None) == E
+    assert L.hc_cu_census(0x100000, 0, 10, None) == E
+    assert L.hc_cu_census(0x100000, 65537, 10, None) == E
+    assert L.hc_cu_census(0x100000, 8, 100001, None) == E
 
 
 def test_step_counts(hc):
