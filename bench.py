@@ -745,13 +745,17 @@ def bench_contention(args):
     main = torch.cuda.Stream()
     rs_bytes = 3 * 2 * n * (R - 1)
 
-    def gemm_alone(iters):
+    def gemm_alone(iters, stream=None):
+        st = stream if stream is not None else main
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(main)
-        with torch.cuda.stream(main):
+        with torch.cuda.stream(st):
+            for _ in range(2):
+                torch.matmul(A, Bm, out=C)
+        e0.record(st)
+        with torch.cuda.stream(st):
             for _ in range(iters):
                 torch.matmul(A, Bm, out=C)
-        e1.record(main)
+        e1.record(st)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / iters
 
@@ -761,7 +765,7 @@ def bench_contention(args):
     torch.cuda.synchronize()
     t_gemm = gemm_alone(10)
 
-    def measure(op, side, cu_used, nbytes, prefix):
+    def measure(op, side, cu_used, nbytes, prefix, gemm_stream=None, t_gemm_ref=None):
         """`op(stream)` alone on `side`, then again while the GEMM loops on the
         main stream for as long as it runs."""
         for _ in range(2):
@@ -773,21 +777,23 @@ def bench_contention(args):
         e1.record(side)
         torch.cuda.synchronize()
         t_alone = e0.elapsed_time(e1)
-        iters = max(4, int(t_alone / t_gemm) + 2)
+        gs = gemm_stream if gemm_stream is not None else main
+        tg = t_gemm_ref if t_gemm_ref is not None else t_gemm
+        iters = max(4, int(t_alone / tg) + 2)
         base = torch.cuda.Event(enable_timing=True)
         ge = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
         r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        base.record(main)
+        base.record(gs)
         side.wait_event(base)
         r0.record(side)
         op(side)
         r1.record(side)
-        ge[0].record(main)
-        with torch.cuda.stream(main):
+        ge[0].record(gs)
+        with torch.cuda.stream(gs):
             for i in range(iters):
                 torch.matmul(A, Bm, out=C)
-                ge[i + 1].record(main)
+                ge[i + 1].record(gs)
         torch.cuda.synchronize()
         gt = [base.elapsed_time(e) for e in ge]
         t0, t1 = base.elapsed_time(r0), base.elapsed_time(r1)
@@ -797,8 +803,8 @@ def bench_contention(args):
         return {f"{prefix}_alone_ms": round(t_alone, 4), f"{prefix}_concurrent_ms": round(t1 - t0, 4),
                 f"{prefix}_alone_gbps": round(nbytes / t_alone / 1e6, 1),
                 f"{prefix}_concurrent_gbps": round(nbytes / (t1 - t0) / 1e6, 1),
-                "gemm_alone_ms": round(t_gemm, 4), "gemm_concurrent_ms": round(t_gemm_conc, 4),
-                "gemm_slowdown": round(t_gemm_conc / t_gemm - 1, 4),
+                "gemm_alone_ms": round(tg, 4), "gemm_concurrent_ms": round(t_gemm_conc, 4),
+                "gemm_slowdown": round(t_gemm_conc / tg - 1, 4),
                 "contention_rate": round(rate, 5) if rate is not None else None}
 
     rows = []
@@ -806,8 +812,26 @@ def bench_contention(args):
         handle = hc.hc_stream_create_cu_budget(k) if k else None
         side = torch.cuda.ExternalStream(handle) if k else torch.cuda.Stream()
         row = {"op": "reduce_scatter", "cu_budget": k if k else "all"}
-        row.update(measure(lambda st: hc.hc_reduce_scatter(send, recv, L, ws, cu_budget=k, stream=st), side,
-                           k if k else N_CU, rs_bytes, "rs"))
+        rs_op = (lambda st, k=k: hc.hc_reduce_scatter(send, recv, L, ws, cu_budget=k, stream=st))
+        row.update(measure(rs_op, side, k if k else N_CU, rs_bytes, "rs"))
+        if k:
+            # The GEMM confined to the other N_CU - k CUs: alone, and beside the
+            # reduce-scatter.  Alone it shows what losing k CUs costs; beside
+            # it, whatever is left is memory-system contention, since the two
+            # share no CU (hc_cu_census measures the split).
+            ch = hc.hc_stream_create_cu_range(k, N_CU - k)
+            comp = torch.cuda.ExternalStream(ch)
+            t_comp = gemm_alone(10, comp)
+            cm = measure(rs_op, side, k, rs_bytes, "rs", gemm_stream=comp, t_gemm_ref=t_comp)
+            row["complement"] = {"gemm_alone_ms": round(t_comp, 4),
+                                 "gemm_alone_slowdown_vs_all_cus": round(t_comp / t_gemm - 1, 4),
+                                 "gemm_concurrent_ms": cm["gemm_concurrent_ms"],
+                                 "gemm_slowdown_vs_complement_alone": cm["gemm_slowdown"],
+                                 "gemm_slowdown_vs_all_cus": round(cm["gemm_concurrent_ms"] / t_gemm - 1, 4),
+                                 "rs_concurrent_gbps": cm["rs_concurrent_gbps"],
+                                 "contention_rate": cm["contention_rate"]}
+            del comp
+            hc.hc_stream_destroy(ch)
         rows.append(row)
         if k:
             del side
