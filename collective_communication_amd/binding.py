@@ -45,7 +45,7 @@ EXPORTED = [
     "hc_status_string", "hc_last_error", "hc_version", "hc_step_count", "hc_allreduce_sgd",
     "hc_compress_bf16_scoped", "hc_compress_bf16_entropy", "hc_decompress_bf16_entropy",
     "hc_compress_bf16_staged", "hc_allreduce_bf16_f32carry", "hc_compress_bf16_noalloc", "hc_cu_census",
-    "hc_stream_create_cu_range",
+    "hc_stream_create_cu_range", "hc_copy_engine_available",
 ]
 
 
@@ -120,6 +120,8 @@ def load(path: str = LIB_PATH):
     L.hc_status_string.restype = ctypes.c_char_p
     L.hc_last_error.argtypes = []
     L.hc_last_error.restype = ctypes.c_char_p
+    L.hc_copy_engine_available.argtypes = []
+    L.hc_copy_engine_available.restype = I
     L.hc_version.argtypes = []
     L.hc_version.restype = ctypes.c_char_p
     _lib = L
@@ -483,6 +485,12 @@ def hc_cu_census(n_workgroups: int, hold_us: int = 50, *, stream=None):
 
 def hc_step_count(op: int, nranks: int) -> int:
     return int(load().hc_step_count(op, nranks))
+
+
+def hc_copy_engine_available() -> bool:
+    """True when this process's HIP runtime puts copy_engine copies on the DMA
+    engines (else copy_engine=1 raises HcError with HC_ERR_UNSUPPORTED)."""
+    return bool(load().hc_copy_engine_available())
 
 
 def hc_version() -> str:

@@ -132,6 +132,19 @@ struct Range {
 };
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
+// Whether this process's HIP runtime runs hipMemcpyDeviceToDeviceNoCU copies
+// on the DMA engines.  Measured on MI355X: the ROCm 7.2 runtime does; the
+// 7.0 runtime bundled with the PyTorch 2.10 wheel runs them as blit kernels
+// on the compute units.  Runtimes before 7.2 are therefore treated as not
+// offloading (version = major * 10^7 + minor * 10^5 + patch).
+bool dma_copies_offload() {
+  static const bool ok = [] {
+    int v = 0;
+    return hipRuntimeGetVersion(&v) == hipSuccess && v >= 70200000;
+  }();
+  return ok;
+}
+
 hc_status_t check_common(int nranks, hc_dtype_t dtype, const hc_opts_t* opts) {
   if (nranks < 1 || nranks > HC_MAX_RANKS)
     return fail(HC_ERR_INVALID_ARGUMENT, "nranks %d outside 1..%d", nranks, HC_MAX_RANKS);
@@ -145,6 +158,13 @@ hc_status_t check_common(int nranks, hc_dtype_t dtype, const hc_opts_t* opts) {
     if (opts->n_step_events < 0) return fail(HC_ERR_INVALID_ARGUMENT, "n_step_events < 0");
     if (opts->copy_engine != 0 && opts->copy_engine != 1)
       return fail(HC_ERR_INVALID_ARGUMENT, "copy_engine %d is neither 0 nor 1", opts->copy_engine);
+    if (opts->copy_engine == 1 && !dma_copies_offload()) {
+      int v = 0;
+      (void)hipRuntimeGetVersion(&v);
+      return fail(HC_ERR_UNSUPPORTED,
+                  "copy_engine: this process's HIP runtime (version %d) runs device-to-device NoCU copies as "
+                  "kernels on the compute units, not on the DMA engines", v);
+    }
     if (opts->step_event_mode != 0 && opts->step_event_mode != 1)
       return fail(HC_ERR_INVALID_ARGUMENT, "step_event_mode %d is neither 0 nor 1", opts->step_event_mode);
   }
@@ -434,6 +454,8 @@ const char* hc_status_string(hc_status_t s) {
 }
 
 const char* hc_last_error(void) { return g_last_error.c_str(); }
+
+int hc_copy_engine_available(void) { return dma_copies_offload() ? 1 : 0; }
 const char* hc_version(void) { return "hc 0.1 gfx950"; }
 
 int hc_step_count(hc_op_t op, int nranks) {

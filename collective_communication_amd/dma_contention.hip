@@ -11,11 +11,14 @@
 // on the compute units.  This program therefore runs outside any torch
 // process, with the GEMM from rocBLAS.
 //
-//   dma_contention verify   small all-gather (R=8 x 65,539 bf16): the
+//   dma_contention verify [dir]
+//                           small all-gather (R=8 x 65,540 bf16): the
 //                           copy-engine output must equal the copy-kernel
-//                           output byte for byte, and the copy-engine run
-//                           must finish while a bounded spin kernel holds
-//                           every wave slot of the GPU.  Exit 0 when both hold.
+//                           output byte for byte (with dir: the inputs and the
+//                           oracle's expected output read from dir, see
+//                           verify_against), and the copy-engine run must
+//                           finish while a bounded spin kernel holds every
+//                           wave slot of the GPU.  Exit 0 when both hold.
 //   dma_contention bench    R=8 slices of 2^25 bf16 -> 8 outputs of 2^28
 //                           (the all-gather after the reduce-scatter of an
 //                           8 x 2^28 bf16 allreduce), on copy kernels and on
@@ -197,7 +200,73 @@ unsigned long long compare_outputs(Ring& a, Ring& b) {
   return h;
 }
 
-int verify() {
+// Reads a whole file into a vector; false when it cannot.
+bool read_file(const std::string& path, std::vector<uint16_t>& out, size_t words) {
+  FILE* f = std::fopen(path.c_str(), "rb");
+  if (!f) return false;
+  out.resize(words);
+  const size_t got = std::fread(out.data(), 2, words, f);
+  std::fclose(f);
+  return got == words;
+}
+
+// verify with inputs and the expected all-gather from a directory written by
+// the test (the oracle's result): meta.txt "R L", in_<r>.bin (L bf16 words),
+// expected_<r>.bin (R * L words).  Returns the mismatched words of the
+// copy-engine all-gather against the expected bytes, or -1 on a bad input.
+long long verify_against(const char* dir, int* R_out, size_t* L_out, Ring* ring) {
+  int R = 0;
+  size_t L = 0;
+  {
+    FILE* f = std::fopen((std::string(dir) + "/meta.txt").c_str(), "r");
+    if (!f) return -1;
+    const int got = std::fscanf(f, "%d %zu", &R, &L);
+    std::fclose(f);
+    if (got != 2 || R < 1 || R > HC_MAX_RANKS || L < 1 || L > ((size_t)1 << 26)) return -1;
+  }
+  Ring g = make_ring(R, L);
+  std::vector<uint16_t> h;
+  for (int r = 0; r < R; ++r) {
+    if (!read_file(std::string(dir) + "/in_" + std::to_string(r) + ".bin", h, L)) return -1;
+    CK(hipMemcpy(g.send[r], h.data(), L * 2, hipMemcpyHostToDevice));
+  }
+  all_gather(g, 1, 0);
+  CK(hipDeviceSynchronize());
+  long long bad = 0;
+  std::vector<uint16_t> got(L * R), want;
+  for (int r = 0; r < R; ++r) {
+    if (!read_file(std::string(dir) + "/expected_" + std::to_string(r) + ".bin", want, L * R)) return -1;
+    CK(hipMemcpy(got.data(), g.out[r], L * R * 2, hipMemcpyDeviceToHost));
+    for (size_t i = 0; i < L * R; ++i) bad += got[i] != want[i];
+  }
+  *R_out = R;
+  *L_out = L;
+  *ring = g;
+  return bad;
+}
+
+int verify(const char* dir) {
+  if (dir) {   // the copy-engine all-gather against the oracle's bytes, then the offload check on the same ring
+    int R = 0;
+    size_t L = 0;
+    Ring g;
+    const long long bad = verify_against(dir, &R, &L, &g);
+    if (bad < 0) {
+      std::fprintf(stderr, "verify: cannot read the inputs in %s\n", dir);
+      return 2;
+    }
+    double t_ag = 0, t_hold = 0;
+    hipStream_t B;
+    CK(hipStreamCreateWithFlags(&B, hipStreamNonBlocking));
+    const bool offloaded = finishes_during_hold(g, B, 200.0, &t_ag, &t_hold);
+    CK(hipStreamDestroy(B));
+    std::printf("{\"mode\": \"verify\", \"against\": \"expected files\", \"ranks\": %d, \"slice\": %zu, "
+                "\"mismatched_words\": %lld, \"copy_engine_done_ms\": %.2f, \"slots_released_ms\": %.2f, "
+                "\"no_compute_units\": %s, \"hip_runtime\": \"%s\"}\n",
+                R, L, bad, t_ag, t_hold, offloaded ? "true" : "false", runtime_path().c_str());
+    free_ring(g);
+    return bad == 0 && offloaded ? 0 : 1;
+  }
   const int R = 8;
   const size_t L = 65536 + 4;  // even: the comparison reads whole words
   Ring cu = make_ring(R, L), dma = make_ring(R, L);
@@ -356,7 +425,7 @@ int bench() {
 
 int main(int argc, char** argv) {
   const char* mode = argc > 1 ? argv[1] : "verify";
-  if (!std::strcmp(mode, "verify")) return verify();
+  if (!std::strcmp(mode, "verify")) return verify(argc > 2 ? argv[2] : nullptr);
   if (!std::strcmp(mode, "bench")) return bench();
   std::fprintf(stderr, "usage: dma_contention verify|bench\n");
   return 2;

@@ -30,7 +30,8 @@
  *     misaligned pointer, count constraints, unknown dtype or option value.
  *   - HC_ERR_INSUFFICIENT_CAPACITY: workspace or output capacity too small.
  *   - HC_ERR_UNSUPPORTED: an option the call cannot honour (the copy engine
- *     for hc_compressed_allreduce).
+ *     for hc_compressed_allreduce, or in a process whose HIP runtime would not
+ *     put the copies on the DMA engines).
  *   - HC_ERR_DEVICE: a HIP call failed; hc_last_error() has the text.
  *   - HC_ERR_CORRUPT_STREAM: only ever written by the device into the
  *     caller's status word of hc_decompress_bf16 / hc_decompress_bf16_entropy.
@@ -116,9 +117,12 @@ typedef enum {
  *     values are HC_ERR_INVALID_ARGUMENT.  Which engine serves such a copy
  *     is the HIP runtime's choice: measured on MI355X, the ROCm 7.2 runtime
  *     in /opt/rocm uses the DMA engines (about 60 GB/s per copy, one copy at
- *     a time per stream), while the runtime bundled with the PyTorch 2.10
- *     wheel runs the same calls as blit kernels on the compute units.  The
- *     values are identical either way. */
+ *     a time per stream), while the 7.0 runtime bundled with the PyTorch
+ *     2.10 wheel runs the same calls as blit kernels on the compute units.
+ *     So a call with copy_engine = 1 in a process whose HIP runtime is older
+ *     than 7.2 returns HC_ERR_UNSUPPORTED (nothing is enqueued) instead of
+ *     silently using the compute units; hc_copy_engine_available() tells in
+ *     advance. */
 typedef struct {
     double chunk_fraction;
     int32_t cu_budget;
@@ -482,6 +486,11 @@ typedef struct {
  * steps then all-gather steps; receiver-major, then chunk, in each step).
  * Returns the number of tasks; writes at most cap (tasks may be NULL). */
 size_t hc_ring_tasks(int nranks, size_t count, size_t chunk, hc_task_t *tasks, size_t cap);
+
+/* 1 when this process's HIP runtime runs copy_engine copies on the DMA
+ * engines (runtime 7.2 or later), else 0: then copy_engine = 1 is
+ * HC_ERR_UNSUPPORTED. */
+int hc_copy_engine_available(void);
 
 const char *hc_status_string(hc_status_t status);
 const char *hc_last_error(void);  /* thread-local, "" when none */

@@ -60,3 +60,22 @@ def fold_chunked(xs, lo: int = 0, hi: int = -1, chunk: int = 1 << 22, threads: i
     with cf.ThreadPoolExecutor(threads) as ex:
         list(ex.map(one, range(lo, hi, chunk)))
     return out
+
+
+def copy_engine_or_unsupported(call):
+    """Runs call() (a library call with copy_engine=1).  When this process's
+    HIP runtime would not put the copies on the DMA engines, the call must
+    refuse with HC_ERR_UNSUPPORTED before enqueueing anything; returns True
+    when the call ran."""
+    import pytest
+
+    from collective_communication_amd import binding as hc
+
+    if hc.hc_copy_engine_available():
+        call()
+        return True
+    with pytest.raises(hc.HcError) as e:
+        call()
+    assert e.value.status == hc.HC_ERR_UNSUPPORTED
+    assert "DMA engines" in str(e.value)
+    return False

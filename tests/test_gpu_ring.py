@@ -17,7 +17,7 @@ import torch
 import oracle
 from collective_communication_amd import binding as hc
 from collective_communication_amd import inputs
-from hc_util import bits, first_mismatch, fold_chunked, to_dev, to_host
+from hc_util import bits, copy_engine_or_unsupported, first_mismatch, fold_chunked, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,13 @@ def test_allreduce_in_place_and_chunk_independent(dtype):
     for kw in ({"inplace": True}, {"chunk_fraction": 0.001}, {"chunk_fraction": 0.37},
                {"chunk_fraction": 1.0}, {"cu_budget": 8}, {"cu_budget": 32},
                {"copy_engine": 1}, {"copy_engine": 1, "inplace": True, "chunk_fraction": 0.01}):
-        got = run_ar(xs, **kw)
+        if kw.get("copy_engine"):
+            out = []
+            if not copy_engine_or_unsupported(lambda: out.append(run_ar(xs, **kw))):
+                continue
+            got = out[0]
+        else:
+            got = run_ar(xs, **kw)
         for r in range(R):
             assert np.array_equal(got[r], bits(ref[r])), f"{kw} rank={r}: {first_mismatch(got[r], bits(ref[r]))}"
 
@@ -93,13 +99,17 @@ def test_reduce_scatter_matches_oracle(dtype, R):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("R", [1, 2, 5, 8])
 def test_all_gather_matches_oracle(dtype, R, copy_engine):
-    """copy_engine=1: the copies run on the DMA engines (no compute unit)."""
+    """copy_engine=1: the copies run on the DMA engines (no compute unit), or
+    the call refuses where the runtime would not offload them."""
     for L in (1, 3, 4096, 20001):
         xs = rand(R, L, dtype, 3 * R + L)
         ref = oracle.all_gather_ring(xs)
         send = [to_dev(x) for x in xs]
         recv = [torch.empty(L * R, dtype=send[0].dtype, device=send[0].device) for _ in range(R)]
-        hc.hc_all_gather(send, recv, L, copy_engine=copy_engine)
+        if copy_engine and not copy_engine_or_unsupported(lambda: hc.hc_all_gather(send, recv, L, copy_engine=1)):
+            return
+        if not copy_engine:
+            hc.hc_all_gather(send, recv, L, copy_engine=copy_engine)
         torch.cuda.synchronize()
         for r in range(R):
             assert np.array_equal(to_host(recv[r]), bits(ref[r])), f"L={L} rank={r}"
@@ -169,29 +179,63 @@ def test_ring_bf16_workload_full_size():
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("R", [1, 3, 8])
 def test_allreduce_copy_engine_matches_oracle(dtype, R):
-    """Reduce-scatter on the compute units, all-gather on the DMA engines."""
+    """Reduce-scatter on the compute units, all-gather on the DMA engines (or a
+    refusal where this process's runtime would not offload the copies)."""
     for n in (1, 1000, 65536 + 5):
         xs = rand(R, n, dtype, 4242 * R + n, 1e-3 if dtype == "bf16" else 1.0)
         ref = oracle.allreduce_fold(xs)
-        got = run_ar(xs, copy_engine=1)
+        out = []
+        if not copy_engine_or_unsupported(lambda: out.append(run_ar(xs, copy_engine=1))):
+            return
+        got = out[0]
         for r in range(R):
             assert np.array_equal(got[r], bits(ref[r])), f"n={n} rank={r}: {first_mismatch(got[r], bits(ref[r]))}"
 
 
-def test_all_gather_copy_engine_under_system_runtime():
+def test_all_gather_copy_engine_under_system_runtime(tmp_path):
     """copy_engine=1 in a process on the system ROCm runtime (dma_contention,
-    no torch): the output equals the copy-kernel output byte for byte, and
-    the all-gather completes while a bounded kernel holds every wave slot of
-    the GPU, i.e. it used no compute unit.  (Inside a torch process the HIP
-    runtime bundled with the wheel may serve the same calls with blit kernels;
-    the tests above check the values there.)"""
+    no torch): the all-gather of seeded inputs written here equals the
+    oracle's all-gather byte for byte, and it completes while a bounded kernel
+    holds every wave slot of the GPU, i.e. it used no compute unit.  A second
+    run checks the tool's own copy-kernel comparison.  (Inside a torch process
+    the HIP runtime bundled with the wheel would serve the same calls with
+    blit kernels, so there the library refuses copy_engine=1.)"""
     tool = os.path.join(os.path.dirname(hc.LIB_PATH), "dma_contention")
     assert os.path.exists(tool), "dma_contention is not built"
-    r = subprocess.run([tool, "verify"], capture_output=True, text=True, timeout=120)
+    R, L = 8, 65536 + 3
+    xs = [inputs.normal_bf16("test", 8800 + r, L, 1e-3) for r in range(R)]
+    want = oracle.all_gather_ring(xs)
+    (tmp_path / "meta.txt").write_text(f"{R} {L}\n")
+    for r in range(R):
+        xs[r].astype("<u2").tofile(tmp_path / f"in_{r}.bin")
+        want[r].astype("<u2").tofile(tmp_path / f"expected_{r}.bin")
+    r = subprocess.run([tool, "verify", str(tmp_path)], capture_output=True, text=True, timeout=120)
     line = json.loads(r.stdout.strip().splitlines()[-1])
-    assert line["mismatched_words"] == 0, line
+    assert line["against"] == "expected files" and line["mismatched_words"] == 0, line
     assert line["no_compute_units"] is True, line
     assert r.returncode == 0, r.stdout + r.stderr
+    r = subprocess.run([tool, "verify"], capture_output=True, text=True, timeout=120)
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["mismatched_words"] == 0 and line["no_compute_units"] is True and r.returncode == 0, line
+
+
+def test_copy_engine_refused_where_it_would_use_compute_units():
+    """In this (torch) process: copy_engine=1 either runs on the DMA engines
+    (a runtime of 7.2 or later) or is refused before anything is enqueued."""
+    import ctypes
+
+    L = hc.load()
+    v = ctypes.c_int(0)
+    assert ctypes.CDLL("libamdhip64.so.7").hipRuntimeGetVersion(ctypes.byref(v)) == 0
+    assert hc.hc_copy_engine_available() == (v.value >= 70200000), v.value
+    xs = rand(3, 999, "bf16", 17)
+    send = [to_dev(x) for x in xs]
+    recv = [torch.full_like(s, 7.0) for s in send]
+    ran = copy_engine_or_unsupported(lambda: hc.hc_allreduce(send, recv, copy_engine=1))
+    torch.cuda.synchronize()
+    if not ran:   # nothing was enqueued
+        assert all(bool((t == 7.0).all()) for t in recv)
+    assert L.hc_copy_engine_available() in (0, 1)
 
 
 def test_hbm_ceiling_tool():

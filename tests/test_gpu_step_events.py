@@ -11,7 +11,7 @@ import torch
 import oracle
 from collective_communication_amd import binding as hc
 from collective_communication_amd import inputs
-from hc_util import first_mismatch, to_dev, to_host
+from hc_util import copy_engine_or_unsupported, first_mismatch, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +57,9 @@ def test_allreduce(copy_engine):
     send = [to_dev(x) for x in xs]
     recv = [torch.empty_like(s) for s in send]
     steps = hc.hc_step_count(hc.HC_OP_ALLREDUCE, R)
+    if copy_engine and not copy_engine_or_unsupported(
+            lambda: stamped(lambda ev: hc.hc_allreduce(send, recv, step_events=ev, copy_engine=1), steps)):
+        return   # this process's runtime would not offload the copies: the call refused
     d, _ = stamped(lambda ev: hc.hc_allreduce(send, recv, step_events=ev, copy_engine=copy_engine), steps)
     check([to_host(t) for t in recv], oracle.allreduce_fold(xs), f"copy_engine {copy_engine}")
     assert all(t > 0 for t in d[:R - 1])          # reduce-scatter kernels
