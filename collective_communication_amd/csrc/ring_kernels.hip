@@ -7,8 +7,9 @@
 // it (recv) during all-gather.  "CCCL: In-GPU Compression-Coupled
 // Collective Communication" (Figure 2, section 5) shows NCCL's version moving
 // 16-byte packs; here every lane moves 16-byte vectors too (4 fp32 or 8
-// bf16), two of them per operand in flight, so a wave64 issues fully
-// coalesced 1 KB loads, marked non-temporal.  Both kernels are HBM bound: a reduce hop reads 2
+// bf16), one to four of them per operand in flight (the launch policy
+// below), so a wave64 issues fully coalesced 1 KB loads, marked
+// non-temporal.  Both kernels are HBM bound: a reduce hop reads 2
 // and writes 1 element per element of the step, a copy hop reads 1, writes 1.
 //
 // The last reduce-scatter step of the fused allreduce + SGD update
@@ -22,18 +23,17 @@
 // receiver), cut into 4096-element (bf16) / 2048-element (fp32) tiles, one
 // tile per workgroup, or a persistent grid-stride loop when the caller gives
 // a CU budget.
+#include <cstdlib>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace hc {
 namespace {
 
-// Tuning knobs (compile-time).  Measured on MI355X for R=8 x 2^26 bf16: two
-// 16-byte vectors per operand per lane and non-temporal loads give the
-// fastest hops; the non-temporal hint matters on the received operand,
-// whose lines would otherwise push the partials that the next step reads
-// out of the caches.  Non-temporal stores are slower (the next hop reads
-// what this one writes).
+// Tuning knobs (compile-time).  Non-temporal loads are the fastest on every
+// hop: the hint matters on the received operand, whose lines would otherwise
+// push the partials that the next step reads out of the caches.
 #ifndef HC_RING_UNROLL
 #define HC_RING_UNROLL 2
 #endif
@@ -49,7 +49,29 @@ namespace {
 #ifndef HC_RING_NT_STORE
 #define HC_RING_NT_STORE 0
 #endif
-constexpr int kUnroll = HC_RING_UNROLL;  // 16-byte vectors per operand in flight per lane
+constexpr int kUnroll = HC_RING_UNROLL;  // 16-byte vectors per operand in flight per lane (carry hops)
+
+// How a step launch moves its tiles, chosen per launch on the host
+// (launch_step).  Measured on MI355X with the R=8 bf16 reduce hop:
+//  - kPolicyCached: 2 vectors per operand per lane, ordinary stores.  The
+//    next hop reads what this one writes; while a launch writes no more than
+//    the 256 MB Infinity Cache holds, much of that comes back from the cache
+//    (R=8 x 2^26: 6.8 TB/s; non-temporal stores lose that and run 6.2-6.4).
+//  - kPolicyStream: 1 vector per operand per lane, non-temporal stores, for
+//    launches that write more than the cache holds, so every byte goes to
+//    HBM anyway (R=8 x 2^28: 6.4 TB/s against 5.9 with the cached policy).
+//  - kPolicyBudget: 4 vectors per operand per lane, ordinary stores, on a CU
+//    budget, where each CU's rate is bound by the loads it keeps in flight
+//    (R=8 x 2^28 on 8 CUs: 471 GB/s against 451 with 2).
+constexpr int kPolicyCached = 0;
+constexpr int kPolicyStream = 1;
+constexpr int kPolicyBudget = 2;
+__host__ __device__ constexpr int policy_unroll(int p) { return p == kPolicyStream ? 1 : p == kPolicyBudget ? 4 : 2; }
+__host__ __device__ constexpr bool policy_nt_store(int p) { return p == kPolicyStream; }
+// Launches that write at least this many bytes take kPolicyStream (between
+// the 256 MiB that still gain from the cache and the 512 MiB that do not);
+// HC_STREAM_STORE_MIN_BYTES in the environment replaces it.
+constexpr uint64_t kStreamStoreMinBytes = 320ull << 20;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -72,8 +94,9 @@ __device__ __forceinline__ uint2 ld_stream8(const char* p) {
     return *reinterpret_cast<const uint2*>(p);
   }
 }
+template <bool NT>
 __device__ __forceinline__ void st_stream(char* p, uint4 v) {
-  if constexpr (HC_RING_NT_STORE) {
+  if constexpr (NT) {
     const u32x4 w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
   } else {
@@ -147,13 +170,15 @@ __device__ __forceinline__ uint4 vec_hop(uint4 a, uint4 b) {
 // kSgdSend).  VEC: every segment pointer is 16-byte aligned, so whole
 // tiles move as 16-byte vectors; otherwise (odd slice offsets) each lane
 // moves elements.
-template <int ES, int OP, bool VEC>
+template <int ES, int OP, bool VEC, int POLICY>
 __global__ __launch_bounds__(kThreads) void step_kernel(SegArgs args) {
   constexpr bool kUsesB = OP == kReduce || OP == kSgd || OP == kReduceSend || OP == kSgdSend;
   constexpr bool kUpdates = OP == kSgd || OP == kSgdOne || OP == kSgdSend;
   constexpr bool kSends = OP == kReduceSend || OP == kSgdSend;
   constexpr int V = 16 / ES;
-  constexpr uint64_t kTile = (uint64_t)kThreads * V * kUnroll;
+  constexpr int U = policy_unroll(POLICY);
+  constexpr bool NTS = policy_nt_store(POLICY);
+  constexpr uint64_t kTile = (uint64_t)kThreads * V * U;
   const uint32_t total = args.tile0[args.nseg];
   const int tid = threadIdx.x;
   for (uint32_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
@@ -170,31 +195,31 @@ __global__ __launch_bounds__(kThreads) void step_kernel(SegArgs args) {
     char* pd = static_cast<char*>(args.dst[s]);
     char* pd2 = kSends ? static_cast<char*>(args.dst2[s]) : nullptr;
     if (VEC && base + kTile <= len) {
-      uint4 va[kUnroll], vb[kUnroll], vw[kUnroll];
+      uint4 va[U], vb[U], vw[U];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < U; ++u) {
         const uint64_t off = (base + (uint64_t)(u * kThreads + tid) * V) * ES;
         va[u] = ld_stream<HC_RING_NT_A>(pa + off);
         if constexpr (kUsesB) vb[u] = ld_stream<HC_RING_NT_B>(pb + off);
         if constexpr (kUpdates) vw[u] = ld16(pd + off);
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < U; ++u) {
         const uint64_t off = (base + (uint64_t)(u * kThreads + tid) * V) * ES;
-        if constexpr (OP == kCopy) st_stream(pd + off, va[u]);
-        else if constexpr (OP == kReduce) st_stream(pd + off, vec_hop<ES>(va[u], vb[u]));
+        if constexpr (OP == kCopy) st_stream<NTS>(pd + off, va[u]);
+        else if constexpr (OP == kReduce) st_stream<NTS>(pd + off, vec_hop<ES>(va[u], vb[u]));
         else if constexpr (OP == kReduceSend) {
           const uint4 r = vec_hop<ES>(va[u], vb[u]);
-          st_stream(pd + off, r);
-          st_stream(pd2 + off, r);
+          st_stream<NTS>(pd + off, r);
+          st_stream<NTS>(pd2 + off, r);
         }
-        else if constexpr (OP == kSgd) st_stream(pd + off, vec_sgd<ES>(vw[u], vec_hop<ES>(va[u], vb[u]), args.lr));
+        else if constexpr (OP == kSgd) st_stream<NTS>(pd + off, vec_sgd<ES>(vw[u], vec_hop<ES>(va[u], vb[u]), args.lr));
         else if constexpr (OP == kSgdSend) {
           const uint4 r = vec_sgd<ES>(vw[u], vec_hop<ES>(va[u], vb[u]), args.lr);
-          st_stream(pd + off, r);
-          st_stream(pd2 + off, r);
+          st_stream<NTS>(pd + off, r);
+          st_stream<NTS>(pd2 + off, r);
         }
-        else st_stream(pd + off, vec_sgd<ES>(vw[u], va[u], args.lr));
+        else st_stream<NTS>(pd + off, vec_sgd<ES>(vw[u], va[u], args.lr));
       }
     } else {
       const uint64_t end = base + kTile < len ? base + kTile : len;
@@ -272,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void carry_kernel(SegArgs args) {
         const uint32_t s0 = hop_f32(wa[q][0], vb[q].x << 16), s1 = hop_f32(wa[q][1], vb[q].x & 0xFFFF0000u);
         const uint32_t s2 = hop_f32(wa[q][2], vb[q].y << 16), s3 = hop_f32(wa[q][3], vb[q].y & 0xFFFF0000u);
         if constexpr (DF) {
-          st_stream(pd + 4 * e, make_uint4(s0, s1, s2, s3));
+          st_stream<HC_RING_NT_STORE>(pd + 4 * e, make_uint4(s0, s1, s2, s3));
         } else {
           const uint2 r = make_uint2(bf16_rne(s0) | (bf16_rne(s1) << 16), bf16_rne(s2) | (bf16_rne(s3) << 16));
           *reinterpret_cast<uint2*>(pd + 2 * e) = r;
@@ -335,13 +360,19 @@ hipError_t launch_carry(const Seg* segs, int nseg, int cu_budget, hipStream_t st
                        dim3(grid), dim3(kThreads), kargs, stream);
 }
 
-template <int ES, int OP>
-hipError_t launch_step(const Seg* segs, int nseg, int cu_budget, hipStream_t stream, float lr = 0.0f) {
+uint64_t stream_store_min_bytes() {
+  const char* e = getenv("HC_STREAM_STORE_MIN_BYTES");
+  if (!e || !*e) return kStreamStoreMinBytes;
+  char* end = nullptr;
+  const unsigned long long v = strtoull(e, &end, 10);
+  return *end == 0 ? (uint64_t)v : kStreamStoreMinBytes;
+}
+
+template <int ES, int OP, int POLICY>
+hipError_t launch_step_as(const Seg* segs, int nseg, int cu_budget, hipStream_t stream, float lr) {
   constexpr bool kUsesB = OP == kReduce || OP == kSgd || OP == kReduceSend || OP == kSgdSend;
   constexpr bool kSends = OP == kReduceSend || OP == kSgdSend;
-  constexpr uint64_t kTile = (uint64_t)kThreads * (16 / ES) * kUnroll;
-  if (nseg <= 0) return hipSuccess;
-  if (nseg > kMaxSegs) return hipErrorInvalidValue;
+  constexpr uint64_t kTile = (uint64_t)kThreads * (16 / ES) * policy_unroll(POLICY);
   SegArgs args;
   uint64_t tiles = 0;
   bool vec = true;
@@ -371,8 +402,24 @@ hipError_t launch_step(const Seg* segs, int nseg, int cu_budget, hipStream_t str
     if (grid > cap) grid = (uint32_t)cap;
   }
   void* kargs[] = {&args};
-  return launch_kernel(vec ? (const void*)step_kernel<ES, OP, true> : (const void*)step_kernel<ES, OP, false>,
+  return launch_kernel(vec ? (const void*)step_kernel<ES, OP, true, POLICY>
+                           : (const void*)step_kernel<ES, OP, false, POLICY>,
                        dim3(grid), dim3(kThreads), kargs, stream);
+}
+
+// One ring step: picks the launch policy (see kPolicyCached) from the CU
+// budget and the bytes the launch writes.
+template <int ES, int OP>
+hipError_t launch_step(const Seg* segs, int nseg, int cu_budget, hipStream_t stream, float lr = 0.0f) {
+  constexpr bool kSends = OP == kReduceSend || OP == kSgdSend;
+  if (nseg <= 0) return hipSuccess;
+  if (nseg > kMaxSegs) return hipErrorInvalidValue;
+  if (cu_budget > 0) return launch_step_as<ES, OP, kPolicyBudget>(segs, nseg, cu_budget, stream, lr);
+  uint64_t written = 0;
+  for (int i = 0; i < nseg; ++i) written += segs[i].len * ES * (kSends ? 2 : 1);
+  if (written >= stream_store_min_bytes())
+    return launch_step_as<ES, OP, kPolicyStream>(segs, nseg, cu_budget, stream, lr);
+  return launch_step_as<ES, OP, kPolicyCached>(segs, nseg, cu_budget, stream, lr);
 }
 
 // Where each workgroup runs: word 2w = its HW_ID register (CU, shader array
