@@ -18,8 +18,10 @@ table_scope (the codec's code tables per block, per group of blocks or global,
 and the per-block encoder in three global rounds, on 2^28 bf16 weights,
 gradients and a multi-layer gradient bucket), entropy
 (the HCE1 variant with per-block Huffman codes for the exponent, next to the
-fixed-length codec on the same 2^28 tensors).  Each prints one JSON line of
-its own.
+fixed-length codec on the same 2^28 tensors), hop_sizes (the reduce-scatter
+hop at 2^24..2^28 elements per rank under each store policy, with and without
+a cold Infinity Cache), rs_budget (the contention test's reduce-scatter on
+k = 8, 16, 32 CUs and on all CUs, without the GEMM).  Each prints one JSON line of its own.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 The headline time is K back-to-back calls with nothing else on the stream.
@@ -52,6 +54,7 @@ CODEC_FILES = ["collective_communication_amd/csrc/codec_kernels.hip", "collectiv
                "collective_communication_amd/csrc/lookback.hpp"]
 ENTROPY_FILES = ["collective_communication_amd/csrc/entropy_kernels.hip", "collective_communication_amd/csrc/codec.hpp",
                  "collective_communication_amd/csrc/lookback.hpp"]
+RING_FILES = ["collective_communication_amd/csrc/ring_kernels.hip", "collective_communication_amd/csrc/common.hpp"]
 
 
 def kernel_hash(files) -> str:
@@ -241,8 +244,7 @@ def bench_ring(args, workload: str):
     algbw = n * es / (ms / 1e3) / 1e9
     hbm = alg_bytes / (ms / 1e3) / 1e9
     achieved = red_launch_bytes / (avg_red / 1e3) / 1e9
-    files = ["collective_communication_amd/csrc/ring_kernels.hip", "collective_communication_amd/csrc/common.hpp"]
-    traffic = load_traffic("reduce_step", workload, files)
+    traffic = load_traffic("reduce_step", workload, RING_FILES)
     line = {
         "metric": METRIC, "value": round(algbw, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
@@ -838,7 +840,8 @@ def bench_contention(args):
             hc.hc_stream_destroy(handle)
     full = rows[-1]
     extra = {"roofline": roofline_obj("step_kernel<reduce> (reduce-scatter alone on all CUs, mean of its launches)",
-                                      3 * 2 * n, full["rs_alone_ms"] / (R - 1), None,
+                                      3 * 2 * n, full["rs_alone_ms"] / (R - 1),
+                                      load_traffic("reduce_step", "contention", RING_FILES),
                                       "one reduce-scatter of R-1 launches by HIP events, divided by R-1")}
     if not args.no_cpu_baseline:
         import oracle
@@ -871,6 +874,134 @@ def bench_contention(args):
             "all_gather": ag, **extra}
 
 
+def bench_hop_sizes(args):
+    """The reduce-scatter hop (R=8 bf16, all CUs) at 2^24..2^28 elements per
+    rank, per ring step, under each store policy and cache state:
+      - policy "auto" (the library's choice), "cached" (2 vectors per lane,
+        ordinary stores) and "stream" (1 vector per lane, non-temporal
+        stores), forced through HC_STREAM_STORE_MIN_BYTES;
+      - "scrub": a 2 GiB read-modify-write before each call evicts the
+        Infinity Cache, so the first step starts cold;
+      - "rotate K" (2^26 only): K sets of buffers used in turn, so a call's
+        inputs were last touched K calls earlier.
+    Step 0 reads only the inputs; every later step also reads the partial
+    sums the step before it wrote (the reduce-scatter's workspace)."""
+    import statistics
+
+    import torch
+
+    from collective_communication_amd import binding as hc
+    from collective_communication_amd import inputs
+
+    R, es = 8, 2
+    steps = hc.hc_step_count(hc.HC_OP_REDUCE_SCATTER, R)
+    iters = max(args.steps, 2)
+    scrub = torch.zeros(1 << 29, dtype=torch.float32, device="cuda")
+
+    def make(n, seed):
+        send = [inputs.normal_bf16_cuda("contention", 1000 * seed + r, n, 1e-3) for r in range(R)]
+        recv = [torch.empty(n // R, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+        ws = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_REDUCE_SCATTER, n, R, hc.HC_BF16), dtype=torch.uint8,
+                         device="cuda")
+        return send, recv, ws
+
+    def run(sets, n, flush):
+        for k in range(args.warmup):
+            s, r, w = sets[k % len(sets)]
+            hc.hc_reduce_scatter(s, r, n // R, w)
+        evs = [hc.StepEvents.for_steps(steps, mode=1) for _ in range(iters)]
+        for k in range(iters):
+            s, r, w = sets[k % len(sets)]
+            if flush:
+                scrub.add_(1.0)
+            hc.hc_reduce_scatter(s, r, n // R, w, step_events=evs[k])
+        torch.cuda.synchronize()
+        d = [e.elapsed_ms() for e in evs]
+        per = [statistics.median(x[i] for x in d) for i in range(steps)]
+        b = 3 * es * n
+        return {"step_us": [round(t * 1e3, 2) for t in per],
+                "first_step_gbps": round(b / (per[0] / 1e3) / 1e9),
+                "later_steps_gbps": round(b / (statistics.mean(per[1:]) / 1e3) / 1e9)}
+
+    env_key = "HC_STREAM_STORE_MIN_BYTES"
+    old = os.environ.get(env_key)
+    rows = []
+    try:
+        for lg in (24, 25, 26, 27, 28):
+            n = 1 << lg
+            bufs = [make(n, lg)]
+            for policy, val in (("auto", None), ("cached", str(1 << 62)), ("stream", "0")):
+                if val is None:
+                    os.environ.pop(env_key, None)
+                else:
+                    os.environ[env_key] = val
+                rows.append({"log2_elems_per_rank": lg, "policy": policy, "scrub": False, **run(bufs, n, False)})
+                if policy == "auto":
+                    rows.append({"log2_elems_per_rank": lg, "policy": policy, "scrub": True, **run(bufs, n, True)})
+            del bufs
+            torch.cuda.empty_cache()
+        os.environ.pop(env_key, None)
+        n = 1 << 26
+        sets = [make(n, 40 + k) for k in range(8)]
+        for K in (1, 2, 4, 8):
+            rows.append({"log2_elems_per_rank": 26, "policy": "auto", "rotate": K, **run(sets[:K], n, False)})
+        del sets
+    finally:
+        if old is None:
+            os.environ.pop(env_key, None)
+        else:
+            os.environ[env_key] = old
+    auto28 = next(r for r in rows if r["log2_elems_per_rank"] == 28 and r["policy"] == "auto" and not r.get("scrub"))
+    return {"metric": "reduce-scatter hop GB/s by operand size, store policy and cache state (R=8 bf16)",
+            "value": auto28["later_steps_gbps"], "unit": "GB/s", "n_gpus": 1, "steps": iters,
+            "warmup": args.warmup, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "reduce-scatter of R=8 x 2^24..2^28 bf16 N(0,1e-3), all CUs; value: 2^28, "
+                                   "library policy, steps after the first"},
+            "bytes_per_step": "3 x 2 bytes x elements per rank (2 reads, 1 write per element of the step)",
+            "rows": rows}
+
+def bench_rs_budget(args):
+    """The contention test's reduce-scatter (R=8 x 2^28 bf16, N(0,1e-3))
+    without the GEMM: on a k-CU stream (hc_stream_create_cu_budget) for
+    k = 8, 16, 32, and on all CUs, each timed alone by HIP events on its
+    stream.  The run the CU-occupancy and traffic counters are taken on."""
+    import torch
+
+    from collective_communication_amd import binding as hc
+    from collective_communication_amd import inputs
+
+    R, n = 8, 1 << 28
+    L = n // R
+    send = inputs.ring_inputs_cuda("contention", R, n)
+    recv = [torch.empty(L, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    ws = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_REDUCE_SCATTER, n, R, hc.HC_BF16), dtype=torch.uint8,
+                     device="cuda")
+    rs_bytes = 3 * 2 * n * (R - 1)
+    rows = []
+    for k in (8, 16, 32, 0):
+        handle = hc.hc_stream_create_cu_budget(k) if k else None
+        side = torch.cuda.ExternalStream(handle) if k else torch.cuda.Stream()
+        for _ in range(args.warmup):
+            hc.hc_reduce_scatter(send, recv, L, ws, cu_budget=k, stream=side)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(side)
+        for _ in range(args.steps):
+            hc.hc_reduce_scatter(send, recv, L, ws, cu_budget=k, stream=side)
+        e1.record(side)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        rows.append({"cu_budget": k if k else "all", "rs_ms": round(ms, 4),
+                     "rs_gbps": round(rs_bytes / (ms / 1e3) / 1e9, 1)})
+        del side
+        if k:
+            hc.hc_stream_destroy(handle)
+    return {"metric": "reduce-scatter GB/s on k CUs (R=8 x 2^28 bf16, no concurrent GEMM)",
+            "value": rows[0]["rs_gbps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"R={R} reduce-scatter of {R} x {n} bf16 N(0,1e-3) on a k-CU stream; value: k = 8"},
+            "bytes_per_call": rs_bytes, "rows": rows}
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -878,7 +1009,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ring_bf16",
                     choices=["ring_bf16", "ring_f32", "ring_bf16_carry", "codec", "compressed", "contention",
-                             "fused_sgd", "table_scope", "entropy"])
+                             "fused_sgd", "table_scope", "entropy", "hop_sizes", "rs_budget"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 26,
                     help="elements per rank the oracle baseline runs on (default: the whole workload)")
@@ -908,6 +1039,10 @@ def main():
         line = bench_table_scope(args)
     elif args.workload == "entropy":
         line = bench_entropy(args)
+    elif args.workload == "hop_sizes":
+        line = bench_hop_sizes(args)
+    elif args.workload == "rs_budget":
+        line = bench_rs_budget(args)
     else:
         line = bench_contention(args)
     print(json.dumps(line), flush=True)
