@@ -6,6 +6,7 @@
 // caller's stream and never synchronize it.
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -101,6 +102,20 @@ Tap::~Tap() {
   if (open) t_stamp = Stamp{};
 }
 
+bool log_enabled() {
+  const char* e = getenv("HC_LOG");
+  return e && *e && strcmp(e, "0") != 0;
+}
+
+void log_line(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "hc: %s\n", buf);
+}
+
 }  // namespace hc
 
 namespace {
@@ -145,7 +160,12 @@ bool dma_copies_offload() {
   return ok;
 }
 
+hc_status_t check_env();
+double chunk_fraction(const hc_opts_t* o);
+int cu_budget(const hc_opts_t* o);
+
 hc_status_t check_common(int nranks, hc_dtype_t dtype, const hc_opts_t* opts) {
+  if (hc_status_t st = check_env()) return st;
   if (nranks < 1 || nranks > HC_MAX_RANKS)
     return fail(HC_ERR_INVALID_ARGUMENT, "nranks %d outside 1..%d", nranks, HC_MAX_RANKS);
   if (dtype != HC_F32 && dtype != HC_BF16)
@@ -184,11 +204,61 @@ hc_status_t make_tap(const hc_opts_t* o, hc_op_t op, int nranks, Tap* tap) {
   return HC_SUCCESS;
 }
 
-double chunk_fraction(const hc_opts_t* o) {
-  return (o && o->chunk_fraction != 0.0) ? o->chunk_fraction : 0.01;
+// Defaults of the chunk fraction and the CU budget, which the environment may
+// replace where a call passes no options or leaves the field 0:
+// HC_CHUNK_FRACTION (a number in (0, 1]) and HC_CU_BUDGET (an integer in
+// 0..4096).  check_common rejects a malformed value before anything runs.
+bool env_chunk_fraction(double* out) {
+  const char* e = getenv("HC_CHUNK_FRACTION");
+  if (!e || !*e) return false;
+  char* end = nullptr;
+  const double v = strtod(e, &end);
+  if (*end != 0 || !(v > 0.0 && v <= 1.0)) return false;
+  *out = v;
+  return true;
 }
-int cu_budget(const hc_opts_t* o) { return o ? o->cu_budget : 0; }
+bool env_cu_budget(int* out) {
+  const char* e = getenv("HC_CU_BUDGET");
+  if (!e || !*e) return false;
+  char* end = nullptr;
+  const long v = strtol(e, &end, 10);
+  if (*end != 0 || v < 0 || v > 4096) return false;
+  *out = (int)v;
+  return true;
+}
+hc_status_t check_env() {
+  const char* f = getenv("HC_CHUNK_FRACTION");
+  double fv;
+  if (f && *f && !env_chunk_fraction(&fv))
+    return fail(HC_ERR_INVALID_ARGUMENT, "environment HC_CHUNK_FRACTION=\"%.64s\" is not a number in (0, 1]", f);
+  const char* b = getenv("HC_CU_BUDGET");
+  int bv;
+  if (b && *b && !env_cu_budget(&bv))
+    return fail(HC_ERR_INVALID_ARGUMENT, "environment HC_CU_BUDGET=\"%.64s\" is not an integer in 0..4096", b);
+  return HC_SUCCESS;
+}
+
+double chunk_fraction(const hc_opts_t* o) {
+  if (o && o->chunk_fraction != 0.0) return o->chunk_fraction;
+  double v;
+  return env_chunk_fraction(&v) ? v : 0.01;
+}
+int cu_budget(const hc_opts_t* o) {
+  if (o && o->cu_budget != 0) return o->cu_budget;
+  int v;
+  return env_cu_budget(&v) ? v : 0;
+}
 bool copy_engine(const hc_opts_t* o) { return o && o->copy_engine == 1; }
+
+// One HC_LOG line for a ring call: its shape and the options in force.
+void log_ring(const char* op, int nranks, size_t count, hc_dtype_t dtype, size_t chunk, const hc_opts_t* opts,
+              const char* note) {
+  if (!hc::log_enabled()) return;
+  hc::log_line("%s: ranks=%d count=%zu dtype=%s chunk=%zu cu_budget=%d copy_engine=%d steps=%d%s%s", op, nranks,
+               count, dtype == HC_F32 ? "f32" : "bf16", chunk, cu_budget(opts), copy_engine(opts) ? 1 : 0,
+               opts && opts->step_events ? (opts->step_event_mode == 1 ? 2 : 1) : 0, note ? " " : "",
+               note ? note : "");
+}
 
 // One copy step: the segments as one copy kernel on the compute units, or as
 // one DMA copy per segment on the copy engines (stream ordered).
@@ -508,6 +578,7 @@ hc_status_t hc_allreduce(void* const* sendbufs, void* const* recvbufs, size_t co
   Tap tap;
   if ((st = make_tap(opts, HC_OP_ALLREDUCE, nranks, &tap))) return st;
   const size_t chunk = hc::chunk_elems(count, chunk_fraction(opts), 1024);
+  log_ring("allreduce", nranks, count, dtype, chunk, opts, "(one segment per receiver and step: a step's chunks are merged)");
   if (nranks == 1)
     return run_single(sendbufs[0], recvbufs[0], count, es, cu_budget(opts), copy_engine(opts), tap, stream);
   return run_allreduce(sendbufs, recvbufs, count, dtype, nranks, chunk, cu_budget(opts), copy_engine(opts), tap,
@@ -543,6 +614,8 @@ hc_status_t hc_allreduce_bf16_f32carry(void* const* sendbufs, void* const* recvb
   }
   Tap tap;
   if ((st = make_tap(opts, HC_OP_ALLREDUCE_F32_CARRY, nranks, &tap))) return st;
+  log_ring("allreduce_bf16_f32carry", nranks, count, HC_BF16, hc::chunk_elems(count, chunk_fraction(opts), 1024), opts,
+           "(one segment per receiver and step)");
   if (nranks == 1)
     return run_single(sendbufs[0], recvbufs[0], count, 2, cu_budget(opts), copy_engine(opts), tap, stream);
   const size_t chunk = hc::chunk_elems(count, chunk_fraction(opts), 1024);
@@ -572,6 +645,8 @@ hc_status_t hc_allreduce_sgd(void* const* grads, void* const* weights, size_t co
         return fail(HC_ERR_INVALID_ARGUMENT, "buffers %zu and %zu overlap (grads 0..R-1, then weights)", i, j);
   Tap tap;
   if ((st = make_tap(opts, HC_OP_ALLREDUCE, nranks, &tap))) return st;
+  log_ring("allreduce_sgd", nranks, count, dtype, hc::chunk_elems(count, chunk_fraction(opts), 1024), opts,
+           "(one segment per receiver and step)");
   if (nranks == 1) {  // the sum is the one gradient: one update step
     hipError_t e = tap.mark(stream);
     hc::Seg seg{grads[0], nullptr, weights[0], count};
@@ -636,6 +711,8 @@ hc_status_t hc_reduce_scatter(void* const* sendbufs, void* const* recvbufs, size
   if ((st = check_disjoint(in, out, ok))) return st;
   Tap tap;
   if ((st = make_tap(opts, HC_OP_REDUCE_SCATTER, R, &tap))) return st;
+  log_ring("reduce_scatter", R, n, dtype, hc::chunk_elems(n, chunk_fraction(opts), 1024), opts,
+           "(one segment per receiver and step)");
   if (R == 1) return run_single(sendbufs[0], recvbufs[0], L, es, cu_budget(opts), copy_engine(opts), tap, stream);
   const size_t need = 2 * n * es;
   if (!d_ws) return fail(HC_ERR_INVALID_ARGUMENT, "d_ws is NULL");
@@ -690,6 +767,8 @@ hc_status_t hc_all_gather(void* const* sendbufs, void* const* recvbufs, size_t s
   const int budget = cu_budget(opts);
   Tap tap;
   if ((st = make_tap(opts, HC_OP_ALL_GATHER, R, &tap))) return st;
+  log_ring("all_gather", R, n, dtype, hc::chunk_elems(n, chunk_fraction(opts), 1024), opts,
+           "(one segment per receiver and step)");
   hipError_t e0 = tap.mark(stream);
   if (e0 != hipSuccess) return device_fail(e0, "hipEventRecord");
   // Local copies (each rank's own slice into its own output), skipped in place.
@@ -751,6 +830,11 @@ hc_status_t compress_common(const uint16_t* d_in, size_t n, void* d_out, size_t 
       wr{(uintptr_t)d_ws, (uintptr_t)d_ws + need};
   if (overlap(ir, orr) || overlap(ir, wr) || overlap(orr, wr))
     return fail(HC_ERR_INVALID_ARGUMENT, "input, output and workspace must not overlap");
+  if (hc::log_enabled()) {
+    static const char* const kName[] = {"compress", "compress_scoped", "compress_entropy", "compress_staged"};
+    hc::log_line("%s: n=%zu blocks=%zu out_cap=%zu table_blocks=%zu", kName[(int)coder], n,
+                 hc::ceil_div(n, (size_t)HC_BLOCK_ELEMS), out_cap, table_blocks);
+  }
   hipError_t e = coder == Coder::kScoped
                      ? hc::launch_compress_scoped(d_in, n, d_out, d_out_bytes, d_ws, table_blocks, stream)
                  : coder == Coder::kEntropy ? hc::launch_hce_compress(d_in, n, d_out, d_out_bytes, d_ws, stream)
@@ -783,6 +867,9 @@ hc_status_t hc_compress_bf16_noalloc(const uint16_t* d_in, size_t n, void* d_out
   void* ws = nullptr;
   hipError_t e = hc::noalloc_scratch(&ws);
   if (e != hipSuccess) return device_fail(e, "static scratch address");
+  if (hc::log_enabled())
+    hc::log_line("compress_noalloc: n=%zu blocks=%zu out_cap=%zu (static workspace)", n,
+                 hc::ceil_div(n, (size_t)HC_BLOCK_ELEMS), out_cap);
   e = hc::launch_compress(d_in, n, d_out, d_out_bytes, ws, stream);
   return e == hipSuccess ? HC_SUCCESS : device_fail(e, "compress launch");
 }
@@ -815,6 +902,8 @@ hc_status_t decompress_common(const void* d_in, size_t in_bytes, uint16_t* d_out
   if (n > ((size_t)1 << 40)) return fail(HC_ERR_INVALID_ARGUMENT, "n %zu too large", n);
   Range ir{(uintptr_t)d_in, (uintptr_t)d_in + in_bytes}, orr{(uintptr_t)d_out, (uintptr_t)d_out + 2 * n};
   if (n && overlap(ir, orr)) return fail(HC_ERR_INVALID_ARGUMENT, "input and output overlap");
+  if (hc::log_enabled())
+    hc::log_line("%s: n=%zu in_bytes=%zu", entropy ? "decompress_entropy" : "decompress", n, in_bytes);
   hipError_t e = entropy ? hc::launch_hce_decompress(d_in, in_bytes, d_out, n, d_status, stream)
                          : hc::launch_decompress(d_in, in_bytes, d_out, n, d_status, stream);
   if (e == hipErrorNotSupported) return fail(HC_ERR_UNSUPPORTED, "decompress not built");
@@ -868,6 +957,8 @@ hc_status_t hc_compressed_allreduce(void* const* sendbufs, void* const* recvbufs
   Tap tap;
   if ((st = make_tap(opts, HC_OP_COMPRESSED_ALLREDUCE, nranks, &tap))) return st;
   const size_t chunk = hc::chunk_elems(count, chunk_fraction(opts), HC_BLOCK_ELEMS);
+  log_ring("compressed_allreduce", nranks, count, HC_BF16, chunk, opts,
+           "(chunks are whole codec blocks; each chunk's hop payload is its own stream)");
   hipError_t e = hc::launch_compressed_allreduce(sendbufs, recvbufs, count, nranks, chunk, d_ws,
                                                  d_wire_bytes, tap, stream);
   if (e == hipSuccess) e = tap.finish(stream);

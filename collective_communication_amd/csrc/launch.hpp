@@ -55,6 +55,11 @@ hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, hip
 hipError_t stamp_host_work(hipStream_t stream);
 constexpr int kWgPerCuBudget = 8;   // workgroups per CU of a CU-budget grid
 
+// HC_LOG set to anything but "" or "0": every call prints its plan, and every
+// ring-step launch its shape, to stderr, one line each, prefixed "hc: ".
+bool log_enabled();
+void log_line(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+
 hipError_t launch_reduce_step(const Seg* segs, int nseg, hc_dtype_t dtype, int cu_budget,
                               hipStream_t stream);
 hipError_t launch_copy_step(const Seg* segs, int nseg, size_t elem_bytes, int cu_budget,

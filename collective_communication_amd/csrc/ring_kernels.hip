@@ -401,6 +401,15 @@ hipError_t launch_step_as(const Seg* segs, int nseg, int cu_budget, hipStream_t 
     const uint64_t cap = (uint64_t)cu_budget * kWgPerCuBudget;
     if (grid > cap) grid = (uint32_t)cap;
   }
+  if (log_enabled()) {
+    static const char* const kOpName[] = {"copy", "reduce", "sgd", "sgd_one", "reduce_send", "sgd_send"};
+    static const char* const kPolicyName[] = {"cached", "stream", "budget"};
+    uint64_t elems = 0;
+    for (int i = 0; i < k; ++i) elems += args.len[i];
+    log_line("step launch: op=%s elem_bytes=%d policy=%s segments=%d elements=%llu tiles=%llu grid=%u%s", kOpName[OP],
+             ES, kPolicyName[POLICY], k, (unsigned long long)elems, (unsigned long long)tiles, grid,
+             vec ? "" : " (element path: a pointer is not 16-byte aligned)");
+  }
   void* kargs[] = {&args};
   return launch_kernel(vec ? (const void*)step_kernel<ES, OP, true, POLICY>
                            : (const void*)step_kernel<ES, OP, false, POLICY>,

@@ -88,6 +88,24 @@ typedef enum {
  *   cu_budget: 0 = size grids for the whole GPU; k > 0 = launch a persistent
  *     grid sized for k compute units (pair it with a stream from
  *     hc_stream_create_cu_budget(k)).
+ *   Environment, read at every call (none is required):
+ *     HC_CHUNK_FRACTION (a number in (0, 1]) and HC_CU_BUDGET (an integer in
+ *       0..4096) replace the two defaults above where opts is NULL or leaves
+ *       the field 0; a malformed value makes every call that takes options
+ *       return HC_ERR_INVALID_ARGUMENT, naming the variable.  (The compressed
+ *       allreduce, which takes no CU budget, ignores HC_CU_BUDGET.)
+ *     HC_LOG (anything but empty or "0") prints each call's plan and each
+ *       ring-step launch's shape and tile policy to stderr, one line each,
+ *       prefixed "hc: ".
+ *     HC_STREAM_STORE_MIN_BYTES (a whole number; default 335544320, 320 MiB):
+ *       a ring-step launch that writes at least this many bytes on all CUs
+ *       moves one 16-byte vector per lane with non-temporal stores, since its
+ *       output no longer fits MI355X's 256 MB Infinity Cache for the next
+ *       step to read back; smaller launches use two vectors and ordinary
+ *       stores, CU-budget launches four.  Values are the same either way.
+ *     HC_LOOKBACK_SPIN_LIMIT (1..2^32-1; default 2^22): polls a compress
+ *       block's look-back makes before the call gives up (see
+ *       hc_compress_bf16).
  *   step_events / n_step_events: optional timing hook.  When step_events is
  *     not NULL it holds n_step_events caller-created HIP events (created
  *     with timing enabled), used as step_event_mode says, with steps =

@@ -1,0 +1,105 @@
+"""GPU checks of the environment defaults and of HC_LOG.
+
+HC_CHUNK_FRACTION and HC_CU_BUDGET replace the chunk fraction and the CU
+budget of calls that pass no options; HC_LOG prints every call's plan and
+every ring-step launch's shape to stderr.  A child process runs small calls
+with these set; its results are compared with the oracle bit for bit and its
+log lines with what the options imply.  Ring operations: "ResCCL:
+Resource-Efficient Scheduling for Collective Communication" (section 1,
+chunks of about 1% of the buffer); the compressed ring: "CCCL: In-GPU
+Compression-Coupled Collective Communication" (section 5)."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from collective_communication_amd import binding as hc
+from collective_communication_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+CHILD = r"""
+import json, sys
+import numpy as np, torch
+sys.path.insert(0, sys.argv[1]); sys.path.insert(0, sys.argv[1] + "/tests")
+from collective_communication_amd import binding as hc
+from hc_util import to_dev, to_host
+xs = [np.load(p) for p in sys.argv[2:]]
+send = [to_dev(x) for x in xs]
+recv = [torch.empty_like(s) for s in send]
+hc.hc_allreduce(send, recv)
+n = xs[0].size
+ws = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_COMPRESSED_ALLREDUCE, n, len(xs)), dtype=torch.uint8, device="cuda")
+wire = torch.zeros(1, dtype=torch.int64, device="cuda")
+out2 = [torch.empty_like(s) for s in send]
+hc.hc_compressed_allreduce(send, out2, n, ws, wire)
+torch.cuda.synchronize()
+for r in range(len(xs)):
+    np.save(sys.argv[2 + r] + ".ar.npy", to_host(recv[r]))
+    np.save(sys.argv[2 + r] + ".car.npy", to_host(out2[r]))
+print(json.dumps({"wire": int(wire.item())}))
+"""
+
+
+def test_environment_defaults_and_log(tmp_path):
+    R, n = 4, 1 << 20            # 16-byte aligned slices of 2^18: the vector path, 128 budget tiles
+    g = np.random.default_rng(41)
+    xs = [inputs.f32_to_bf16_bits((g.standard_normal(n) * 1e-3).astype(np.float32)) for _ in range(R)]
+    paths = []
+    for r, x in enumerate(xs):
+        p = tmp_path / f"x{r}.npy"
+        np.save(p, x)
+        paths.append(str(p))
+    env = dict(os.environ, HC_LOG="1", HC_CHUNK_FRACTION="0.25", HC_CU_BUDGET="8")
+    print("child: allreduce and compressed allreduce, R=4, n=%d, HC_CU_BUDGET=8 HC_CHUNK_FRACTION=0.25" % n,
+          flush=True)
+    r = subprocess.run([sys.executable, "-c", CHILD, ROOT, *paths], capture_output=True, text=True, env=env,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-3000:]
+    got = json.loads(r.stdout.strip().splitlines()[-1])
+    ref = oracle.allreduce_fold(xs)
+    for q in range(R):
+        assert np.array_equal(np.load(paths[q] + ".ar.npy"), ref[q]), f"allreduce rank {q}"
+    chunk = hc.hc_chunk_elems(n, 0.25, 16384)
+    ref2, ref_wire = oracle.compressed_allreduce(xs, chunk=chunk)
+    for q in range(R):
+        assert np.array_equal(np.load(paths[q] + ".car.npy"), ref2[q]), f"compressed rank {q}"
+    assert got["wire"] == ref_wire
+    # the default chunk would give other wire bytes: the environment took effect
+    _, default_wire = oracle.compressed_allreduce(xs, chunk=hc.hc_chunk_elems(n, 0.01, 16384))
+    assert default_wire != ref_wire
+    log = [ln for ln in r.stderr.splitlines() if ln.startswith("hc: ")]
+    ar = [ln for ln in log if ln.startswith("hc: allreduce: ")]
+    assert len(ar) == 1 and f"ranks=4 count={n} dtype=bf16 chunk={hc.hc_chunk_elems(n, 0.25, 1024)}" in ar[0]
+    assert "cu_budget=8" in ar[0]
+    steps = [ln for ln in log if ln.startswith("hc: step launch: ")]
+    assert len(steps) == 2 * (R - 1) - 1          # the last reduce step also does the first all-gather copy
+    # 4 x 2^18 elements in tiles of 8192 = 128 tiles, on a grid of 8 CUs x 8 workgroups
+    assert all("policy=budget" in ln and "tiles=128 grid=64" in ln and "element path" not in ln
+               for ln in steps), steps
+    assert sum("op=reduce " in ln for ln in steps) == R - 2
+    assert sum("op=reduce_send " in ln for ln in steps) == 1
+    assert sum("op=copy " in ln for ln in steps) == R - 2
+    car = [ln for ln in log if ln.startswith("hc: compressed_allreduce: ")]
+    assert len(car) == 1 and f"chunk={chunk}" in car[0]
+
+
+def test_no_log_without_hc_log(tmp_path):
+    x = np.zeros(1000, dtype=np.uint16)
+    paths = []
+    for r in range(2):
+        p = tmp_path / f"z{r}.npy"
+        np.save(p, x)
+        paths.append(str(p))
+    env = {k: v for k, v in os.environ.items() if k not in ("HC_LOG", "HC_CHUNK_FRACTION", "HC_CU_BUDGET")}
+    print("child: R=2, n=1000, no HC_LOG", flush=True)
+    r = subprocess.run([sys.executable, "-c", CHILD, ROOT, *paths], capture_output=True, text=True, env=env,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-3000:]
+    assert not [ln for ln in r.stderr.splitlines() if ln.startswith("hc: ")]

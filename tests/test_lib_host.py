@@ -225,3 +225,36 @@ def test_status_strings(hc):
                        (4, b"corrupt stream"), (5, b"device error")):
         assert L.hc_status_string(code) == text
     assert hc.hc_version().startswith("hc ")
+
+
+@pytest.mark.parametrize("name,value", [("HC_CHUNK_FRACTION", "0"), ("HC_CHUNK_FRACTION", "1.5"),
+                                        ("HC_CHUNK_FRACTION", "0.01x"), ("HC_CU_BUDGET", "-1"),
+                                        ("HC_CU_BUDGET", "4097"), ("HC_CU_BUDGET", "8.5")])
+def test_malformed_environment_defaults_are_rejected(hc, monkeypatch, name, value):
+    """HC_CHUNK_FRACTION and HC_CU_BUDGET replace the defaults of calls that
+    pass no options; a malformed value fails every ring call up front,
+    naming the variable, before anything is enqueued."""
+    L = _raw(hc)
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    a = (ctypes.c_void_p * 2)(0x100000, 0x200000)
+    b = (ctypes.c_void_p * 2)(0x300000, 0x400000)
+    monkeypatch.setenv(name, value)
+    st = L.hc_allreduce(ctypes.cast(a, PP), ctypes.cast(b, PP), 16, hc.HC_F32, 2, None, None)
+    assert st == hc.HC_ERR_INVALID_ARGUMENT
+    assert name.encode() in L.hc_last_error()
+    st = L.hc_reduce_scatter(ctypes.cast(a, PP), ctypes.cast(b, PP), 8, hc.HC_F32, 2, None, 0, None, None)
+    assert st == hc.HC_ERR_INVALID_ARGUMENT and name.encode() in L.hc_last_error()
+
+
+def test_wellformed_environment_defaults_pass_the_checks(hc, monkeypatch):
+    """Valid values pass the up-front checks: the call then fails on the
+    next check (here a NULL workspace), not on the environment."""
+    L = _raw(hc)
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    a = (ctypes.c_void_p * 2)(0x100000, 0x200000)
+    b = (ctypes.c_void_p * 2)(0x300000, 0x400000)
+    monkeypatch.setenv("HC_CHUNK_FRACTION", "0.05")
+    monkeypatch.setenv("HC_CU_BUDGET", "8")
+    st = L.hc_reduce_scatter(ctypes.cast(a, PP), ctypes.cast(b, PP), 8, hc.HC_F32, 2, None, 0, None, None)
+    assert st == hc.HC_ERR_INVALID_ARGUMENT
+    assert b"d_ws" in L.hc_last_error()
