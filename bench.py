@@ -245,6 +245,12 @@ def bench_ring(args, workload: str):
     hbm = alg_bytes / (ms / 1e3) / 1e9
     achieved = red_launch_bytes / (avg_red / 1e3) / 1e9
     traffic = load_traffic("reduce_step", workload, RING_FILES)
+    # Allreduces whose R buffers hold at most HC_CHAIN_MAX_BYTES (256 MiB by
+    # default, as in the library) run as one launch that carries each tile
+    # through every hop; the per-step stamps above come from the
+    # step-per-launch schedule, which step events always select.
+    chain_max = int(os.environ.get("HC_CHAIN_MAX_BYTES", str(256 << 20)) or 0)
+    one_launch = R * n * es <= chain_max
     line = {
         "metric": METRIC, "value": round(algbw, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
@@ -272,8 +278,23 @@ def bench_ring(args, workload: str):
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": red_launch_bytes, "launch_ms": round(avg_red, 6),
                      "duration": "mean reduce-scatter step by its kernel's start and end stamps (HIP events)"},
+        "schedule": "one launch, each tile through every hop" if one_launch else "one launch per ring step",
     }
-    if traffic is not None:
+    if one_launch:
+        # the headline call is a single chain_kernel launch: its bytes are the
+        # whole allreduce's, its duration the call's (back to back, launch gaps
+        # included); the step-per-launch figures stay beside it
+        line["step_schedule"] = {"reduce_launch_ms": line.pop("reduce_launch_ms"),
+                                 "reduce_send_launch_ms": line.pop("reduce_send_launch_ms"),
+                                 "copy_launch_ms": line.pop("copy_launch_ms"),
+                                 "copy_launch_gbps": line.pop("copy_launch_gbps"),
+                                 "roofline": line["roofline"]}
+        line["roofline"] = {"bound": "hbm", "kernel": "chain_kernel (the whole allreduce in one launch)",
+                            "achieved": round(hbm, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                            "frac": round(hbm / PEAK_HBM_GBPS, 4), "traffic": None,
+                            "alg_bytes_per_launch": alg_bytes, "launch_ms": round(ms, 6),
+                            "duration": "per call, back to back (HIP events around the calls)"}
+    if line["roofline"]["traffic"] is not None:
         line["roofline"]["traffic_source"] = TRAFFIC_SOURCE
     if workload == "ring_bf16":
         # What a plain streaming kernel with the reduce hop's traffic (two

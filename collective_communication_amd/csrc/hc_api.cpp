@@ -161,6 +161,12 @@ bool dma_copies_offload() {
 }
 
 hc_status_t check_env();
+// Measured on MI355X (one allreduce, us, step-per-launch / one launch):
+// R=4 x 2^20 fp32 30.6 / 13.7; R=8 x 2^20 bf16 51.7 / 15.8; R=8 x 2^22 bf16
+// 75 / 46; R=8 x 2^24 bf16 199 / 149.  Up to the 256 MB Infinity Cache the
+// one-launch schedule wins; above it the step-per-launch schedule streams
+// every hop through HBM, which is the ring data path this library measures.
+constexpr uint64_t kChainMaxBytes = 256ull << 20;
 double chunk_fraction(const hc_opts_t* o);
 int cu_budget(const hc_opts_t* o);
 
@@ -236,6 +242,20 @@ hc_status_t check_env() {
   if (b && *b && !env_cu_budget(&bv))
     return fail(HC_ERR_INVALID_ARGUMENT, "environment HC_CU_BUDGET=\"%.64s\" is not an integer in 0..4096", b);
   return HC_SUCCESS;
+}
+
+// Allreduces whose R buffers hold at most this many bytes run as one launch
+// that carries each chunk through every hop (launch_chain_allreduce); larger
+// ones launch once per ring step.  HC_CHAIN_MAX_BYTES (a whole number)
+// replaces it.
+uint64_t chain_max_bytes() {
+  const char* e = getenv("HC_CHAIN_MAX_BYTES");
+  if (e && *e) {
+    char* end = nullptr;
+    const unsigned long long v = strtoull(e, &end, 10);
+    if (*end == 0) return v;
+  }
+  return kChainMaxBytes;
 }
 
 double chunk_fraction(const hc_opts_t* o) {
@@ -578,9 +598,16 @@ hc_status_t hc_allreduce(void* const* sendbufs, void* const* recvbufs, size_t co
   Tap tap;
   if ((st = make_tap(opts, HC_OP_ALLREDUCE, nranks, &tap))) return st;
   const size_t chunk = hc::chunk_elems(count, chunk_fraction(opts), 1024);
-  log_ring("allreduce", nranks, count, dtype, chunk, opts, "(one segment per receiver and step: a step's chunks are merged)");
-  if (nranks == 1)
+  if (nranks == 1) {
+    log_ring("allreduce", nranks, count, dtype, chunk, opts, "(one rank: a copy)");
     return run_single(sendbufs[0], recvbufs[0], count, es, cu_budget(opts), copy_engine(opts), tap, stream);
+  }
+  if (!copy_engine(opts) && !tap.ev && (uint64_t)count * es * (uint64_t)nranks <= chain_max_bytes()) {
+    log_ring("allreduce", nranks, count, dtype, chunk, opts, "(one launch: each tile through every hop)");
+    hipError_t e = hc::launch_chain_allreduce(sendbufs, recvbufs, count, es, nranks, cu_budget(opts), stream);
+    return e == hipSuccess ? HC_SUCCESS : device_fail(e, "chain launch");
+  }
+  log_ring("allreduce", nranks, count, dtype, chunk, opts, "(one segment per receiver and step: a step's chunks are merged)");
   return run_allreduce(sendbufs, recvbufs, count, dtype, nranks, chunk, cu_budget(opts), copy_engine(opts), tap,
                        stream);
 }

@@ -64,6 +64,11 @@ hipError_t launch_reduce_step(const Seg* segs, int nseg, hc_dtype_t dtype, int c
                               hipStream_t stream);
 hipError_t launch_copy_step(const Seg* segs, int nseg, size_t elem_bytes, int cu_budget,
                             hipStream_t stream);
+// The whole ring allreduce in one launch, one tile per workgroup carried
+// through every hop in ring order (see chain_kernel).  send/recv: host
+// arrays of R device pointers.
+hipError_t launch_chain_allreduce(void* const* send, void* const* recv, size_t count, size_t es, int R,
+                                  int cu_budget, hipStream_t stream);
 // A reduce step that stores each sum twice, at dst and dst2: the last
 // reduce-scatter step writing the slice's final sum into its owner's output
 // and sending it on into the next rank's output (that rank's first

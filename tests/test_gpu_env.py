@@ -56,7 +56,8 @@ def test_environment_defaults_and_log(tmp_path):
         p = tmp_path / f"x{r}.npy"
         np.save(p, x)
         paths.append(str(p))
-    env = dict(os.environ, HC_LOG="1", HC_CHUNK_FRACTION="0.25", HC_CU_BUDGET="8")
+    env = dict(os.environ, HC_LOG="1", HC_CHUNK_FRACTION="0.25", HC_CU_BUDGET="8",
+               HC_CHAIN_MAX_BYTES="0")   # the step-per-launch schedule, one log line per step launch
     print("child: allreduce and compressed allreduce, R=4, n=%d, HC_CU_BUDGET=8 HC_CHUNK_FRACTION=0.25" % n,
           flush=True)
     r = subprocess.run([sys.executable, "-c", CHILD, ROOT, *paths], capture_output=True, text=True, env=env,
@@ -103,3 +104,30 @@ def test_no_log_without_hc_log(tmp_path):
                        timeout=300)
     assert r.returncode == 0, r.stderr[-3000:]
     assert not [ln for ln in r.stderr.splitlines() if ln.startswith("hc: ")]
+
+
+def test_one_launch_schedule_logs_its_launch(tmp_path):
+    """Small allreduces run as one launch by default; with HC_CU_BUDGET its
+    grid is the budget's 8 workgroups per CU."""
+    R, n = 4, 1 << 20
+    g = np.random.default_rng(43)
+    xs = [inputs.f32_to_bf16_bits((g.standard_normal(n) * 1e-3).astype(np.float32)) for _ in range(R)]
+    paths = []
+    for r, x in enumerate(xs):
+        p = tmp_path / f"y{r}.npy"
+        np.save(p, x)
+        paths.append(str(p))
+    env = {k: v for k, v in os.environ.items() if k != "HC_CHAIN_MAX_BYTES"}
+    env.update(HC_LOG="1", HC_CU_BUDGET="8")
+    print("child: one-launch allreduce, R=4, n=%d, HC_CU_BUDGET=8" % n, flush=True)
+    r = subprocess.run([sys.executable, "-c", CHILD, ROOT, *paths], capture_output=True, text=True, env=env,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-3000:]
+    ref = oracle.allreduce_fold(xs)
+    for q in range(R):
+        assert np.array_equal(np.load(paths[q] + ".ar.npy"), ref[q]), f"allreduce rank {q}"
+    log = [ln for ln in r.stderr.splitlines() if ln.startswith("hc: ")]
+    assert not [ln for ln in log if ln.startswith("hc: step launch: ")]
+    chain = [ln for ln in log if ln.startswith("hc: chain launch: ")]
+    # 4 slices of 2^18 bf16 in tiles of 4096: 256 chains on 8 CUs x 8 workgroups
+    assert len(chain) == 1 and "chains=256 grid=64" in chain[0] and "element path" not in chain[0], chain

@@ -41,9 +41,18 @@ def run_ar(xs, inplace=False, **kw):
 SIZES = [1, 7, 8, 64, 1000, 8192 * 3 + 17, 65536, 300_001]
 
 
+# Allreduces up to HC_CHAIN_MAX_BYTES (256 MiB by default) run as one launch that
+# carries each tile through every hop; larger ones launch once per ring step.
+# Both schedules are run on the small shapes.
+SCHEDULES = [pytest.param({}, id="default"), pytest.param({"HC_CHAIN_MAX_BYTES": "0"}, id="steps")]
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 8])
-def test_allreduce_matches_oracle(dtype, R):
+def test_allreduce_matches_oracle(monkeypatch, schedule, dtype, R):
+    for k, v in schedule.items():
+        monkeypatch.setenv(k, v)
     for n in SIZES:
         xs = rand(R, n, dtype, 1000 * R + n, 1e-3 if dtype == "bf16" else 1.0)
         ref = oracle.allreduce_fold(xs)
@@ -52,8 +61,11 @@ def test_allreduce_matches_oracle(dtype, R):
             assert np.array_equal(got[r], bits(ref[r])), f"n={n} rank={r}: {first_mismatch(got[r], bits(ref[r]))}"
 
 
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_allreduce_in_place_and_chunk_independent(dtype):
+def test_allreduce_in_place_and_chunk_independent(monkeypatch, schedule, dtype):
+    for k, v in schedule.items():
+        monkeypatch.setenv(k, v)
     R, n = 8, 8 * 40000 + 24
     xs = rand(R, n, dtype, 5)
     ref = oracle.allreduce_fold(xs)
