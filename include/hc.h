@@ -103,6 +103,12 @@ typedef enum {
  *       output no longer fits MI355X's 256 MB Infinity Cache for the next
  *       step to read back; smaller launches use two vectors and ordinary
  *       stores, CU-budget launches four.  Values are the same either way.
+ *     HC_CHAIN_MAX_BYTES (a whole number; default 268435456, 256 MiB): an
+ *       hc_allreduce whose R buffers hold at most this many bytes runs as
+ *       one launch in which each workgroup carries one tile through every
+ *       hop in ring order (unless step_events or copy_engine ask for per-step
+ *       launches); larger ones launch once per ring step.  Values are the
+ *       same either way.
  *     HC_LOOKBACK_SPIN_LIMIT (1..2^32-1; default 2^22): polls a compress
  *       block's look-back makes before the call gives up (see
  *       hc_compress_bf16).
@@ -167,6 +173,12 @@ typedef struct {
  *   sendbufs[r], recvbufs[r]: count elements each.  In place is allowed:
  *   sendbufs[r] == recvbufs[r] for every r.  Slices are ceil(count/R) long
  *   (the last ones short or empty when R does not divide count).
+ *   Schedule: up to HC_CHAIN_MAX_BYTES of buffers (256 MiB by default) the
+ *   hops run in one launch, each workgroup taking one tile of one slice
+ *   through all 2(R-1) hops in order ("ResCCL ...", section 3: dependencies
+ *   exist only within a chunk); above it, or with step_events or
+ *   copy_engine, one launch per ring step.  Both make the same reads and
+ *   writes and give the same bits.
  */
 hc_status_t hc_allreduce(void *const *sendbufs, void *const *recvbufs, size_t count,
                          hc_dtype_t dtype, int nranks, const hc_opts_t *opts,
