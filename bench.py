@@ -291,7 +291,8 @@ def bench_ring(args, workload: str):
                                  "roofline": line["roofline"]}
         line["roofline"] = {"bound": "hbm", "kernel": "chain_kernel (the whole allreduce in one launch)",
                             "achieved": round(hbm, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                            "frac": round(hbm / PEAK_HBM_GBPS, 4), "traffic": None,
+                            "frac": round(hbm / PEAK_HBM_GBPS, 4),
+                            "traffic": load_traffic("chain", workload, RING_FILES),
                             "alg_bytes_per_launch": alg_bytes, "launch_ms": round(ms, 6),
                             "duration": "per call, back to back (HIP events around the calls)"}
     if line["roofline"]["traffic"] is not None:
