@@ -21,7 +21,10 @@ gradients and a multi-layer gradient bucket), entropy
 fixed-length codec on the same 2^28 tensors), hop_sizes (the reduce-scatter
 hop at 2^24..2^28 elements per rank under each store policy, with and without
 a cold Infinity Cache), rs_budget (the contention test's reduce-scatter on
-k = 8, 16, 32 CUs and on all CUs, without the GEMM).  Each prints one JSON line of its own.
+k = 8, 16, 32 CUs and on all CUs, without the GEMM), compressed_schedules (the
+compressed ring at R = 2, 4, 8 and 2^18..2^25 elements per rank, one launch per
+ring step against one launch for the whole allreduce).  Each prints one JSON
+line of its own.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 The headline time is K back-to-back calls with nothing else on the stream.
@@ -51,9 +54,9 @@ N_CU = 256
 METRIC = "AllReduce algbw GB/s and achieved HBM GB/s (% of peak), R=8, 1 MI355X"
 # sources whose change voids the recorded traffic counters of a kernel
 CODEC_FILES = ["collective_communication_amd/csrc/codec_kernels.hip", "collective_communication_amd/csrc/codec.hpp",
-               "collective_communication_amd/csrc/lookback.hpp"]
+               "collective_communication_amd/csrc/lookback.hpp", "collective_communication_amd/csrc/common.hpp"]
 ENTROPY_FILES = ["collective_communication_amd/csrc/entropy_kernels.hip", "collective_communication_amd/csrc/codec.hpp",
-                 "collective_communication_amd/csrc/lookback.hpp"]
+                 "collective_communication_amd/csrc/lookback.hpp", "collective_communication_amd/csrc/common.hpp"]
 RING_FILES = ["collective_communication_amd/csrc/ring_kernels.hip", "collective_communication_amd/csrc/common.hpp"]
 
 
@@ -982,6 +985,74 @@ def bench_hop_sizes(args):
             "bytes_per_step": "3 x 2 bytes x elements per rank (2 reads, 1 write per element of the step)",
             "rows": rows}
 
+def bench_compressed_schedules(args):
+    """The compressed allreduce (R = 2, 4, 8 bf16 N(0,1e-3), 2^18..2^25
+    elements per rank) under its two schedules, forced through
+    HC_CHAIN_MAX_BYTES: one launch per ring step ("steps"), or one launch in
+    which each codec block of each slice goes through every hop ("one
+    launch"); and with the variable unset ("auto", the library's rule: one
+    launch while the grid of count / 16384 workgroups is at most two per CU).
+    Each call is timed alone by two HIP events; the median over the calls is
+    reported.  The wire bytes of the two schedules are checked equal."""
+    import statistics
+
+    import torch
+
+    from collective_communication_amd import binding as hc
+    from collective_communication_amd import inputs
+
+    key = "HC_CHAIN_MAX_BYTES"
+    old = os.environ.get(key)
+    iters = max(args.steps, 3)
+    rows = []
+    try:
+        for R in (2, 4, 8):
+            for lg in (18, 20, 21, 22, 23, 24, 25):
+                n = 1 << lg
+                send = inputs.ring_inputs_cuda("compressed", R, n)
+                recv = [torch.empty_like(t) for t in send]
+                ws = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_COMPRESSED_ALLREDUCE, n, R), dtype=torch.uint8,
+                                 device="cuda")
+                slice_len = -(-n // R)
+                row = {"R": R, "log2_elems_per_rank": lg, "grid": R * -(-slice_len // hc.HC_BLOCK_ELEMS)}
+                wires = {}
+                for name, val in (("steps", "0"), ("one_launch", str(1 << 62)), ("auto", None)):
+                    if val is None:
+                        os.environ.pop(key, None)
+                    else:
+                        os.environ[key] = val
+                    wire = torch.zeros(1, dtype=torch.int64, device="cuda")
+                    for _ in range(args.warmup):
+                        hc.hc_compressed_allreduce(send, recv, n, ws)
+                    hc.hc_compressed_allreduce(send, recv, n, ws, wire)
+                    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                           for _ in range(iters)]
+                    for a, b in evs:
+                        a.record()
+                        hc.hc_compressed_allreduce(send, recv, n, ws)
+                        b.record()
+                    torch.cuda.synchronize()
+                    row[name + "_us"] = round(statistics.median(a.elapsed_time(b) for a, b in evs) * 1e3, 1)
+                    wires[name] = int(wire.item())
+                if len(set(wires.values())) != 1:
+                    raise RuntimeError(f"wire bytes differ between schedules: {wires}")
+                row["one_launch_over_steps"] = round(row["one_launch_us"] / row["steps_us"], 3)
+                rows.append(row)
+                del send, recv, ws
+                torch.cuda.empty_cache()
+    finally:
+        if old is None:
+            os.environ.pop(key, None)
+        else:
+            os.environ[key] = old
+    r8 = next(r for r in rows if r["R"] == 8 and r["log2_elems_per_rank"] == 22)
+    return {"metric": "compressed allreduce time by schedule (R=2, 4, 8 bf16, 2^18..2^25 elements per rank)",
+            "value": r8["auto_us"], "unit": "us", "n_gpus": 1, "steps": iters, "warmup": args.warmup,
+            "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "compressed allreduce of R x n bf16 N(0,1e-3), chunk 1%; value: R=8 x 2^22, "
+                                   "the library's schedule"},
+            "rows": rows}
+
 def bench_rs_budget(args):
     """The contention test's reduce-scatter (R=8 x 2^28 bf16, N(0,1e-3))
     without the GEMM: on a k-CU stream (hc_stream_create_cu_budget) for
@@ -1031,7 +1102,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ring_bf16",
                     choices=["ring_bf16", "ring_f32", "ring_bf16_carry", "codec", "compressed", "contention",
-                             "fused_sgd", "table_scope", "entropy", "hop_sizes", "rs_budget"])
+                             "fused_sgd", "table_scope", "entropy", "hop_sizes", "rs_budget",
+                             "compressed_schedules"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 26,
                     help="elements per rank the oracle baseline runs on (default: the whole workload)")
@@ -1065,6 +1137,8 @@ def main():
         line = bench_hop_sizes(args)
     elif args.workload == "rs_budget":
         line = bench_rs_budget(args)
+    elif args.workload == "compressed_schedules":
+        line = bench_compressed_schedules(args)
     else:
         line = bench_contention(args)
     print(json.dumps(line), flush=True)

@@ -59,6 +59,18 @@ constexpr uint32_t kStage16 = kRawFull / 16;    // 2049 uint4 of LDS staging
 constexpr uint32_t kMagic = 0x315A4348u;
 constexpr uint32_t kHistCopies = 32;            // 256 bins x 32 words = 32 KB of staging
 
+// A global-memory pointer that a device function receives as an argument
+// (arguments travel in vector registers, and the address space is lost at the
+// call): read it from the first lane, since every caller passes the same
+// pointer in all lanes, and rebuild it in the global address space, so that
+// accesses through it compile to global, not flat, instructions.
+template <class T>
+__device__ __forceinline__ T* uniform_global(T* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint64_t u = ((uint64_t)first_lane_read((uint32_t)(a >> 32)) << 32) | first_lane_read((uint32_t)a);
+  return (T*)(__attribute__((address_space(1))) T*)(uintptr_t)u;
+}
+
 struct Plan {
   uint32_t mode;       // 0 raw, 1 coded
   uint32_t b;          // code bits (coded)

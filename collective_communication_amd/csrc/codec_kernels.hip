@@ -552,6 +552,91 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
   }
 }
 
+// One hop of a chain (see car_chain_kernel), kept out of line so that each
+// call gets the register budget of a one-hop kernel (inlined into the
+// chain's loops, the encoder spilled).  Reduce-scatter hop: fold the record
+// in slot_in (none for the first hop) with the own block `own`, write the
+// sum to `out` when given (the last step), compress it into slot_out.
+__device__ __attribute__((noinline)) void chain_rs_hop(const uint8_t* slot_in, const uint16_t* own, uint16_t* out,
+                                                      uint8_t* slot_out, uint64_t* wire_bytes, uint32_t m,
+                                                      Smem& s) {
+  slot_in = uniform_global(slot_in);
+  own = uniform_global(own);
+  out = uniform_global(out);
+  slot_out = uniform_global(slot_out);
+  wire_bytes = uniform_global(wire_bytes);
+  m = first_lane_read(m);
+  uint4 v[kPer];
+  if (!slot_in) {
+    load_block(own, m, v);
+  } else {
+    read_slot(s, slot_in, m, v);
+    load_block_lds(own, m, s);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      v[k] = hop_bf16x8(v[k], s.stage[threadIdx.x + kCT * k]);
+      asm volatile("" : "+v"(v[k].x), "+v"(v[k].y), "+v"(v[k].z), "+v"(v[k].w));
+    }
+    __syncthreads();
+    if (out) store_block(out, m, v);
+  }
+  const Plan pl = plan_block(v, m, s);
+  write_block(v, pl, s);
+  copy_out(s, slot_out, pl.rec_bytes);
+  if (wire_bytes && threadIdx.x == 0) atomicAdd((unsigned long long*)wire_bytes, (unsigned long long)pl.rec_bytes);
+  __syncthreads();   // the record is out of the staging buffer
+}
+
+// All-gather hop: decode the record in slot_in into `out`; forward the same
+// bytes into slot_out when given.
+__device__ __attribute__((noinline)) void chain_ag_hop(const uint8_t* slot_in, uint16_t* out, uint8_t* slot_out,
+                                                      uint64_t* wire_bytes, uint32_t m, Smem& s) {
+  slot_in = uniform_global(slot_in);
+  out = uniform_global(out);
+  slot_out = uniform_global(slot_out);
+  wire_bytes = uniform_global(wire_bytes);
+  m = first_lane_read(m);
+  uint4 v[kPer];
+  read_slot(s, slot_in, m, v);
+  store_block(out, m, v);
+  if (slot_out) {
+    const uint32_t rb = s.plan[4];
+    copy_out(s, slot_out, rb);
+    if (wire_bytes && threadIdx.x == 0) atomicAdd((unsigned long long*)wire_bytes, (unsigned long long)rb);
+  }
+  __syncthreads();
+}
+
+// The whole compressed allreduce in one launch: workgroup (j, blk) carries
+// codec block blk of slice j through every hop, in the ring's order, with
+// the operations of the kernels above (the first sender compresses it; each
+// reduce-scatter receiver decompresses, adds its own block, writes the sum at
+// the last step and compresses again; each all-gather receiver decompresses
+// into its output and forwards the same bytes).  A chunk's hops depend only
+// on one another ("ResCCL: Resource-Efficient Scheduling for Collective
+// Communication", section 3), so blocks never wait for each other; the slots
+// are indexed by slice instead of by sending rank, since chains of different
+// slices are at different hops at once (the same number of slots).  Same
+// records, same wire bytes, same output as the step-per-launch schedule.
+__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void car_chain_kernel(RingPtrs ptr, CarGeom g) {
+  __shared__ Smem s;
+  const uint32_t j = blockIdx.x / g.nbs, blk = blockIdx.x % g.nbs;
+  const uint32_t m = block_elems(g, j, blk);
+  if (m == 0) return;
+  const uint32_t R = g.R;
+  const uint64_t e0 = (uint64_t)j * g.L + (uint64_t)blk * kB;
+  for (uint32_t h = 0; h < R; ++h) {   // hop 0: the first sender j + 1; hop h: reduce-scatter step h - 1
+    const uint32_t q = (j + 1 + h) % R;
+    chain_rs_hop(h ? slot(g, j, (h - 1) & 1, blk) : nullptr, ptr.send[q] + e0,
+                 h + 1 == R ? ptr.recv[q] + e0 : nullptr, slot(g, j, h & 1, blk), g.wire_bytes, m, s);
+  }
+  for (uint32_t step = 0; step + 1 < R; ++step) {   // all-gather step: receiver j + 1 + step
+    const uint32_t q = (j + 1 + step) % R, buf = (R - 1 + step) & 1u;
+    chain_ag_hop(slot(g, j, buf, blk), ptr.recv[q] + e0, step + 2 < R ? slot(g, j, buf ^ 1u, blk) : nullptr,
+                 g.wire_bytes, m, s);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_fill_u32(void* dst, uint32_t value, size_t words, hipStream_t stream) {
@@ -730,7 +815,8 @@ size_t compressed_ar_ws_bytes(size_t count, int R) {
 }
 
 hipError_t launch_compressed_allreduce(void* const* send, void* const* recv, size_t count, int R, size_t chunk,
-                                       void* ws, uint64_t* wire_bytes, Tap& tap, hipStream_t stream) {
+                                       void* ws, uint64_t* wire_bytes, bool one_launch, Tap& tap,
+                                       hipStream_t stream) {
   auto mark = [&]() -> hipError_t { return tap.mark(stream); };
   if (count == 0) {
     if (wire_bytes) hipLaunchKernelGGL(set_u64_kernel, dim3(1), dim3(1), 0, stream, wire_bytes, (uint64_t)0);
@@ -782,6 +868,10 @@ hipError_t launch_compressed_allreduce(void* const* send, void* const* recv, siz
   g.wire = static_cast<uint8_t*>(ws);
   g.wire_bytes = wire_bytes;
   const dim3 grid((uint32_t)(R * nbs)), block(kCT);
+  if (!tap.ev && one_launch) {   // no per-step timing asked for: one launch, each block through every hop
+    void* args[] = {&ptr, &g};
+    return launch_kernel((const void*)car_chain_kernel, grid, block, args, stream);
+  }
   hipError_t e = mark();
   if (e != hipSuccess) return e;
   void* first_args[] = {&ptr, &g};

@@ -244,18 +244,46 @@ hc_status_t check_env() {
   return HC_SUCCESS;
 }
 
+// HC_CHAIN_MAX_BYTES, when set to a whole number: the largest allreduce (bytes
+// of its R buffers) that runs as one launch, for both allreduces.
+bool env_chain_max_bytes(uint64_t* v) {
+  const char* e = getenv("HC_CHAIN_MAX_BYTES");
+  if (!e || !*e) return false;
+  char* end = nullptr;
+  const unsigned long long x = strtoull(e, &end, 10);
+  if (*end != 0) return false;
+  *v = x;
+  return true;
+}
+
 // Allreduces whose R buffers hold at most this many bytes run as one launch
 // that carries each chunk through every hop (launch_chain_allreduce); larger
-// ones launch once per ring step.  HC_CHAIN_MAX_BYTES (a whole number)
-// replaces it.
+// ones launch once per ring step.
 uint64_t chain_max_bytes() {
-  const char* e = getenv("HC_CHAIN_MAX_BYTES");
-  if (e && *e) {
-    char* end = nullptr;
-    const unsigned long long v = strtoull(e, &end, 10);
-    if (*end == 0) return v;
-  }
-  return kChainMaxBytes;
+  uint64_t v;
+  return env_chain_max_bytes(&v) ? v : kChainMaxBytes;
+}
+
+// The compressed allreduce runs as one launch (each codec block of each slice
+// through every hop) while its grid, one workgroup per block and slice, holds
+// at most two workgroups per CU; a codec workgroup's LDS admits four per CU.
+// Measured on MI355X (us, step-per-launch / one launch; grid = count / 16384):
+// R=2 x 2^23 (grid 512) 39.9 / 39.9, x 2^24 59.0 / 65.6; R=4 x 2^21 (128)
+// 88.7 / 53.3, x 2^23 (512) 95.2 / 85.8, x 2^24 144 / 157; R=8 x 2^22 (256)
+// 149 / 116, x 2^23 (512) 205 / 188, x 2^24 (1024) 309 / 311, x 2^25 568 /
+// 608.  Beyond that the chains, each 2R-1 hops long, run in rounds, and the
+// step launches fill the device better.  HC_CHAIN_MAX_BYTES, when set,
+// replaces the rule by the same byte threshold as the plain allreduce's.
+bool compressed_one_launch(size_t count, int nranks) {
+  uint64_t v;
+  if (env_chain_max_bytes(&v)) return (uint64_t)count * 2u * (uint64_t)nranks <= v;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+    return false;
+  const uint64_t L = (count + (size_t)nranks - 1) / (size_t)nranks;
+  const uint64_t grid = (uint64_t)nranks * ((L + HC_BLOCK_ELEMS - 1) / HC_BLOCK_ELEMS);
+  return grid <= 2u * (uint64_t)ncu;
 }
 
 double chunk_fraction(const hc_opts_t* o) {
@@ -984,10 +1012,12 @@ hc_status_t hc_compressed_allreduce(void* const* sendbufs, void* const* recvbufs
   Tap tap;
   if ((st = make_tap(opts, HC_OP_COMPRESSED_ALLREDUCE, nranks, &tap))) return st;
   const size_t chunk = hc::chunk_elems(count, chunk_fraction(opts), HC_BLOCK_ELEMS);
+  const bool one_launch = !tap.ev && compressed_one_launch(count, nranks);
   log_ring("compressed_allreduce", nranks, count, HC_BF16, chunk, opts,
-           "(chunks are whole codec blocks; each chunk's hop payload is its own stream)");
-  hipError_t e = hc::launch_compressed_allreduce(sendbufs, recvbufs, count, nranks, chunk, d_ws,
-                                                 d_wire_bytes, tap, stream);
+           one_launch ? "(one launch: each codec block of each slice through every hop)"
+                      : "(chunks are whole codec blocks; each chunk's hop payload is its own stream)");
+  hipError_t e = hc::launch_compressed_allreduce(sendbufs, recvbufs, count, nranks, chunk, d_ws, d_wire_bytes,
+                                                 one_launch, tap, stream);
   if (e == hipSuccess) e = tap.finish(stream);
   if (e == hipErrorNotSupported) return fail(HC_ERR_UNSUPPORTED, "compressed allreduce not built");
   return e == hipSuccess ? HC_SUCCESS : device_fail(e, "compressed allreduce launch");

@@ -138,7 +138,7 @@ hipError_t launch_compress_scoped(const uint16_t* in, size_t n, void* out, uint6
 size_t compressed_ar_ws_bytes(size_t count, int R);
 // tap: the call's step events (marked once per step and after the last).
 hipError_t launch_compressed_allreduce(void* const* send, void* const* recv, size_t count, int R,
-                                       size_t chunk, void* ws, uint64_t* wire_bytes, Tap& tap,
+                                       size_t chunk, void* ws, uint64_t* wire_bytes, bool one_launch, Tap& tap,
                                        hipStream_t stream);
 
 }  // namespace hc

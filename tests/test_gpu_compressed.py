@@ -4,7 +4,13 @@ is lossless) and wire bytes equal to the oracle's count.
 
 "CCCL: In-GPU Compression-Coupled Collective Communication", section 5
 ("Selective compression"), on the ring of "ResCCL: Resource-Efficient
-Scheduling for Collective Communication" (section 1)."""
+Scheduling for Collective Communication" (section 1).
+
+Allreduces up to HC_CHAIN_MAX_BYTES run as one launch in which each workgroup
+carries one codec block of one slice through every hop; the tests run under
+that default and with the threshold at 0 (one launch per ring step).  Both
+schedules take the same hops in the same order, so the bits and the wire
+bytes must not depend on the schedule."""
 import numpy as np
 import pytest
 import torch
@@ -16,6 +22,8 @@ from hc_util import first_mismatch, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 B = 16384
+SCHEDULES = [pytest.param({}, id="default"), pytest.param({"HC_CHAIN_MAX_BYTES": "0"}, id="steps"),
+             pytest.param({"HC_CHAIN_MAX_BYTES": str(1 << 40)}, id="one_launch")]
 
 
 def run_car(xs, inplace=False, chunk_fraction=0.0):
@@ -32,7 +40,10 @@ def run_car(xs, inplace=False, chunk_fraction=0.0):
 
 @pytest.mark.parametrize("R,n", [(1, 1000), (2, 2 * B), (2, 7), (3, 3 * B + 300), (4, 8 * B), (5, 5 * B + 17),
                                  (8, 16 * B), (8, 64 * B + 8 * 1000 + 5), (7, 3)])
-def test_compressed_allreduce_matches_oracle(R, n):
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_compressed_allreduce_matches_oracle(monkeypatch, schedule, R, n):
+    for k, v in schedule.items():
+        monkeypatch.setenv(k, v)
     xs = [inputs.normal_bf16("test", 500 + r, n, 1e-3) for r in range(R)]
     ref = oracle.allreduce_fold(xs)
     chunk = oracle.chunk_elems(n, B)
@@ -43,7 +54,10 @@ def test_compressed_allreduce_matches_oracle(R, n):
     assert wire == ref_wire
 
 
-def test_compressed_allreduce_in_place_and_chunking():
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_compressed_allreduce_in_place_and_chunking(monkeypatch, schedule):
+    for k, v in schedule.items():
+        monkeypatch.setenv(k, v)
     R, n = 4, 40 * B + 123
     xs = [inputs.normal_bf16("test", 600 + r, n, 1e-3) for r in range(R)]
     ref = oracle.allreduce_fold(xs)
@@ -58,11 +72,12 @@ def test_compressed_allreduce_in_place_and_chunking():
 
 
 @pytest.mark.timeout(600)
-def test_compressed_allreduce_full_size_matches_oracle():
+def test_compressed_allreduce_full_size_matches_oracle(monkeypatch):
     """R=8 x 2^25 bf16 N(0,1e-3): every element of every rank's output and
     the wire byte count equal the oracle's compressed ring (whose output is
     the uncompressed fold, bit for bit), and the compressed ring equals the
-    uncompressed one on the GPU."""
+    uncompressed one on the GPU.  The one-launch schedule, forced at this
+    size, gives the same bits and wire bytes."""
     R, n = 8, 1 << 25
     send = inputs.ring_inputs_cuda("compressed", R, n)
     xs = [inputs.host_bits(s) for s in send]
@@ -75,6 +90,13 @@ def test_compressed_allreduce_full_size_matches_oracle():
     torch.cuda.synchronize()
     for r in range(R):
         assert torch.equal(out_c[r].view(torch.int16), out_u[r].view(torch.int16)), f"rank {r}"
+    monkeypatch.setenv("HC_CHAIN_MAX_BYTES", str(1 << 40))
+    wire1 = torch.zeros(1, dtype=torch.int64, device="cuda")
+    hc.hc_compressed_allreduce(send, out_u, n, ws, wire1)
+    torch.cuda.synchronize()
+    for r in range(R):
+        assert torch.equal(out_c[r].view(torch.int16), out_u[r].view(torch.int16)), f"one launch, rank {r}"
+    assert int(wire1.item()) == int(wire.item())
     del send, out_u, ws
     torch.cuda.empty_cache()
     print("compressed ring equals the uncompressed ring; running the oracle", flush=True)

@@ -88,7 +88,7 @@ def test_environment_defaults_and_log(tmp_path):
     assert sum("op=reduce_send " in ln for ln in steps) == 1
     assert sum("op=copy " in ln for ln in steps) == R - 2
     car = [ln for ln in log if ln.startswith("hc: compressed_allreduce: ")]
-    assert len(car) == 1 and f"chunk={chunk}" in car[0]
+    assert len(car) == 1 and f"chunk={chunk}" in car[0] and "one launch" not in car[0]
 
 
 def test_no_log_without_hc_log(tmp_path):
@@ -108,7 +108,9 @@ def test_no_log_without_hc_log(tmp_path):
 
 def test_one_launch_schedule_logs_its_launch(tmp_path):
     """Small allreduces run as one launch by default; with HC_CU_BUDGET its
-    grid is the budget's 8 workgroups per CU."""
+    grid is the budget's 8 workgroups per CU.  The compressed allreduce of the
+    same buffers (a grid of 64 codec workgroups) also runs as one launch, with
+    the oracle's bits and wire bytes."""
     R, n = 4, 1 << 20
     g = np.random.default_rng(43)
     xs = [inputs.f32_to_bf16_bits((g.standard_normal(n) * 1e-3).astype(np.float32)) for _ in range(R)]
@@ -126,8 +128,16 @@ def test_one_launch_schedule_logs_its_launch(tmp_path):
     ref = oracle.allreduce_fold(xs)
     for q in range(R):
         assert np.array_equal(np.load(paths[q] + ".ar.npy"), ref[q]), f"allreduce rank {q}"
+    chunk = hc.hc_chunk_elems(n, 0.01, 16384)
+    ref2, ref_wire = oracle.compressed_allreduce(xs, chunk=chunk)
+    for q in range(R):
+        assert np.array_equal(np.load(paths[q] + ".car.npy"), ref2[q]), f"compressed rank {q}"
+    assert json.loads(r.stdout.strip().splitlines()[-1])["wire"] == ref_wire
     log = [ln for ln in r.stderr.splitlines() if ln.startswith("hc: ")]
     assert not [ln for ln in log if ln.startswith("hc: step launch: ")]
     chain = [ln for ln in log if ln.startswith("hc: chain launch: ")]
     # 4 slices of 2^18 bf16 in tiles of 4096: 256 chains on 8 CUs x 8 workgroups
     assert len(chain) == 1 and "chains=256 grid=64" in chain[0] and "element path" not in chain[0], chain
+    # the compressed allreduce's grid is 2^20 / 16384 = 64 workgroups, within two per CU: one launch
+    car = [ln for ln in log if ln.startswith("hc: compressed_allreduce: ")]
+    assert len(car) == 1 and "one launch" in car[0], car

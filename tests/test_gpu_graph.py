@@ -93,12 +93,14 @@ def test_captured_collective_replays_match_eager(op, dtype):
             assert np.array_equal(got, bits(ref[r])), f"replay {k} rank {r}: {first_mismatch(got, bits(ref[r]))}"
 
 
-def test_captured_compressed_allreduce_and_codec_replays():
+@pytest.mark.parametrize("chain_max", ["0", str(1 << 40)], ids=["steps", "one_launch"])
+def test_captured_compressed_allreduce_and_codec_replays(monkeypatch, chain_max):
     """The compressed allreduce and the stream codec (ticket counters and
     look-back descriptors cleared by a fill kernel inside the launch) replayed
     from one graph: the wire bytes, the sums, the stream and its decode match
     the oracle on every replay."""
     from collective_communication_amd import inputs
+    monkeypatch.setenv("HC_CHAIN_MAX_BYTES", chain_max)
     B = 16384
     R, n = 4, 3 * B + 517
     send = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(R)]

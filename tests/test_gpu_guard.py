@@ -225,8 +225,10 @@ def test_corrupt_stream_zeroes_only_the_output():
     status.check("status")
 
 
+@pytest.mark.parametrize("chain_max", ["0", str(1 << 40)], ids=["steps", "one_launch"])
 @pytest.mark.parametrize("R,n", [(4, 40 * B + 123), (3, 3 * B + 5), (8, 16 * B)])
-def test_compressed_allreduce_writes_nothing_outside(R, n):
+def test_compressed_allreduce_writes_nothing_outside(monkeypatch, chain_max, R, n):
+    monkeypatch.setenv("HC_CHAIN_MAX_BYTES", chain_max)
     xs = [inputs.normal_bf16("test", 9900 + r, n, 1e-3) for r in range(R)]
     send = [guarded_from(x) for x in xs]
     recv = [Guarded(2 * n) for _ in range(R)]
