@@ -59,13 +59,28 @@ constexpr uint32_t kStage16 = kRawFull / 16;    // 2049 uint4 of LDS staging
 constexpr uint32_t kMagic = 0x315A4348u;
 constexpr uint32_t kHistCopies = 32;            // 256 bins x 32 words = 32 KB of staging
 
-// A global-memory pointer that a device function receives as an argument
-// (arguments travel in vector registers, and the address space is lost at the
-// call): read it from the first lane, since every caller passes the same
-// pointer in all lanes, and rebuild it in the global address space, so that
-// accesses through it compile to global, not flat, instructions.
+// Thread and lane index of a codec thread (one-dimensional workgroups of kCT
+// threads), read through an empty volatile asm.  Every helper below takes its
+// index from a call of its own, so nothing the compiler derives from it (the
+// per-lane LDS and global offsets) is shared between helper calls: a kernel
+// that runs several blocks or hops in a loop then keeps no such value live
+// across the loop, where it would be hoisted out and spilled.  Within one
+// helper the values are shared as usual.
+__device__ __forceinline__ uint32_t ctid() {
+  uint32_t t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+__device__ __forceinline__ uint32_t clane() { return ctid() & 63u; }
+
+// A global-memory pointer that every lane holds with the same value, read
+// from the first lane (a convergent operation, which the compiler neither
+// hoists out of a loop nor merges with another call) and rebuilt in the
+// global address space.  A kernel that runs several hops in a loop passes its
+// per-hop pointers through it, so that the per-lane addresses derived from
+// them are formed inside each hop instead of being held across the loop.
 template <class T>
-__device__ __forceinline__ T* uniform_global(T* p) {
+__device__ __forceinline__ T* hop_ptr(T* p) {
   const uint64_t a = (uint64_t)(uintptr_t)p;
   const uint64_t u = ((uint64_t)first_lane_read((uint32_t)(a >> 32)) << 32) | first_lane_read((uint32_t)a);
   return (T*)(__attribute__((address_space(1))) T*)(uintptr_t)u;
@@ -210,8 +225,8 @@ __device__ __forceinline__ uint32_t block_excl_scan(const uint32_t (&em)[kEmWord
     mine[i] = __popc(mask_of(em, 2 * i)) | (__popc(mask_of(em, 2 * i + 1)) << 16);
     incl[i] = wave_incl_scan(mine[i]);
   }
-  const int wave = threadIdx.x >> 6;
-  if (__lane_id() == 63) {
+  const int wave = ctid() >> 6;
+  if (clane() == 63) {
 #pragma unroll
     for (int i = 0; i < kW; ++i) s.wsum[wave][i] = incl[i];
   }
@@ -240,7 +255,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(const uint32_t (&em)[kEmWord
 // Loads a block's elements: thread t gets chunks t + 512k.  Elements at or
 // past m read as zero.
 __device__ __forceinline__ void load_block(const uint16_t* src, uint32_t m, uint4 (&v)[kPer]) {
-  const int t = threadIdx.x;
+  const int t = ctid();
   if (m == kB) {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) v[k] = ld16(src + 8 * (t + kCT * k));
@@ -262,9 +277,9 @@ __device__ __forceinline__ void load_block(const uint16_t* src, uint32_t m, uint
 // fills 1 KB of LDS from 64 consecutive chunks and holds no registers), a
 // partial one element by element with zeros past m.  Ends with a barrier.
 __device__ __forceinline__ void load_block_lds(const uint16_t* src, uint32_t m, Smem& s) {
-  const uint32_t t = threadIdx.x;
+  const uint32_t t = ctid();
   if (m == kB) {
-    const uint32_t lane = __lane_id(), wave = t >> 6;
+    const uint32_t lane = clane(), wave = t >> 6;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const uint32_t c0 = kCT * k + 64u * wave;  // first chunk of this wave's 1 KB
@@ -291,7 +306,7 @@ __device__ __forceinline__ void load_block_lds(const uint16_t* src, uint32_t m, 
 
 // Stores a block's elements (first m only).
 __device__ __forceinline__ void store_block(uint16_t* dst, uint32_t m, const uint4 (&v)[kPer]) {
-  const int t = threadIdx.x;
+  const int t = ctid();
   if (m == kB) {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) st16(dst + 8 * (t + kCT * k), v[k]);
@@ -318,7 +333,7 @@ __device__ __forceinline__ void store_block(uint16_t* dst, uint32_t m, const uin
 template <class S>
 __device__ __forceinline__ void zero_hist(S& s) {
 #pragma unroll
-  for (int i = 0; i < (int)(kHistCopies * 256 / 4 / kCT); ++i) s.stage[threadIdx.x + kCT * i] = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < (int)(kHistCopies * 256 / 4 / kCT); ++i) s.stage[ctid() + kCT * i] = make_uint4(0, 0, 0, 0);
 }
 
 // 256-bin histogram of a full block's exponents.  Returns the count of
@@ -336,7 +351,7 @@ __device__ __forceinline__ void zero_hist(S& s) {
 // eight lanes to spread the banks.
 template <bool ZEROED = false, class S>
 __device__ __forceinline__ uint32_t block_histogram(const uint4 (&v)[kPer], S& s) {
-  const uint32_t t = threadIdx.x, lane = __lane_id();
+  const uint32_t t = ctid(), lane = clane();
   uint8_t* sub8 = stage8(s);
   if constexpr (!ZEROED) {
     zero_hist(s);
@@ -370,7 +385,7 @@ __device__ __forceinline__ uint32_t block_histogram(const uint4 (&v)[kPer], S& s
 // passed a barrier since.
 template <bool ZEROED = false>
 __device__ __forceinline__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, Smem& s) {
-  const uint32_t t = threadIdx.x, lane = __lane_id();
+  const uint32_t t = ctid(), lane = clane();
   Plan p;
   p.m = m;
   if (m != kB) {  // partial blocks travel raw
@@ -474,7 +489,7 @@ __device__ __forceinline__ Plan plan_block(const uint4 (&v)[kPer], uint32_t m, S
 // not smaller than the raw one travels raw.  Leaves code_of[] and the
 // dictionary in LDS like plan_block.  Ends with a barrier.
 __device__ __forceinline__ Plan given_plan(const uint8_t* order, uint32_t b, uint32_t n_esc, uint32_t m, Smem& s) {
-  const uint32_t t = threadIdx.x;
+  const uint32_t t = ctid();
   Plan p;
   p.m = m;
   p.mode = 0; p.b = 0; p.K = 0; p.n_esc = 0; p.rec_bytes = raw_bytes(m);
@@ -505,7 +520,7 @@ __device__ __forceinline__ uint32_t codes4(const uint8_t* code_of, uint32_t w0, 
 template <int B>
 __device__ __forceinline__ void write_coded(const uint4 (&v)[kPer], const Plan& p, Smem& s) {
   constexpr uint32_t poff = planes_off(B), soff = sm_off(B), eoff = esc_off(B);
-  const uint32_t t = threadIdx.x, lane = __lane_id(), qi = lane & 3u;
+  const uint32_t t = ctid(), lane = clane(), qi = lane & 3u;
   uint8_t* st = stage8(s);
   uint32_t* st32 = stage32(s);
   uint32_t escmask[kEmWords] = {};
@@ -551,7 +566,7 @@ __device__ __forceinline__ void write_coded(const uint4 (&v)[kPer], const Plan& 
 // Phase 2 of encoding: writes the record for plan p into the LDS staging
 // buffer.  Ends with a barrier.
 __device__ __forceinline__ void write_block(const uint4 (&v)[kPer], const Plan& p, Smem& s) {
-  const uint32_t t = threadIdx.x;
+  const uint32_t t = ctid();
   if (t == 0) {
     uint32_t* h = stage32(s);
     h[0] = p.mode | (p.b << 8);
@@ -584,14 +599,14 @@ __device__ __forceinline__ void write_block(const uint4 (&v)[kPer], const Plan& 
 template <class S>
 __device__ __forceinline__ void copy_out(const S& s, uint8_t* dst, uint32_t rec_bytes) {
   const uint32_t n16 = rec_bytes / 16u;
-  for (uint32_t i = threadIdx.x; i < n16; i += kCT) st16(dst + 16 * i, s.stage[i]);
+  for (uint32_t i = ctid(); i < n16; i += kCT) st16(dst + 16 * i, s.stage[i]);
 }
 
 // Copies a record from global memory into the staging buffer.
 template <class S>
 __device__ __forceinline__ void copy_in(S& s, const uint8_t* src, uint32_t rec_bytes) {
   const uint32_t n16 = rec_bytes / 16u;
-  for (uint32_t i = threadIdx.x; i < n16; i += kCT) s.stage[i] = ld16(src + 16 * i);
+  for (uint32_t i = ctid(); i < n16; i += kCT) s.stage[i] = ld16(src + 16 * i);
 }
 
 // ---------------------------------------------------------------------------
@@ -620,7 +635,7 @@ template <int B>
 __device__ __forceinline__ bool read_coded(Smem& s, uint32_t n_esc, uint4 (&v)[kPer]) {
   constexpr uint32_t K = (1u << B) - 1u;
   constexpr uint32_t poff = planes_off(B), soff = sm_off(B), eoff = esc_off(B);
-  const uint32_t t = threadIdx.x;
+  const uint32_t t = ctid();
   const uint8_t* st = stage8(s);
   const uint32_t* st32 = stage32(s);
   bool bad = false;
@@ -688,7 +703,7 @@ __device__ __forceinline__ bool read_coded(Smem& s, uint32_t n_esc, uint4 (&v)[k
 // padding byte disagrees with the format.  Ends with a barrier.
 __device__ __forceinline__ bool read_block(Smem& s, uint32_t mode, uint32_t b, uint32_t m, uint32_t n_esc,
                            uint32_t rec_bytes, uint4 (&v)[kPer]) {
-  const int t = threadIdx.x;
+  const int t = ctid();
   const uint8_t* st = stage8(s);
   if (mode == 0) {
     const uint32_t n16 = (rec_bytes - 16u) / 16u;

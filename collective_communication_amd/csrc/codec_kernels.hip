@@ -445,7 +445,7 @@ __device__ __forceinline__ uint32_t block_elems(const CarGeom& g, uint32_t j, ui
 }
 
 __device__ __forceinline__ void count_wire(const CarGeom& g, uint32_t rec_bytes) {
-  if (g.wire_bytes && threadIdx.x == 0) atomicAdd((unsigned long long*)g.wire_bytes, (unsigned long long)rec_bytes);
+  if (g.wire_bytes && ctid() == 0) atomicAdd((unsigned long long*)g.wire_bytes, (unsigned long long)rec_bytes);
 }
 
 // Reads a wire record produced by this library from a slot into LDS and
@@ -459,7 +459,7 @@ constexpr uint32_t kSpecVecs = kSpecPer * kCT;      // 1536 vectors = 24 KB
 static_assert(kSpecVecs <= kStage16, "read-ahead stays inside a slot");
 
 __device__ __forceinline__ void read_slot(Smem& s, const uint8_t* src, uint32_t m, uint4 (&v)[kPer]) {
-  const uint32_t t = threadIdx.x;
+  const uint32_t t = ctid();
   uint4 pre[kSpecPer];
 #pragma unroll
   for (uint32_t i = 0; i < kSpecPer; ++i) pre[i] = ld16(src + 16 * (t + kCT * i));
@@ -518,7 +518,7 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
   load_block_lds(ptr.send[q] + e0, m, s);
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    v[k] = hop_bf16x8(v[k], s.stage[threadIdx.x + kCT * k]);
+    v[k] = hop_bf16x8(v[k], s.stage[ctid() + kCT * k]);
     // Pin each packed word: left alone, the compiler carries the two unpacked
     // halves of every sum into the encoder and runs out of registers there.
     asm volatile("" : "+v"(v[k].x), "+v"(v[k].y), "+v"(v[k].z), "+v"(v[k].w));
@@ -552,19 +552,16 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
   }
 }
 
-// One hop of a chain (see car_chain_kernel), kept out of line so that each
-// call gets the register budget of a one-hop kernel (inlined into the
-// chain's loops, the encoder spilled).  Reduce-scatter hop: fold the record
-// in slot_in (none for the first hop) with the own block `own`, write the
-// sum to `out` when given (the last step), compress it into slot_out.
-__device__ __attribute__((noinline)) void chain_rs_hop(const uint8_t* slot_in, const uint16_t* own, uint16_t* out,
-                                                      uint8_t* slot_out, uint64_t* wire_bytes, uint32_t m,
-                                                      Smem& s) {
-  slot_in = uniform_global(slot_in);
-  own = uniform_global(own);
-  out = uniform_global(out);
-  slot_out = uniform_global(slot_out);
-  wire_bytes = uniform_global(wire_bytes);
+// One hop of a chain (see car_chain_kernel).  Reduce-scatter hop: fold the
+// record in slot_in (none for the first hop) with the own block `own`, write
+// the sum to `out` when given (the last step), compress it into slot_out.
+__device__ __forceinline__ void chain_rs_hop(const uint8_t* slot_in, const uint16_t* own, uint16_t* out,
+                                             uint8_t* slot_out, uint64_t* wire_bytes, uint32_t m, Smem& s) {
+  slot_in = hop_ptr(slot_in);
+  own = hop_ptr(own);
+  out = hop_ptr(out);
+  slot_out = hop_ptr(slot_out);
+  wire_bytes = hop_ptr(wire_bytes);
   m = first_lane_read(m);
   uint4 v[kPer];
   if (!slot_in) {
@@ -574,7 +571,7 @@ __device__ __attribute__((noinline)) void chain_rs_hop(const uint8_t* slot_in, c
     load_block_lds(own, m, s);
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-      v[k] = hop_bf16x8(v[k], s.stage[threadIdx.x + kCT * k]);
+      v[k] = hop_bf16x8(v[k], s.stage[ctid() + kCT * k]);
       asm volatile("" : "+v"(v[k].x), "+v"(v[k].y), "+v"(v[k].z), "+v"(v[k].w));
     }
     __syncthreads();
@@ -583,18 +580,18 @@ __device__ __attribute__((noinline)) void chain_rs_hop(const uint8_t* slot_in, c
   const Plan pl = plan_block(v, m, s);
   write_block(v, pl, s);
   copy_out(s, slot_out, pl.rec_bytes);
-  if (wire_bytes && threadIdx.x == 0) atomicAdd((unsigned long long*)wire_bytes, (unsigned long long)pl.rec_bytes);
+  if (wire_bytes && ctid() == 0) atomicAdd((unsigned long long*)wire_bytes, (unsigned long long)pl.rec_bytes);
   __syncthreads();   // the record is out of the staging buffer
 }
 
 // All-gather hop: decode the record in slot_in into `out`; forward the same
 // bytes into slot_out when given.
-__device__ __attribute__((noinline)) void chain_ag_hop(const uint8_t* slot_in, uint16_t* out, uint8_t* slot_out,
-                                                      uint64_t* wire_bytes, uint32_t m, Smem& s) {
-  slot_in = uniform_global(slot_in);
-  out = uniform_global(out);
-  slot_out = uniform_global(slot_out);
-  wire_bytes = uniform_global(wire_bytes);
+__device__ __forceinline__ void chain_ag_hop(const uint8_t* slot_in, uint16_t* out, uint8_t* slot_out,
+                                             uint64_t* wire_bytes, uint32_t m, Smem& s) {
+  slot_in = hop_ptr(slot_in);
+  out = hop_ptr(out);
+  slot_out = hop_ptr(slot_out);
+  wire_bytes = hop_ptr(wire_bytes);
   m = first_lane_read(m);
   uint4 v[kPer];
   read_slot(s, slot_in, m, v);
@@ -602,7 +599,7 @@ __device__ __attribute__((noinline)) void chain_ag_hop(const uint8_t* slot_in, u
   if (slot_out) {
     const uint32_t rb = s.plan[4];
     copy_out(s, slot_out, rb);
-    if (wire_bytes && threadIdx.x == 0) atomicAdd((unsigned long long*)wire_bytes, (unsigned long long)rb);
+    if (wire_bytes && ctid() == 0) atomicAdd((unsigned long long*)wire_bytes, (unsigned long long)rb);
   }
   __syncthreads();
 }

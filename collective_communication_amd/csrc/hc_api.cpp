@@ -265,25 +265,16 @@ uint64_t chain_max_bytes() {
 }
 
 // The compressed allreduce runs as one launch (each codec block of each slice
-// through every hop) while its grid, one workgroup per block and slice, holds
-// at most two workgroups per CU; a codec workgroup's LDS admits four per CU.
-// Measured on MI355X (us, step-per-launch / one launch; grid = count / 16384):
-// R=2 x 2^23 (grid 512) 39.9 / 39.9, x 2^24 59.0 / 65.6; R=4 x 2^21 (128)
-// 88.7 / 53.3, x 2^23 (512) 95.2 / 85.8, x 2^24 144 / 157; R=8 x 2^22 (256)
-// 149 / 116, x 2^23 (512) 205 / 188, x 2^24 (1024) 309 / 311, x 2^25 568 /
-// 608.  Beyond that the chains, each 2R-1 hops long, run in rounds, and the
-// step launches fill the device better.  HC_CHAIN_MAX_BYTES, when set,
-// replaces the rule by the same byte threshold as the plain allreduce's.
+// through every hop) unless HC_CHAIN_MAX_BYTES is set, which then applies the
+// plain allreduce's byte threshold.  Measured on MI355X (us, step-per-launch /
+// one launch): R=2 x 2^18 24.4 / 21.6, x 2^25 106 / 101; R=4 x 2^22 70.9 /
+// 54.3, x 2^25 257 / 217; R=8 x 2^22 149 / 105, x 2^25 545 / 446.  Every hop
+// of a block depends only on the hop before it, so one launch needs no wait
+// between workgroups and saves the ramps and tails of 2R-1 launches.
 bool compressed_one_launch(size_t count, int nranks) {
   uint64_t v;
   if (env_chain_max_bytes(&v)) return (uint64_t)count * 2u * (uint64_t)nranks <= v;
-  int dev = 0, ncu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
-    return false;
-  const uint64_t L = (count + (size_t)nranks - 1) / (size_t)nranks;
-  const uint64_t grid = (uint64_t)nranks * ((L + HC_BLOCK_ELEMS - 1) / HC_BLOCK_ELEMS);
-  return grid <= 2u * (uint64_t)ncu;
+  return true;
 }
 
 double chunk_fraction(const hc_opts_t* o) {

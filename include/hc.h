@@ -108,10 +108,9 @@ typedef enum {
  *       one launch in which each workgroup carries one tile through every
  *       hop in ring order (unless step_events or copy_engine ask for per-step
  *       launches); larger ones launch once per ring step.  When set, it is
- *       also hc_compressed_allreduce's threshold (bytes of its R buffers), in
- *       place of that call's default rule (one launch while count / 16384,
- *       rounded up per slice, is at most two workgroups per CU).  Values and
- *       wire bytes are the same either way.
+ *       also hc_compressed_allreduce's threshold (bytes of its R buffers),
+ *       which otherwise always runs as one launch.  Values and wire bytes are
+ *       the same either way.
  *     HC_LOOKBACK_SPIN_LIMIT (1..2^32-1; default 2^22): polls a compress
  *       block's look-back makes before the call gives up (see
  *       hc_compress_bf16).
@@ -433,12 +432,11 @@ hc_status_t hc_decompress_bf16(const void *d_in, size_t in_bytes, uint16_t *d_ou
  *   block (the preallocated regions of "CCCL ...", section 4.4).
  *   d_wire_bytes: optional device u64; receives the bytes that would cross
  *   the links: the sum over every (hop, chunk) stream of its HCZ1 size.
- *   Schedule: while the grid of one workgroup per codec block and slice holds
- *   at most two workgroups per CU (count <= 2^23 on MI355X's 256 CUs), or
- *   within HC_CHAIN_MAX_BYTES when that is set, the hops run in one launch,
- *   each workgroup carrying its block through every hop in ring order, with
- *   the wire slots indexed by slice; otherwise (and with step_events) one
- *   launch per ring step.  Same records, wire bytes and output either way.
+ *   Schedule: one launch, one workgroup per codec block and slice, each
+ *   carrying its block through every hop in ring order, with the wire slots
+ *   indexed by slice; with step_events, or beyond HC_CHAIN_MAX_BYTES when that
+ *   is set, one launch per ring step.  Same records, wire bytes and output
+ *   either way.
  */
 hc_status_t hc_compressed_allreduce(void *const *sendbufs, void *const *recvbufs, size_t count,
                                     int nranks, void *d_ws, size_t ws_bytes,
