@@ -54,7 +54,8 @@ N_CU = 256
 METRIC = "AllReduce algbw GB/s and achieved HBM GB/s (% of peak), R=8, 1 MI355X"
 # sources whose change voids the recorded traffic counters of a kernel
 CODEC_FILES = ["collective_communication_amd/csrc/codec_kernels.hip", "collective_communication_amd/csrc/codec.hpp",
-               "collective_communication_amd/csrc/lookback.hpp", "collective_communication_amd/csrc/common.hpp"]
+               "collective_communication_amd/csrc/lookback.hpp", "collective_communication_amd/csrc/common.hpp",
+               "collective_communication_amd/csrc/car.hpp", "collective_communication_amd/csrc/car_chain.hip"]
 ENTROPY_FILES = ["collective_communication_amd/csrc/entropy_kernels.hip", "collective_communication_amd/csrc/codec.hpp",
                  "collective_communication_amd/csrc/lookback.hpp", "collective_communication_amd/csrc/common.hpp"]
 RING_FILES = ["collective_communication_amd/csrc/ring_kernels.hip", "collective_communication_amd/csrc/common.hpp"]

@@ -26,7 +26,8 @@ CEILING_TOOL = os.path.join(PKG, "hbm_ceiling")
 ARCH = os.environ.get("HC_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["hc_api.cpp", "schedule.cpp", "ring_kernels.hip", "codec_kernels.hip", "entropy_kernels.hip"]
+SOURCES = ["hc_api.cpp", "schedule.cpp", "ring_kernels.hip", "codec_kernels.hip", "car_chain.hip",
+           "entropy_kernels.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math",
           "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]

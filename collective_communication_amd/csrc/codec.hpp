@@ -43,8 +43,25 @@
 
 #include "common.hpp"
 
+// HC_CODEC_OPAQUE_TID (0 unless the including file sets it first): the codec
+// helpers read their thread index through an opaque read (see ctid below).
+// Only a kernel that runs several blocks or hops in one loop wants it; the
+// one-block kernels keep the plain read, whose values the compiler shares
+// between helpers.  The two builds of the helpers live in differently named
+// inline namespaces, so files built with different settings never share a
+// definition.
+#ifndef HC_CODEC_OPAQUE_TID
+#define HC_CODEC_OPAQUE_TID 0
+#endif
+#if HC_CODEC_OPAQUE_TID
+#define HC_CODEC_TID_NS opaque_tid
+#else
+#define HC_CODEC_TID_NS plain_tid
+#endif
+
 namespace hc {
 namespace codec {
+inline namespace HC_CODEC_TID_NS {
 
 constexpr uint32_t kB = 16384;                  // elements per block
 constexpr uint32_t kChunks = kB / 8;            // 16-byte chunks per block
@@ -60,15 +77,17 @@ constexpr uint32_t kMagic = 0x315A4348u;
 constexpr uint32_t kHistCopies = 32;            // 256 bins x 32 words = 32 KB of staging
 
 // Thread and lane index of a codec thread (one-dimensional workgroups of kCT
-// threads), read through an empty volatile asm.  Every helper below takes its
-// index from a call of its own, so nothing the compiler derives from it (the
-// per-lane LDS and global offsets) is shared between helper calls: a kernel
-// that runs several blocks or hops in a loop then keeps no such value live
-// across the loop, where it would be hoisted out and spilled.  Within one
-// helper the values are shared as usual.
+// threads).  With HC_CODEC_OPAQUE_TID the index passes through an empty
+// volatile asm, and every helper below takes it from a call of its own, so
+// nothing the compiler derives from it (the per-lane LDS and global offsets)
+// is shared between helper calls: a kernel that runs several hops in a loop
+// then keeps no such value live across the loop, where it would be hoisted
+// out and spilled.  Within one helper the values are shared as usual.
 __device__ __forceinline__ uint32_t ctid() {
   uint32_t t = threadIdx.x;
+#if HC_CODEC_OPAQUE_TID
   asm volatile("" : "+v"(t));
+#endif
   return t;
 }
 __device__ __forceinline__ uint32_t clane() { return ctid() & 63u; }
@@ -740,5 +759,6 @@ __device__ __forceinline__ bool read_block(Smem& s, uint32_t mode, uint32_t b, u
   }
 }
 
+}  // inline namespace HC_CODEC_TID_NS
 }  // namespace codec
 }  // namespace hc

@@ -24,6 +24,7 @@
 
 #include <mutex>
 
+#include "car.hpp"
 #include "codec.hpp"
 #include "launch.hpp"
 #include "lookback.hpp"
@@ -216,7 +217,10 @@ __global__ __launch_bounds__(256) void staged_copy_kernel(const uint8_t* __restr
 
 // Table scope, step 1: each full block's exponent histogram.  A workgroup
 // walks blocks blockIdx.x, + gridDim.x, ... and loads the next block while it
-// counts the current one.
+// counts the current one.  The next block's loads are issued on every
+// iteration (the last one loads its own block again): behind a condition,
+// the wait before the count had to allow for the path without them, and
+// then also waited for them, so no load overlapped a count.
 __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void scope_hist_kernel(
     const uint16_t* __restrict__ in, ScopeWs sc, uint32_t full) {
   __shared__ Smem s;
@@ -225,8 +229,8 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
   uint4 v[kPer], nv[kPer];
   if (k < full) load_block(in + (uint64_t)k * kB, kB, v);
   for (; k < full; k += stride) {
-    const uint32_t kn = k + stride;
-    if (kn < full) load_block(in + (uint64_t)kn * kB, kB, nv);
+    const uint32_t kn = k + stride < full ? k + stride : k;
+    load_block(in + (uint64_t)kn * kB, kB, nv);
     const uint32_t cnt = block_histogram<false>(v, s);   // cnt <= 16384
     if (t < 256u) sc.bhist[256ull * k + t] = (uint16_t)cnt;
     __syncthreads();   // the counts are read before the next block clears them
@@ -416,74 +420,6 @@ __global__ void zero_if_corrupt_kernel(const int32_t* status, uint32_t* out, siz
 // compressed ring allreduce
 // ---------------------------------------------------------------------------
 
-struct RingPtrs {
-  const uint16_t* send[kMaxRanks];
-  uint16_t* recv[kMaxRanks];
-};
-
-struct CarGeom {
-  uint64_t count;      // elements per rank buffer
-  uint64_t L;          // slice length
-  uint32_t R;
-  uint32_t nbs;        // block slots per slice
-  uint8_t* wire;       // R x 2 x nbs slots of kRawFull bytes
-  uint64_t* wire_bytes;
-};
-
-__device__ __forceinline__ uint8_t* slot(const CarGeom& g, uint32_t rank, uint32_t buf, uint32_t blk) {
-  return g.wire + (((uint64_t)rank * 2 + buf) * g.nbs + blk) * kRawFull;
-}
-
-// Elements of block blk of slice j (0 when the block lies past the slice).
-__device__ __forceinline__ uint32_t block_elems(const CarGeom& g, uint32_t j, uint32_t blk) {
-  uint64_t lo = (uint64_t)j * g.L, hi = lo + g.L;
-  if (lo > g.count) lo = g.count;
-  if (hi > g.count) hi = g.count;
-  const uint64_t b0 = lo + (uint64_t)blk * kB;
-  if (b0 >= hi) return 0;
-  return (uint32_t)((hi - b0) < kB ? (hi - b0) : kB);
-}
-
-__device__ __forceinline__ void count_wire(const CarGeom& g, uint32_t rec_bytes) {
-  if (g.wire_bytes && ctid() == 0) atomicAdd((unsigned long long*)g.wire_bytes, (unsigned long long)rec_bytes);
-}
-
-// Reads a wire record produced by this library from a slot into LDS and
-// decodes it.  The first kSpecVecs vectors of the slot are loaded with the
-// record header, before its length is known (they lie inside the slot
-// whatever the record is), so a record of up to kSpecVecs * 16 bytes takes
-// one round trip.  The record header is clamped to the slot so that a
-// damaged slot can never send a read out of bounds.
-constexpr uint32_t kSpecPer = 3;                    // vectors per thread read ahead
-constexpr uint32_t kSpecVecs = kSpecPer * kCT;      // 1536 vectors = 24 KB
-static_assert(kSpecVecs <= kStage16, "read-ahead stays inside a slot");
-
-__device__ __forceinline__ void read_slot(Smem& s, const uint8_t* src, uint32_t m, uint4 (&v)[kPer]) {
-  const uint32_t t = ctid();
-  uint4 pre[kSpecPer];
-#pragma unroll
-  for (uint32_t i = 0; i < kSpecPer; ++i) pre[i] = ld16(src + 16 * (t + kCT * i));
-  if (t == 0) {
-    const uint32_t mode = pre[0].x & 0xFFu, b = (pre[0].x >> 8) & 0xFFu, ne = pre[0].z, rb = pre[0].w;
-    const bool ok = (mode == 0 && rb == raw_bytes(m)) ||
-                    (mode == 1 && m == kB && b >= 1 && b <= 7 && ne <= kB && rb == coded_bytes(b, ne) &&
-                     rb < kRawFull);
-    s.plan[1] = ok ? mode : 0u;
-    s.plan[2] = ok ? b : 0u;
-    s.plan[3] = ok ? ne : 0u;
-    s.plan[4] = ok ? rb : raw_bytes(m);
-  }
-  __syncthreads();
-  const uint32_t mode = s.plan[1], b = s.plan[2], ne = s.plan[3], rb = s.plan[4];
-  const uint32_t n16 = rb / 16u;
-#pragma unroll
-  for (uint32_t i = 0; i < kSpecPer; ++i)
-    if (t + kCT * i < n16) s.stage[t + kCT * i] = pre[i];
-  for (uint32_t i = kSpecVecs + t; i < n16; i += kCT) s.stage[i] = ld16(src + 16 * i);
-  __syncthreads();
-  read_block(s, mode, b, m, ne, rb, v);
-}
-
 // Reduce-scatter step 0: every rank compresses the slice it sends first.
 __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void car_first_kernel(RingPtrs ptr, CarGeom g) {
   __shared__ Smem s;
@@ -549,88 +485,6 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
     const uint32_t rb = s.plan[4];
     copy_out(s, slot(g, q, buf_in ^ 1u, blk), rb);
     count_wire(g, rb);
-  }
-}
-
-// One hop of a chain (see car_chain_kernel).  Reduce-scatter hop: fold the
-// record in slot_in (none for the first hop) with the own block `own`, write
-// the sum to `out` when given (the last step), compress it into slot_out.
-__device__ __forceinline__ void chain_rs_hop(const uint8_t* slot_in, const uint16_t* own, uint16_t* out,
-                                             uint8_t* slot_out, uint64_t* wire_bytes, uint32_t m, Smem& s) {
-  slot_in = hop_ptr(slot_in);
-  own = hop_ptr(own);
-  out = hop_ptr(out);
-  slot_out = hop_ptr(slot_out);
-  wire_bytes = hop_ptr(wire_bytes);
-  m = first_lane_read(m);
-  uint4 v[kPer];
-  if (!slot_in) {
-    load_block(own, m, v);
-  } else {
-    read_slot(s, slot_in, m, v);
-    load_block_lds(own, m, s);
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      v[k] = hop_bf16x8(v[k], s.stage[ctid() + kCT * k]);
-      asm volatile("" : "+v"(v[k].x), "+v"(v[k].y), "+v"(v[k].z), "+v"(v[k].w));
-    }
-    __syncthreads();
-    if (out) store_block(out, m, v);
-  }
-  const Plan pl = plan_block(v, m, s);
-  write_block(v, pl, s);
-  copy_out(s, slot_out, pl.rec_bytes);
-  if (wire_bytes && ctid() == 0) atomicAdd((unsigned long long*)wire_bytes, (unsigned long long)pl.rec_bytes);
-  __syncthreads();   // the record is out of the staging buffer
-}
-
-// All-gather hop: decode the record in slot_in into `out`; forward the same
-// bytes into slot_out when given.
-__device__ __forceinline__ void chain_ag_hop(const uint8_t* slot_in, uint16_t* out, uint8_t* slot_out,
-                                             uint64_t* wire_bytes, uint32_t m, Smem& s) {
-  slot_in = hop_ptr(slot_in);
-  out = hop_ptr(out);
-  slot_out = hop_ptr(slot_out);
-  wire_bytes = hop_ptr(wire_bytes);
-  m = first_lane_read(m);
-  uint4 v[kPer];
-  read_slot(s, slot_in, m, v);
-  store_block(out, m, v);
-  if (slot_out) {
-    const uint32_t rb = s.plan[4];
-    copy_out(s, slot_out, rb);
-    if (wire_bytes && ctid() == 0) atomicAdd((unsigned long long*)wire_bytes, (unsigned long long)rb);
-  }
-  __syncthreads();
-}
-
-// The whole compressed allreduce in one launch: workgroup (j, blk) carries
-// codec block blk of slice j through every hop, in the ring's order, with
-// the operations of the kernels above (the first sender compresses it; each
-// reduce-scatter receiver decompresses, adds its own block, writes the sum at
-// the last step and compresses again; each all-gather receiver decompresses
-// into its output and forwards the same bytes).  A chunk's hops depend only
-// on one another ("ResCCL: Resource-Efficient Scheduling for Collective
-// Communication", section 3), so blocks never wait for each other; the slots
-// are indexed by slice instead of by sending rank, since chains of different
-// slices are at different hops at once (the same number of slots).  Same
-// records, same wire bytes, same output as the step-per-launch schedule.
-__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void car_chain_kernel(RingPtrs ptr, CarGeom g) {
-  __shared__ Smem s;
-  const uint32_t j = blockIdx.x / g.nbs, blk = blockIdx.x % g.nbs;
-  const uint32_t m = block_elems(g, j, blk);
-  if (m == 0) return;
-  const uint32_t R = g.R;
-  const uint64_t e0 = (uint64_t)j * g.L + (uint64_t)blk * kB;
-  for (uint32_t h = 0; h < R; ++h) {   // hop 0: the first sender j + 1; hop h: reduce-scatter step h - 1
-    const uint32_t q = (j + 1 + h) % R;
-    chain_rs_hop(h ? slot(g, j, (h - 1) & 1, blk) : nullptr, ptr.send[q] + e0,
-                 h + 1 == R ? ptr.recv[q] + e0 : nullptr, slot(g, j, h & 1, blk), g.wire_bytes, m, s);
-  }
-  for (uint32_t step = 0; step + 1 < R; ++step) {   // all-gather step: receiver j + 1 + step
-    const uint32_t q = (j + 1 + step) % R, buf = (R - 1 + step) & 1u;
-    chain_ag_hop(slot(g, j, buf, blk), ptr.recv[q] + e0, step + 2 < R ? slot(g, j, buf ^ 1u, blk) : nullptr,
-                 g.wire_bytes, m, s);
   }
 }
 
@@ -865,10 +719,8 @@ hipError_t launch_compressed_allreduce(void* const* send, void* const* recv, siz
   g.wire = static_cast<uint8_t*>(ws);
   g.wire_bytes = wire_bytes;
   const dim3 grid((uint32_t)(R * nbs)), block(kCT);
-  if (!tap.ev && one_launch) {   // no per-step timing asked for: one launch, each block through every hop
-    void* args[] = {&ptr, &g};
-    return launch_kernel((const void*)car_chain_kernel, grid, block, args, stream);
-  }
+  if (!tap.ev && one_launch)   // no per-step timing asked for: one launch, each block through every hop
+    return launch_car_chain(ptr, g, stream);
   hipError_t e = mark();
   if (e != hipSuccess) return e;
   void* first_args[] = {&ptr, &g};
