@@ -52,6 +52,11 @@ PEAK_BF16_TFLOPS = 2500.0       # dense bf16 MFMA, published
 N_CU = 256
 
 METRIC = "AllReduce algbw GB/s and achieved HBM GB/s (% of peak), R=8, 1 MI355X"
+
+
+def ring_metric(R: int) -> str:
+    """The headline metric (R=8), with the rank count of a workload that uses another."""
+    return METRIC.replace("R=8,", f"R={R},")
 # sources whose change voids the recorded traffic counters of a kernel
 CODEC_FILES = ["collective_communication_amd/csrc/codec_kernels.hip", "collective_communication_amd/csrc/codec.hpp",
                "collective_communication_amd/csrc/lookback.hpp", "collective_communication_amd/csrc/common.hpp",
@@ -256,7 +261,7 @@ def bench_ring(args, workload: str):
     chain_max = int(os.environ.get("HC_CHAIN_MAX_BYTES", str(256 << 20)) or 0)
     one_launch = R * n * es <= chain_max
     line = {
-        "metric": METRIC, "value": round(algbw, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "metric": ring_metric(R), "value": round(algbw, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": f"emulated ring allreduce (sum), R={R} ranks x {n} {dtype} per rank, "

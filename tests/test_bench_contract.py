@@ -87,3 +87,9 @@ def test_cpu_baseline_names_its_host():
     rec = bench.oracle_timed(lambda: sum(range(1000)), 1000, "a sample")
     assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["nproc"] == info["nproc"]
     assert "cpu_model" in rec
+
+
+def test_ring_metric_names_its_rank_count():
+    # the headline line carries the metric string as given; another rank count names its own
+    assert bench.ring_metric(8) == bench.METRIC
+    assert "R=4," in bench.ring_metric(4) and "R=8" not in bench.ring_metric(4)
