@@ -107,3 +107,28 @@ def test_compressed_allreduce_full_size_matches_oracle(monkeypatch):
     assert int(wire.item()) == ref_wire, (int(wire.item()), ref_wire)
     raw = 2 * (R - 1) * n * 2   # uncompressed wire bytes of the ring (both phases)
     assert 0.6 < ref_wire / raw < 0.8, ref_wire / raw
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("R,n", [(2, 1 << 28), (16, 1 << 22), (3, (1 << 26) + 12345)])
+def test_one_launch_equals_step_schedule_at_scale(monkeypatch, R, n):
+    """Beyond the oracle-checked sizes: the one-launch schedule gives the
+    step schedule's bits and wire bytes at 2^28 elements per rank, at 16
+    ranks, and with a ragged tail (the step schedule is itself checked
+    against the oracle at R=8 x 2^25 above)."""
+    send = inputs.ring_inputs_cuda("compressed", R, n)
+    ws = torch.empty(hc.hc_workspace_bytes(hc.HC_OP_COMPRESSED_ALLREDUCE, n, R), dtype=torch.uint8, device="cuda")
+    outs, wires = {}, {}
+    for name, val in (("steps", "0"), ("one_launch", str(1 << 62))):
+        monkeypatch.setenv("HC_CHAIN_MAX_BYTES", val)
+        recv = [torch.empty_like(s) for s in send]
+        wire = torch.zeros(1, dtype=torch.int64, device="cuda")
+        hc.hc_compressed_allreduce(send, recv, n, ws, wire)
+        torch.cuda.synchronize()
+        outs[name], wires[name] = recv, int(wire.item())
+    assert wires["steps"] == wires["one_launch"] > 0
+    for r in range(R):
+        assert torch.equal(outs["steps"][r].view(torch.int16), outs["one_launch"][r].view(torch.int16)), f"rank {r}"
+    # every rank holds the same sums
+    for r in range(1, R):
+        assert torch.equal(outs["one_launch"][0].view(torch.int16), outs["one_launch"][r].view(torch.int16))
