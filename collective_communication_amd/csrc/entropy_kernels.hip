@@ -31,7 +31,7 @@
 // segments of a lane share is merged afterwards.
 //
 // decompress: one wave per block (the 64 lanes are the 64 streams).  The
-// code lengths give a 4,096-entry table (12-bit window -> symbol, length) in
+// code lengths give a two-level table (12-bit window -> symbol, length) in
 // LDS; the next 128 words of the record sit in two registers across the
 // wave and a lane takes its word by a lane shuffle, so the only memory on
 // the per-step chain is the table read.
@@ -599,36 +599,43 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
 // window.  Codes of 11 and 12 bits cover at most 2 windows each, so the
 // secondary table needs at most 2 * 256 entries plus the rounding of kraft up
 // to 4.  A block thus takes 4.1 KB of LDS instead of the 9.2 KB of one
-// 4096-entry table, and more blocks stay resident per compute unit.
+// 4096-entry table, and more blocks stay resident per compute unit.  Both
+// tables are stored at bit-reversed indices (lookup).
 constexpr uint16_t kNoCode = 0xFFFFu;
 constexpr uint32_t kPrimBits = 10;
 constexpr uint32_t kLongMark = 14u;
 constexpr uint32_t kSecMax = 2 * 256 + 4;
 
 struct HceDecSmem {
-  uint16_t lut[1u << kPrimBits];  // top 10 window bits -> entry, or a pointer into lut2
-  uint16_t lut2[kSecMax];         // windows T .. round_up(kraft, 4) - 1 -> entry
+  uint16_t lut[1u << kPrimBits];  // first 10 window bits (reversed) -> entry, or a pointer into lut2
+  uint16_t lut2[kSecMax];         // windows T .. round_up(kraft, 4) - 1 (last 2 bits reversed) -> entry
   uint16_t start[257];            // window value where each code (in length, exponent order) begins
   uint16_t ent[256];              // table entry of each code in that order
 };
 
-// Entry of the code at the top of buf (the next stream bits, first bit on top).
+// Entry of the code at the bottom of buf (the next stream bits, first bit in
+// bit 0).  The tables are indexed by the window's bits in stream order from
+// the low bit up, i.e. by the bit-reversed window (fill_table stores them so):
+// the primary by stream bits 0..9, the secondary by its range offset plus
+// stream bits 10 and 11.  A decoder that holds its bits this way adds a word
+// with one shift and needs no bit reversal per word.
 __device__ __forceinline__ uint32_t lookup(const HceDecSmem& s, uint64_t buf) {
-  const uint32_t w = (uint32_t)(buf >> (64u - kLmax));
-  uint32_t e = s.lut[w >> (kLmax - kPrimBits)];
-  if ((e & 15u) == kLongMark) e = s.lut2[(e >> 4) | (w & ((1u << (kLmax - kPrimBits)) - 1u))];
+  const uint32_t w = (uint32_t)buf;
+  uint32_t e = s.lut[w & ((1u << kPrimBits) - 1u)];
+  if ((e & 15u) == kLongMark) e = s.lut2[(e >> 4) | ((w >> kPrimBits) & ((1u << (kLmax - kPrimBits)) - 1u))];
   return e;
 }
 
-// Fills tbl[i] for i in [0, cnt) with the entry of the code holding window
-// base + stride*i: kNoCode at or past kraft, a pointer into lut2 at or past
-// long_from, else the code's own entry.  Lane l takes entries
+// Fills tbl[rev(i)] for i in [0, cnt) with the entry of the code holding
+// window base + stride*i: kNoCode at or past kraft, a pointer into lut2 at
+// or past long_from, else the code's own entry.  rev reverses the low
+// rev_bits bits of i (the lookup indexes by stream bits, first bit lowest).  Lane l takes entries
 // [per*l, per*l + per); it starts at a lane-dependent point of its run and
 // wraps, so that the lanes' writes fall in different banks, and walks the
 // codes forward (they are consecutive in window order).
 __device__ __forceinline__ void fill_table(const HceDecSmem& s, uint16_t* tbl, uint32_t cnt, uint32_t per,
                                            uint32_t base, uint32_t stride, uint32_t long_from, uint32_t n_sym,
-                                           uint32_t kraft) {
+                                           uint32_t kraft, uint32_t rev_bits) {
   const uint32_t lane = threadIdx.x, i0 = per * lane;
   if (i0 >= cnt) return;
   const uint32_t len = (cnt - i0) < per ? (cnt - i0) : per, r = lane % len;
@@ -654,8 +661,9 @@ __device__ __forceinline__ void fill_table(const HceDecSmem& s, uint16_t* tbl, u
     if (o == 0 && j != 0) { k = k0; next = s.start[k + 1]; cur = s.ent[k]; }
     const uint32_t x = base + stride * (i0 + o);
     while (x >= next && k + 1 < n_sym) { ++k; next = s.start[k + 1]; cur = s.ent[k]; }
-    tbl[i0 + o] = x >= kraft ? kNoCode
-                             : x >= long_from ? (uint16_t)(((x - long_from) << 4) | kLongMark) : (uint16_t)cur;
+    const uint32_t i = i0 + o, lowmask = (1u << rev_bits) - 1u;
+    tbl[(i & ~lowmask) | (__builtin_bitreverse32(i & lowmask) >> (32u - rev_bits))] =
+        x >= kraft ? kNoCode : x >= long_from ? (uint16_t)(((x - long_from) << 4) | kLongMark) : (uint16_t)cur;
   }
 }
 
@@ -668,19 +676,26 @@ __device__ __forceinline__ bool decode_steps(const HceDecSmem& s, const uint8_t*
                                              uint16_t* __restrict__ dst) {
   const uint32_t lane = threadIdx.x;
   const uint32_t* wg = reinterpret_cast<const uint32_t*>(rec + kWordsOff);
-  uint32_t win = lane < n_words ? wg[lane] : 0u;
-  uint32_t win2 = 64u + lane < n_words ? wg[64u + lane] : 0u;
+  // Window words are loaded without a condition: a lane whose word would lie
+  // past the last one reads the record's first word instead (always in
+  // bounds), a value that a valid stream never takes.  A select between the
+  // loaded word and a constant would make the wave wait for the load at once
+  // (and, counters being in order, for every load and store before it); as
+  // it is, the first wait comes when the window is used, steps later.
+  const uint32_t* hdr = reinterpret_cast<const uint32_t*>(rec);
+  uint32_t win = *(lane < n_words ? wg + lane : hdr);
+  uint32_t win2 = *(64u + lane < n_words ? wg + 64u + lane : hdr);
   uint32_t wbase = 0, base = 0, avail = 0;
-  uint64_t buf = 0;   // the lane's next `avail` stream bits, from the top bit down
+  uint64_t buf = 0;   // the lane's next `avail` stream bits, from bit 0 up; zero above them
   bool bad = false;
   const uint8_t* smp = rec + kSmOff + lane;
   uint32_t smn[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) smn[q] = smp[64u * q];
   for (uint32_t i0 = 0; i0 < kSteps; i0 += 8) {
-    uint32_t smv[8];   // sign at bit 15, fraction in bits 0..6
+    uint32_t smv[8];   // sign at bit 15 (and 7), fraction in bits 0..6 (and 8..14)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) smv[q] = (smn[q] * 0x101u) & 0x807Fu;
+    for (int q = 0; q < 8; ++q) smv[q] = smn[q] * 0x101u;
     if (i0 + 8 < kSteps) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) smn[q] = smp[64u * (i0 + 8 + q)];
@@ -692,30 +707,34 @@ __device__ __forceinline__ bool decode_steps(const HceDecSmem& s, const uint8_t*
       const bool need = L > avail;
       const uint64_t mask = __ballot(need);
       if (mask) {
+        const uint32_t taken = (uint32_t)__popcll(mask);
         const uint32_t rel = base - wbase + lanemask_lt_count(mask);   // < 128: base - wbase < 64 at every step
         uint32_t word = __shfl(win, (int)(rel & 63u), 64);
-        if (__ballot(need && rel >= 64u)) {
+        if (base - wbase + taken > 64u) {   // the last word taken here lies in the second window
           const uint32_t w2 = __shfl(win2, (int)(rel & 63u), 64);
           word = rel >= 64u ? w2 : word;
         }
         if (need) {
-          buf |= (uint64_t)__builtin_bitreverse32(word) << (32u - avail);
+          buf |= (uint64_t)word << avail;
           avail += 32;
           e = lookup(s, buf);
           L = e & 15u;
         }
-        base += (uint32_t)__popcll(mask);
+        base += taken;
         if (base - wbase >= 64u) {
           wbase += 64;
           win = win2;
           const uint32_t nx = wbase + 64u + lane;
-          win2 = nx < n_words ? wg[nx] : 0u;
+          win2 = *(nx < n_words ? wg + nx : hdr);
         }
       }
       bad |= L == 15u;   // no code in the window: a corrupt stream
-      buf <<= L;
+      buf >>= L;
       avail -= L;
-      dst[64u * (i0 + q) + lane] = (uint16_t)(smv[q] | (e & 0x7F80u));
+      // sign and fraction from the plane, the exponent (bits 7..14) from the entry, whose bits 4..6 and 15 are zero
+      uint32_t o;   // one bitfield insert (the compiler splits the plain form into an AND and an AND-OR)
+      asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(o) : "s"(0x807Fu), "v"(smv[q]), "v"(e));
+      dst[64u * (i0 + q) + lane] = (uint16_t)o;
     }
   }
   return bad || base != n_words || buf != 0;
@@ -823,9 +842,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(8))) void hc
         for (uint32_t L = 1; L <= kPrimBits; ++L) T += cnt[L] << (kLmax - L);
         const uint32_t sec = ((kraft + 3u) & ~3u) - T;   // <= 2 * 256 + 3 (codes of 11, 12 bits)
         fill_table(s, s.lut, 1u << kPrimBits, (1u << kPrimBits) / 64u, 0u, 1u << (kLmax - kPrimBits), T, n_sym,
-                   kraft);
+                   kraft, kPrimBits);
         fill_table(s, s.lut2, sec < kSecMax ? sec : kSecMax, (kSecMax + 63u) / 64u, T, 1u, 0xFFFFFFFFu, n_sym,
-                   kraft);
+                   kraft, kLmax - kPrimBits);
       }
       __syncthreads();
       bad = decode_steps(s, rec, n_words, dst);
