@@ -227,12 +227,14 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void
   const uint32_t t = threadIdx.x, stride = gridDim.x;
   uint32_t k = blockIdx.x;
   uint4 v[kPer], nv[kPer];
-  if (k < full) load_block(in + (uint64_t)k * kB, kB, v);
+  // Blocks are visited from the last one down, so that the encoder, which
+  // starts from block 0, finds the blocks read last still in the cache.
+  if (k < full) load_block(in + (uint64_t)(full - 1u - k) * kB, kB, v);
   for (; k < full; k += stride) {
     const uint32_t kn = k + stride < full ? k + stride : k;
-    load_block(in + (uint64_t)kn * kB, kB, nv);
+    load_block(in + (uint64_t)(full - 1u - kn) * kB, kB, nv);
     const uint32_t cnt = block_histogram<false>(v, s);   // cnt <= 16384
-    if (t < 256u) sc.bhist[256ull * k + t] = (uint16_t)cnt;
+    if (t < 256u) sc.bhist[256ull * (full - 1u - k) + t] = (uint16_t)cnt;
     __syncthreads();   // the counts are read before the next block clears them
 #pragma unroll
     for (int i = 0; i < kPer; ++i) v[i] = nv[i];
@@ -248,7 +250,15 @@ __global__ __launch_bounds__(256) void scope_sum_kernel(ScopeWs sc, uint32_t gro
   const uint64_t gend = g0 + group < full ? g0 + group : full;
   const uint64_t k1 = k0 + chunk < gend ? k0 + chunk : gend;
   uint32_t sum = 0;
-  for (uint64_t k = k0; k < k1; ++k) sum += sc.bhist[256ull * k + t];
+  uint64_t k = k0;
+  for (; k + 8u <= k1; k += 8u) {   // eight rows in flight: the loop is latency-bound
+    uint32_t x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = sc.bhist[256ull * (k + u) + t];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += x[u];
+  }
+  for (; k < k1; ++k) sum += sc.bhist[256ull * k + t];
   if (sum) atomicAdd(&sc.ghist[256ull * g + t], sum);
 }
 
@@ -333,10 +343,29 @@ __global__ __launch_bounds__(256) void scope_pick_kernel(ScopeWs sc, uint32_t gr
   const uint64_t g0 = (uint64_t)g * group;
   const uint64_t gend = g0 + group < full ? g0 + group : full;
   unsigned long long sum[8] = {};
-  for (uint64_t k = g0 + t; k < gend; k += 256) {
+  // a block's escapes as two 16-byte vectors (b = 0..3, 4..7; entry 0 unused)
+  const uint4* e4 = reinterpret_cast<const uint4*>(sc.esc);
+  auto add = [&](const uint4& lo, const uint4& hi) {
+    sum[1] += coded_bytes(1, lo.y);
+    sum[2] += coded_bytes(2, lo.z);
+    sum[3] += coded_bytes(3, lo.w);
+    sum[4] += coded_bytes(4, hi.x);
+    sum[5] += coded_bytes(5, hi.y);
+    sum[6] += coded_bytes(6, hi.z);
+    sum[7] += coded_bytes(7, hi.w);
+  };
+  uint64_t k = g0 + t;
+  for (; k + 768u < gend; k += 1024u) {   // four blocks per thread in flight: the loop is latency-bound
+    uint4 lo[4], hi[4];
 #pragma unroll
-    for (uint32_t b = 1; b <= 7; ++b) sum[b] += coded_bytes(b, sc.esc[8ull * k + b]);
+    for (int u = 0; u < 4; ++u) {
+      lo[u] = e4[2 * (k + 256u * u)];
+      hi[u] = e4[2 * (k + 256u * u) + 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) add(lo[u], hi[u]);
   }
+  for (; k < gend; k += 256u) add(e4[2 * k], e4[2 * k + 1]);
 #pragma unroll
   for (uint32_t b = 1; b <= 7; ++b) {
 #pragma unroll
