@@ -111,12 +111,10 @@ def median(xs):
 
 
 def hbm_ceiling(operand_bytes: int) -> dict:
-    """Runs the hbm_ceiling tool built next to libhc (streaming add, copy and
+    """Runs the hbm_ceiling tool built in measure/ (streaming add, copy and
     read kernels at the given operand size) and returns its JSON object, or
     {"error": ...}."""
-    from collective_communication_amd import binding as hc
-
-    tool = os.path.join(os.path.dirname(hc.LIB_PATH), "hbm_ceiling")
+    tool = os.path.join(ROOT, "measure", "hbm_ceiling")
     try:
         r = subprocess.run([tool, str(operand_bytes >> 20)], capture_output=True, text=True, timeout=120)
         if r.returncode != 0:
@@ -925,7 +923,7 @@ def bench_contention(args):
     # wheel serves hipMemcpyDeviceToDeviceNoCU with blit kernels on the CUs.
     del send, recv, ws
     torch.cuda.empty_cache()
-    tool = os.path.join(os.path.dirname(hc.LIB_PATH), "dma_contention")
+    tool = os.path.join(ROOT, "measure", "dma_contention")
     try:
         r = subprocess.run([tool, "bench"], capture_output=True, text=True, timeout=600)
         ag = json.loads(r.stdout.strip().splitlines()[-1]) if r.returncode == 0 else {"error": r.stderr[-2000:]}

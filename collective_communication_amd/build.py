@@ -4,9 +4,9 @@ Flags: -O3, -ffp-contract=off (no fused multiply-add contraction: every hop is
 one IEEE add), no fast-math, no flush-to-zero, packed-fp32 instructions
 disabled on the device (-Xclang -target-feature -Xclang -packed-fp32-ops).
 Objects go to _build/ at the repository root; the library lands next to this
-file so that it travels with the tree.  dma_contention (a measurement program
-of its own, linked against libhc and rocBLAS from the system ROCm) is built
-next to it.
+file so that it travels with the tree.  The two measurement programs of
+measure/ at the repository root are built there: dma_contention (linked
+against libhc and rocBLAS from the system ROCm) and hbm_ceiling.
 """
 from __future__ import annotations
 
@@ -21,8 +21,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhc.so")
-DMA_TOOL = os.path.join(PKG, "dma_contention")
-CEILING_TOOL = os.path.join(PKG, "hbm_ceiling")
+MEASURE = os.path.join(ROOT, "measure")
+DMA_TOOL = os.path.join(MEASURE, "dma_contention")
+CEILING_TOOL = os.path.join(MEASURE, "hbm_ceiling")
 ARCH = os.environ.get("HC_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -56,14 +57,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
     tmp = DMA_TOOL + ".tmp"
-    cmd = [HIPCC, *COMMON, *DEVICE, "-x", "hip", os.path.join(PKG, "dma_contention.hip"), "-o", tmp,
-           "-L", PKG, "-lhc", "-Wl,-rpath,$ORIGIN", "-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
+    cmd = [HIPCC, *COMMON, *DEVICE, "-x", "hip", os.path.join(MEASURE, "dma_contention.hip"), "-o", tmp,
+           "-L", PKG, "-lhc", "-Wl,-rpath,$ORIGIN/../collective_communication_amd", "-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"dma_contention build failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, DMA_TOOL)
     tmp = CEILING_TOOL + ".tmp"
-    cmd = [HIPCC, *COMMON, *DEVICE, "-x", "hip", os.path.join(PKG, "hbm_ceiling.hip"), "-o", tmp]
+    cmd = [HIPCC, *COMMON, *DEVICE, "-x", "hip", os.path.join(MEASURE, "hbm_ceiling.hip"), "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hbm_ceiling build failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

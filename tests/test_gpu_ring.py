@@ -19,6 +19,8 @@ from collective_communication_amd import binding as hc
 from collective_communication_amd import inputs
 from hc_util import bits, copy_engine_or_unsupported, first_mismatch, fold_chunked, to_dev, to_host
 
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
 pytestmark = pytest.mark.gpu
 
 
@@ -212,7 +214,7 @@ def test_all_gather_copy_engine_under_system_runtime(tmp_path):
     run checks the tool's own copy-kernel comparison.  (Inside a torch process
     the HIP runtime bundled with the wheel would serve the same calls with
     blit kernels, so there the library refuses copy_engine=1.)"""
-    tool = os.path.join(os.path.dirname(hc.LIB_PATH), "dma_contention")
+    tool = os.path.join(ROOT, "measure", "dma_contention")
     assert os.path.exists(tool), "dma_contention is not built"
     R, L = 8, 65536 + 3
     xs = [inputs.normal_bf16("test", 8800 + r, L, 1e-3) for r in range(R)]
@@ -253,7 +255,7 @@ def test_copy_engine_refused_where_it_would_use_compute_units():
 def test_hbm_ceiling_tool():
     """The streaming-ceiling tool (the bar the reduce hop is held against next
     to the published peak) runs and reports every mix with its bytes."""
-    tool = os.path.join(os.path.dirname(hc.LIB_PATH), "hbm_ceiling")
+    tool = os.path.join(ROOT, "measure", "hbm_ceiling")
     assert os.path.exists(tool), "hbm_ceiling is not built"
     r = subprocess.run([tool, "64", "3"], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
