@@ -215,30 +215,22 @@ __global__ __launch_bounds__(256) void staged_copy_kernel(const uint8_t* __restr
   }
 }
 
-// Table scope, step 1: each full block's exponent histogram.  A workgroup
-// walks blocks blockIdx.x, + gridDim.x, ... and loads the next block while it
-// counts the current one.  The next block's loads are issued on every
-// iteration (the last one loads its own block again): behind a condition,
-// the wait before the count had to allow for the path without them, and
-// then also waited for them, so no load overlapped a count.
+// Table scope, step 1: each full block's exponent histogram, one block per
+// workgroup.  Workgroup i counts block full - 1 - i: the blocks are read from
+// the last one down, so that the encoder, which starts from block 0, finds
+// the blocks read last still in the cache.  (Workgroups that each walked 16
+// blocks, loading the next while counting the current one, ran 108 us on
+// 2^28 elements; one block per workgroup, with the dispatcher overlapping
+// workgroups, 103 us.)
 __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kCW))) void scope_hist_kernel(
     const uint16_t* __restrict__ in, ScopeWs sc, uint32_t full) {
   __shared__ Smem s;
-  const uint32_t t = threadIdx.x, stride = gridDim.x;
-  uint32_t k = blockIdx.x;
-  uint4 v[kPer], nv[kPer];
-  // Blocks are visited from the last one down, so that the encoder, which
-  // starts from block 0, finds the blocks read last still in the cache.
-  if (k < full) load_block(in + (uint64_t)(full - 1u - k) * kB, kB, v);
-  for (; k < full; k += stride) {
-    const uint32_t kn = k + stride < full ? k + stride : k;
-    load_block(in + (uint64_t)(full - 1u - kn) * kB, kB, nv);
-    const uint32_t cnt = block_histogram<false>(v, s);   // cnt <= 16384
-    if (t < 256u) sc.bhist[256ull * (full - 1u - k) + t] = (uint16_t)cnt;
-    __syncthreads();   // the counts are read before the next block clears them
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) v[i] = nv[i];
-  }
+  const uint32_t t = threadIdx.x;
+  const uint32_t k = full - 1u - blockIdx.x;   // the grid covers the full blocks
+  uint4 v[kPer];
+  load_block(in + (uint64_t)k * kB, kB, v);
+  const uint32_t cnt = block_histogram<false>(v, s);   // cnt <= 16384
+  if (t < 256u) sc.bhist[256ull * k + t] = (uint16_t)cnt;
 }
 
 // Step 2: each group's histogram, `chunk` blocks per workgroup (grid:
@@ -625,12 +617,10 @@ hipError_t launch_compress_scoped(const uint16_t* in, size_t n, void* out, uint6
   if (e != hipSuccess) return e;
   if (full) {
     const uint32_t F = (uint32_t)full, Gu = (uint32_t)G;
-    // one resident round of workgroups (4 per CU of 256), each walking blocks
-    const uint32_t hist_grid = F < 1024u ? F : 1024u;
     size_t chunk = kSumChunk;
     while (ceil_div(G, chunk) > 32768) chunk *= 2;   // keeps grid.y small
     const uint32_t chunks = (uint32_t)ceil_div(G, chunk);
-    hipLaunchKernelGGL(scope_hist_kernel, dim3(hist_grid), dim3(kCT), 0, stream, in, sc, F);
+    hipLaunchKernelGGL(scope_hist_kernel, dim3(F), dim3(kCT), 0, stream, in, sc, F);
     hipLaunchKernelGGL(scope_sum_kernel, dim3((uint32_t)groups, chunks), dim3(256), 0, stream, sc, Gu, F,
                        (uint32_t)chunk);
     hipLaunchKernelGGL(scope_rank_kernel, dim3((uint32_t)groups), dim3(256), 0, stream, sc);
